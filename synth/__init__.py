@@ -1,0 +1,136 @@
+"""Seeded synthetic teacher/student attention inputs.
+
+This module only draws random numbers and casts them; it holds none of the
+attention-KL arithmetic.  Both the HIP path (tests, bench) and the oracle read
+the tensors it produces.
+
+Workloads follow the shapes the StreamKL pages evaluate: context lengths
+4K-512K, causal and non-causal masking, and a short-query / long-key case for
+the split-K variant (StreamKL: arXiv 2606.20005, gist.science "Resultados
+Experimentales" and "Optimizaciones de Kernel de GPU").  The pages publish no
+dataset; Gaussian queries/keys stand in for real teacher/student projections.
+
+Seeding is per (config, batch, head, tensor) so any single head can be drawn on
+its own: seed = 1_000_003*cfg_id + 1009*(b*H + h) + tensor_id, tensor_id
+Q1=0, K1=1, Q2-noise (or Q2)=2, K2-noise (or K2)=3.  Normals are drawn in fp32
+and the student is formed in fp32; bf16 workloads then cast with
+round-to-nearest-even, and everything downstream reads the cast values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Iterable, Optional
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "get", "make_head", "make_inputs", "upstream_grad"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    cfg_id: int
+    name: str
+    B: int
+    H: int
+    NQ: int
+    NK: int
+    D: int
+    dtype: str            # "fp32" or "bf16"
+    causal: bool
+    teacher_std: float = 1.0
+    student: str = "noise"    # "noise": Q2=Q1+s*N, K2=K1+s*N ; "independent": Q2,K2 ~ N(0,1)
+    noise: float = 0.1
+    splits: int = 1           # split-K chunk count used for this workload (1 = unsplit)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    def visible_pairs(self) -> int:
+        """Number of (query, key) pairs the mask keeps, over all batch*heads."""
+        if not self.causal:
+            per_head = self.NQ * self.NK
+        else:
+            # bottom-right alignment: row i sees keys 0..i+(NK-NQ), i.e. i+NK-NQ+1 keys
+            off = self.NK - self.NQ
+            per_head = self.NQ * (off + 1) + self.NQ * (self.NQ - 1) // 2
+        return self.B * self.H * per_head
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in [
+        Workload(0, "tiny_fp32", 1, 2, 256, 256, 64, "fp32", False, noise=0.3),
+        Workload(1, "causal_4k", 2, 32, 4096, 4096, 128, "bf16", True, noise=0.1),
+        Workload(2, "noncausal_16k", 1, 32, 16384, 16384, 128, "bf16", False,
+                 teacher_std=1.5, student="independent"),
+        Workload(3, "causal_64k", 1, 32, 65536, 65536, 128, "bf16", True, noise=0.1),
+        Workload(4, "splitk_512k", 1, 32, 1024, 524288, 128, "bf16", False, noise=0.2, splits=64),
+        Workload(5, "splitk_bwd_128k", 1, 32, 1024, 131072, 128, "bf16", False, noise=0.2),
+    ]
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def _seed(w: Workload, b: int, h: int, tensor_id: int) -> int:
+    return 1_000_003 * w.cfg_id + 1009 * (b * w.H + h) + tensor_id
+
+
+def _normal(shape, seed: int, device: str) -> torch.Tensor:
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+
+
+def make_head(w: Workload, b: int, h: int, device: str = "cpu"):
+    """Return (q1, k1, q2, k2) for one (batch, head): [NQ,D] and [NK,D] in w's dtype."""
+    q1 = _normal((w.NQ, w.D), _seed(w, b, h, 0), device) * w.teacher_std
+    k1 = _normal((w.NK, w.D), _seed(w, b, h, 1), device) * w.teacher_std
+    if w.student == "noise":
+        q2 = q1 + w.noise * _normal((w.NQ, w.D), _seed(w, b, h, 2), device)
+        k2 = k1 + w.noise * _normal((w.NK, w.D), _seed(w, b, h, 3), device)
+    elif w.student == "independent":
+        q2 = _normal((w.NQ, w.D), _seed(w, b, h, 2), device)
+        k2 = _normal((w.NK, w.D), _seed(w, b, h, 3), device)
+    else:
+        raise ValueError(w.student)
+    dt = w.torch_dtype
+    return q1.to(dt), k1.to(dt), q2.to(dt), k2.to(dt)
+
+
+def make_inputs(w: Workload, device: str = "cpu", heads: Optional[Iterable] = None):
+    """Full [B,H,N,D] tensors (contiguous) drawn head by head on `device`.
+
+    `heads`, if given, is an iterable of (b, h) pairs to fill; other heads stay
+    zero (used to keep host-side work bounded)."""
+    dt = w.torch_dtype
+    q1 = torch.empty((w.B, w.H, w.NQ, w.D), dtype=dt, device=device)
+    k1 = torch.empty((w.B, w.H, w.NK, w.D), dtype=dt, device=device)
+    q2 = torch.empty_like(q1)
+    k2 = torch.empty_like(k1)
+    todo = list(heads) if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
+    if heads is not None:
+        for t in (q1, k1, q2, k2):
+            t.zero_()
+    for b, h in todo:
+        a, bb, c, d = make_head(w, b, h, device)
+        q1[b, h].copy_(a)
+        k1[b, h].copy_(bb)
+        q2[b, h].copy_(c)
+        k2[b, h].copy_(d)
+    return q1, k1, q2, k2
+
+
+def upstream_grad(w: Workload, device: str = "cpu") -> torch.Tensor:
+    """Per-row upstream gradient g of a mean-reduced loss: 1/(B*H*NQ) everywhere."""
+    return torch.full((w.B, w.H, w.NQ), 1.0 / (w.B * w.H * w.NQ), dtype=torch.float32, device=device)
