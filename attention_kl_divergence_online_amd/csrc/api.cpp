@@ -1,0 +1,289 @@
+// C ABI of the attention-KL library: argument validation, grid set-up and
+// launches.  Every check runs on the host before anything is enqueued, so a
+// rejected call writes nothing.
+#include "../../include/streamkl.h"
+
+#include <stdint.h>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Shape / dtype checks common to every entry point.
+streamkl_status check_problem(const streamkl_problem *p) {
+  if (!p) return STREAMKL_ERR_NULL;
+  if (p->dtype != STREAMKL_BF16 && p->dtype != STREAMKL_FP32) return STREAMKL_ERR_DTYPE;
+  if (p->B < 0 || p->H < 0 || p->NQ < 0 || p->NK < 0) return STREAMKL_ERR_SHAPE;
+  if (p->D != 64 && p->D != 128) return STREAMKL_ERR_SHAPE;
+  const int64_t rows = p->B * p->H * p->NQ;
+  // A row with no visible key has no distribution to compare.
+  if (p->B > 0 && p->H > 0 && p->NQ > 0 && p->NK == 0) return STREAMKL_ERR_SHAPE;
+  if (p->causal && p->NQ > p->NK) return STREAMKL_ERR_SHAPE;
+  // In-head offsets are 32-bit; whole tensors use 64-bit bases.
+  const int64_t lim = (int64_t)1 << 31;
+  if (p->NQ * p->D >= lim || p->NK * p->D >= lim) return STREAMKL_ERR_SHAPE;
+  if (p->B * p->H >= lim || rows < 0) return STREAMKL_ERR_SHAPE;
+  if (!(p->scale == p->scale)) return STREAMKL_ERR_SHAPE;  // NaN scale
+  return STREAMKL_OK;
+}
+
+bool empty_rows(const streamkl_problem *p) { return p->B == 0 || p->H == 0 || p->NQ == 0; }
+
+streamkl_status check_inputs(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                             const void *k2) {
+  if (!q1 || !k1 || !q2 || !k2) return STREAMKL_ERR_NULL;
+  if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2)) return STREAMKL_ERR_ALIGN;
+  (void)p;
+  return STREAMKL_OK;
+}
+
+streamkl_status check_rowvecs(float *a, float *b, float *c) {
+  if (!a || !b || !c) return STREAMKL_ERR_NULL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return STREAMKL_ERR_ALIGN;
+  return STREAMKL_OK;
+}
+
+int fwd_splits_max(const streamkl_problem *p) {
+  return (int)((p->NK + skl::kFwdBK - 1) / skl::kFwdBK);
+}
+
+skl::FwdParams make_fwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                        const void *k2, float *kl, float *lse1, float *lse2) {
+  skl::FwdParams f{};
+  f.q1 = q1;
+  f.k1 = k1;
+  f.q2 = q2;
+  f.k2 = k2;
+  f.kl = kl;
+  f.lse1 = lse1;
+  f.lse2 = lse2;
+  f.ws = nullptr;
+  f.BH = p->B * p->H;
+  f.NQ = p->NQ;
+  f.NK = p->NK;
+  f.scale = p->scale;
+  f.causal = p->causal ? 1 : 0;
+  const int bq = skl::fwd_block_queries(p->dtype, (int)p->D);
+  f.nqt = (int)((p->NQ + bq - 1) / bq);
+  f.splits = 1;
+  f.chunk = (int)p->NK;
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *streamkl_status_string(int status) {
+  switch (status) {
+    case STREAMKL_OK: return "ok";
+    case STREAMKL_ERR_NULL: return "required pointer is NULL";
+    case STREAMKL_ERR_SHAPE: return "invalid problem shape";
+    case STREAMKL_ERR_DTYPE: return "unsupported dtype";
+    case STREAMKL_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case STREAMKL_ERR_WORKSPACE: return "workspace missing or too small";
+    case STREAMKL_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int streamkl_version(void) { return kVersion; }
+
+streamkl_status streamkl_fwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                             const void *k2, float *kl, float *lse1, float *lse2, void *stream) {
+  streamkl_status st = check_problem(p);
+  if (st != STREAMKL_OK) return st;
+  if (empty_rows(p)) return STREAMKL_OK;
+  if ((st = check_inputs(p, q1, k1, q2, k2)) != STREAMKL_OK) return st;
+  if ((st = check_rowvecs(kl, lse1, lse2)) != STREAMKL_OK) return st;
+  skl::FwdParams f = make_fwd(p, q1, k1, q2, k2, kl, lse1, lse2);
+  if (skl::launch_fwd(p->dtype, (int)p->D, f, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return STREAMKL_ERR_HIP;
+  return STREAMKL_OK;
+}
+
+size_t streamkl_fwd_splitk_workspace_size(const streamkl_problem *p, int num_splits) {
+  if (check_problem(p) != STREAMKL_OK) return 0;
+  if (num_splits < 1 || (p->NK > 0 && num_splits > fwd_splits_max(p))) return 0;
+  return (size_t)5 * (size_t)num_splits * (size_t)(p->B * p->H * p->NQ) * sizeof(float);
+}
+
+streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                                    const void *k2, float *kl, float *lse1, float *lse2, int num_splits,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  streamkl_status st = check_problem(p);
+  if (st != STREAMKL_OK) return st;
+  if (num_splits < 1) return STREAMKL_ERR_SHAPE;
+  if (empty_rows(p)) return STREAMKL_OK;
+  if (num_splits > fwd_splits_max(p)) return STREAMKL_ERR_SHAPE;
+  if ((st = check_inputs(p, q1, k1, q2, k2)) != STREAMKL_OK) return st;
+  if ((st = check_rowvecs(kl, lse1, lse2)) != STREAMKL_OK) return st;
+  skl::FwdParams f = make_fwd(p, q1, k1, q2, k2, kl, lse1, lse2);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (num_splits == 1) {
+    return skl::launch_fwd(p->dtype, (int)p->D, f, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+  }
+  const size_t need = streamkl_fwd_splitk_workspace_size(p, num_splits);
+  if (!workspace || workspace_bytes < need) return STREAMKL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
+  // Whole 64-key tiles per chunk; trailing chunks past NK are empty.
+  const int64_t tiles = (p->NK + skl::kFwdBK - 1) / skl::kFwdBK;
+  const int64_t tiles_per = (tiles + num_splits - 1) / num_splits;
+  f.splits = num_splits;
+  f.chunk = (int)(tiles_per * skl::kFwdBK);
+  f.ws = reinterpret_cast<float *>(workspace);
+  if (skl::launch_fwd(p->dtype, (int)p->D, f, s) != hipSuccess) return STREAMKL_ERR_HIP;
+  if (skl::launch_splitk_merge(f, s) != hipSuccess) return STREAMKL_ERR_HIP;
+  return STREAMKL_OK;
+}
+
+size_t streamkl_bwd_workspace_size(const streamkl_problem *p) {
+  if (check_problem(p) != STREAMKL_OK) return 0;
+  const size_t bh = (size_t)(p->B * p->H);
+  const size_t bytes = bh * sizeof(float);
+  return bytes < 16 ? 16 : (bytes + 15) & ~(size_t)15;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the backward entry points.  `outs` lists the gradient
+// pointers of the call (pairs already checked); `need_ws` the workspace rule.
+streamkl_status check_bwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                          const void *k2, const float *kl, const float *lse1, const float *lse2,
+                          const float *g, float *const *outs, int nouts, const void *workspace,
+                          size_t workspace_bytes) {
+  streamkl_status st = check_inputs(p, q1, k1, q2, k2);
+  if (st != STREAMKL_OK) return st;
+  for (int i = 0; i < nouts; ++i)
+    if (outs[i] && !aligned16(outs[i])) return STREAMKL_ERR_ALIGN;
+  if (p->NQ == 0) return STREAMKL_OK;
+  if (!kl || !lse1 || !lse2 || !g) return STREAMKL_ERR_NULL;
+  if (!aligned16(kl) || !aligned16(lse1) || !aligned16(lse2) || !aligned16(g)) return STREAMKL_ERR_ALIGN;
+  if (!workspace || workspace_bytes < streamkl_bwd_workspace_size(p)) return STREAMKL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
+  return STREAMKL_OK;
+}
+
+skl::BwdParams make_bwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2, const void *k2,
+                        const float *kl, const float *lse1, const float *lse2, const float *g, float *dq1,
+                        float *dk1, float *dq2, float *dk2, const void *workspace) {
+  skl::BwdParams b{};
+  b.q1 = q1;
+  b.k1 = k1;
+  b.q2 = q2;
+  b.k2 = k2;
+  b.kl = kl;
+  b.lse1 = lse1;
+  b.lse2 = lse2;
+  b.g = g;
+  b.sigma = reinterpret_cast<const float *>(workspace);
+  b.dq1 = dq1;
+  b.dk1 = dk1;
+  b.dq2 = dq2;
+  b.dk2 = dk2;
+  b.BH = p->B * p->H;
+  b.NQ = p->NQ;
+  b.NK = p->NK;
+  b.scale = p->scale;
+  b.causal = p->causal ? 1 : 0;
+  return b;
+}
+
+// dK pass; with no query rows every key gradient is zero.
+streamkl_status run_dk(const streamkl_problem *p, skl::BwdParams b, hipStream_t s) {
+  if (p->NQ == 0) {
+    const int64_t n = b.BH * p->NK * p->D;
+    if (b.dk1 && skl::launch_zero(b.dk1, n, s) != hipSuccess) return STREAMKL_ERR_HIP;
+    if (b.dk2 && skl::launch_zero(b.dk2, n, s) != hipSuccess) return STREAMKL_ERR_HIP;
+    return STREAMKL_OK;
+  }
+  b.want1 = b.dk1 != nullptr;
+  b.want2 = b.dk2 != nullptr;
+  return skl::launch_bwd_dk(p->dtype, (int)p->D, b, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+}
+
+streamkl_status run_dq(const streamkl_problem *p, skl::BwdParams b, hipStream_t s) {
+  if (p->NQ == 0) return STREAMKL_OK;
+  b.want1 = b.dq1 != nullptr;
+  b.want2 = b.dq2 != nullptr;
+  return skl::launch_bwd_dq(p->dtype, (int)p->D, b, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+}
+
+streamkl_status run_prepare(const streamkl_problem *p, const float *g, void *workspace, hipStream_t s) {
+  if (p->NQ == 0) return STREAMKL_OK;
+  return skl::launch_grad_scale(p->dtype, g, p->B * p->H, p->NQ, reinterpret_cast<float *>(workspace), s) ==
+                 hipSuccess
+             ? STREAMKL_OK
+             : STREAMKL_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                             const void *k2, const float *kl, const float *lse1, const float *lse2,
+                             const float *g, float *dq1, float *dk1, float *dq2, float *dk2, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  streamkl_status st = check_problem(p);
+  if (st != STREAMKL_OK) return st;
+  if ((dq1 == nullptr) != (dk1 == nullptr) || (dq2 == nullptr) != (dk2 == nullptr)) return STREAMKL_ERR_NULL;
+  if (p->B * p->H == 0 || (p->NQ == 0 && p->NK == 0)) return STREAMKL_OK;
+  if (!dq1 && !dq2) return STREAMKL_OK;
+  float *outs[4] = {dq1, dk1, dq2, dk2};
+  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 4, workspace, workspace_bytes);
+  if (st != STREAMKL_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, dk1, dq2, dk2, workspace);
+  if ((st = run_prepare(p, g, workspace, s)) != STREAMKL_OK) return st;
+  if ((st = run_dk(p, b, s)) != STREAMKL_OK) return st;
+  return run_dq(p, b, s);
+}
+
+streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const float *g, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  streamkl_status st = check_problem(p);
+  if (st != STREAMKL_OK) return st;
+  if (p->B * p->H == 0 || p->NQ == 0) return STREAMKL_OK;
+  if (!g) return STREAMKL_ERR_NULL;
+  if (!aligned16(g)) return STREAMKL_ERR_ALIGN;
+  if (!workspace || workspace_bytes < streamkl_bwd_workspace_size(p)) return STREAMKL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
+  return run_prepare(p, g, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+streamkl_status streamkl_bwd_dk(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                                const void *k2, const float *kl, const float *lse1, const float *lse2,
+                                const float *g, float *dk1, float *dk2, const void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  streamkl_status st = check_problem(p);
+  if (st != STREAMKL_OK) return st;
+  if (p->B * p->H == 0 || p->NK == 0 || (!dk1 && !dk2)) return STREAMKL_OK;
+  float *outs[2] = {dk1, dk2};
+  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 2, workspace, workspace_bytes);
+  if (st != STREAMKL_OK) return st;
+  skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, nullptr, dk1, nullptr, dk2, workspace);
+  return run_dk(p, b, reinterpret_cast<hipStream_t>(stream));
+}
+
+streamkl_status streamkl_bwd_dq(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                                const void *k2, const float *kl, const float *lse1, const float *lse2,
+                                const float *g, float *dq1, float *dq2, const void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  streamkl_status st = check_problem(p);
+  if (st != STREAMKL_OK) return st;
+  if (p->B * p->H == 0 || p->NQ == 0 || (!dq1 && !dq2)) return STREAMKL_OK;
+  float *outs[2] = {dq1, dq2};
+  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 2, workspace, workspace_bytes);
+  if (st != STREAMKL_OK) return st;
+  skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, nullptr, dq2, nullptr, workspace);
+  return run_dq(p, b, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

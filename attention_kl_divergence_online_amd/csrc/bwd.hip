@@ -1,0 +1,437 @@
+// Backward of the fused attention KL divergence by tile-wise recomputation.
+//
+// StreamKL (arXiv 2606.20005), gist.science "Estrategia de Recomputacion":
+// only KL and the two LSE vectors are kept from the forward; attention
+// probabilities are rebuilt tile by tile as P_t = exp(s_t - LSE_t).  For
+// L = sum_i g_i KL_i the logit gradients are
+//     dS2 = g (P2 - P1)                      (student, "Configuracion 1")
+//     dS1 = g P1 (log P1 - log P2 - KL)      (teacher, "Configuracion 2")
+// with log P1 - log P2 formed from logits and the saved LSEs, never from logs
+// of probabilities ("Estabilidad Numerica").  Through s = scale * q.k,
+// dQ_t = scale dS_t K_t and dK_t = scale dS_t^T Q_t.
+//
+// The pages fuse both products into one kernel with dQ atomics and fall back
+// to separate kernels under contention.  Here the separate, atomic-free form
+// is the design: one pass keeps a tile of keys resident and streams queries
+// (dK), the other keeps queries resident and streams keys (dQ).  Both are the
+// same kernel template: a wave owns 32 resident rows, whose fragments stay in
+// registers, and 64-row tiles of the streamed operand pass through LDS twice
+// over -- row-major (bf16/fp32) for the logits and transposed (fp16/fp32) for
+// the gradient product.
+//
+// Logits come out as (streamed x resident) accumulator blocks, so a lane holds
+// one resident row and 16 streamed rows; that accumulator is, element for
+// element, the B operand of the gradient product dR^T += X^T dS, which needs
+// no shuffle.  bf16 inputs use fp16 for the gradient product: dS in bf16
+// loses too much (8-bit significand) for the 2e-3 relative bound, fp16 keeps
+// 11 bits.  dS is scaled by a per-(b,h) power of two sigma with
+// max|g| * sigma in [2^7, 2^8) so it sits in fp16's normal range; the factor
+// is divided out exactly at the end.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace skl {
+
+template <typename T> struct GradOp { using type = f16; };
+template <> struct GradOp<float> { using type = float; };
+
+template <typename T, int D, bool KEYS_RES>
+struct BwdTraits {
+  using G = typename GradOp<T>::type;
+  static constexpr int WAVES = 4;
+  static constexpr int BR = kBwdBR;                              // resident rows per workgroup
+  static constexpr int BX = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // streamed rows per stage
+  static constexpr int XB = BX / 32;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int ROW_BYTES = D * (int)sizeof(T);
+  static constexpr int XROW = ROW_BYTES + 16;
+  static constexpr int XT_STRIDE = BX * (int)sizeof(G) + (sizeof(G) == 2 ? 8 : 16);
+  static constexpr int CPR = ROW_BYTES / 16;
+  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int ITEMS = (BX / 4) * CPR;     // staging items: 4 rows x 1 chunk
+  static constexpr int IPT = (ITEMS + 255) / 256;
+  static constexpr int XROW_BYTES = BX * XROW;
+  static constexpr int XT_BYTES = D * XT_STRIDE;
+  static constexpr int STAT_BYTES = KEYS_RES ? 4 * BX * 4 : 0;
+  static constexpr int OFF_XT = 2 * XROW_BYTES;
+  static constexpr int OFF_STAT = 2 * XROW_BYTES + 2 * XT_BYTES;
+  static constexpr int STAGE_BYTES = OFF_STAT + STAT_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static_assert(BR == WAVES * 32, "resident tile");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(XROW_BYTES % 16 == 0 && XT_BYTES % 16 == 0, "LDS alignment");
+};
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float clamp_f16(float x) { return __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f); }
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const f16x2 v = {(f16)a, (f16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <typename T, int D, bool KEYS_RES>
+__global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
+  using Tr = BwdTraits<T, D, KEYS_RES>;
+  using G = typename Tr::G;
+  using CT = chunk_t<T>;
+  using CG = chunk_t<G>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c32 = lane & 31;
+
+  const int NQ = (int)p.NQ, NK = (int)p.NK;
+  const int off = NK - NQ;
+  const int NR = KEYS_RES ? NK : NQ;  // resident row count
+  const int NX = KEYS_RES ? NQ : NK;  // streamed row count
+  const int nrt = (NR + Tr::BR - 1) / Tr::BR;
+
+  // Heaviest resident tiles first: under the causal mask low keys see the
+  // most queries, high queries see the most keys.
+  const uint32_t L = blockIdx.x;
+  const int64_t bh = L / (uint32_t)nrt;
+  const int rt = KEYS_RES ? (int)(L % (uint32_t)nrt) : nrt - 1 - (int)(L % (uint32_t)nrt);
+
+  const T *R1 = reinterpret_cast<const T *>(KEYS_RES ? p.k1 : p.q1) + bh * (int64_t)NR * D;
+  const T *R2 = reinterpret_cast<const T *>(KEYS_RES ? p.k2 : p.q2) + bh * (int64_t)NR * D;
+  const char *X1 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(KEYS_RES ? p.q1 : p.k1) +
+                                                  bh * (int64_t)NX * D);
+  const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(KEYS_RES ? p.q2 : p.k2) +
+                                                  bh * (int64_t)NX * D);
+  const float *KLr = p.kl + bh * (int64_t)NQ;
+  const float *LS1 = p.lse1 + bh * (int64_t)NQ;
+  const float *LS2 = p.lse2 + bh * (int64_t)NQ;
+  const float *Gr = p.g + bh * (int64_t)NQ;
+  const float sigma = p.sigma[bh];
+
+  const int r0 = rt * Tr::BR;
+  const int rlast_wg = min(r0 + Tr::BR, NR) - 1;
+  const int ra = r0 + wave * 32;  // this wave's resident rows [ra, ra + 32)
+  const int my_r = ra + c32;      // this lane's resident row
+  const bool r_ok = my_r < NR;
+
+  // Streamed range.
+  int x_lo = 0, x_hi = NX;
+  if (p.causal) {
+    if (KEYS_RES) {
+      x_lo = max(0, r0 - off);
+      x_lo -= x_lo % Tr::BX;
+    } else {
+      x_hi = min(NK, rlast_wg + off + 1);
+    }
+  }
+  const int ntiles = x_hi > x_lo ? (x_hi - x_lo + Tr::BX - 1) / Tr::BX : 0;
+
+  // Resident fragments (B operand of the logits product).
+  CT rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
+#pragma unroll
+  for (int s = 0; s < Tr::KSTEPS; ++s) {
+    rf1[s] = r_ok ? load_chunk<T>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : CT{};
+    rf2[s] = r_ok ? load_chunk<T>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : CT{};
+  }
+
+  const float c = p.scale * kLog2e;
+  // Per-query statistics when queries are resident: exponent offsets LSE*log2e, KL, g*sigma.
+  float qb1 = 0.f, qb2 = 0.f, qkl = 0.f, qgs = 0.f;
+  if (!KEYS_RES && r_ok) {
+    qb1 = LS1[my_r] * kLog2e;
+    qb2 = LS2[my_r] * kLog2e;
+    qkl = KLr[my_r];
+    qgs = Gr[my_r] * sigma;
+  }
+
+  f32x16 acc1[Tr::NDB], acc2[Tr::NDB];
+#pragma unroll
+  for (int db = 0; db < Tr::NDB; ++db) {
+    acc1[db] = f32x16{};
+    acc2[db] = f32x16{};
+  }
+
+  // ---- staging: global -> registers -> LDS (row-major copy + transposed copy) ----
+  u32x4 st[Tr::IPT][2][4];
+  float sv[4];
+  auto gload = [&](int t) {
+    const int xb0 = x_lo + t * Tr::BX;
+#pragma unroll
+    for (int k = 0; k < Tr::IPT; ++k) {
+      const int item = tid + 256 * k;
+      const int cc = item % Tr::CPR, a = item / Tr::CPR;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = xb0 + 4 * a + u;
+        const bool ok = (item < Tr::ITEMS) && row < NX;
+        const int64_t o = (int64_t)row * Tr::ROW_BYTES + cc * 16;
+        st[k][0][u] = ok ? *reinterpret_cast<const u32x4 *>(X1 + o) : u32x4{0u, 0u, 0u, 0u};
+        st[k][1][u] = ok ? *reinterpret_cast<const u32x4 *>(X2 + o) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (KEYS_RES && tid < Tr::BX) {
+      const int q = xb0 + tid;
+      if (q < NQ) {
+        sv[0] = LS1[q] * kLog2e;
+        sv[1] = LS2[q] * kLog2e;
+        sv[2] = KLr[q];
+        sv[3] = Gr[q] * sigma;
+      } else {
+        sv[0] = sv[1] = sv[2] = sv[3] = 0.f;
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    char *base = smem + buf * Tr::STAGE_BYTES;
+#pragma unroll
+    for (int k = 0; k < Tr::IPT; ++k) {
+      const int item = tid + 256 * k;
+      if (item >= Tr::ITEMS) continue;
+      const int cc = item % Tr::CPR, a = item / Tr::CPR;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        char *xr = base + t2 * Tr::XROW_BYTES;
+        char *xt = base + Tr::OFF_XT + t2 * Tr::XT_BYTES;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          *reinterpret_cast<u32x4 *>(xr + (4 * a + u) * Tr::XROW + cc * 16) = st[k][t2][u];
+        if constexpr (sizeof(T) == 2) {
+          // 8 bf16 columns d = 8cc + e of rows 4a..4a+3 -> fp16, 4 rows per 8-byte store.
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint32_t w = st[k][t2][u][e >> 1];
+              v[u] = clamp_f16((e & 1) ? bf16hi_to_f32(w) : bf16lo_to_f32(w));
+            }
+            const u32x2 pk = {pack_f16(v[0], v[1]), pack_f16(v[2], v[3])};
+            *reinterpret_cast<u32x2 *>(xt + (8 * cc + e) * Tr::XT_STRIDE + 4 * a * 2) = pk;
+          }
+        } else {
+          // 4 fp32 columns d = 4cc + e of rows 4a..4a+3, 16-byte stores.
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u32x4 col = {st[k][t2][0][e], st[k][t2][1][e], st[k][t2][2][e], st[k][t2][3][e]};
+            *reinterpret_cast<u32x4 *>(xt + (4 * cc + e) * Tr::XT_STRIDE + 4 * a * 4) = col;
+          }
+        }
+      }
+    }
+    if (KEYS_RES && tid < Tr::BX) {
+      float *sb = reinterpret_cast<float *>(base + Tr::OFF_STAT);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) sb[f * Tr::BX + tid] = sv[f];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) gload(t + 1);
+    const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
+#pragma unroll
+    for (int xb = 0; xb < Tr::XB; ++xb) {
+      const int xa = x_lo + t * Tr::BX + xb * 32;  // streamed rows [xa, xa + 32)
+      bool full, empty;
+      if (KEYS_RES) {  // resident keys j, streamed queries i
+        full = xa + 31 < NQ && ra + 31 < NK && (!p.causal || ra + 31 <= xa + off);
+        empty = xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
+      } else {  // resident queries i, streamed keys j
+        full = ra + 31 < NQ && xa + 31 < NK && (!p.causal || xa + 31 <= ra + off);
+        empty = ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
+      }
+      if (empty) continue;
+
+      // Logits block: lane = resident row, element r = streamed row xa + acc_row(r, h).
+      f32x16 x1 = f32x16{}, x2 = f32x16{};
+      {
+        const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 8 * h * (int)sizeof(T);
+        const char *a2p = a1p + Tr::XROW_BYTES;
+#pragma unroll
+        for (int s = 0; s < Tr::KSTEPS; ++s) {
+          const CT a1 = *reinterpret_cast<const CT *>(a1p + 16 * s * (int)sizeof(T));
+          const CT a2 = *reinterpret_cast<const CT *>(a2p + 16 * s * (int)sizeof(T));
+          x1 = mma16(a1, rf1[s], x1);
+          x2 = mma16(a2, rf2[s], x2);
+        }
+      }
+
+      // dS, elementwise.
+      f32x16 d1, d2;
+      const float *sb = reinterpret_cast<const float *>(base + Tr::OFF_STAT);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 B1, B2, KV, GS;
+        if (KEYS_RES) {
+          const int q = xb * 32 + 8 * j + 4 * h;
+          B1 = *reinterpret_cast<const f32x4 *>(sb + 0 * Tr::BX + q);
+          B2 = *reinterpret_cast<const f32x4 *>(sb + 1 * Tr::BX + q);
+          KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
+          GS = *reinterpret_cast<const f32x4 *>(sb + 3 * Tr::BX + q);
+        } else {
+          B1 = f32x4{qb1, qb1, qb1, qb1};
+          B2 = f32x4{qb2, qb2, qb2, qb2};
+          KV = f32x4{qkl, qkl, qkl, qkl};
+          GS = f32x4{qgs, qgs, qgs, qgs};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * j + u;
+          const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
+          const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
+          const float p1 = fast_exp2(y1);
+          const float p2 = fast_exp2(y2);
+          const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
+          float v2 = GS[u] * (p2 - p1);
+          float v1 = (GS[u] * p1) * dl;
+          if (!full) {
+            const int srow = xa + acc_row(r, h);
+            const int qi = KEYS_RES ? srow : my_r;
+            const int kj = KEYS_RES ? my_r : srow;
+            const bool vis = qi < NQ && kj < NK && (!p.causal || kj <= qi + off);
+            v1 = vis ? v1 : 0.f;
+            v2 = vis ? v2 : 0.f;
+          }
+          d1[r] = v1;
+          d2[r] = v2;
+        }
+      }
+
+      // Gradient product dR^T[d, resident] += X^T[d, streamed] * dS[streamed, resident].
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        CG b1, b2;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          b1[u] = (G)d1[8 * ks + u];
+          b2[u] = (G)d2[8 * ks + u];
+        }
+        const int so = xb * 32 + 16 * ks + 4 * h;  // streamed-row offset of slots 0..3 (slots 4..7: +8)
+#pragma unroll
+        for (int db = 0; db < Tr::NDB; ++db) {
+          const char *t1 = base + Tr::OFF_XT + (db * 32 + c32) * Tr::XT_STRIDE + so * (int)sizeof(G);
+          const char *t2 = t1 + Tr::XT_BYTES;
+          CG a1, a2;
+          if constexpr (sizeof(G) == 2) {
+            const f16x4 l1 = *reinterpret_cast<const f16x4 *>(t1);
+            const f16x4 h1 = *reinterpret_cast<const f16x4 *>(t1 + 16);
+            const f16x4 l2 = *reinterpret_cast<const f16x4 *>(t2);
+            const f16x4 h2 = *reinterpret_cast<const f16x4 *>(t2 + 16);
+            a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(t1);
+            const f32x4 h1 = *reinterpret_cast<const f32x4 *>(t1 + 32);
+            const f32x4 l2 = *reinterpret_cast<const f32x4 *>(t2);
+            const f32x4 h2 = *reinterpret_cast<const f32x4 *>(t2 + 32);
+            a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+          if (p.want1) acc1[db] = mma16(a1, b1, acc1[db]);
+          if (p.want2) acc2[db] = mma16(a2, b2, acc2[db]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) sstore((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane writes its resident row, d = db*32 + 8j + 4h + (0..3).
+  if (r_ok) {
+    const float f = p.scale / sigma;
+    float *O1 = KEYS_RES ? p.dk1 : p.dq1;
+    float *O2 = KEYS_RES ? p.dk2 : p.dq2;
+    const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + 8 * j + 4 * h;
+        if (p.want1) {
+          const f32x4 v = {acc1[db][4 * j] * f, acc1[db][4 * j + 1] * f, acc1[db][4 * j + 2] * f,
+                           acc1[db][4 * j + 3] * f};
+          *reinterpret_cast<f32x4 *>(O1 + rowoff + d) = v;
+        }
+        if (p.want2) {
+          const f32x4 v = {acc2[db][4 * j] * f, acc2[db][4 * j + 1] * f, acc2[db][4 * j + 2] * f,
+                           acc2[db][4 * j + 3] * f};
+          *reinterpret_cast<f32x4 *>(O2 + rowoff + d) = v;
+        }
+      }
+    }
+  }
+}
+
+// sigma[b,h] = 2^(kGradExp - e) with 2^(e-1) <= max_i |g[b,h,i]| < 2^e (1 if g is all zero,
+// and 1 everywhere when `unit` is set: fp32 inputs need no scaling).
+__global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, int64_t NQ, float *sigma, int unit) {
+  const int64_t bh = blockIdx.x;
+  if (unit) {
+    if (threadIdx.x == 0) sigma[bh] = 1.f;
+    return;
+  }
+  const float *gp = g + bh * NQ;
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < NQ; i += 256) m = fmaxf(m, fabsf(gp[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float s = 1.f;
+    if (m > 0.f && m <= 3.4e38f) {
+      int k = kGradExp - (ilogbf(m) + 1);
+      k = min(max(k, -126), 126);
+      s = ldexpf(1.f, k);
+    }
+    sigma[bh] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float *dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = 0.f;
+}
+
+template <typename T, int D, bool KEYS_RES>
+static hipError_t launch_pass(const BwdParams &p, hipStream_t s) {
+  using Tr = BwdTraits<T, D, KEYS_RES>;
+  const int64_t NR = KEYS_RES ? p.NK : p.NQ;
+  if (NR == 0) return hipSuccess;
+  const void *fn = reinterpret_cast<const void *>(&bwd_kernel<T, D, KEYS_RES>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR);
+  hipLaunchKernelGGL((bwd_kernel<T, D, KEYS_RES>), dim3((uint32_t)nblk), dim3(256), Tr::LDS_BYTES, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_scale(int dtype, const float *g, int64_t BH, int64_t NQ, float *sigma, hipStream_t s) {
+  hipLaunchKernelGGL(grad_scale_kernel, dim3((uint32_t)BH), dim3(256), 0, s, g, NQ, sigma, dtype == 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s) {
+  if (dtype == 0) return D == 128 ? launch_pass<bf16, 128, true>(p, s) : launch_pass<bf16, 64, true>(p, s);
+  return D == 128 ? launch_pass<float, 128, true>(p, s) : launch_pass<float, 64, true>(p, s);
+}
+
+hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s) {
+  if (dtype == 0) return D == 128 ? launch_pass<bf16, 128, false>(p, s) : launch_pass<bf16, 64, false>(p, s);
+  return D == 128 ? launch_pass<float, 128, false>(p, s) : launch_pass<float, 64, false>(p, s);
+}
+
+hipError_t launch_zero(float *dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t nblk = (n + 255) / 256;
+  if (nblk > 65536) nblk = 65536;
+  hipLaunchKernelGGL(zero_kernel, dim3((uint32_t)nblk), dim3(256), 0, s, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace skl

@@ -1,0 +1,80 @@
+// Device-side building blocks shared by the attention-KL kernels (gfx950 / CDNA4).
+//
+// Matrix-core convention used throughout: every contraction is issued as
+// 32x32 output blocks, 16 contraction elements per step.  In a step each lane
+// supplies 8 consecutive contraction elements for one row of A (lane % 32)
+// and one column of B (lane % 32); lane half h = lane / 32 supplies elements
+// [8h, 8h+8) of the step.  Any assignment of contraction indices to (h, slot)
+// pairs is valid as long as A and B use the same one, which lets the
+// accumulator of one product feed the next product without a transpose.
+//
+// Accumulator layout of a 32x32 block (16 fp32 per lane): element r of lane l
+// holds row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skl {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running-max start value: finite so that (m_old - m_new) never forms inf - inf.
+constexpr float kNegBig = -3.0e38f;
+
+// Eight consecutive contraction elements of one operand row, as one lane holds them.
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16> { using type = bf16x8; };
+template <> struct Chunk<f16> { using type = f16x8; };
+template <> struct Chunk<float> { using type = f32x8; };
+template <typename T> using chunk_t = typename Chunk<T>::type;
+
+// C += A * B for one 16-deep contraction step of a 32x32 block.
+__device__ __forceinline__ f32x16 mma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// fp32 inputs: eight 32x32x2 steps; slot u of both lane halves forms step u.
+__device__ __forceinline__ f32x16 mma16(f32x8 a, f32x8 b, f32x16 c) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row of the 32x32 accumulator block held in element r by lane half h.
+__device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Loads 8 consecutive elements (16 B for 2-byte types, 32 B for fp32) from an
+// aligned address.
+template <typename T>
+__device__ __forceinline__ chunk_t<T> load_chunk(const T* p) {
+  return *reinterpret_cast<const chunk_t<T>*>(p);
+}
+
+// Work-group id remap so that consecutive logical ids land on the same XCD:
+// the dispatcher hands workgroup w to XCD w % 8, so logical id
+// (w % 8) * (n / 8) + w / 8 gives each XCD a contiguous run of logical ids.
+// Only applied when n is a multiple of 8 (otherwise identity).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
+  if ((n & 7u) != 0u) return w;
+  return (w & 7u) * (n >> 3) + (w >> 3);
+}
+
+}  // namespace skl

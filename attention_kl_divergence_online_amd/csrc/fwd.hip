@@ -1,0 +1,368 @@
+// Forward of the fused attention KL divergence: one online pass over key tiles.
+//
+// StreamKL (arXiv 2606.20005), gist.science "Formulacion Online": per query row
+// keep running maxima m1, m2, exponential sums l1, l2 and an accumulator acc of
+// the P1-weighted logit difference; emit KL = acc/l1 + LSE2 - LSE1 with
+// LSE_t = m_t + log l_t.  Causal key tiles beyond the boundary are skipped
+// outright.  The split-K variant ("Variante Split-K") cuts the key range into
+// chunks handled by separate workgroups; a merge kernel combines their row
+// states with log-sum-exp rescaling.
+//
+// gfx950 mapping
+//  * workgroup = 4 waves x 64 queries (two 32-query blocks per wave); the
+//    wave's Q1/Q2 fragments stay in registers for the whole pass;
+//  * K1/K2 tiles of 64 keys are double-buffered in LDS (rows padded by 16 B so
+//    the 32 rows a matrix-core operand read touches fall in distinct banks);
+//  * logits are produced transposed (keys x queries) so that every lane owns
+//    one query: each lane keeps its own online state over its 16 keys of a
+//    block, no cross-lane reduction happens inside the loop, and the two lane
+//    halves sharing a query are merged once at the end;
+//  * scores stay in raw dot-product units x = q.k; exponentials are
+//    exp2((x - m) * scale * log2 e).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace skl {
+
+template <typename T, int D>
+struct FwdTraits {
+  static constexpr int WAVES = 4;
+  // 32-query blocks per wave (fp32 at D=128 keeps one so its fragments fit in registers)
+  static constexpr int QB = (sizeof(T) == 4 && D == 128) ? 1 : 2;
+  static constexpr int BQ = WAVES * QB * 32;
+  static constexpr int BK = kFwdBK;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int ROW_BYTES = D * (int)sizeof(T);
+  static constexpr int LDS_ROW = ROW_BYTES + 16;
+  static constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per row
+  static constexpr int LOADS = BK * CPR / (WAVES * 64);
+  static constexpr int STAGE_BYTES = 2 * BK * LDS_ROW;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static_assert(LOADS * WAVES * 64 == BK * CPR, "staging split");
+};
+
+// v + cv carries a running sum; replace it by a * (v + cv) + s.  The product
+// and the sum are split into result + exact rounding error (fma residual and
+// Knuth's two-sum), so the error of the running sum stays at a few ulp however
+// many blocks are folded in.  Used for fp32 inputs, whose 1e-5 relative bound
+// on KL leaves no room for the ~sqrt(#blocks) ulp drift of plain accumulation.
+__device__ __forceinline__ void fold_compensated(float &v, float &cv, float a, float s) {
+#pragma clang fp contract(off)
+  const float x = v * a;
+  const float ex = __builtin_fmaf(v, a, -x);
+  const float t = x + s;
+  const float bv = t - x;
+  const float es = (x - (t - bv)) + (s - bv);
+  cv = __builtin_fmaf(cv, a, ex + es);
+  v = t;
+}
+
+// Running online state of one query as held by one lane (its share of the keys).
+struct RowState {
+  float m1, l1, m2, l2, acc;
+  float c1, c2, cacc;  // compensation terms (fp32 inputs only)
+};
+
+// Fold one 32-key block of raw scores into a lane's running state.
+// Element r of x1/x2 is key kbase + acc_row(r, h); keys >= klim are masked.
+template <bool MASK, bool COMP>
+__device__ __forceinline__ void online_update(const f32x16 &x1, const f32x16 &x2, RowState &st, float c,
+                                              int kbase, int h, int klim) {
+  float mx1 = st.m1, mx2 = st.m2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const bool v = !MASK || (kbase + acc_row(r, h) < klim);
+    if (v) {
+      mx1 = fmaxf(mx1, x1[r]);
+      mx2 = fmaxf(mx2, x2[r]);
+    }
+  }
+  const float a1 = fast_exp2((st.m1 - mx1) * c);
+  const float a2 = fast_exp2((st.m2 - mx2) * c);
+  st.m1 = mx1;
+  st.m2 = mx2;
+  const float b1 = mx1 * c, b2 = mx2 * c;
+  float s1 = 0.f, s2 = 0.f, sa = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float p1 = fast_exp2(__builtin_fmaf(x1[r], c, -b1));
+    float p2 = fast_exp2(__builtin_fmaf(x2[r], c, -b2));
+    float d = x1[r] - x2[r];
+    if (MASK) {
+      const bool v = kbase + acc_row(r, h) < klim;
+      p1 = v ? p1 : 0.f;
+      p2 = v ? p2 : 0.f;
+      d = v ? d : 0.f;
+    }
+    s1 += p1;
+    s2 += p2;
+    sa = __builtin_fmaf(p1, d, sa);
+  }
+  if (COMP) {
+    fold_compensated(st.l1, st.c1, a1, s1);
+    fold_compensated(st.l2, st.c2, a2, s2);
+    fold_compensated(st.acc, st.cacc, a1, sa);
+  } else {
+    st.l1 = __builtin_fmaf(st.l1, a1, s1);
+    st.l2 = __builtin_fmaf(st.l2, a2, s2);
+    st.acc = __builtin_fmaf(st.acc, a1, sa);
+  }
+}
+
+// KL, LSE1, LSE2 of a row from its merged state (raw-score units for m).
+__device__ __forceinline__ void finish_row(float m1, float l1, float m2, float l2, float acc, float scale,
+                                           float *kl, float *lse1, float *lse2) {
+  const float ln1 = logf(l1), ln2 = logf(l2);
+  *lse1 = __builtin_fmaf(scale, m1, ln1);
+  *lse2 = __builtin_fmaf(scale, m2, ln2);
+  *kl = scale * (acc / l1 - (m1 - m2)) - (ln1 - ln2);
+}
+
+template <typename T, int D, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
+  using Tr = FwdTraits<T, D>;
+  using CT = chunk_t<T>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c32 = lane & 31;
+
+  // Workgroup -> (head, query tile, key chunk).
+  int qt, sp;
+  int64_t bh;
+  if (SPLIT) {
+    // Workgroups that share a key chunk are adjacent logical ids on one XCD.
+    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    qt = (int)(L % (uint32_t)p.nqt);
+    const uint32_t rest = L / (uint32_t)p.nqt;
+    sp = (int)(rest % (uint32_t)p.splits);
+    bh = rest / (uint32_t)p.splits;
+  } else {
+    // Head-major; within a head the longest (last) query tiles go first.
+    const uint32_t L = blockIdx.x;
+    bh = L / (uint32_t)p.nqt;
+    qt = p.nqt - 1 - (int)(L % (uint32_t)p.nqt);
+    sp = 0;
+  }
+
+  const int NQ = (int)p.NQ, NK = (int)p.NK;
+  const int off = NK - NQ;
+  const T *Q1 = reinterpret_cast<const T *>(p.q1) + bh * (int64_t)NQ * D;
+  const T *Q2 = reinterpret_cast<const T *>(p.q2) + bh * (int64_t)NQ * D;
+  const char *K1 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(p.k1) + bh * (int64_t)NK * D);
+  const char *K2 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(p.k2) + bh * (int64_t)NK * D);
+
+  const int q0 = qt * Tr::BQ;
+  const int qend = min(q0 + Tr::BQ, NQ);
+  const int qw0 = q0 + wave * Tr::QB * 32;
+  const int qw_last = min(qw0 + Tr::QB * 32 - 1, qend - 1);
+  const bool wave_live = qw0 <= qw_last;
+
+  const int kwg_end = p.causal ? min(NK, qend - 1 + off + 1) : NK;
+  const int k_lo = SPLIT ? sp * p.chunk : 0;
+  const int k_hi = SPLIT ? min(k_lo + p.chunk, kwg_end) : kwg_end;
+  const int ntiles = k_hi > k_lo ? (k_hi - k_lo + Tr::BK - 1) / Tr::BK : 0;
+
+  // Keys below vis_all are visible to every query of this wave; none at or above vis_any is.
+  const int vis_all = min(k_hi, p.causal ? qw0 + off + 1 : NK);
+  const int vis_any = min(k_hi, p.causal ? qw_last + off + 1 : NK);
+
+  // Resident query fragments: lane owns query qw0 + qb*32 + c32, elements [16s + 8h, +8).
+  CT qf1[Tr::QB][Tr::KSTEPS], qf2[Tr::QB][Tr::KSTEPS];
+  int klim[Tr::QB];
+#pragma unroll
+  for (int qb = 0; qb < Tr::QB; ++qb) {
+    const int row = qw0 + qb * 32 + c32;
+    const bool ok = row < qend;
+    klim[qb] = min(k_hi, p.causal ? row + off + 1 : NK);
+#pragma unroll
+    for (int s = 0; s < Tr::KSTEPS; ++s) {
+      qf1[qb][s] = ok ? load_chunk<T>(Q1 + (int64_t)row * D + 16 * s + 8 * h) : CT{};
+      qf2[qb][s] = ok ? load_chunk<T>(Q2 + (int64_t)row * D + 16 * s + 8 * h) : CT{};
+    }
+  }
+
+  const float c = p.scale * kLog2e;
+  constexpr bool COMP = sizeof(T) == 4;
+  RowState st[Tr::QB];
+#pragma unroll
+  for (int qb = 0; qb < Tr::QB; ++qb) st[qb] = RowState{kNegBig, 0.f, kNegBig, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+  // Global -> register staging of the next key tile (16-byte chunks, coalesced rows).
+  u32x4 stg1[Tr::LOADS], stg2[Tr::LOADS];
+  auto gload = [&](int t) {
+    const int kb0 = k_lo + t * Tr::BK;
+#pragma unroll
+    for (int i = 0; i < Tr::LOADS; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / Tr::CPR, col = cidx % Tr::CPR;
+      const int key = kb0 + row;
+      if (key < NK) {
+        stg1[i] = *reinterpret_cast<const u32x4 *>(K1 + (int64_t)key * Tr::ROW_BYTES + col * 16);
+        stg2[i] = *reinterpret_cast<const u32x4 *>(K2 + (int64_t)key * Tr::ROW_BYTES + col * 16);
+      } else {
+        stg1[i] = u32x4{0u, 0u, 0u, 0u};
+        stg2[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    char *base = smem + buf * Tr::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < Tr::LOADS; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / Tr::CPR, col = cidx % Tr::CPR;
+      *reinterpret_cast<u32x4 *>(base + row * Tr::LDS_ROW + col * 16) = stg1[i];
+      *reinterpret_cast<u32x4 *>(base + Tr::BK * Tr::LDS_ROW + row * Tr::LDS_ROW + col * 16) = stg2[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) gload(t + 1);
+    const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
+    if (wave_live) {
+#pragma unroll
+      for (int kb = 0; kb < Tr::BK / 32; ++kb) {
+        const int kbase = k_lo + t * Tr::BK + kb * 32;
+        if (kbase >= vis_any) continue;
+        const bool full = kbase + 32 <= vis_all;
+        f32x16 s1[Tr::QB], s2[Tr::QB];
+#pragma unroll
+        for (int qb = 0; qb < Tr::QB; ++qb) {
+          s1[qb] = f32x16{};
+          s2[qb] = f32x16{};
+        }
+        const char *r1 = base + (kb * 32 + c32) * Tr::LDS_ROW + 8 * h * (int)sizeof(T);
+        const char *r2 = r1 + Tr::BK * Tr::LDS_ROW;
+#pragma unroll
+        for (int s = 0; s < Tr::KSTEPS; ++s) {
+          const CT a1 = *reinterpret_cast<const CT *>(r1 + 16 * s * (int)sizeof(T));
+          const CT a2 = *reinterpret_cast<const CT *>(r2 + 16 * s * (int)sizeof(T));
+#pragma unroll
+          for (int qb = 0; qb < Tr::QB; ++qb) {
+            s1[qb] = mma16(a1, qf1[qb][s], s1[qb]);
+            s2[qb] = mma16(a2, qf2[qb][s], s2[qb]);
+          }
+        }
+        if (full) {
+#pragma unroll
+          for (int qb = 0; qb < Tr::QB; ++qb)
+            online_update<false, COMP>(s1[qb], s2[qb], st[qb], c, kbase, h, 0);
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < Tr::QB; ++qb)
+            online_update<true, COMP>(s1[qb], s2[qb], st[qb], c, kbase, h, klim[qb]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) sstore((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // Merge the two lane halves that hold disjoint keys of the same query.
+#pragma unroll
+  for (int qb = 0; qb < Tr::QB; ++qb) {
+    const float m1 = st[qb].m1, m2 = st[qb].m2;
+    const float l1 = COMP ? st[qb].l1 + st[qb].c1 : st[qb].l1;
+    const float l2 = COMP ? st[qb].l2 + st[qb].c2 : st[qb].l2;
+    const float acc = COMP ? st[qb].acc + st[qb].cacc : st[qb].acc;
+    const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32);
+    const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
+    const float oacc = __shfl_xor(acc, 32);
+    const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
+    const float wa = fast_exp2((m1 - M1) * c), wb = fast_exp2((om1 - M1) * c);
+    const float va = fast_exp2((m2 - M2) * c), vb = fast_exp2((om2 - M2) * c);
+    const float L1 = __builtin_fmaf(l1, wa, ol1 * wb);
+    const float A = __builtin_fmaf(acc, wa, oacc * wb);
+    const float L2 = __builtin_fmaf(l2, va, ol2 * vb);
+    const int row = qw0 + qb * 32 + c32;
+    if (h == 0 && row < qend) {
+      const int64_t idx = bh * (int64_t)NQ + row;
+      if (SPLIT) {
+        const int64_t rows = p.BH * (int64_t)NQ;
+        float *w = p.ws + (int64_t)sp * rows + idx;
+        const int64_t fstride = (int64_t)p.splits * rows;
+        w[0] = M1;
+        w[fstride] = L1;
+        w[2 * fstride] = M2;
+        w[3 * fstride] = L2;
+        w[4 * fstride] = A;
+      } else {
+        finish_row(M1, L1, M2, L2, A, p.scale, p.kl + idx, p.lse1 + idx, p.lse2 + idx);
+      }
+    }
+  }
+}
+
+// One thread per row: merge the per-chunk states in chunk order (deterministic).
+__global__ __launch_bounds__(256) void splitk_merge_kernel(FwdParams p) {
+  const int64_t rows = p.BH * p.NQ;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows) return;
+  const float c = p.scale * kLog2e;
+  const int64_t fstride = (int64_t)p.splits * rows;
+  const float *w = p.ws + idx;
+  float M1 = kNegBig, M2 = kNegBig;
+  for (int s = 0; s < p.splits; ++s) {
+    const float *ws = w + (int64_t)s * rows;
+    if (ws[fstride] > 0.f) {
+      M1 = fmaxf(M1, ws[0]);
+      M2 = fmaxf(M2, ws[2 * fstride]);
+    }
+  }
+  float L1 = 0.f, L2 = 0.f, A = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float *ws = w + (int64_t)s * rows;
+    const float l1 = ws[fstride];
+    if (l1 > 0.f) {
+      const float w1 = fast_exp2((ws[0] - M1) * c);
+      const float w2 = fast_exp2((ws[2 * fstride] - M2) * c);
+      L1 = __builtin_fmaf(w1, l1, L1);
+      A = __builtin_fmaf(w1, ws[4 * fstride], A);
+      L2 = __builtin_fmaf(w2, ws[3 * fstride], L2);
+    }
+  }
+  finish_row(M1, L1, M2, L2, A, p.scale, p.kl + idx, p.lse1 + idx, p.lse2 + idx);
+}
+
+template <typename T, int D, bool SPLIT>
+static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s) {
+  using Tr = FwdTraits<T, D>;
+  const void *fn = reinterpret_cast<const void *>(&fwd_kernel<T, D, SPLIT>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const int64_t nblk = p.BH * (int64_t)p.nqt * p.splits;
+  hipLaunchKernelGGL((fwd_kernel<T, D, SPLIT>), dim3((uint32_t)nblk), dim3(256), Tr::LDS_BYTES, s, p);
+  return hipGetLastError();
+}
+
+int fwd_block_queries(int dtype, int D) {
+  if (dtype == 0) return D == 128 ? FwdTraits<bf16, 128>::BQ : FwdTraits<bf16, 64>::BQ;
+  return D == 128 ? FwdTraits<float, 128>::BQ : FwdTraits<float, 64>::BQ;
+}
+
+hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s) {
+  const bool split = p.splits > 1;
+  if (dtype == 0) {
+    if (D == 128) return split ? launch_fwd_t<bf16, 128, true>(p, s) : launch_fwd_t<bf16, 128, false>(p, s);
+    return split ? launch_fwd_t<bf16, 64, true>(p, s) : launch_fwd_t<bf16, 64, false>(p, s);
+  }
+  if (D == 128) return split ? launch_fwd_t<float, 128, true>(p, s) : launch_fwd_t<float, 128, false>(p, s);
+  return split ? launch_fwd_t<float, 64, true>(p, s) : launch_fwd_t<float, 64, false>(p, s);
+}
+
+hipError_t launch_splitk_merge(const FwdParams &p, hipStream_t s) {
+  const int64_t rows = p.BH * p.NQ;
+  const int64_t nblk = (rows + 255) / 256;
+  hipLaunchKernelGGL(splitk_merge_kernel, dim3((uint32_t)nblk), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace skl

@@ -1,0 +1,185 @@
+/*
+ * streamkl.h -- C ABI of the fused attention KL-divergence primitive for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (StreamKL, arXiv 2606.20005; abstract on paperdance.org and
+ * fugumt.com): for every (batch b, head h, query row i)
+ *
+ *     s_t,ij = scale * <Q_t[b,h,i,:], K_t[b,h,j,:]>          t = 1 teacher, 2 student
+ *     P_t,ij = exp(s_t,ij) / sum_{k visible} exp(s_t,ik)
+ *     KL_i   = sum_{j visible} P1_ij * log(P1_ij / P2_ij)    = KL(P1 || P2), row i
+ *     LSE_t,i = log sum_{j visible} exp(s_t,ij)              (natural log)
+ *
+ * Key j is visible to row i iff j < NK and, when `causal` is set,
+ * j <= i + NK - NQ (bottom-right aligned mask; for NQ == NK this is j <= i).
+ * Neither N_Q x N_K probability matrix is ever stored: the forward streams
+ * key tiles through on-chip memory keeping five running scalars per row
+ * (gist.science, "Formulacion Online"), and the backward recomputes the
+ * probabilities tile by tile from the saved LSE vectors (gist.science,
+ * "Estrategia de Recomputacion").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory and keeps no mutable global state.
+ *  - Q1, Q2 are [B, H, NQ, D] and K1, K2 are [B, H, NK, D], contiguous,
+ *    row-major, element type `dtype` (bf16 or fp32).  Per-row vectors (KL,
+ *    LSE1, LSE2, g) are fp32 [B, H, NQ].  Gradients are fp32 and have the
+ *    shape of the tensor they belong to.
+ *  - Every pointer must be 16-byte aligned.  D must be 64 or 128.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    and the call returns without waiting for it.
+ *  - Argument errors are detected on the host before anything is enqueued;
+ *    then nothing is written.  A failed kernel launch returns
+ *    STREAMKL_ERR_HIP.  No call throws.
+ *  - Calls that share no output buffer may run concurrently on different
+ *    streams.
+ */
+#ifndef STREAMKL_H
+#define STREAMKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STREAMKL_OK = 0,
+    STREAMKL_ERR_NULL = 1,      /* a required pointer is NULL */
+    STREAMKL_ERR_SHAPE = 2,     /* bad sizes: negative, D not 64/128, NK == 0 with rows,
+                                   causal with NQ > NK, per-head tensor >= 2^31 elements,
+                                   split count out of range */
+    STREAMKL_ERR_DTYPE = 3,     /* dtype is not STREAMKL_BF16 / STREAMKL_FP32 */
+    STREAMKL_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+    STREAMKL_ERR_WORKSPACE = 5, /* workspace missing or smaller than the size query */
+    STREAMKL_ERR_HIP = 6        /* the HIP runtime rejected a launch */
+} streamkl_status;
+
+typedef enum { STREAMKL_BF16 = 0, STREAMKL_FP32 = 1 } streamkl_dtype;
+
+typedef struct {
+    int64_t B, H;   /* batch, heads */
+    int64_t NQ;     /* query rows per head */
+    int64_t NK;     /* key rows per head */
+    int64_t D;      /* head dimension: 64 or 128 */
+    float scale;    /* logit scale (1/sqrt(D) for plain attention; 1/(tau*sqrt(D))
+                       folds a distillation temperature tau into both distributions) */
+    int32_t causal; /* nonzero: bottom-right aligned causal mask */
+    int32_t dtype;  /* streamkl_dtype of Q1, K1, Q2, K2 */
+} streamkl_problem;
+
+/*
+ * Forward: one online pass over the key tiles (gist.science, "Formulacion
+ * Online"; arXiv abstract, "single one-pass forward kernel").  Writes per row
+ * KL(P1||P2), LSE1 and LSE2 -- the only state the backward needs
+ * (gist.science, "Estrategia de Recomputacion", saved state).
+ * Extra device memory: none.
+ */
+streamkl_status streamkl_fwd(const streamkl_problem *p,
+                             const void *q1, const void *k1,
+                             const void *q2, const void *k2,
+                             float *kl, float *lse1, float *lse2,
+                             void *stream);
+
+/*
+ * Bytes of device workspace streamkl_fwd_splitk needs for `num_splits`
+ * chunks: 5 fp32 partial row states (m1, l1, m2, l2, acc) per split per row.
+ * Returns 0 if the problem or split count is invalid.
+ */
+size_t streamkl_fwd_splitk_workspace_size(const streamkl_problem *p, int num_splits);
+
+/*
+ * Split-K forward for short-query, long-key shapes (gist.science,
+ * "Optimizaciones de Kernel de GPU", Split-K variant): the key range is cut
+ * into `num_splits` contiguous chunks processed by separate workgroups, each
+ * producing a partial row state; a second kernel merges the states with
+ * log-sum-exp rescaling and writes KL, LSE1, LSE2 exactly as streamkl_fwd
+ * does.  1 <= num_splits <= ceil(NK / 64); chunks are whole 64-key tiles.
+ * `workspace` (device, caller-owned, >= the size query) is scratch between
+ * the two kernels; its contents on return are unspecified.
+ */
+streamkl_status streamkl_fwd_splitk(const streamkl_problem *p,
+                                    const void *q1, const void *k1,
+                                    const void *q2, const void *k2,
+                                    float *kl, float *lse1, float *lse2,
+                                    int num_splits, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/*
+ * Bytes of device workspace streamkl_bwd needs (one fp32 per (batch, head)).
+ * Returns 0 if the problem is invalid.
+ */
+size_t streamkl_bwd_workspace_size(const streamkl_problem *p);
+
+/*
+ * Backward of L = sum_{b,h,i} g[b,h,i] * KL[b,h,i] (gist.science, "Estrategia
+ * de Recomputacion"): probabilities are recomputed tile by tile as
+ * P_t = exp(s_t - LSE_t) from Q, K and the saved LSE vectors, and
+ *     dS2 = g * (P2 - P1)                                   ("Configuracion 1")
+ *     dS1 = g * P1 * ((s1 - LSE1) - (s2 - LSE2) - KL_row)   ("Configuracion 2"),
+ * the log-ratio taken from logits and the saved LSEs ("Estabilidad Numerica").
+ * Then dQ_t = scale * dS_t K_t and dK_t = scale * dS_t^T Q_t, in two passes
+ * with no atomics (one over key tiles for dK, one over query tiles for dQ);
+ * results are bitwise repeatable.
+ *
+ * kl, lse1, lse2 must be the outputs of streamkl_fwd / streamkl_fwd_splitk for
+ * the same inputs.  Gradient outputs come in pairs: pass dq1 = dk1 = NULL to
+ * skip the teacher gradients (teacher fixed) or dq2 = dk2 = NULL to skip the
+ * student's; a half-NULL pair is STREAMKL_ERR_NULL.  Outputs are overwritten.
+ * The gradient products run on fp16 matrix cores with fp32 accumulation:
+ * entries of Q and K above 65504 in magnitude are clamped to the fp16 range
+ * for those products.
+ */
+streamkl_status streamkl_bwd(const streamkl_problem *p,
+                             const void *q1, const void *k1,
+                             const void *q2, const void *k2,
+                             const float *kl, const float *lse1, const float *lse2,
+                             const float *g,
+                             float *dq1, float *dk1, float *dq2, float *dk2,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * The backward in steps: streamkl_bwd is exactly streamkl_bwd_prepare, then
+ * streamkl_bwd_dk, then streamkl_bwd_dq, on one stream.  The two passes only
+ * read their inputs and the prepared workspace, so once the prepare step has
+ * completed they may run on different streams.
+ *
+ * streamkl_bwd_prepare writes into `workspace` one fp32 per (batch, head): the
+ * power of two sigma with max_i |g_i| * sigma in [2^7, 2^8), by which the
+ * passes scale dS before rounding it to fp16 (1 for fp32 inputs).
+ * streamkl_bwd_dk writes dK1, dK2 (one pass over key tiles, queries streamed);
+ * streamkl_bwd_dq writes dQ1, dQ2 (one pass over query tiles, keys streamed).
+ * NULL-pair rules, layouts and errors are those of streamkl_bwd; the pass
+ * calls read `workspace` and never write it.
+ */
+streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const float *g,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+streamkl_status streamkl_bwd_dk(const streamkl_problem *p,
+                                const void *q1, const void *k1,
+                                const void *q2, const void *k2,
+                                const float *kl, const float *lse1, const float *lse2,
+                                const float *g, float *dk1, float *dk2,
+                                const void *workspace, size_t workspace_bytes, void *stream);
+
+streamkl_status streamkl_bwd_dq(const streamkl_problem *p,
+                                const void *q1, const void *k1,
+                                const void *q2, const void *k2,
+                                const float *kl, const float *lse1, const float *lse2,
+                                const float *g, float *dq1, float *dq2,
+                                const void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *streamkl_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int streamkl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMKL_H */

@@ -1,0 +1,151 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+Loads libstreamkl.so, checks that it exports every function include/streamkl.h
+declares, and drives the validation paths: each call below carries an
+argument error that the library must reject on the host, before any HIP call
+or launch.  No call here reaches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_kl_divergence_online_amd import _lib
+from attention_kl_divergence_online_amd._lib import Problem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "streamkl.h")
+CSRC = os.path.join(ROOT, "attention_kl_divergence_online_amd", "csrc")
+
+# Fake, 16-byte aligned device addresses: never dereferenced, because every
+# call that uses them fails validation on another argument first.
+A = 0x10000
+MIS = 0x10008  # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from attention_kl_divergence_online_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(streamkl_\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert names, "header parse found no functions"
+    assert tuple(names) == _lib.EXPORTS
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_library_allocates_no_device_memory():
+    # The library owns no device buffers: callers pass every buffer in.
+    for f in os.listdir(CSRC):
+        src = open(os.path.join(CSRC, f)).read()
+        assert not re.search(r"\bhip(Malloc|Free|MallocAsync|HostMalloc)\w*\s*\(", src), f
+
+
+def test_status_strings(L):
+    assert _lib.status_string(0) == "ok"
+    for s in range(1, 7):
+        assert _lib.status_string(s) not in ("ok", "unknown status")
+    assert _lib.status_string(99) == "unknown status"
+    assert L.streamkl_version() >= 100
+
+
+def P(**kw):
+    base = dict(B=1, H=2, NQ=8, NK=8, D=64, scale=0.125, causal=0, dtype=_lib.STREAMKL_BF16)
+    base.update(kw)
+    return Problem(**base)
+
+
+def fwd(L, p, q1=A, k1=A, q2=A, k2=A, kl=A, l1=A, l2=A):
+    return L.streamkl_fwd(ctypes.byref(p) if p is not None else None, q1, k1, q2, k2, kl, l1, l2, None)
+
+
+def test_forward_validation(L):
+    assert L.streamkl_fwd(None, A, A, A, A, A, A, A, None) == _lib.STREAMKL_ERR_NULL
+    assert fwd(L, P(dtype=7)) == _lib.STREAMKL_ERR_DTYPE
+    assert fwd(L, P(D=96)) == _lib.STREAMKL_ERR_SHAPE
+    assert fwd(L, P(NQ=-1)) == _lib.STREAMKL_ERR_SHAPE
+    assert fwd(L, P(NK=0)) == _lib.STREAMKL_ERR_SHAPE
+    assert fwd(L, P(causal=1, NQ=9, NK=8)) == _lib.STREAMKL_ERR_SHAPE
+    assert fwd(L, P(NK=1 << 25, D=64)) == _lib.STREAMKL_ERR_SHAPE  # per-head tensor >= 2^31
+    assert fwd(L, P(scale=float("nan"))) == _lib.STREAMKL_ERR_SHAPE
+    assert fwd(L, P(), q1=None) == _lib.STREAMKL_ERR_NULL
+    assert fwd(L, P(), k2=None) == _lib.STREAMKL_ERR_NULL
+    assert fwd(L, P(), kl=None) == _lib.STREAMKL_ERR_NULL
+    assert fwd(L, P(), q2=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert fwd(L, P(), l2=MIS) == _lib.STREAMKL_ERR_ALIGN
+
+
+def test_empty_problems_are_no_ops(L):
+    # Nothing to compute: success without touching any pointer.
+    assert fwd(L, P(B=0), q1=None, kl=None) == _lib.STREAMKL_OK
+    assert fwd(L, P(NQ=0), q1=None, kl=None) == _lib.STREAMKL_OK
+    assert fwd(L, P(H=0, NK=0), q1=None) == _lib.STREAMKL_OK
+
+
+def test_splitk_validation(L):
+    p = P(NK=200)  # 4 key tiles of 64
+    assert L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 4) == 5 * 4 * 2 * 8 * 4
+    assert L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 5) == 0
+    assert L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 0) == 0
+    args = (A, A, A, A, A, A, A)
+    assert L.streamkl_fwd_splitk(ctypes.byref(p), *args, 0, A, 1 << 20, None) == _lib.STREAMKL_ERR_SHAPE
+    assert L.streamkl_fwd_splitk(ctypes.byref(p), *args, 5, A, 1 << 20, None) == _lib.STREAMKL_ERR_SHAPE
+    assert L.streamkl_fwd_splitk(ctypes.byref(p), *args, 3, None, 0, None) == _lib.STREAMKL_ERR_WORKSPACE
+    assert L.streamkl_fwd_splitk(ctypes.byref(p), *args, 3, A, 10, None) == _lib.STREAMKL_ERR_WORKSPACE
+    assert L.streamkl_fwd_splitk(ctypes.byref(p), *args, 3, MIS, 1 << 20, None) == _lib.STREAMKL_ERR_ALIGN
+    assert L.streamkl_fwd_splitk(ctypes.byref(p), None, A, A, A, A, A, A, 3, A, 1 << 20,
+                                 None) == _lib.STREAMKL_ERR_NULL
+
+
+def bwd(L, p, dq1=A, dk1=A, dq2=A, dk2=A, ws=A, wsb=1 << 20, g=A, kl=A):
+    return L.streamkl_bwd(ctypes.byref(p), A, A, A, A, kl, A, A, g, dq1, dk1, dq2, dk2, ws, wsb, None)
+
+
+def test_backward_validation(L):
+    p = P()
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == 16
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7))) == 96
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(D=32))) == 0
+    assert bwd(L, p, dq1=None) == _lib.STREAMKL_ERR_NULL       # half pair
+    assert bwd(L, p, dk2=None) == _lib.STREAMKL_ERR_NULL
+    assert bwd(L, p, ws=None) == _lib.STREAMKL_ERR_WORKSPACE
+    assert bwd(L, P(B=4, H=8), wsb=64) == _lib.STREAMKL_ERR_WORKSPACE
+    assert bwd(L, p, g=None) == _lib.STREAMKL_ERR_NULL
+    assert bwd(L, p, kl=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert bwd(L, p, dk1=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert bwd(L, P(D=100)) == _lib.STREAMKL_ERR_SHAPE
+    # Both pairs skipped: nothing to do.
+    assert bwd(L, p, dq1=None, dk1=None, dq2=None, dk2=None, ws=None) == _lib.STREAMKL_OK
+
+
+def test_backward_step_validation(L):
+    p = P()
+    prep = lambda g=A, ws=A, wsb=1 << 20, pp=p: L.streamkl_bwd_prepare(ctypes.byref(pp), g, ws, wsb, None)
+    assert prep(g=None) == _lib.STREAMKL_ERR_NULL
+    assert prep(ws=None) == _lib.STREAMKL_ERR_WORKSPACE
+    assert prep(wsb=4) == _lib.STREAMKL_ERR_WORKSPACE
+    assert prep(ws=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert prep(g=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert prep(g=None, pp=P(NQ=0)) == _lib.STREAMKL_OK
+    for name in ("streamkl_bwd_dk", "streamkl_bwd_dq"):
+        fn = getattr(L, name)
+        call = lambda a=A, b=A, ws=A, wsb=1 << 20, kl=A: fn(ctypes.byref(p), A, A, A, A, kl, A, A, A, a, b,
+                                                             ws, wsb, None)
+        assert call(ws=None) == _lib.STREAMKL_ERR_WORKSPACE, name
+        assert call(wsb=8) == _lib.STREAMKL_ERR_WORKSPACE, name
+        assert call(a=MIS) == _lib.STREAMKL_ERR_ALIGN, name
+        assert call(kl=None) == _lib.STREAMKL_ERR_NULL, name
+        assert call(a=None, b=None, ws=None) == _lib.STREAMKL_OK, name
+        assert fn(ctypes.byref(P(dtype=5)), A, A, A, A, A, A, A, A, A, A, A, 64, None) == _lib.STREAMKL_ERR_DTYPE

@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small shapes span several tiles with ragged tails in both N_Q and N_K and are
+compared element by element.  The full-size workloads (causal 4K, non-causal
+16K, causal 64K, split-K 512K keys, 128K-key backward) run in the launch
+configuration the benchmark times and are compared on sampled rows the oracle
+computes one by one; key gradients at full size are compared in full with an
+upstream gradient that is nonzero only on the sampled rows (dK is linear in g),
+plus the any-size invariant sum_j dK[j] = 0.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from attention_kl_divergence_online_amd import (StreamKLError, attention_kl, streamkl_bwd, streamkl_fwd,
+                                                streamkl_fwd_splitk)
+from parity_util import TOL, assert_within, compare_backward, compare_forward, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _rand(B, H, NQ, NK, D, dtype, seed, noise=0.3, std=1.0):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q1 = torch.randn(B, H, NQ, D, generator=g) * std
+    k1 = torch.randn(B, H, NK, D, generator=g) * std
+    q2 = q1 + noise * torch.randn(B, H, NQ, D, generator=g)
+    k2 = k1 + noise * torch.randn(B, H, NK, D, generator=g)
+    return [t.to(dtype).to(DEV).contiguous() for t in (q1, k1, q2, k2)]
+
+
+def _heads(B, H):
+    return [(b, h) for b in range(B) for h in range(H)]
+
+
+def test_device_present():
+    assert torch.cuda.is_available(), "no HIP device visible"
+
+
+def test_tiny_fp32_workload_full():
+    w = synth.get("tiny_fp32")
+    q1, k1, q2, k2 = (t.to(DEV) for t in synth.make_inputs(w))
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal)
+    g = synth.upstream_grad(w, DEV)
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal)
+    torch.cuda.synchronize()
+    heads = _heads(w.B, w.H)
+    assert_within(compare_forward(q1, k1, q2, k2, w.scale, w.causal, kl, l1, l2, heads), TOL["fp32"], "fwd")
+    assert_within(compare_backward(q1, k1, q2, k2, w.scale, w.causal, g, grads, heads), TOL["fp32"], "bwd")
+
+
+SMALL = [
+    # B, H, NQ, NK, D, causal
+    (1, 2, 300, 517, 128, False),
+    (1, 2, 300, 517, 128, True),
+    (2, 1, 700, 700, 128, True),
+    (1, 3, 129, 1000, 64, False),
+    (1, 2, 257, 333, 64, True),
+    (1, 1, 1, 37, 128, False),
+    (1, 1, 1, 1, 128, False),
+    (1, 1, 5, 5, 128, True),
+    (1, 2, 64, 4100, 128, False),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,H,NQ,NK,D,causal", SMALL)
+def test_small_shapes_full(dtype, B, H, NQ, NK, D, causal):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    print(f"case {dtype} B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal}", flush=True)
+    q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, tdt, seed=NQ * 7 + NK + D)
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    g = torch.rand(B, H, NQ, generator=gen).mul_(2).sub_(0.5).to(DEV)  # mixed signs
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal)
+    torch.cuda.synchronize()
+    heads = _heads(B, H)
+    case = f"{dtype} B{B} H{H} NQ{NQ} NK{NK} D{D} causal={causal}"
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL[dtype], f"fwd {case}")
+    assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, grads, heads), TOL[dtype], f"bwd {case}")
+
+
+def test_backward_steps_equal_combined_call():
+    from attention_kl_divergence_online_amd import streamkl_bwd_dk, streamkl_bwd_dq, streamkl_bwd_prepare
+    q1, k1, q2, k2 = _rand(2, 2, 300, 400, 128, torch.bfloat16, seed=12)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, True)
+    g = torch.rand(2, 2, 300, device=DEV) * 1e-3
+    full = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True)
+    ws = streamkl_bwd_prepare(q1, k1, g, None, True)
+    dk1, dk2 = streamkl_bwd_dk(q1, k1, q2, k2, kl, l1, l2, g, None, True, workspace=ws)
+    dq1, dq2 = streamkl_bwd_dq(q1, k1, q2, k2, kl, l1, l2, g, None, True, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip((dq1, dk1, dq2, dk2), full):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitk_small(splits, causal):
+    B, H, NQ, NK, D = 1, 2, 300, 1000, 128
+    q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, torch.bfloat16, seed=11 + splits)
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd_splitk(q1, k1, q2, k2, splits, scale, causal)
+    ukl, ul1, ul2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    torch.cuda.synchronize()
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, _heads(B, H)), TOL["bf16"], "split")
+    for a, b in ((kl, ukl), (l1, ul1), (l2, ul2)):
+        d = (a - b).abs().max().item() / max(b.abs().max().item(), 1e-30)
+        assert d <= 1e-5, d
+
+
+def test_identical_teacher_student_is_exact_zero():
+    q1, k1, _, _ = _rand(1, 2, 300, 300, 128, torch.bfloat16, seed=5)
+    for causal in (False, True):
+        kl, l1, l2 = streamkl_fwd(q1, k1, q1, k1, None, causal)
+        g = torch.ones(1, 2, 300, device=DEV)
+        grads = streamkl_bwd(q1, k1, q1, k1, kl, l1, l2, g, None, causal)
+        torch.cuda.synchronize()
+        assert torch.equal(kl, torch.zeros_like(kl))
+        assert torch.equal(l1, l2)
+        for t in grads:
+            assert torch.equal(t, torch.zeros_like(t))
+
+
+def test_zero_queries_uniform_rows():
+    B, H, NQ, NK, D = 1, 1, 200, 300, 128
+    _, k1, _, k2 = _rand(B, H, NQ, NK, D, torch.bfloat16, seed=6)
+    z = torch.zeros(B, H, NQ, D, dtype=torch.bfloat16, device=DEV)
+    for causal in (False, True):
+        kl, l1, l2 = streamkl_fwd(z, k1, z, k2, None, causal)
+        torch.cuda.synchronize()
+        n = torch.arange(NQ, device=DEV) + (NK - NQ) + 1 if causal else torch.full((NQ,), NK, device=DEV)
+        assert kl.abs().max().item() <= 1e-6
+        torch.testing.assert_close(l1[0, 0], n.double().log().float(), rtol=2e-7, atol=2e-6)
+
+
+def test_bitwise_repeatable():
+    q1, k1, q2, k2 = _rand(1, 4, 700, 900, 128, torch.bfloat16, seed=7)
+    g = torch.full((1, 4, 700), 1e-3, device=DEV)
+    outs = []
+    for _ in range(2):
+        kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, True)
+        sk = streamkl_fwd_splitk(q1, k1, q2, k2, 5, None, True)
+        grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True)
+        outs.append([t.clone() for t in (kl, l1, l2, *sk, *grads)])
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_gradient_pairs_can_be_skipped():
+    q1, k1, q2, k2 = _rand(1, 2, 200, 300, 128, torch.bfloat16, seed=8)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, False)
+    g = torch.full((1, 2, 200), 0.01, device=DEV)
+    full = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g)
+    t_only = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, student=False)
+    s_only = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, teacher=False)
+    torch.cuda.synchronize()
+    assert t_only[2] is None and s_only[0] is None
+    assert torch.equal(t_only[0], full[0]) and torch.equal(t_only[1], full[1])
+    assert torch.equal(s_only[2], full[2]) and torch.equal(s_only[3], full[3])
+
+
+def test_autograd_function():
+    q1, k1, q2, k2 = _rand(1, 2, 130, 260, 64, torch.float32, seed=9)
+    ts = [t.clone().requires_grad_(True) for t in (q1, k1, q2, k2)]
+    kl = attention_kl(*ts, causal=True)
+    (kl * 0.5).sum().backward()
+    kl2, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, True)
+    ref = streamkl_bwd(q1, k1, q2, k2, kl2, l1, l2, torch.full_like(kl2, 0.5), None, True)
+    for t, r in zip(ts, ref):
+        assert torch.equal(t.grad, r)
+
+
+def test_errors_surface_as_exceptions():
+    q1, k1, q2, k2 = _rand(1, 1, 16, 8, 128, torch.bfloat16, seed=10)
+    with pytest.raises(StreamKLError):
+        streamkl_fwd(q1, k1, q2, k2, None, True)  # causal with NQ > NK
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def _full_size(name, rows_per_head=48, heads=None, bwd=True):
+    w = synth.get(name)
+    print(f"workload {name}", flush=True)
+    q1, k1, q2, k2 = synth.make_inputs(w, device=DEV)
+    heads = heads or [(0, 0), (w.B - 1, w.H - 1)]
+    rows = sample_rows(w.NQ, rows_per_head, seed=w.cfg_id)
+    if w.splits > 1:
+        kl, l1, l2 = streamkl_fwd_splitk(q1, k1, q2, k2, w.splits, w.scale, w.causal)
+    else:
+        kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(kl).all() and torch.isfinite(l1).all() and torch.isfinite(l2).all()
+    assert (kl >= -1e-5).all()
+    assert_within(compare_forward(q1, k1, q2, k2, w.scale, w.causal, kl, l1, l2, heads, rows),
+                  TOL[w.dtype], f"{name} fwd")
+    if not bwd:
+        return
+    g = synth.upstream_grad(w, DEV)
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal)
+    torch.cuda.synchronize()
+    for t in grads:
+        assert torch.isfinite(t).all()
+    assert_within(compare_backward(q1, k1, q2, k2, w.scale, w.causal, g, grads, heads, rows, check_dk=False),
+                  TOL[w.dtype], f"{name} dq")
+    # Any-size invariant: key gradients of each head sum to zero.
+    for dk in (grads[1], grads[3]):
+        colsum = dk.double().sum(2).abs().max().item()
+        assert colsum <= 1e-3 * dk.abs().max().item() * math.sqrt(w.NK), colsum
+    del grads
+    # Full dK check with g nonzero only on the sampled rows.
+    gs = torch.zeros_like(g)
+    gs[:, :, rows] = g[:, :, rows]
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, gs, w.scale, w.causal)
+    torch.cuda.synchronize()
+    assert_within(compare_backward(q1, k1, q2, k2, w.scale, w.causal, gs, grads, heads, rows, check_dk=True),
+                  TOL[w.dtype], f"{name} dk (sampled g)")
+
+
+def test_causal_4k_full_size():
+    _full_size("causal_4k")
+
+
+def test_noncausal_16k_full_size():
+    _full_size("noncausal_16k")
+
+
+def test_causal_64k_full_size():
+    _full_size("causal_64k", rows_per_head=24)
+
+
+def test_splitk_512k_forward_full_size():
+    _full_size("splitk_512k", rows_per_head=24, bwd=False)
+
+
+def test_splitk_bwd_128k_full_size():
+    _full_size("splitk_bwd_128k", rows_per_head=24)
