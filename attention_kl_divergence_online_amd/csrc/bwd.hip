@@ -27,6 +27,8 @@
 // 11 bits.  dS is scaled by a per-(b,h) power of two sigma with
 // max|g| * sigma in [2^7, 2^8) so it sits in fp16's normal range; the factor
 // is divided out exactly at the end.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -53,7 +55,7 @@ struct BwdTraits {
   static constexpr int IPT = (ITEMS + 255) / 256;
   static constexpr int XROW_BYTES = BX * XROW;
   static constexpr int XT_BYTES = D * XT_STRIDE;
-  static constexpr int STAT_BYTES = KEYS_RES ? 4 * BX * 4 : 0;
+  static constexpr int STAT_BYTES = KEYS_RES ? 3 * BX * 4 : 0;
   static constexpr int OFF_XT = 2 * XROW_BYTES;
   static constexpr int OFF_STAT = 2 * XROW_BYTES + 2 * XT_BYTES;
   static constexpr int STAGE_BYTES = OFF_STAT + STAT_BYTES;
@@ -65,10 +67,30 @@ struct BwdTraits {
 
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float clamp_f16(float x) { return __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f); }
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   const f16x2 v = {(f16)a, (f16)b};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Exponent offset for rows with g = 0: every exp2 underflows to 0 and the
+// log-ratio difference (y1 - y2) stays finite (both offsets equal).
+constexpr float kNoGrad = 1.0e30f;
+
+// Per-query constants of the recomputation.  |g| * sigma is folded into the
+// exponent offsets, so exp2(x * scale * log2e - b) is already P * |g| * sigma:
+//   b_t = LSE_t * log2e - log2(|g| * sigma),  kl = KL,  sg = sign(g).
+__device__ __forceinline__ void query_stats(float lse1, float lse2, float kl, float g, float sigma, float &b1,
+                                            float &b2, float &klo, float &sg) {
+  const float ag = fabsf(g) * sigma;
+  sg = g < 0.f ? -1.f : 1.f;
+  klo = kl;
+  if (ag > 0.f) {
+    const float lg = __log2f(ag);
+    b1 = __builtin_fmaf(lse1, kLog2e, -lg);
+    b2 = __builtin_fmaf(lse2, kLog2e, -lg);
+  } else {
+    b1 = b2 = kNoGrad;
+  }
 }
 
 template <typename T, int D, bool KEYS_RES>
@@ -105,7 +127,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   const float *LS1 = p.lse1 + bh * (int64_t)NQ;
   const float *LS2 = p.lse2 + bh * (int64_t)NQ;
   const float *Gr = p.g + bh * (int64_t)NQ;
-  const float sigma = p.sigma[bh];
+  // Prepared per-head factor; stored negated when some g of the head is negative.
+  const float sigma_raw = p.sigma[bh];
+  const float sigma = fabsf(sigma_raw);
+  const bool any_neg = sigma_raw < 0.f;
 
   const int r0 = rt * Tr::BR;
   const int rlast_wg = min(r0 + Tr::BR, NR) - 1;
@@ -134,14 +159,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   }
 
   const float c = p.scale * kLog2e;
-  // Per-query statistics when queries are resident: exponent offsets LSE*log2e, KL, g*sigma.
-  float qb1 = 0.f, qb2 = 0.f, qkl = 0.f, qgs = 0.f;
-  if (!KEYS_RES && r_ok) {
-    qb1 = LS1[my_r] * kLog2e;
-    qb2 = LS2[my_r] * kLog2e;
-    qkl = KLr[my_r];
-    qgs = Gr[my_r] * sigma;
-  }
+  // Per-query statistics when queries are resident (see query_stats).
+  float qb1 = kNoGrad, qb2 = kNoGrad, qkl = 0.f, qsg = 1.f;
+  if (!KEYS_RES && r_ok) query_stats(LS1[my_r], LS2[my_r], KLr[my_r], Gr[my_r], sigma, qb1, qb2, qkl, qsg);
 
   f32x16 acc1[Tr::NDB], acc2[Tr::NDB];
 #pragma unroll
@@ -152,7 +172,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 
   // ---- staging: global -> registers -> LDS (row-major copy + transposed copy) ----
   u32x4 st[Tr::IPT][2][4];
-  float sv[4];
+  float sv[3];
+  // Key-resident pass: rows of the streamed Q tile whose g is negative are
+  // stored negated in the transposed copy, which carries sign(g) into dK.
+  uint32_t sgn[Tr::IPT][2];
   auto gload = [&](int t) {
     const int xb0 = x_lo + t * Tr::BX;
 #pragma unroll
@@ -167,17 +190,26 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
         st[k][0][u] = ok ? *reinterpret_cast<const u32x4 *>(X1 + o) : u32x4{0u, 0u, 0u, 0u};
         st[k][1][u] = ok ? *reinterpret_cast<const u32x4 *>(X2 + o) : u32x4{0u, 0u, 0u, 0u};
       }
+      if (KEYS_RES) {
+        sgn[k][0] = sgn[k][1] = 0u;
+        if (any_neg) {
+          uint32_t m[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int row = xb0 + 4 * a + u;
+            m[u] = (item < Tr::ITEMS && row < NX && Gr[row] < 0.f) ? 1u : 0u;
+          }
+          sgn[k][0] = (m[0] << 15) | (m[1] << 31);
+          sgn[k][1] = (m[2] << 15) | (m[3] << 31);
+        }
+      }
     }
     if (KEYS_RES && tid < Tr::BX) {
       const int q = xb0 + tid;
-      if (q < NQ) {
-        sv[0] = LS1[q] * kLog2e;
-        sv[1] = LS2[q] * kLog2e;
-        sv[2] = KLr[q];
-        sv[3] = Gr[q] * sigma;
-      } else {
-        sv[0] = sv[1] = sv[2] = sv[3] = 0.f;
-      }
+      float sg;
+      sv[0] = sv[1] = kNoGrad;
+      sv[2] = 0.f;
+      if (q < NQ) query_stats(LS1[q], LS2[q], KLr[q], Gr[q], sigma, sv[0], sv[1], sv[2], sg);
     }
   };
   auto sstore = [&](int buf) {
@@ -202,16 +234,26 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const uint32_t w = st[k][t2][u][e >> 1];
-              v[u] = clamp_f16((e & 1) ? bf16hi_to_f32(w) : bf16lo_to_f32(w));
+              v[u] = (e & 1) ? bf16hi_to_f32(w) : bf16lo_to_f32(w);
             }
-            const u32x2 pk = {pack_f16(v[0], v[1]), pack_f16(v[2], v[3])};
+            u32x2 pk = {pack_f16(v[0], v[1]), pack_f16(v[2], v[3])};
+            if (KEYS_RES && any_neg) {
+              pk[0] ^= sgn[k][0];
+              pk[1] ^= sgn[k][1];
+            }
             *reinterpret_cast<u32x2 *>(xt + (8 * cc + e) * Tr::XT_STRIDE + 4 * a * 2) = pk;
           }
         } else {
           // 4 fp32 columns d = 4cc + e of rows 4a..4a+3, 16-byte stores.
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const u32x4 col = {st[k][t2][0][e], st[k][t2][1][e], st[k][t2][2][e], st[k][t2][3][e]};
+            u32x4 col = {st[k][t2][0][e], st[k][t2][1][e], st[k][t2][2][e], st[k][t2][3][e]};
+            if (KEYS_RES && any_neg) {
+              col[0] ^= (sgn[k][0] & 0x8000u) << 16;
+              col[1] ^= sgn[k][0] & 0x80000000u;
+              col[2] ^= (sgn[k][1] & 0x8000u) << 16;
+              col[3] ^= sgn[k][1] & 0x80000000u;
+            }
             *reinterpret_cast<u32x4 *>(xt + (4 * cc + e) * Tr::XT_STRIDE + 4 * a * 4) = col;
           }
         }
@@ -220,7 +262,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     if (KEYS_RES && tid < Tr::BX) {
       float *sb = reinterpret_cast<float *>(base + Tr::OFF_STAT);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) sb[f * Tr::BX + tid] = sv[f];
+      for (int f = 0; f < 3; ++f) sb[f * Tr::BX + tid] = sv[f];
     }
   };
 
@@ -230,119 +272,150 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) gload(t + 1);
-    const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
+  // One 32-row block of the streamed tile at `base`: logits, dS, gradient products.
+  // MASK is false when every (query, key) pair of the block is visible.
+  auto block = [&](const char *base, int xb, int xa, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // Logits block: lane = resident row, element r = streamed row xa + acc_row(r, h).
+    f32x16 x1 = f32x16{}, x2 = f32x16{};
+    {
+      const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 8 * h * (int)sizeof(T);
+      const char *a2p = a1p + Tr::XROW_BYTES;
 #pragma unroll
-    for (int xb = 0; xb < Tr::XB; ++xb) {
-      const int xa = x_lo + t * Tr::BX + xb * 32;  // streamed rows [xa, xa + 32)
-      bool full, empty;
-      if (KEYS_RES) {  // resident keys j, streamed queries i
-        full = xa + 31 < NQ && ra + 31 < NK && (!p.causal || ra + 31 <= xa + off);
-        empty = xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
-      } else {  // resident queries i, streamed keys j
-        full = ra + 31 < NQ && xa + 31 < NK && (!p.causal || xa + 31 <= ra + off);
-        empty = ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
-      }
-      if (empty) continue;
-
-      // Logits block: lane = resident row, element r = streamed row xa + acc_row(r, h).
-      f32x16 x1 = f32x16{}, x2 = f32x16{};
-      {
-        const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 8 * h * (int)sizeof(T);
-        const char *a2p = a1p + Tr::XROW_BYTES;
-#pragma unroll
-        for (int s = 0; s < Tr::KSTEPS; ++s) {
-          const CT a1 = *reinterpret_cast<const CT *>(a1p + 16 * s * (int)sizeof(T));
-          const CT a2 = *reinterpret_cast<const CT *>(a2p + 16 * s * (int)sizeof(T));
-          x1 = mma16(a1, rf1[s], x1);
-          x2 = mma16(a2, rf2[s], x2);
-        }
-      }
-
-      // dS, elementwise.
-      f32x16 d1, d2;
-      const float *sb = reinterpret_cast<const float *>(base + Tr::OFF_STAT);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 B1, B2, KV, GS;
-        if (KEYS_RES) {
-          const int q = xb * 32 + 8 * j + 4 * h;
-          B1 = *reinterpret_cast<const f32x4 *>(sb + 0 * Tr::BX + q);
-          B2 = *reinterpret_cast<const f32x4 *>(sb + 1 * Tr::BX + q);
-          KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
-          GS = *reinterpret_cast<const f32x4 *>(sb + 3 * Tr::BX + q);
-        } else {
-          B1 = f32x4{qb1, qb1, qb1, qb1};
-          B2 = f32x4{qb2, qb2, qb2, qb2};
-          KV = f32x4{qkl, qkl, qkl, qkl};
-          GS = f32x4{qgs, qgs, qgs, qgs};
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * j + u;
-          const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
-          const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
-          const float p1 = fast_exp2(y1);
-          const float p2 = fast_exp2(y2);
-          const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
-          float v2 = GS[u] * (p2 - p1);
-          float v1 = (GS[u] * p1) * dl;
-          if (!full) {
-            const int srow = xa + acc_row(r, h);
-            const int qi = KEYS_RES ? srow : my_r;
-            const int kj = KEYS_RES ? my_r : srow;
-            const bool vis = qi < NQ && kj < NK && (!p.causal || kj <= qi + off);
-            v1 = vis ? v1 : 0.f;
-            v2 = vis ? v2 : 0.f;
-          }
-          d1[r] = v1;
-          d2[r] = v2;
-        }
-      }
-
-      // Gradient product dR^T[d, resident] += X^T[d, streamed] * dS[streamed, resident].
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        CG b1, b2;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          b1[u] = (G)d1[8 * ks + u];
-          b2[u] = (G)d2[8 * ks + u];
-        }
-        const int so = xb * 32 + 16 * ks + 4 * h;  // streamed-row offset of slots 0..3 (slots 4..7: +8)
-#pragma unroll
-        for (int db = 0; db < Tr::NDB; ++db) {
-          const char *t1 = base + Tr::OFF_XT + (db * 32 + c32) * Tr::XT_STRIDE + so * (int)sizeof(G);
-          const char *t2 = t1 + Tr::XT_BYTES;
-          CG a1, a2;
-          if constexpr (sizeof(G) == 2) {
-            const f16x4 l1 = *reinterpret_cast<const f16x4 *>(t1);
-            const f16x4 h1 = *reinterpret_cast<const f16x4 *>(t1 + 16);
-            const f16x4 l2 = *reinterpret_cast<const f16x4 *>(t2);
-            const f16x4 h2 = *reinterpret_cast<const f16x4 *>(t2 + 16);
-            a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-            a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
-          } else {
-            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(t1);
-            const f32x4 h1 = *reinterpret_cast<const f32x4 *>(t1 + 32);
-            const f32x4 l2 = *reinterpret_cast<const f32x4 *>(t2);
-            const f32x4 h2 = *reinterpret_cast<const f32x4 *>(t2 + 32);
-            a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-            a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-          if (p.want1) acc1[db] = mma16(a1, b1, acc1[db]);
-          if (p.want2) acc2[db] = mma16(a2, b2, acc2[db]);
-        }
+      for (int s = 0; s < Tr::KSTEPS; ++s) {
+        const CT a1 = *reinterpret_cast<const CT *>(a1p + 16 * s * (int)sizeof(T));
+        const CT a2 = *reinterpret_cast<const CT *>(a2p + 16 * s * (int)sizeof(T));
+        x1 = mma16(a1, rf1[s], x1);
+        x2 = mma16(a2, rf2[s], x2);
       }
     }
-    if (t + 1 < ntiles) sstore((t + 1) & 1);
-    __syncthreads();
+    // dS, elementwise.
+    f32x16 d1, d2;
+    const float *sb = reinterpret_cast<const float *>(base + Tr::OFF_STAT);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 B1, B2, KV;
+      if (KEYS_RES) {
+        const int q = xb * 32 + 8 * j + 4 * h;
+        B1 = *reinterpret_cast<const f32x4 *>(sb + 0 * Tr::BX + q);
+        B2 = *reinterpret_cast<const f32x4 *>(sb + 1 * Tr::BX + q);
+        KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
+      } else {
+        B1 = f32x4{qb1, qb1, qb1, qb1};
+        B2 = f32x4{qb2, qb2, qb2, qb2};
+        KV = f32x4{qkl, qkl, qkl, qkl};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * j + u;
+        // p_t = P_t * |g| * sigma; (y1 - y2) * ln 2 = (s1 - LSE1) - (s2 - LSE2).
+        const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
+        const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
+        const float p1 = fast_exp2(y1);
+        const float p2 = fast_exp2(y2);
+        const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
+        float v2 = p2 - p1;
+        float v1 = p1 * dl;
+        if (MASK) {
+          const int srow = xa + acc_row(r, h);
+          const int qi = KEYS_RES ? srow : my_r;
+          const int kj = KEYS_RES ? my_r : srow;
+          const bool vis = qi < NQ && kj < NK && (!p.causal || kj <= qi + off);
+          v1 = vis ? v1 : 0.f;
+          v2 = vis ? v2 : 0.f;
+        }
+        d1[r] = v1;
+        d2[r] = v2;
+      }
+    }
+    // Gradient product dR^T[d, resident] += X^T[d, streamed] * dS[streamed, resident].
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      CG b1, b2;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        b1[u] = (G)d1[8 * ks + u];
+        b2[u] = (G)d2[8 * ks + u];
+      }
+      const int so = xb * 32 + 16 * ks + 4 * h;  // streamed-row offset of slots 0..3 (slots 4..7: +8)
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+        const char *t1 = base + Tr::OFF_XT + (db * 32 + c32) * Tr::XT_STRIDE + so * (int)sizeof(G);
+        const char *t2 = t1 + Tr::XT_BYTES;
+        CG a1, a2;
+        if constexpr (sizeof(G) == 2) {
+          const f16x4 l1 = *reinterpret_cast<const f16x4 *>(t1);
+          const f16x4 h1 = *reinterpret_cast<const f16x4 *>(t1 + 16);
+          const f16x4 l2 = *reinterpret_cast<const f16x4 *>(t2);
+          const f16x4 h2 = *reinterpret_cast<const f16x4 *>(t2 + 16);
+          a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+          a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          const f32x4 l1 = *reinterpret_cast<const f32x4 *>(t1);
+          const f32x4 h1 = *reinterpret_cast<const f32x4 *>(t1 + 32);
+          const f32x4 l2 = *reinterpret_cast<const f32x4 *>(t2);
+          const f32x4 h2 = *reinterpret_cast<const f32x4 *>(t2 + 32);
+          a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+          a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        acc1[db] = mma16(a1, b1, acc1[db]);
+        acc2[db] = mma16(a2, b2, acc2[db]);
+      }
+    }
+  };
+
+  // Streamed tiles in which every (query, key) pair of the workgroup is
+  // visible form one contiguous run [t_a, t_b): under the causal mask the
+  // diagonal tiles come first (key-resident pass) or last (query-resident
+  // pass), and a ragged streamed tail is always last.  The run is processed
+  // without any mask test; the tiles around it test every block.
+  int t_a = 0, t_b = 0;
+  {
+    const int rlast = r0 + Tr::BR - 1;  // all resident rows of the tile, valid or not
+    auto tile_full = [&](int t) {
+      const int xt = x_lo + t * Tr::BX, xl = xt + Tr::BX - 1;
+      if (KEYS_RES) return xl < NQ && rlast < NK && (!p.causal || rlast <= xt + off);
+      return rlast < NQ && xl < NK && (!p.causal || xl <= r0 + off);
+    };
+    // Full tiles are contiguous, so a linear scan from each end finds the run.
+    int a = 0;
+    while (a < ntiles && !tile_full(a)) ++a;
+    int b = a;
+    while (b < ntiles && tile_full(b)) ++b;
+    t_a = a;
+    t_b = b;
   }
+
+  auto run_tiles = [&](int t0, int t1, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    for (int t = t0; t < t1; ++t) {
+      if (t + 1 < ntiles) gload(t + 1);
+      const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
+#pragma unroll
+      for (int xb = 0; xb < Tr::XB; ++xb) {
+        const int xa = x_lo + t * Tr::BX + xb * 32;  // streamed rows [xa, xa + 32)
+        if (!MASK) {
+          block(base, xb, xa, std::integral_constant<bool, false>{});
+          continue;
+        }
+        bool empty;
+        if (KEYS_RES)  // resident keys j, streamed queries i
+          empty = xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
+        else  // resident queries i, streamed keys j
+          empty = ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
+        if (!empty) block(base, xb, xa, std::integral_constant<bool, true>{});
+      }
+      if (t + 1 < ntiles) sstore((t + 1) & 1);
+      __syncthreads();
+    }
+  };
+  run_tiles(0, t_a, std::integral_constant<bool, true>{});
+  run_tiles(t_a, t_b, std::integral_constant<bool, false>{});
+  run_tiles(t_b, ntiles, std::integral_constant<bool, true>{});
 
   // Epilogue: lane writes its resident row, d = db*32 + 8j + 4h + (0..3).
   if (r_ok) {
-    const float f = p.scale / sigma;
+    const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
     float *O1 = KEYS_RES ? p.dk1 : p.dq1;
     float *O2 = KEYS_RES ? p.dk2 : p.dq2;
     const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
@@ -367,30 +440,48 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
 }
 
 // sigma[b,h] = 2^(kGradExp - e) with 2^(e-1) <= max_i |g[b,h,i]| < 2^e (1 if g is all zero,
-// and 1 everywhere when `unit` is set: fp32 inputs need no scaling).
+// and 1 everywhere when `unit` is set: fp32 inputs need no scaling), stored
+// negated when some g[b,h,:] is negative.
 __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, int64_t NQ, float *sigma, int unit) {
   const int64_t bh = blockIdx.x;
   if (unit) {
-    if (threadIdx.x == 0) sigma[bh] = 1.f;
+    // fp32 inputs: no dS scaling, but the sign flag is still needed.
+    const float *gu = g + bh * NQ;
+    int neg = 0;
+    for (int64_t i = threadIdx.x; i < NQ; i += 256) neg |= gu[i] < 0.f;
+    neg = __syncthreads_or(neg);
+    if (threadIdx.x == 0) sigma[bh] = neg ? -1.f : 1.f;
     return;
   }
   const float *gp = g + bh * NQ;
   float m = 0.f;
-  for (int64_t i = threadIdx.x; i < NQ; i += 256) m = fmaxf(m, fabsf(gp[i]));
+  int neg = 0;
+  for (int64_t i = threadIdx.x; i < NQ; i += 256) {
+    m = fmaxf(m, fabsf(gp[i]));
+    neg |= gp[i] < 0.f;
+  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  for (int o = 32; o > 0; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o));
+    neg |= __shfl_xor(neg, o);
+  }
   __shared__ float red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __shared__ int rneg[4];
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = m;
+    rneg[threadIdx.x >> 6] = neg;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    neg = rneg[0] | rneg[1] | rneg[2] | rneg[3];
     float s = 1.f;
     if (m > 0.f && m <= 3.4e38f) {
       int k = kGradExp - (ilogbf(m) + 1);
       k = min(max(k, -126), 126);
       s = ldexpf(1.f, k);
     }
-    sigma[bh] = s;
+    sigma[bh] = neg ? -s : s;
   }
 }
 

@@ -24,21 +24,37 @@
 
 namespace skl {
 
+#ifndef SKL_FWD_WAVES
+#define SKL_FWD_WAVES 8
+#endif
+#ifndef SKL_FWD_QB
+#define SKL_FWD_QB 1
+#endif
+#ifndef SKL_FWD_BK
+#define SKL_FWD_BK 64
+#endif
+
+
+constexpr int kFwdThreads = SKL_FWD_WAVES * 64;
+
 template <typename T, int D>
 struct FwdTraits {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = SKL_FWD_WAVES;
   // 32-query blocks per wave (fp32 at D=128 keeps one so its fragments fit in registers)
-  static constexpr int QB = (sizeof(T) == 4 && D == 128) ? 1 : 2;
+  static constexpr int QB = (sizeof(T) == 4 && D == 128) ? 1 : SKL_FWD_QB;
+  static constexpr int NT = WAVES * 64;
   static constexpr int BQ = WAVES * QB * 32;
-  static constexpr int BK = kFwdBK;
+  // Keys per LDS stage (fp32 at D=128 keeps 64 to fit two stages in LDS).
+  static constexpr int BK = (sizeof(T) == 4 && D == 128) ? 64 : SKL_FWD_BK;
+  static constexpr int NB = BK / 32;  // 32-key blocks per stage
   static constexpr int KSTEPS = D / 16;
   static constexpr int ROW_BYTES = D * (int)sizeof(T);
   static constexpr int LDS_ROW = ROW_BYTES + 16;
   static constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per row
-  static constexpr int LOADS = BK * CPR / (WAVES * 64);
+  static constexpr int LOADS = BK * CPR / NT;
   static constexpr int STAGE_BYTES = 2 * BK * LDS_ROW;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static_assert(LOADS * WAVES * 64 == BK * CPR, "staging split");
+  static_assert(LOADS * NT == BK * CPR, "staging split");
 };
 
 // v + cv carries a running sum; replace it by a * (v + cv) + s.  The product
@@ -119,7 +135,7 @@ __device__ __forceinline__ void finish_row(float m1, float l1, float m2, float l
 }
 
 template <typename T, int D, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
   using Tr = FwdTraits<T, D>;
   using CT = chunk_t<T>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -195,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     const int kb0 = k_lo + t * Tr::BK;
 #pragma unroll
     for (int i = 0; i < Tr::LOADS; ++i) {
-      const int cidx = tid + 256 * i;
+      const int cidx = tid + Tr::NT * i;
       const int row = cidx / Tr::CPR, col = cidx % Tr::CPR;
       const int key = kb0 + row;
       if (key < NK) {
@@ -211,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     char *base = smem + buf * Tr::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < Tr::LOADS; ++i) {
-      const int cidx = tid + 256 * i;
+      const int cidx = tid + Tr::NT * i;
       const int row = cidx / Tr::CPR, col = cidx % Tr::CPR;
       *reinterpret_cast<u32x4 *>(base + row * Tr::LDS_ROW + col * 16) = stg1[i];
       *reinterpret_cast<u32x4 *>(base + Tr::BK * Tr::LDS_ROW + row * Tr::LDS_ROW + col * 16) = stg2[i];
@@ -224,34 +240,38 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   }
   __syncthreads();
 
+  // Scores of one 32-key block of the stage at `base` for every query block of the wave.
+  auto block_scores = [&](const char *base, int kb, f32x16 *s1, f32x16 *s2) {
+#pragma unroll
+    for (int qb = 0; qb < Tr::QB; ++qb) {
+      s1[qb] = f32x16{};
+      s2[qb] = f32x16{};
+    }
+    const char *r1 = base + (kb * 32 + c32) * Tr::LDS_ROW + 8 * h * (int)sizeof(T);
+    const char *r2 = r1 + Tr::BK * Tr::LDS_ROW;
+#pragma unroll
+    for (int s = 0; s < Tr::KSTEPS; ++s) {
+      const CT a1 = *reinterpret_cast<const CT *>(r1 + 16 * s * (int)sizeof(T));
+      const CT a2 = *reinterpret_cast<const CT *>(r2 + 16 * s * (int)sizeof(T));
+#pragma unroll
+      for (int qb = 0; qb < Tr::QB; ++qb) {
+        s1[qb] = mma16(a1, qf1[qb][s], s1[qb]);
+        s2[qb] = mma16(a2, qf2[qb][s], s2[qb]);
+      }
+    }
+  };
+
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) gload(t + 1);
     const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
     if (wave_live) {
 #pragma unroll
-      for (int kb = 0; kb < Tr::BK / 32; ++kb) {
+      for (int kb = 0; kb < Tr::NB; ++kb) {
         const int kbase = k_lo + t * Tr::BK + kb * 32;
         if (kbase >= vis_any) continue;
-        const bool full = kbase + 32 <= vis_all;
         f32x16 s1[Tr::QB], s2[Tr::QB];
-#pragma unroll
-        for (int qb = 0; qb < Tr::QB; ++qb) {
-          s1[qb] = f32x16{};
-          s2[qb] = f32x16{};
-        }
-        const char *r1 = base + (kb * 32 + c32) * Tr::LDS_ROW + 8 * h * (int)sizeof(T);
-        const char *r2 = r1 + Tr::BK * Tr::LDS_ROW;
-#pragma unroll
-        for (int s = 0; s < Tr::KSTEPS; ++s) {
-          const CT a1 = *reinterpret_cast<const CT *>(r1 + 16 * s * (int)sizeof(T));
-          const CT a2 = *reinterpret_cast<const CT *>(r2 + 16 * s * (int)sizeof(T));
-#pragma unroll
-          for (int qb = 0; qb < Tr::QB; ++qb) {
-            s1[qb] = mma16(a1, qf1[qb][s], s1[qb]);
-            s2[qb] = mma16(a2, qf2[qb][s], s2[qb]);
-          }
-        }
-        if (full) {
+        block_scores(base, kb, s1, s2);
+        if (kbase + 32 <= vis_all) {
 #pragma unroll
           for (int qb = 0; qb < Tr::QB; ++qb)
             online_update<false, COMP>(s1[qb], s2[qb], st[qb], c, kbase, h, 0);
@@ -339,7 +359,7 @@ static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int64_t nblk = p.BH * (int64_t)p.nqt * p.splits;
-  hipLaunchKernelGGL((fwd_kernel<T, D, SPLIT>), dim3((uint32_t)nblk), dim3(256), Tr::LDS_BYTES, s, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, SPLIT>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
   return hipGetLastError();
 }
 

@@ -128,9 +128,10 @@ size_t streamkl_bwd_workspace_size(const streamkl_problem *p);
  * the same inputs.  Gradient outputs come in pairs: pass dq1 = dk1 = NULL to
  * skip the teacher gradients (teacher fixed) or dq2 = dk2 = NULL to skip the
  * student's; a half-NULL pair is STREAMKL_ERR_NULL.  Outputs are overwritten.
- * The gradient products run on fp16 matrix cores with fp32 accumulation:
- * entries of Q and K above 65504 in magnitude are clamped to the fp16 range
- * for those products.
+ * With bf16 inputs the two gradient products run on fp16 matrix cores with
+ * fp32 accumulation (dS in bf16 would exceed a 2e-3 relative error): entries
+ * of Q and K must lie within the fp16 range, |x| <= 65504; larger entries give
+ * non-finite gradients.
  */
 streamkl_status streamkl_bwd(const streamkl_problem *p,
                              const void *q1, const void *k1,
@@ -149,7 +150,8 @@ streamkl_status streamkl_bwd(const streamkl_problem *p,
  *
  * streamkl_bwd_prepare writes into `workspace` one fp32 per (batch, head): the
  * power of two sigma with max_i |g_i| * sigma in [2^7, 2^8), by which the
- * passes scale dS before rounding it to fp16 (1 for fp32 inputs).
+ * passes scale dS before rounding it to fp16 (1 for fp32 inputs), negated
+ * when some g of that head is negative.
  * streamkl_bwd_dk writes dK1, dK2 (one pass over key tiles, queries streamed);
  * streamkl_bwd_dq writes dQ1, dQ2 (one pass over query tiles, keys streamed).
  * NULL-pair rules, layouts and errors are those of streamkl_bwd; the pass
