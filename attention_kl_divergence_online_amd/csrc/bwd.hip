@@ -15,9 +15,10 @@
 // is the design: one pass keeps a tile of keys resident and streams queries
 // (dK), the other keeps queries resident and streams keys (dQ).  Both are the
 // same kernel template: a wave owns 32 resident rows, whose fragments stay in
-// registers, and 64-row tiles of the streamed operand pass through LDS twice
-// over -- row-major (bf16/fp32) for the logits and transposed (fp16/fp32) for
-// the gradient product.
+// registers, and 64-row tiles of the streamed operand pass through LDS.  With
+// bf16 inputs the tile is staged once, as fp16 rows: the logits product reads
+// rows of it and the gradient product reads columns of it through the
+// transposing LDS loads.  fp32 inputs stage a row-major and a transposed copy.
 //
 // Logits come out as (streamed x resident) accumulator blocks, so a lane holds
 // one resident row and 16 streamed rows; that accumulator is, element for
@@ -26,7 +27,8 @@
 // loses too much (8-bit significand) for the 2e-3 relative bound, fp16 keeps
 // 11 bits.  dS is scaled by a per-(b,h) power of two sigma with
 // max|g| * sigma in [2^7, 2^8) so it sits in fp16's normal range; the factor
-// is divided out exactly at the end.
+// is divided out exactly at the end.  Q and K themselves convert to fp16
+// exactly as long as they lie within the fp16 range.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -39,28 +41,39 @@ template <> struct GradOp<float> { using type = float; };
 
 template <typename T, int D, bool KEYS_RES>
 struct BwdTraits {
+  // bf16 inputs run both products on fp16 operands converted (exactly, within
+  // the fp16 range) from one fp16 row-major copy of the streamed tile; the
+  // gradient product reads it through the transposing LDS loads.  fp32 inputs
+  // keep an fp32 row-major copy plus an fp32 transposed copy.
+  static constexpr bool F16 = sizeof(T) == 2;
   using G = typename GradOp<T>::type;
   static constexpr int WAVES = 4;
-  static constexpr int BR = kBwdBR;                              // resident rows per workgroup
-  static constexpr int BX = (sizeof(T) == 4 && D == 128) ? 32 : 64;  // streamed rows per stage
+  static constexpr int BR = kBwdBR;                        // resident rows per workgroup
+  static constexpr int BX = (!F16 && D == 128) ? 32 : 64;  // streamed rows per stage
   static constexpr int XB = BX / 32;
   static constexpr int KSTEPS = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int ROW_BYTES = D * (int)sizeof(T);
-  static constexpr int XROW = ROW_BYTES + 16;
-  static constexpr int XT_STRIDE = BX * (int)sizeof(G) + (sizeof(G) == 2 ? 8 : 16);
-  static constexpr int CPR = ROW_BYTES / 16;
-  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  static constexpr int ITEMS = (BX / 4) * CPR;     // staging items: 4 rows x 1 chunk
-  static constexpr int IPT = (ITEMS + 255) / 256;
+  static constexpr int ROW_BYTES = D * (int)sizeof(T);  // one row in HBM
+  static constexpr int CPR = ROW_BYTES / 16;            // 16-byte chunks per HBM row
+  static constexpr int ES = (int)sizeof(G);             // element size of the LDS copy
+  // fp16 row stride D*2 + 48 B: the 16 rows of a logits-operand read and the
+  // 4 rows x 32 B of a transposing read both fall in distinct banks.
+  static constexpr int XROW = F16 ? D * 2 + 48 : ROW_BYTES + 16;
+  static constexpr int XT_STRIDE = F16 ? 0 : BX * 4 + 16;
   static constexpr int XROW_BYTES = BX * XROW;
-  static constexpr int XT_BYTES = D * XT_STRIDE;
-  static constexpr int STAT_BYTES = KEYS_RES ? 3 * BX * 4 : 0;
+  static constexpr int XT_BYTES = F16 ? 0 : D * XT_STRIDE;
+  static constexpr int NSTAT = 4;  // b1, b2, KL, sign(g) of each streamed query
+  static constexpr int STAT_BYTES = KEYS_RES ? NSTAT * BX * 4 : 0;
   static constexpr int OFF_XT = 2 * XROW_BYTES;
-  static constexpr int OFF_STAT = 2 * XROW_BYTES + 2 * XT_BYTES;
+  static constexpr int OFF_STAT = OFF_XT + 2 * XT_BYTES;
   static constexpr int STAGE_BYTES = OFF_STAT + STAT_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  // Staging work per thread: bf16 -> 16-byte chunks; fp32 -> items of 4 rows x 1 chunk.
+  static constexpr int CPT = F16 ? BX * CPR / 256 : 1;
+  static constexpr int ITEMS = (BX / 4) * CPR;
+  static constexpr int IPT = F16 ? 1 : (ITEMS + 255) / 256;
   static_assert(BR == WAVES * 32, "resident tile");
+  static_assert(!F16 || CPT * 256 == BX * CPR, "staging split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(XROW_BYTES % 16 == 0 && XT_BYTES % 16 == 0, "LDS alignment");
 };
@@ -70,6 +83,23 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_fl
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   const f16x2 v = {(f16)a, (f16)b};
   return __builtin_bit_cast(uint32_t, v);
+}
+// Eight bf16 -> eight fp16 (round to nearest even; exact inside the fp16 range).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_f16(bf16lo_to_f32(w[i]), bf16hi_to_f32(w[i]));
+  return o;
+}
+
+// Four consecutive-row fp16 elements of one column, gathered by the
+// transposing LDS load: within each 16-lane group, lane 4k + q reads 8 bytes
+// at `p` and lane i receives element i%4 of the reads of lanes 4k + i/4.
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+__device__ __forceinline__ f16x4 lds_read_tr16(const char *p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+  return __builtin_bit_cast(f16x4, v);
 }
 
 // Exponent offset for rows with g = 0: every exp2 underflows to 0 and the
@@ -97,7 +127,6 @@ template <typename T, int D, bool KEYS_RES>
 __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   using Tr = BwdTraits<T, D, KEYS_RES>;
   using G = typename Tr::G;
-  using CT = chunk_t<T>;
   using CG = chunk_t<G>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -150,12 +179,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   }
   const int ntiles = x_hi > x_lo ? (x_hi - x_lo + Tr::BX - 1) / Tr::BX : 0;
 
-  // Resident fragments (B operand of the logits product).
-  CT rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
+  // Resident fragments (B operand of the logits product): lane's row, elements [16s + 8h, +8).
+  CG rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
 #pragma unroll
   for (int s = 0; s < Tr::KSTEPS; ++s) {
-    rf1[s] = r_ok ? load_chunk<T>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : CT{};
-    rf2[s] = r_ok ? load_chunk<T>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : CT{};
+    if constexpr (Tr::F16) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 w1 = r_ok ? *reinterpret_cast<const u32x4 *>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : z;
+      const u32x4 w2 = r_ok ? *reinterpret_cast<const u32x4 *>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : z;
+      rf1[s] = __builtin_bit_cast(CG, bf16x8_to_f16x8(w1));
+      rf2[s] = __builtin_bit_cast(CG, bf16x8_to_f16x8(w2));
+    } else {
+      rf1[s] = r_ok ? load_chunk<T>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : CG{};
+      rf2[s] = r_ok ? load_chunk<T>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : CG{};
+    }
   }
 
   const float c = p.scale * kLog2e;
@@ -163,97 +200,74 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   float qb1 = kNoGrad, qb2 = kNoGrad, qkl = 0.f, qsg = 1.f;
   if (!KEYS_RES && r_ok) query_stats(LS1[my_r], LS2[my_r], KLr[my_r], Gr[my_r], sigma, qb1, qb2, qkl, qsg);
 
-  f32x16 acc1[Tr::NDB], acc2[Tr::NDB];
-#pragma unroll
-  for (int db = 0; db < Tr::NDB; ++db) {
-    acc1[db] = f32x16{};
-    acc2[db] = f32x16{};
-  }
-
-  // ---- staging: global -> registers -> LDS (row-major copy + transposed copy) ----
-  u32x4 st[Tr::IPT][2][4];
-  float sv[3];
-  // Key-resident pass: rows of the streamed Q tile whose g is negative are
-  // stored negated in the transposed copy, which carries sign(g) into dK.
-  uint32_t sgn[Tr::IPT][2];
+  // ---- staging: global -> registers -> LDS ----
+  u32x4 st[2][Tr::F16 ? Tr::CPT : 4 * Tr::IPT];
+  float sv[Tr::NSTAT];
   auto gload = [&](int t) {
     const int xb0 = x_lo + t * Tr::BX;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if constexpr (Tr::F16) {
 #pragma unroll
-    for (int k = 0; k < Tr::IPT; ++k) {
-      const int item = tid + 256 * k;
-      const int cc = item % Tr::CPR, a = item / Tr::CPR;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = xb0 + 4 * a + u;
-        const bool ok = (item < Tr::ITEMS) && row < NX;
-        const int64_t o = (int64_t)row * Tr::ROW_BYTES + cc * 16;
-        st[k][0][u] = ok ? *reinterpret_cast<const u32x4 *>(X1 + o) : u32x4{0u, 0u, 0u, 0u};
-        st[k][1][u] = ok ? *reinterpret_cast<const u32x4 *>(X2 + o) : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < Tr::CPT; ++i) {
+        const int cidx = tid + 256 * i;
+        const int row = xb0 + cidx / Tr::CPR, col = cidx % Tr::CPR;
+        const int64_t o = (int64_t)row * Tr::ROW_BYTES + col * 16;
+        st[0][i] = row < NX ? *reinterpret_cast<const u32x4 *>(X1 + o) : z;
+        st[1][i] = row < NX ? *reinterpret_cast<const u32x4 *>(X2 + o) : z;
       }
-      if (KEYS_RES) {
-        sgn[k][0] = sgn[k][1] = 0u;
-        if (any_neg) {
-          uint32_t m[4];
+    } else {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int row = xb0 + 4 * a + u;
-            m[u] = (item < Tr::ITEMS && row < NX && Gr[row] < 0.f) ? 1u : 0u;
-          }
-          sgn[k][0] = (m[0] << 15) | (m[1] << 31);
-          sgn[k][1] = (m[2] << 15) | (m[3] << 31);
+      for (int k = 0; k < Tr::IPT; ++k) {
+        const int item = tid + 256 * k;
+        const int cc = item % Tr::CPR, a = item / Tr::CPR;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = xb0 + 4 * a + u;
+          const bool ok = (item < Tr::ITEMS) && row < NX;
+          const int64_t o = (int64_t)row * Tr::ROW_BYTES + cc * 16;
+          st[0][4 * k + u] = ok ? *reinterpret_cast<const u32x4 *>(X1 + o) : z;
+          st[1][4 * k + u] = ok ? *reinterpret_cast<const u32x4 *>(X2 + o) : z;
         }
       }
     }
     if (KEYS_RES && tid < Tr::BX) {
       const int q = xb0 + tid;
-      float sg;
       sv[0] = sv[1] = kNoGrad;
       sv[2] = 0.f;
-      if (q < NQ) query_stats(LS1[q], LS2[q], KLr[q], Gr[q], sigma, sv[0], sv[1], sv[2], sg);
+      sv[3] = 1.f;
+      if (q < NQ) query_stats(LS1[q], LS2[q], KLr[q], Gr[q], sigma, sv[0], sv[1], sv[2], sv[3]);
     }
   };
   auto sstore = [&](int buf) {
     char *base = smem + buf * Tr::STAGE_BYTES;
+    if constexpr (Tr::F16) {
 #pragma unroll
-    for (int k = 0; k < Tr::IPT; ++k) {
-      const int item = tid + 256 * k;
-      if (item >= Tr::ITEMS) continue;
-      const int cc = item % Tr::CPR, a = item / Tr::CPR;
+      for (int i = 0; i < Tr::CPT; ++i) {
+        const int cidx = tid + 256 * i;
+        const int row = cidx / Tr::CPR, col = cidx % Tr::CPR;
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        char *xr = base + t2 * Tr::XROW_BYTES;
-        char *xt = base + Tr::OFF_XT + t2 * Tr::XT_BYTES;
+        for (int t2 = 0; t2 < 2; ++t2)
+          *reinterpret_cast<u32x4 *>(base + t2 * Tr::XROW_BYTES + row * Tr::XROW + col * 16) =
+              bf16x8_to_f16x8(st[t2][i]);
+      }
+    } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          *reinterpret_cast<u32x4 *>(xr + (4 * a + u) * Tr::XROW + cc * 16) = st[k][t2][u];
-        if constexpr (sizeof(T) == 2) {
-          // 8 bf16 columns d = 8cc + e of rows 4a..4a+3 -> fp16, 4 rows per 8-byte store.
+      for (int k = 0; k < Tr::IPT; ++k) {
+        const int item = tid + 256 * k;
+        if (item >= Tr::ITEMS) continue;
+        const int cc = item % Tr::CPR, a = item / Tr::CPR;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float v[4];
+        for (int t2 = 0; t2 < 2; ++t2) {
+          char *xr = base + t2 * Tr::XROW_BYTES;
+          char *xt = base + Tr::OFF_XT + t2 * Tr::XT_BYTES;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint32_t w = st[k][t2][u][e >> 1];
-              v[u] = (e & 1) ? bf16hi_to_f32(w) : bf16lo_to_f32(w);
-            }
-            u32x2 pk = {pack_f16(v[0], v[1]), pack_f16(v[2], v[3])};
-            if (KEYS_RES && any_neg) {
-              pk[0] ^= sgn[k][0];
-              pk[1] ^= sgn[k][1];
-            }
-            *reinterpret_cast<u32x2 *>(xt + (8 * cc + e) * Tr::XT_STRIDE + 4 * a * 2) = pk;
-          }
-        } else {
+          for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<u32x4 *>(xr + (4 * a + u) * Tr::XROW + cc * 16) = st[t2][4 * k + u];
           // 4 fp32 columns d = 4cc + e of rows 4a..4a+3, 16-byte stores.
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            u32x4 col = {st[k][t2][0][e], st[k][t2][1][e], st[k][t2][2][e], st[k][t2][3][e]};
-            if (KEYS_RES && any_neg) {
-              col[0] ^= (sgn[k][0] & 0x8000u) << 16;
-              col[1] ^= sgn[k][0] & 0x80000000u;
-              col[2] ^= (sgn[k][1] & 0x8000u) << 16;
-              col[3] ^= sgn[k][1] & 0x80000000u;
-            }
+            const u32x4 col = {st[t2][4 * k][e], st[t2][4 * k + 1][e], st[t2][4 * k + 2][e],
+                               st[t2][4 * k + 3][e]};
             *reinterpret_cast<u32x4 *>(xt + (4 * cc + e) * Tr::XT_STRIDE + 4 * a * 4) = col;
           }
         }
@@ -262,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     if (KEYS_RES && tid < Tr::BX) {
       float *sb = reinterpret_cast<float *>(base + Tr::OFF_STAT);
 #pragma unroll
-      for (int f = 0; f < 3; ++f) sb[f * Tr::BX + tid] = sv[f];
+      for (int f = 0; f < Tr::NSTAT; ++f) sb[f * Tr::BX + tid] = sv[f];
     }
   };
 
@@ -271,98 +285,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     sstore(0);
   }
   __syncthreads();
-
-  // One 32-row block of the streamed tile at `base`: logits, dS, gradient products.
-  // MASK is false when every (query, key) pair of the block is visible.
-  auto block = [&](const char *base, int xb, int xa, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    // Logits block: lane = resident row, element r = streamed row xa + acc_row(r, h).
-    f32x16 x1 = f32x16{}, x2 = f32x16{};
-    {
-      const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 8 * h * (int)sizeof(T);
-      const char *a2p = a1p + Tr::XROW_BYTES;
-#pragma unroll
-      for (int s = 0; s < Tr::KSTEPS; ++s) {
-        const CT a1 = *reinterpret_cast<const CT *>(a1p + 16 * s * (int)sizeof(T));
-        const CT a2 = *reinterpret_cast<const CT *>(a2p + 16 * s * (int)sizeof(T));
-        x1 = mma16(a1, rf1[s], x1);
-        x2 = mma16(a2, rf2[s], x2);
-      }
-    }
-    // dS, elementwise.
-    f32x16 d1, d2;
-    const float *sb = reinterpret_cast<const float *>(base + Tr::OFF_STAT);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4 B1, B2, KV;
-      if (KEYS_RES) {
-        const int q = xb * 32 + 8 * j + 4 * h;
-        B1 = *reinterpret_cast<const f32x4 *>(sb + 0 * Tr::BX + q);
-        B2 = *reinterpret_cast<const f32x4 *>(sb + 1 * Tr::BX + q);
-        KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
-      } else {
-        B1 = f32x4{qb1, qb1, qb1, qb1};
-        B2 = f32x4{qb2, qb2, qb2, qb2};
-        KV = f32x4{qkl, qkl, qkl, qkl};
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * j + u;
-        // p_t = P_t * |g| * sigma; (y1 - y2) * ln 2 = (s1 - LSE1) - (s2 - LSE2).
-        const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
-        const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
-        const float p1 = fast_exp2(y1);
-        const float p2 = fast_exp2(y2);
-        const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
-        float v2 = p2 - p1;
-        float v1 = p1 * dl;
-        if (MASK) {
-          const int srow = xa + acc_row(r, h);
-          const int qi = KEYS_RES ? srow : my_r;
-          const int kj = KEYS_RES ? my_r : srow;
-          const bool vis = qi < NQ && kj < NK && (!p.causal || kj <= qi + off);
-          v1 = vis ? v1 : 0.f;
-          v2 = vis ? v2 : 0.f;
-        }
-        d1[r] = v1;
-        d2[r] = v2;
-      }
-    }
-    // Gradient product dR^T[d, resident] += X^T[d, streamed] * dS[streamed, resident].
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      CG b1, b2;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        b1[u] = (G)d1[8 * ks + u];
-        b2[u] = (G)d2[8 * ks + u];
-      }
-      const int so = xb * 32 + 16 * ks + 4 * h;  // streamed-row offset of slots 0..3 (slots 4..7: +8)
-#pragma unroll
-      for (int db = 0; db < Tr::NDB; ++db) {
-        const char *t1 = base + Tr::OFF_XT + (db * 32 + c32) * Tr::XT_STRIDE + so * (int)sizeof(G);
-        const char *t2 = t1 + Tr::XT_BYTES;
-        CG a1, a2;
-        if constexpr (sizeof(G) == 2) {
-          const f16x4 l1 = *reinterpret_cast<const f16x4 *>(t1);
-          const f16x4 h1 = *reinterpret_cast<const f16x4 *>(t1 + 16);
-          const f16x4 l2 = *reinterpret_cast<const f16x4 *>(t2);
-          const f16x4 h2 = *reinterpret_cast<const f16x4 *>(t2 + 16);
-          a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-          a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-          const f32x4 l1 = *reinterpret_cast<const f32x4 *>(t1);
-          const f32x4 h1 = *reinterpret_cast<const f32x4 *>(t1 + 32);
-          const f32x4 l2 = *reinterpret_cast<const f32x4 *>(t2);
-          const f32x4 h2 = *reinterpret_cast<const f32x4 *>(t2 + 32);
-          a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-          a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        acc1[db] = mma16(a1, b1, acc1[db]);
-        acc2[db] = mma16(a2, b2, acc2[db]);
-      }
-    }
-  };
 
   // Streamed tiles in which every (query, key) pair of the workgroup is
   // visible form one contiguous run [t_a, t_b): under the causal mask the
@@ -377,7 +299,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
       if (KEYS_RES) return xl < NQ && rlast < NK && (!p.causal || rlast <= xt + off);
       return rlast < NQ && xl < NK && (!p.causal || xl <= r0 + off);
     };
-    // Full tiles are contiguous, so a linear scan from each end finds the run.
     int a = 0;
     while (a < ntiles && !tile_full(a)) ++a;
     int b = a;
@@ -386,57 +307,175 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     t_b = b;
   }
 
-  auto run_tiles = [&](int t0, int t1, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    for (int t = t0; t < t1; ++t) {
-      if (t + 1 < ntiles) gload(t + 1);
-      const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
-#pragma unroll
-      for (int xb = 0; xb < Tr::XB; ++xb) {
-        const int xa = x_lo + t * Tr::BX + xb * 32;  // streamed rows [xa, xa + 32)
-        if (!MASK) {
-          block(base, xb, xa, std::integral_constant<bool, false>{});
-          continue;
-        }
-        bool empty;
-        if (KEYS_RES)  // resident keys j, streamed queries i
-          empty = xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
-        else  // resident queries i, streamed keys j
-          empty = ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
-        if (!empty) block(base, xb, xa, std::integral_constant<bool, true>{});
-      }
-      if (t + 1 < ntiles) sstore((t + 1) & 1);
-      __syncthreads();
-    }
-  };
-  run_tiles(0, t_a, std::integral_constant<bool, true>{});
-  run_tiles(t_a, t_b, std::integral_constant<bool, false>{});
-  run_tiles(t_b, ntiles, std::integral_constant<bool, true>{});
-
-  // Epilogue: lane writes its resident row, d = db*32 + 8j + 4h + (0..3).
-  if (r_ok) {
-    const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
-    float *O1 = KEYS_RES ? p.dk1 : p.dq1;
-    float *O2 = KEYS_RES ? p.dk2 : p.dq2;
-    const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
+  // Everything that accumulates lives in `body`; NEG (key-resident pass, some
+  // g of the head negative) multiplies dS by sign(g) of its query row.
+  auto body = [&](auto neg_tag) {
+    constexpr bool NEG = decltype(neg_tag)::value;
+    f32x16 acc1[Tr::NDB], acc2[Tr::NDB];
 #pragma unroll
     for (int db = 0; db < Tr::NDB; ++db) {
+      acc1[db] = f32x16{};
+      acc2[db] = f32x16{};
+    }
+
+    // One 32-row block of the streamed tile at `base`: logits, dS, gradient products.
+    // MASK is false when every (query, key) pair of the block is visible.
+    auto block = [&](const char *base, int xb, int xa, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // Logits block: lane = resident row, element r = streamed row xa + acc_row(r, h).
+      f32x16 x1 = f32x16{}, x2 = f32x16{};
+      {
+        const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 8 * h * Tr::ES;
+        const char *a2p = a1p + Tr::XROW_BYTES;
+#pragma unroll
+        for (int s = 0; s < Tr::KSTEPS; ++s) {
+          const CG a1 = *reinterpret_cast<const CG *>(a1p + 16 * s * Tr::ES);
+          const CG a2 = *reinterpret_cast<const CG *>(a2p + 16 * s * Tr::ES);
+          x1 = mma16(a1, rf1[s], x1);
+          x2 = mma16(a2, rf2[s], x2);
+        }
+      }
+      // dS, elementwise.
+      f32x16 d1, d2;
+      const float *sb = reinterpret_cast<const float *>(base + Tr::OFF_STAT);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + 8 * j + 4 * h;
-        if (p.want1) {
-          const f32x4 v = {acc1[db][4 * j] * f, acc1[db][4 * j + 1] * f, acc1[db][4 * j + 2] * f,
-                           acc1[db][4 * j + 3] * f};
-          *reinterpret_cast<f32x4 *>(O1 + rowoff + d) = v;
+        f32x4 B1, B2, KV, SG;
+        if (KEYS_RES) {
+          const int q = xb * 32 + 8 * j + 4 * h;
+          B1 = *reinterpret_cast<const f32x4 *>(sb + 0 * Tr::BX + q);
+          B2 = *reinterpret_cast<const f32x4 *>(sb + 1 * Tr::BX + q);
+          KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
+          if (NEG) SG = *reinterpret_cast<const f32x4 *>(sb + 3 * Tr::BX + q);
+        } else {
+          B1 = f32x4{qb1, qb1, qb1, qb1};
+          B2 = f32x4{qb2, qb2, qb2, qb2};
+          KV = f32x4{qkl, qkl, qkl, qkl};
         }
-        if (p.want2) {
-          const f32x4 v = {acc2[db][4 * j] * f, acc2[db][4 * j + 1] * f, acc2[db][4 * j + 2] * f,
-                           acc2[db][4 * j + 3] * f};
-          *reinterpret_cast<f32x4 *>(O2 + rowoff + d) = v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * j + u;
+          // p_t = P_t * |g| * sigma; (y1 - y2) * ln 2 = (s1 - LSE1) - (s2 - LSE2).
+          const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
+          const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
+          const float p1 = fast_exp2(y1);
+          const float p2 = fast_exp2(y2);
+          const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
+          float v2 = p2 - p1;
+          float v1 = p1 * dl;
+          if (NEG) {
+            v1 *= SG[u];
+            v2 *= SG[u];
+          }
+          if (MASK) {
+            const int srow = xa + acc_row(r, h);
+            const int qi = KEYS_RES ? srow : my_r;
+            const int kj = KEYS_RES ? my_r : srow;
+            const bool vis = qi < NQ && kj < NK && (!p.causal || kj <= qi + off);
+            v1 = vis ? v1 : 0.f;
+            v2 = vis ? v2 : 0.f;
+          }
+          d1[r] = v1;
+          d2[r] = v2;
+        }
+      }
+      // Gradient product dR^T[d, resident] += X^T[d, streamed] * dS[streamed, resident].
+      // Slot u of lane half h in k-step ks is streamed row 16ks + 8(u/4) + 4h + u%4.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        CG b1, b2;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          b1[u] = (G)d1[8 * ks + u];
+          b2[u] = (G)d2[8 * ks + u];
+        }
+#pragma unroll
+        for (int db = 0; db < Tr::NDB; ++db) {
+          CG a1, a2;
+          if constexpr (Tr::F16) {
+            // 16-lane group g: columns db*32 + 16(g&1) + (0..15), rows 16ks + 4(g>>1) + (0..3) (+8).
+            const int j16 = lane & 15, grp = lane >> 4;
+            const int rb = xb * 32 + 16 * ks + 4 * (grp >> 1) + (j16 >> 2);
+            const int d0 = db * 32 + 16 * (grp & 1) + 4 * (j16 & 3);
+            const char *t1 = base + rb * Tr::XROW + d0 * 2;
+            const char *t2 = t1 + Tr::XROW_BYTES;
+            const f16x4 l1 = lds_read_tr16(t1), h1 = lds_read_tr16(t1 + 8 * Tr::XROW);
+            const f16x4 l2 = lds_read_tr16(t2), h2 = lds_read_tr16(t2 + 8 * Tr::XROW);
+            a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            const int so = xb * 32 + 16 * ks + 4 * h;
+            const char *t1 = base + Tr::OFF_XT + (db * 32 + c32) * Tr::XT_STRIDE + so * 4;
+            const char *t2 = t1 + Tr::XT_BYTES;
+            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(t1);
+            const f32x4 h1 = *reinterpret_cast<const f32x4 *>(t1 + 32);
+            const f32x4 l2 = *reinterpret_cast<const f32x4 *>(t2);
+            const f32x4 h2 = *reinterpret_cast<const f32x4 *>(t2 + 32);
+            a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+          acc1[db] = mma16(a1, b1, acc1[db]);
+          acc2[db] = mma16(a2, b2, acc2[db]);
+        }
+      }
+    };
+
+    auto run_tiles = [&](int t0, int t1, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      for (int t = t0; t < t1; ++t) {
+        if (t + 1 < ntiles) gload(t + 1);
+        const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
+#pragma unroll
+        for (int xb = 0; xb < Tr::XB; ++xb) {
+          const int xa = x_lo + t * Tr::BX + xb * 32;  // streamed rows [xa, xa + 32)
+          if (!MASK) {
+            block(base, xb, xa, std::false_type{});
+            continue;
+          }
+          bool empty;
+          if (KEYS_RES)  // resident keys j, streamed queries i
+            empty = xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
+          else  // resident queries i, streamed keys j
+            empty = ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
+          if (!empty) block(base, xb, xa, std::true_type{});
+        }
+        if (t + 1 < ntiles) sstore((t + 1) & 1);
+        __syncthreads();
+      }
+    };
+    run_tiles(0, t_a, std::true_type{});
+    run_tiles(t_a, t_b, std::false_type{});
+    run_tiles(t_b, ntiles, std::true_type{});
+
+    // Epilogue: lane writes its resident row, d = db*32 + 8j + 4h + (0..3).
+    if (r_ok) {
+      const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
+      float *O1 = KEYS_RES ? p.dk1 : p.dq1;
+      float *O2 = KEYS_RES ? p.dk2 : p.dq2;
+      const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = db * 32 + 8 * j + 4 * h;
+          if (p.want1) {
+            const f32x4 v = {acc1[db][4 * j] * f, acc1[db][4 * j + 1] * f, acc1[db][4 * j + 2] * f,
+                             acc1[db][4 * j + 3] * f};
+            *reinterpret_cast<f32x4 *>(O1 + rowoff + d) = v;
+          }
+          if (p.want2) {
+            const f32x4 v = {acc2[db][4 * j] * f, acc2[db][4 * j + 1] * f, acc2[db][4 * j + 2] * f,
+                             acc2[db][4 * j + 3] * f};
+            *reinterpret_cast<f32x4 *>(O2 + rowoff + d) = v;
+          }
         }
       }
     }
-  }
+  };
+  if (KEYS_RES && any_neg)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
 }
 
 // sigma[b,h] = 2^(kGradExp - e) with 2^(e-1) <= max_i |g[b,h,i]| < 2^e (1 if g is all zero,
