@@ -49,7 +49,10 @@ struct BwdTraits {
   using G = typename GradOp<T>::type;
   static constexpr int WAVES = 4;
   static constexpr int BR = kBwdBR;                        // resident rows per workgroup
-  static constexpr int BX = (!F16 && D == 128) ? 32 : 64;  // streamed rows per stage
+#ifndef SKL_BWD_BX
+#define SKL_BWD_BX 64
+#endif
+  static constexpr int BX = (!F16 && D == 128) ? 32 : (F16 ? SKL_BWD_BX : 64);  // streamed rows per stage
   static constexpr int XB = BX / 32;
   static constexpr int KSTEPS = D / 16;
   static constexpr int NDB = D / 32;
@@ -140,9 +143,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   const int NX = KEYS_RES ? NQ : NK;  // streamed row count
   const int nrt = (NR + Tr::BR - 1) / Tr::BR;
 
-  // Heaviest resident tiles first: under the causal mask low keys see the
+  // Head-major order, each XCD taking a contiguous run of heads (so one
+  // head's streamed tiles are shared through one L2); within a head the
+  // heaviest resident tiles go first: under the causal mask low keys see the
   // most queries, high queries see the most keys.
-  const uint32_t L = blockIdx.x;
+  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = L / (uint32_t)nrt;
   const int rt = KEYS_RES ? (int)(L % (uint32_t)nrt) : nrt - 1 - (int)(L % (uint32_t)nrt);
 
@@ -178,6 +183,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     }
   }
   const int ntiles = x_hi > x_lo ? (x_hi - x_lo + Tr::BX - 1) / Tr::BX : 0;
+  // Streamed tile t starts at row x_of(t).  The key-resident pass walks the
+  // queries downward from the last tile: every workgroup of a head then
+  // starts on the same tile and they move through L2 together, whereas their
+  // causal starting points differ.
+  auto x_of = [&](int t) { return x_lo + (KEYS_RES ? ntiles - 1 - t : t) * Tr::BX; };
 
   // Resident fragments (B operand of the logits product): lane's row, elements [16s + 8h, +8).
   CG rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
@@ -204,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   u32x4 st[2][Tr::F16 ? Tr::CPT : 4 * Tr::IPT];
   float sv[Tr::NSTAT];
   auto gload = [&](int t) {
-    const int xb0 = x_lo + t * Tr::BX;
+    const int xb0 = x_of(t);
     const u32x4 z = {0u, 0u, 0u, 0u};
     if constexpr (Tr::F16) {
 #pragma unroll
@@ -287,15 +297,15 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   __syncthreads();
 
   // Streamed tiles in which every (query, key) pair of the workgroup is
-  // visible form one contiguous run [t_a, t_b): under the causal mask the
-  // diagonal tiles come first (key-resident pass) or last (query-resident
-  // pass), and a ragged streamed tail is always last.  The run is processed
-  // without any mask test; the tiles around it test every block.
+  // visible form one contiguous run [t_a, t_b) in processing order: a ragged
+  // last streamed tile (first, in the key-resident pass) and the causal
+  // diagonal tiles (last in both passes) lie outside it.  The run is
+  // processed without any mask test; the tiles around it test every block.
   int t_a = 0, t_b = 0;
   {
     const int rlast = r0 + Tr::BR - 1;  // all resident rows of the tile, valid or not
     auto tile_full = [&](int t) {
-      const int xt = x_lo + t * Tr::BX, xl = xt + Tr::BX - 1;
+      const int xt = x_of(t), xl = xt + Tr::BX - 1;
       if (KEYS_RES) return xl < NQ && rlast < NK && (!p.causal || rlast <= xt + off);
       return rlast < NQ && xl < NK && (!p.causal || xl <= r0 + off);
     };
@@ -427,7 +437,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
         const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
 #pragma unroll
         for (int xb = 0; xb < Tr::XB; ++xb) {
-          const int xa = x_lo + t * Tr::BX + xb * 32;  // streamed rows [xa, xa + 32)
+          const int xa = x_of(t) + xb * 32;  // streamed rows [xa, xa + 32)
           if (!MASK) {
             block(base, xb, xa, std::false_type{});
             continue;

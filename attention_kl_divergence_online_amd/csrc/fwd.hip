@@ -33,6 +33,12 @@ namespace skl {
 #ifndef SKL_FWD_BK
 #define SKL_FWD_BK 64
 #endif
+#ifndef SKL_FWD_PP
+#define SKL_FWD_PP 0
+#endif
+#ifndef SKL_FWD_PRIO
+#define SKL_FWD_PRIO 0
+#endif
 
 
 constexpr int kFwdThreads = SKL_FWD_WAVES * 64;
@@ -155,8 +161,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
     sp = (int)(rest % (uint32_t)p.splits);
     bh = rest / (uint32_t)p.splits;
   } else {
-    // Head-major; within a head the longest (last) query tiles go first.
-    const uint32_t L = blockIdx.x;
+    // Head-major with each XCD on a contiguous run of heads (one head's key
+    // tiles shared through one L2); within a head the longest (last) query
+    // tiles go first.
+    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
     bh = L / (uint32_t)p.nqt;
     qt = p.nqt - 1 - (int)(L % (uint32_t)p.nqt);
     sp = 0;
@@ -261,6 +269,65 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
     }
   };
 
+#if SKL_FWD_PP
+  // Ping-pong: waves w and w + WAVES/2 share a SIMD.  Group A issues block j's
+  // matrix products while group B runs the online update of block j - 1, then
+  // they swap; a workgroup barrier separates the phases.  A block's scores
+  // stay in s1/s2 from its product phase to its update phase.  Tile t + 1 is
+  // stored during the update of block t*NB (by each group) and tile t + 2 is
+  // fetched right after, so every LDS buffer is rewritten only after both
+  // groups finished reading it and is complete before either group reads it.
+  const bool grp_b = wave >= Tr::WAVES / 2;
+  const int nblk = ntiles * Tr::NB;
+  f32x16 s1[Tr::QB], s2[Tr::QB];
+  auto mphase = [&](int j) {
+    const int t = j / Tr::NB, kb = j % Tr::NB;
+    const int kbase = k_lo + j * 32;
+    if (wave_live && kbase < vis_any) {
+#if SKL_FWD_PRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
+      block_scores(smem + (t & 1) * Tr::STAGE_BYTES, kb, s1, s2);
+#if SKL_FWD_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
+    }
+  };
+  auto vphase = [&](int j) {
+    const int kbase = k_lo + j * 32;
+    if (wave_live && kbase < vis_any) {
+      if (kbase + 32 <= vis_all) {
+#pragma unroll
+        for (int qb = 0; qb < Tr::QB; ++qb) online_update<false, COMP>(s1[qb], s2[qb], st[qb], c, kbase, h, 0);
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < Tr::QB; ++qb)
+          online_update<true, COMP>(s1[qb], s2[qb], st[qb], c, kbase, h, klim[qb]);
+      }
+    }
+    if (j % Tr::NB == 0) {
+      const int t = j / Tr::NB;
+      if (t + 1 < ntiles) {
+        sstore((t + 1) & 1);
+        if (t + 2 < ntiles) gload(t + 2);
+      }
+    }
+  };
+  if (ntiles > 1) gload(1);
+  for (int j = 0; j < nblk; ++j) {
+    if (!grp_b)
+      mphase(j);
+    else if (j > 0)
+      vphase(j - 1);
+    __syncthreads();
+    if (!grp_b)
+      vphase(j);
+    else
+      mphase(j);
+    __syncthreads();
+  }
+  if (grp_b && nblk > 0) vphase(nblk - 1);
+#else
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) gload(t + 1);
     const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
@@ -285,6 +352,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
     if (t + 1 < ntiles) sstore((t + 1) & 1);
     __syncthreads();
   }
+
+#endif
 
   // Merge the two lane halves that hold disjoint keys of the same query.
 #pragma unroll

@@ -25,6 +25,118 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attn-KL fwd and fwd+bwd TFLOP/s + ms at 64K ctx, 32 heads, d=128 bf16"
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_kl_causal_64k_hbm_traffic.json")
+COPY_BYTES = 1 << 30
+KERNELS = {  # bench key -> mangled kernel symbol
+    "fwd": "_ZN3skl10fwd_kernelIDF16bLi128ELb0EEEvNS_9FwdParamsE",
+    "bwd_dk": "_ZN3skl10bwd_kernelIDF16bLi128ELb1EEEvNS_9BwdParamsE",
+    "bwd_dq": "_ZN3skl10bwd_kernelIDF16bLi128ELb0EEEvNS_9BwdParamsE",
+}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources; counter records are valid only for this hash."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_kl_divergence_online_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str) -> None:
+    """Per-launch HBM bytes of the bench kernels from two rocprofv3 --pmc runs.
+
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counter reads for the calibration copy of COPY_BYTES (the device copy
+    kernel whose FETCH_SIZE is closest to COPY_BYTES)."""
+    import csv
+
+    def load(path, counter):
+        per = {}
+        copy_vals = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            name = r["Kernel_Name"]
+            for key, sym in KERNELS.items():
+                if name.startswith(sym):
+                    per.setdefault(key, []).append(v)
+            if "copy" in name.lower() or "elementwise" in name.lower():
+                copy_vals.append(v)
+        ref = min(copy_vals, key=lambda v: abs(v - COPY_BYTES)) if copy_vals else None
+        return per, ref
+
+    fetch, fref = load(fetch_csv, "FETCH_SIZE")
+    write, wref = load(write_csv, "WRITE_SIZE")
+    if not fref or not wref:
+        raise SystemExit("calibration copy not found in the counter CSVs (run bench.py --calibrate-copy)")
+    fs, wsc = COPY_BYTES / fref, COPY_BYTES / wref
+    rec = {"source_sha256": kernel_source_hash(), "copy_bytes": COPY_BYTES,
+           "fetch_scale": fs, "write_scale": wsc, "kernels": {}}
+    for key in KERNELS:
+        if key in fetch and key in write:
+            f = sum(fetch[key]) / len(fetch[key]) * fs
+            w = sum(write[key]) / len(write[key]) * wsc
+            rec["kernels"][key] = {"fetch_bytes": f, "write_bytes": w, "bytes": f + w}
+    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
+    with open(TRAFFIC_RECORD, "w") as fo:
+        json.dump(rec, fo, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def recorded_traffic(key: str):
+    """HBM bytes per launch of kernel `key` from the committed record, or None if
+    absent or taken on different kernel sources."""
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(key)
+    return None if k is None else k["bytes"]
+
+
+def summarize_counters(csvs, out_path: str) -> None:
+    """Utilisation table of the bench kernels from rocprofv3 --pmc counter CSVs.
+
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs * kernel cycles), with kernel
+    cycles = GRBM_GUI_ACTIVE / XCDs; the per-wave shares divide SQ_* cycle counts
+    (in units of 4 cycles) by SQ_WAVE_CYCLES."""
+    import csv
+    vals = {}
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            for key, sym in KERNELS.items():
+                if r["Kernel_Name"].startswith(sym):
+                    vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    simds, xcds = 1024, 8
+    lines = [f"{'kernel':8s} {'ms':>7s} {'MFMA busy':>10s} {'VALU/wave':>10s} {'wait/wave':>10s} "
+             f"{'LDS conflict':>13s} {'VALU lane-op/pair':>18s} {'exp/pair':>9s}"]
+    import synth
+    pairs = synth.get("causal_64k").visible_pairs()
+    for key in KERNELS:
+        d = {k: sum(v) / len(v) for k, v in vals.get(key, {}).items()}
+        if "GRBM_GUI_ACTIVE" not in d:
+            continue
+        cyc = d["GRBM_GUI_ACTIVE"] / xcds
+        wc = d.get("SQ_WAVE_CYCLES", float("nan"))
+        g = lambda name: d.get(name, float("nan"))
+        lines.append(
+            f"{key:8s} {cyc / 2.4e6:7.1f} {g('SQ_VALU_MFMA_BUSY_CYCLES') / (simds * cyc):10.1%} "
+            f"{g('SQ_ACTIVE_INST_VALU') / wc:10.1%} {g('SQ_WAIT_INST_ANY') / wc:10.1%} "
+            f"{g('SQ_LDS_BANK_CONFLICT') / g('SQ_LDS_IDX_ACTIVE'):13.1%} "
+            f"{(g('SQ_INSTS_VALU') - g('SQ_INSTS_MFMA')) * 64 / pairs:18.2f} "
+            f"{g('SQ_INSTS_VALU_TRANS_F32') * 64 / pairs:9.2f}")
+    text = "\n".join(lines) + "\n"
+    with open(out_path, "w") as fo:
+        fo.write(text)
+    print(text)
+
+
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0
 
@@ -38,6 +150,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy first (scale reference for HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="print the utilisation table of rocprofv3 --pmc counter CSVs to "
+                         "profiles/attention_kl_causal_64k_counters.table and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--calibrate-copy run into the traffic record under profiles/ and exit")
     return ap.parse_args()
 
 
@@ -60,7 +180,6 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s: float):
         return time.perf_counter() - t0, pairs
 
     dt, pairs = run(16)
-    per_pair = dt / pairs
     nrows = int(max(16, min(w.NQ, 16 * target_s / max(dt, 1e-6))))
     dt, pairs = run(nrows)
     flops = pairs * 16 * w.D
@@ -77,6 +196,13 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s: float):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters,
+                           os.path.join(ROOT, "profiles", "attention_kl_causal_64k_counters.table"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(each GPU's share would run the same kernels independently).", file=sys.stderr)
@@ -89,6 +215,13 @@ def main():
     w = synth.get(args.workload)
     dev = "cuda"
     torch.cuda.init()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     q1, k1, q2, k2 = synth.make_inputs(w, device=dev)
     g = synth.upstream_grad(w, dev)
     kl, l1, l2 = (torch.empty((w.B, w.H, w.NQ), dtype=torch.float32, device=dev) for _ in range(3))
@@ -184,7 +317,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(dom),
         },
     }
 
