@@ -488,6 +488,352 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     body(std::false_type{});
 }
 
+// ---- bf16 inputs: two waves per SIMD ----
+//
+// A single wave per SIMD leaves the VALU half idle (one wave issues a VALU op
+// only every few cycles; two waves fill the gaps) and exposes every LDS and
+// barrier wait.  This variant runs eight waves.  Waves p and p + 4 form a pair
+// that shares 32 resident rows: per 64-row streamed stage, wave p + 4e
+// computes logits and dS of streamed block e (rows 32e..32e+31) and posts its
+// dS operands to LDS; after a barrier each wave of the pair accumulates the
+// gradient product over both streamed blocks for its half of D (columns
+// 64e..64e+63 at D = 128).  Per wave that halves the gradient accumulators,
+// which keeps a wave within 256 registers.
+template <int D, bool KEYS_RES>
+struct Bwd2Traits {
+  static constexpr int NT = 512;
+  static constexpr int BR = kBwdBR;        // resident rows per workgroup: 4 pairs x 32
+  static constexpr int BX = 64;            // streamed rows per stage
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int NDH = D / 64;       // 32-column gradient blocks per wave
+  static constexpr int ROW_BYTES = D * 2;  // one bf16 row in HBM
+  static constexpr int CPR = ROW_BYTES / 16;
+  static constexpr int XROW = D * 2 + 48;  // fp16 row stride in LDS
+  static constexpr int XROW_BYTES = BX * XROW;
+  // Key-resident pass: per streamed query the fp32 stats b1, b2, KL and a
+  // 16-bit sign mask (0x8000 where g < 0), XORed onto the fp16 dS operands.
+  static constexpr int NSTAT = 3;
+  static constexpr int STAT_BYTES = KEYS_RES ? NSTAT * BX * 4 + BX * 2 : 0;
+  static constexpr int OFF_STAT = 2 * XROW_BYTES;
+  static constexpr int STAGE_BYTES = OFF_STAT + STAT_BYTES;
+  static constexpr int DSX_SLOT = 64 * 16;             // one lane-ordered 16-byte operand per lane
+  static constexpr int DSX_BYTES = 4 * 2 * 4 * DSX_SLOT;  // [pair][block][tensor * 2 + ks]
+  static constexpr int OFF_DSX = 2 * STAGE_BYTES;
+  static constexpr int LDS_BYTES = OFF_DSX + DSX_BYTES;
+  static constexpr int CPT = BX * CPR / NT;  // 16-byte staging chunks per thread per tensor
+  static_assert(BR == 4 * 32, "resident tile");
+  static_assert(CPT * NT == BX * CPR, "staging split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGE_BYTES % 16 == 0, "LDS alignment");
+};
+
+template <int D, bool KEYS_RES>
+__global__ __launch_bounds__(512, 1) void bwd2_kernel(BwdParams p) {
+  using Tr = Bwd2Traits<D, KEYS_RES>;
+  using CG = f16x8;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int pr = wave & 3;   // pair: resident rows
+  const int e = wave >> 2;   // streamed block for dS, half of D for the gradient
+  const int h = lane >> 5, c32 = lane & 31;
+
+  const int NQ = (int)p.NQ, NK = (int)p.NK;
+  const int off = NK - NQ;
+  const int NR = KEYS_RES ? NK : NQ;
+  const int NX = KEYS_RES ? NQ : NK;
+  const int nrt = (NR + Tr::BR - 1) / Tr::BR;
+
+  // Same workgroup order as the one-wave kernel: head-major per XCD, heaviest
+  // resident tiles of a head first.
+  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bh = L / (uint32_t)nrt;
+  const int rt = KEYS_RES ? (int)(L % (uint32_t)nrt) : nrt - 1 - (int)(L % (uint32_t)nrt);
+
+  const bf16 *R1 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k1 : p.q1) + bh * (int64_t)NR * D;
+  const bf16 *R2 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k2 : p.q2) + bh * (int64_t)NR * D;
+  const char *X1 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q1 : p.k1) +
+                                                  bh * (int64_t)NX * D);
+  const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q2 : p.k2) +
+                                                  bh * (int64_t)NX * D);
+  const float *KLr = p.kl + bh * (int64_t)NQ;
+  const float *LS1 = p.lse1 + bh * (int64_t)NQ;
+  const float *LS2 = p.lse2 + bh * (int64_t)NQ;
+  const float *Gr = p.g + bh * (int64_t)NQ;
+  const float sigma_raw = p.sigma[bh];
+  const float sigma = fabsf(sigma_raw);
+  const bool any_neg = sigma_raw < 0.f;
+
+  const int r0 = rt * Tr::BR;
+  const int rlast_wg = min(r0 + Tr::BR, NR) - 1;
+  const int ra = r0 + pr * 32;
+  const int my_r = ra + c32;
+  const bool r_ok = my_r < NR;
+
+  int x_lo = 0, x_hi = NX;
+  if (p.causal) {
+    if (KEYS_RES) {
+      x_lo = max(0, r0 - off);
+      x_lo -= x_lo % Tr::BX;
+    } else {
+      x_hi = min(NK, rlast_wg + off + 1);
+    }
+  }
+  const int ntiles = x_hi > x_lo ? (x_hi - x_lo + Tr::BX - 1) / Tr::BX : 0;
+  auto x_of = [&](int t) { return x_lo + (KEYS_RES ? ntiles - 1 - t : t) * Tr::BX; };
+
+  // Resident fragments (B operand of the logits product), converted to fp16.
+  CG rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
+#pragma unroll
+  for (int s = 0; s < Tr::KSTEPS; ++s) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 w1 = r_ok ? *reinterpret_cast<const u32x4 *>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : z;
+    const u32x4 w2 = r_ok ? *reinterpret_cast<const u32x4 *>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : z;
+    rf1[s] = __builtin_bit_cast(CG, bf16x8_to_f16x8(w1));
+    rf2[s] = __builtin_bit_cast(CG, bf16x8_to_f16x8(w2));
+  }
+
+  const float c = p.scale * kLog2e;
+  float qb1 = kNoGrad, qb2 = kNoGrad, qkl = 0.f, qsg = 1.f;
+  if (!KEYS_RES && r_ok) query_stats(LS1[my_r], LS2[my_r], KLr[my_r], Gr[my_r], sigma, qb1, qb2, qkl, qsg);
+
+  // ---- staging: global -> registers -> LDS (fp16 rows) ----
+  u32x4 st[2][Tr::CPT];
+  float sv[Tr::NSTAT];
+  uint32_t sgn = 0;
+  auto gload = [&](int t) {
+    const int xb0 = x_of(t);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < Tr::CPT; ++i) {
+      const int cidx = tid + Tr::NT * i;
+      const int row = xb0 + cidx / Tr::CPR, col = cidx % Tr::CPR;
+      const int64_t o = (int64_t)row * Tr::ROW_BYTES + col * 16;
+      st[0][i] = row < NX ? *reinterpret_cast<const u32x4 *>(X1 + o) : z;
+      st[1][i] = row < NX ? *reinterpret_cast<const u32x4 *>(X2 + o) : z;
+    }
+    if (KEYS_RES && tid < Tr::BX) {
+      const int q = xb0 + tid;
+      sv[0] = sv[1] = kNoGrad;
+      sv[2] = 0.f;
+      float sg = 1.f;
+      if (q < NQ) query_stats(LS1[q], LS2[q], KLr[q], Gr[q], sigma, sv[0], sv[1], sv[2], sg);
+      sgn = sg < 0.f ? 0x8000u : 0u;
+    }
+  };
+  auto sstore = [&](int buf) {
+    char *base = smem + buf * Tr::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < Tr::CPT; ++i) {
+      const int cidx = tid + Tr::NT * i;
+      const int row = cidx / Tr::CPR, col = cidx % Tr::CPR;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+        *reinterpret_cast<u32x4 *>(base + t2 * Tr::XROW_BYTES + row * Tr::XROW + col * 16) =
+            bf16x8_to_f16x8(st[t2][i]);
+    }
+    if (KEYS_RES && tid < Tr::BX) {
+      float *sb = reinterpret_cast<float *>(base + Tr::OFF_STAT);
+#pragma unroll
+      for (int f = 0; f < Tr::NSTAT; ++f) sb[f * Tr::BX + tid] = sv[f];
+      reinterpret_cast<uint16_t *>(sb + Tr::NSTAT * Tr::BX)[tid] = (uint16_t)sgn;
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+
+  int t_a = 0, t_b = 0;
+  {
+    const int rlast = r0 + Tr::BR - 1;
+    auto tile_full = [&](int t) {
+      const int xt = x_of(t), xl = xt + Tr::BX - 1;
+      if (KEYS_RES) return xl < NQ && rlast < NK && (!p.causal || rlast <= xt + off);
+      return rlast < NQ && xl < NK && (!p.causal || xl <= r0 + off);
+    };
+    int a = 0;
+    while (a < ntiles && !tile_full(a)) ++a;
+    int b = a;
+    while (b < ntiles && tile_full(b)) ++b;
+    t_a = a;
+    t_b = b;
+  }
+
+  // dS operand slots of this wave and of its partner (lane-ordered, conflict-free).
+  char *own_slot = smem + Tr::OFF_DSX + (pr * 2 + e) * 4 * Tr::DSX_SLOT + lane * 16;
+  const char *par_slot = smem + Tr::OFF_DSX + (pr * 2 + (1 - e)) * 4 * Tr::DSX_SLOT + lane * 16;
+
+  {
+    f32x16 acc1[Tr::NDH], acc2[Tr::NDH];
+#pragma unroll
+    for (int db = 0; db < Tr::NDH; ++db) {
+      acc1[db] = f32x16{};
+      acc2[db] = f32x16{};
+    }
+    // No visible pair between this pair's resident rows and streamed rows [xa, xa + 32).
+    auto empty_blk = [&](int xa) -> bool {
+      if (KEYS_RES) return xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
+      return ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
+    };
+    // Logits and dS of streamed block xb (rows xa..xa+31) -> gradient-product B
+    // operands: bo[ks] (teacher), bo[2 + ks] (student).
+    auto dsblock = [&](const char *base, int xb, int xa, auto mask_tag, CG(&bo)[4]) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 x1 = f32x16{}, x2 = f32x16{};
+      {
+        const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 16 * h;
+        const char *a2p = a1p + Tr::XROW_BYTES;
+#pragma unroll
+        for (int s = 0; s < Tr::KSTEPS; ++s) {
+          const CG a1 = *reinterpret_cast<const CG *>(a1p + 32 * s);
+          const CG a2 = *reinterpret_cast<const CG *>(a2p + 32 * s);
+          x1 = mma16(a1, rf1[s], x1);
+          x2 = mma16(a2, rf2[s], x2);
+        }
+      }
+      const float *sb = reinterpret_cast<const float *>(base + Tr::OFF_STAT);
+      f32x16 d1, d2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 B1, B2, KV;
+        if (KEYS_RES) {
+          const int q = xb * 32 + 8 * j + 4 * h;
+          B1 = *reinterpret_cast<const f32x4 *>(sb + 0 * Tr::BX + q);
+          B2 = *reinterpret_cast<const f32x4 *>(sb + 1 * Tr::BX + q);
+          KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
+        } else {
+          B1 = f32x4{qb1, qb1, qb1, qb1};
+          B2 = f32x4{qb2, qb2, qb2, qb2};
+          KV = f32x4{qkl, qkl, qkl, qkl};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * j + u;
+          const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
+          const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
+          const float p1 = fast_exp2(y1);
+          const float p2 = fast_exp2(y2);
+          const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
+          float v2 = p2 - p1;
+          float v1 = p1 * dl;
+          if (MASK) {
+            const int srow = xa + acc_row(r, h);
+            const int qi = KEYS_RES ? srow : my_r;
+            const int kj = KEYS_RES ? my_r : srow;
+            const bool vis = qi < NQ && kj < NK && (!p.causal || kj <= qi + off);
+            v1 = vis ? v1 : 0.f;
+            v2 = vis ? v2 : 0.f;
+          }
+          d1[r] = v1;
+          d2[r] = v2;
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          bo[ks][u] = (f16)d1[8 * ks + u];
+          bo[2 + ks][u] = (f16)d2[8 * ks + u];
+        }
+      }
+      // Key-resident pass with some g < 0: dS of query q carries sign(g_q).
+      // Slot pair (2m, 2m+1) of k-step ks holds queries 16ks + 4h + {0,2,8,10}[m] + (0, 1).
+      if (KEYS_RES && any_neg) {
+        const char *sgp = reinterpret_cast<const char *>(sb + Tr::NSTAT * Tr::BX) + (xb * 32 + 4 * h) * 2;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint2 lo = *reinterpret_cast<const uint2 *>(sgp + 32 * ks);
+          const uint2 hi = *reinterpret_cast<const uint2 *>(sgp + 32 * ks + 16);
+          const u32x4 m = {lo.x, lo.y, hi.x, hi.y};
+          bo[ks] = __builtin_bit_cast(CG, __builtin_bit_cast(u32x4, bo[ks]) ^ m);
+          bo[2 + ks] = __builtin_bit_cast(CG, __builtin_bit_cast(u32x4, bo[2 + ks]) ^ m);
+        }
+      }
+    };
+    // Gradient product over streamed block xb for this wave's half of D:
+    // dR^T[d, resident] += X^T[d, streamed] * dS[streamed, resident].
+    auto grad = [&](const char *base, int xb, const CG(&bo)[4]) {
+      const int j16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int db = 0; db < Tr::NDH; ++db) {
+          const int rb = xb * 32 + 16 * ks + 4 * (grp >> 1) + (j16 >> 2);
+          const int d0 = (e * Tr::NDH + db) * 32 + 16 * (grp & 1) + 4 * (j16 & 3);
+          const char *t1 = base + rb * Tr::XROW + d0 * 2;
+          const char *t2 = t1 + Tr::XROW_BYTES;
+          const f16x4 l1 = lds_read_tr16(t1), h1 = lds_read_tr16(t1 + 8 * Tr::XROW);
+          const f16x4 l2 = lds_read_tr16(t2), h2 = lds_read_tr16(t2 + 8 * Tr::XROW);
+          const CG a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+          const CG a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc1[db] = mma16(a1, bo[ks], acc1[db]);
+          acc2[db] = mma16(a2, bo[2 + ks], acc2[db]);
+        }
+      }
+    };
+
+    auto run_tiles = [&](int t0, int t1, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      for (int t = t0; t < t1; ++t) {
+        const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
+        const int xt = x_of(t);
+        const bool own_live = !MASK || !empty_blk(xt + 32 * e);
+        const bool par_live = !MASK || !empty_blk(xt + 32 * (1 - e));
+        CG bo[4];
+        if (own_live) {
+          dsblock(base, e, xt + 32 * e, mask_tag, bo);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *reinterpret_cast<CG *>(own_slot + i * Tr::DSX_SLOT) = bo[i];
+        }
+        __syncthreads();
+        // The next stage's global loads overlap the gradient products.
+        if (t + 1 < ntiles) gload(t + 1);
+        if (own_live) grad(base, e, bo);
+        if (par_live) {
+          CG pb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pb[i] = *reinterpret_cast<const CG *>(par_slot + i * Tr::DSX_SLOT);
+          grad(base, 1 - e, pb);
+        }
+        if (t + 1 < ntiles) sstore((t + 1) & 1);
+        __syncthreads();
+      }
+    };
+    run_tiles(0, t_a, std::true_type{});
+    run_tiles(t_a, t_b, std::false_type{});
+    run_tiles(t_b, ntiles, std::true_type{});
+
+    // Epilogue: lane writes its resident row, d = (e*NDH + db)*32 + 8j + 4h + (0..3).
+    if (r_ok) {
+      const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
+      float *O1 = KEYS_RES ? p.dk1 : p.dq1;
+      float *O2 = KEYS_RES ? p.dk2 : p.dq2;
+      const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
+#pragma unroll
+      for (int db = 0; db < Tr::NDH; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = (e * Tr::NDH + db) * 32 + 8 * j + 4 * h;
+          if (p.want1) {
+            const f32x4 v = {acc1[db][4 * j] * f, acc1[db][4 * j + 1] * f, acc1[db][4 * j + 2] * f,
+                             acc1[db][4 * j + 3] * f};
+            *reinterpret_cast<f32x4 *>(O1 + rowoff + d) = v;
+          }
+          if (p.want2) {
+            const f32x4 v = {acc2[db][4 * j] * f, acc2[db][4 * j + 1] * f, acc2[db][4 * j + 2] * f,
+                             acc2[db][4 * j + 3] * f};
+            *reinterpret_cast<f32x4 *>(O2 + rowoff + d) = v;
+          }
+        }
+      }
+    }
+  }
+}
+
 // sigma[b,h] = 2^(kGradExp - e) with 2^(e-1) <= max_i |g[b,h,i]| < 2^e (1 if g is all zero,
 // and 1 everywhere when `unit` is set: fp32 inputs need no scaling), stored
 // negated when some g[b,h,:] is negative.
@@ -556,13 +902,32 @@ hipError_t launch_grad_scale(int dtype, const float *g, int64_t BH, int64_t NQ, 
   return hipGetLastError();
 }
 
+template <int D, bool KEYS_RES>
+static hipError_t launch_pass2(const BwdParams &p, hipStream_t s) {
+  using Tr = Bwd2Traits<D, KEYS_RES>;
+  const int64_t NR = KEYS_RES ? p.NK : p.NQ;
+  if (NR == 0) return hipSuccess;
+  const void *fn = reinterpret_cast<const void *>(&bwd2_kernel<D, KEYS_RES>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR);
+  hipLaunchKernelGGL((bwd2_kernel<D, KEYS_RES>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  return hipGetLastError();
+}
+
+#ifdef SKL_BWD_ONE_WAVE
+#define SKL_BF16_PASS(D, KR) launch_pass<bf16, D, KR>(p, s)
+#else
+#define SKL_BF16_PASS(D, KR) launch_pass2<D, KR>(p, s)
+#endif
+
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s) {
-  if (dtype == 0) return D == 128 ? launch_pass<bf16, 128, true>(p, s) : launch_pass<bf16, 64, true>(p, s);
+  if (dtype == 0) return D == 128 ? SKL_BF16_PASS(128, true) : SKL_BF16_PASS(64, true);
   return D == 128 ? launch_pass<float, 128, true>(p, s) : launch_pass<float, 64, true>(p, s);
 }
 
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s) {
-  if (dtype == 0) return D == 128 ? launch_pass<bf16, 128, false>(p, s) : launch_pass<bf16, 64, false>(p, s);
+  if (dtype == 0) return D == 128 ? SKL_BF16_PASS(128, false) : SKL_BF16_PASS(64, false);
   return D == 128 ? launch_pass<float, 128, false>(p, s) : launch_pass<float, 64, false>(p, s);
 }
 
