@@ -138,13 +138,16 @@ def _workspace(p, dev, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def streamkl_bwd_prepare(q1, k1, g, scale: Optional[float] = None, causal: bool = False,
+def streamkl_bwd_prepare(q1, k1, q2, k2, g, scale: Optional[float] = None, causal: bool = False,
                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-(b,h) dS scale factors for the backward passes; returns the workspace."""
+    """Per-(b,h) dS scale factors (and, for bf16 inputs, the transposed fp16
+    operand copies) for the backward passes; returns the workspace."""
+    _check_inputs(q1, k1, q2, k2)
     p = problem_for(q1, k1, scale, causal)
     _check_rowvecs(q1, g)
     workspace, nbytes = _workspace(p, q1.device, workspace)
-    st = _lib.lib().streamkl_bwd_prepare(p, _ptr(g), _ptr(workspace), nbytes, _stream_handle(q1.device))
+    st = _lib.lib().streamkl_bwd_prepare(p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(g), _ptr(workspace),
+                                         nbytes, _stream_handle(q1.device))
     _lib.check(st, "streamkl_bwd_prepare")
     return workspace
 

@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
         L.streamkl_bwd_workspace_size.restype = sz
         L.streamkl_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.streamkl_bwd.restype = ctypes.c_int
-        L.streamkl_bwd_prepare.argtypes = [pp, vp, vp, sz, vp]
+        L.streamkl_bwd_prepare.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.streamkl_bwd_prepare.restype = ctypes.c_int
         for name in ("streamkl_bwd_dk", "streamkl_bwd_dq"):
             fn = getattr(L, name)

@@ -9,6 +9,31 @@
 
 namespace {
 
+// Backward workspace: the per-(b,h) factors sigma, then for bf16 inputs the
+// transposed fp16 copies of q1, q2, k1, k2 ([BH][ceil(N/64)][D][64] each).
+struct BwdLayout {
+  size_t tq1, tq2, tk1, tk2, total;
+};
+inline size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+BwdLayout bwd_layout(const streamkl_problem *p) {
+  BwdLayout l{};
+  const size_t bh = (size_t)(p->B * p->H);
+  size_t o = round_up(bh * sizeof(float) > 16 ? bh * sizeof(float) : 16, 256);
+  if (p->dtype != STREAMKL_BF16) {
+    l.total = round_up(bh * sizeof(float) > 16 ? bh * sizeof(float) : 16, 16);
+    return l;
+  }
+  const size_t tile = (size_t)skl::kBwdTile;
+  const size_t qt = bh * (((size_t)p->NQ + tile - 1) / tile) * tile * (size_t)p->D * 2;
+  const size_t kt = bh * (((size_t)p->NK + tile - 1) / tile) * tile * (size_t)p->D * 2;
+  l.tq1 = o;
+  l.tq2 = l.tq1 + round_up(qt, 256);
+  l.tk1 = l.tq2 + round_up(qt, 256);
+  l.tk2 = l.tk1 + round_up(kt, 256);
+  l.total = l.tk2 + round_up(kt, 256);
+  return l;
+}
+
 constexpr int kVersion = 100;  // 0.1.0
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -143,9 +168,7 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, c
 
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p) {
   if (check_problem(p) != STREAMKL_OK) return 0;
-  const size_t bh = (size_t)(p->B * p->H);
-  const size_t bytes = bh * sizeof(float);
-  return bytes < 16 ? 16 : (bytes + 15) & ~(size_t)15;
+  return bwd_layout(p).total;
 }
 
 }  // extern "C"
@@ -183,6 +206,14 @@ skl::BwdParams make_bwd(const streamkl_problem *p, const void *q1, const void *k
   b.lse2 = lse2;
   b.g = g;
   b.sigma = reinterpret_cast<const float *>(workspace);
+  if (p->dtype == STREAMKL_BF16) {
+    const BwdLayout l = bwd_layout(p);
+    const char *w = reinterpret_cast<const char *>(workspace);
+    b.tq1 = w + l.tq1;
+    b.tq2 = w + l.tq2;
+    b.tk1 = w + l.tk1;
+    b.tk2 = w + l.tk2;
+  }
   b.dq1 = dq1;
   b.dk1 = dk1;
   b.dq2 = dq2;
@@ -215,12 +246,22 @@ streamkl_status run_dq(const streamkl_problem *p, skl::BwdParams b, hipStream_t 
   return skl::launch_bwd_dq(p->dtype, (int)p->D, b, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
 }
 
-streamkl_status run_prepare(const streamkl_problem *p, const float *g, void *workspace, hipStream_t s) {
+streamkl_status run_prepare(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                            const void *k2, const float *g, void *workspace, hipStream_t s) {
   if (p->NQ == 0) return STREAMKL_OK;
-  return skl::launch_grad_scale(p->dtype, g, p->B * p->H, p->NQ, reinterpret_cast<float *>(workspace), s) ==
-                 hipSuccess
-             ? STREAMKL_OK
-             : STREAMKL_ERR_HIP;
+  const int64_t bh = p->B * p->H;
+  if (skl::launch_grad_scale(p->dtype, g, bh, p->NQ, reinterpret_cast<float *>(workspace), s) != hipSuccess)
+    return STREAMKL_ERR_HIP;
+  if (p->dtype != STREAMKL_BF16) return STREAMKL_OK;
+  const BwdLayout l = bwd_layout(p);
+  char *w = reinterpret_cast<char *>(workspace);
+  const int D = (int)p->D;
+  if (skl::launch_bwd_transpose(D, q1, bh, p->NQ, w + l.tq1, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, q2, bh, p->NQ, w + l.tq2, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, k1, bh, p->NK, w + l.tk1, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, k2, bh, p->NK, w + l.tk2, s) != hipSuccess)
+    return STREAMKL_ERR_HIP;
+  return STREAMKL_OK;
 }
 
 }  // namespace
@@ -241,21 +282,23 @@ streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const vo
   if (st != STREAMKL_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, dk1, dq2, dk2, workspace);
-  if ((st = run_prepare(p, g, workspace, s)) != STREAMKL_OK) return st;
+  if ((st = run_prepare(p, q1, k1, q2, k2, g, workspace, s)) != STREAMKL_OK) return st;
   if ((st = run_dk(p, b, s)) != STREAMKL_OK) return st;
   return run_dq(p, b, s);
 }
 
-streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const float *g, void *workspace,
-                                     size_t workspace_bytes, void *stream) {
+streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                                     const void *k2, const float *g, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
   streamkl_status st = check_problem(p);
   if (st != STREAMKL_OK) return st;
   if (p->B * p->H == 0 || p->NQ == 0) return STREAMKL_OK;
+  if ((st = check_inputs(p, q1, k1, q2, k2)) != STREAMKL_OK) return st;
   if (!g) return STREAMKL_ERR_NULL;
   if (!aligned16(g)) return STREAMKL_ERR_ALIGN;
   if (!workspace || workspace_bytes < streamkl_bwd_workspace_size(p)) return STREAMKL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
-  return run_prepare(p, g, workspace, reinterpret_cast<hipStream_t>(stream));
+  return run_prepare(p, q1, k1, q2, k2, g, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 streamkl_status streamkl_bwd_dk(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,

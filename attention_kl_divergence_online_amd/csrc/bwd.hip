@@ -488,55 +488,72 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
     body(std::false_type{});
 }
 
-// ---- bf16 inputs: two waves per SIMD ----
+// ---- bf16 inputs: two waves per SIMD, software-pipelined stages ----
 //
-// A single wave per SIMD leaves the VALU half idle (one wave issues a VALU op
-// only every few cycles; two waves fill the gaps) and exposes every LDS and
-// barrier wait.  This variant runs eight waves.  Waves p and p + 4 form a pair
-// that shares 32 resident rows: per 64-row streamed stage, wave p + 4e
-// computes logits and dS of streamed block e (rows 32e..32e+31) and posts its
-// dS operands to LDS; after a barrier each wave of the pair accumulates the
-// gradient product over both streamed blocks for its half of D (columns
-// 64e..64e+63 at D = 128).  Per wave that halves the gradient accumulators,
-// which keeps a wave within 256 registers.
+// Eight waves.  Waves p and p + 4 (one SIMD) form a pair that shares 32
+// resident rows; per 64-row streamed stage, wave p + 4e computes the logits
+// and dS of streamed block e (rows 32e..32e+31) for both distributions and
+// accumulates the gradient of distribution e (teacher for e = 0, student for
+// e = 1) over both blocks, for all of D.  The dS of the other distribution is
+// posted to LDS for the partner.  Per wave this keeps 64 accumulator
+// registers, and the exchange is one fp16 operand pair per wave and stage.
+//
+// A single wave per SIMD serialises matrix and vector work; two waves running
+// the same phases do too.  So each wave's stream is pipelined by one stage:
+// after the logits of stage t, the gradient products of stage t - 1 (whose dS
+// is complete) are independent of the dS arithmetic of stage t, and the two
+// are interleaved in one instruction stream.
+//
+// Both products read their streamed operand 16 bytes per lane from LDS: the
+// logits the original bf16 rows (exact products, as in the forward), the
+// gradient product a transposed fp16 copy of the streamed operand written by
+// the prepare step.  Both reach LDS through global_load_lds (no staging
+// registers, no LDS write instructions) into XOR-swizzled layouts.
 template <int D, bool KEYS_RES>
-struct Bwd2Traits {
+struct Bwd4Traits {
   static constexpr int NT = 512;
-  static constexpr int BR = kBwdBR;        // resident rows per workgroup: 4 pairs x 32
-  static constexpr int BX = 64;            // streamed rows per stage
+  static constexpr int BR = kBwdBR;         // resident rows per workgroup: 4 pairs x 32
+  static constexpr int BX = kBwdTile;       // streamed rows per stage
   static constexpr int KSTEPS = D / 16;
-  static constexpr int NDH = D / 64;       // 32-column gradient blocks per wave
-  static constexpr int ROW_BYTES = D * 2;  // one bf16 row in HBM
-  static constexpr int CPR = ROW_BYTES / 16;
-  static constexpr int XROW = D * 2 + 48;  // fp16 row stride in LDS
-  static constexpr int XROW_BYTES = BX * XROW;
-  // Key-resident pass: per streamed query the fp32 stats b1, b2, KL and a
-  // 16-bit sign mask (0x8000 where g < 0), XORed onto the fp16 dS operands.
-  static constexpr int NSTAT = 3;
-  static constexpr int STAT_BYTES = KEYS_RES ? NSTAT * BX * 4 + BX * 2 : 0;
-  static constexpr int OFF_STAT = 2 * XROW_BYTES;
-  static constexpr int STAGE_BYTES = OFF_STAT + STAT_BYTES;
-  static constexpr int DSX_SLOT = 64 * 16;             // one lane-ordered 16-byte operand per lane
-  static constexpr int DSX_BYTES = 4 * 2 * 4 * DSX_SLOT;  // [pair][block][tensor * 2 + ks]
-  static constexpr int OFF_DSX = 2 * STAGE_BYTES;
-  static constexpr int LDS_BYTES = OFF_DSX + DSX_BYTES;
-  static constexpr int CPT = BX * CPR / NT;  // 16-byte staging chunks per thread per tensor
-  static_assert(BR == 4 * 32, "resident tile");
-  static_assert(CPT * NT == BX * CPR, "staging split");
+  static constexpr int NDB = D / 32;        // 32-column gradient blocks
+  static constexpr int RB = D * 2;          // bf16 row bytes
+  static constexpr int CPROW = RB / 16;     // 16-byte chunks per row
+  static constexpr int ROW_T = BX * RB;     // one tensor's row tile
+  static constexpr int TR_T = D * BX * 2;   // one tensor's transposed tile: D rows of 64 fp16
+  static constexpr int OFF_TR = 2 * ROW_T;  // two buffers of 2 * TR_T
+  static constexpr int DSX_SLOT = 64 * 16;  // one lane-ordered 16-byte operand
+  static constexpr int DSX_T = 8 * 2 * DSX_SLOT;  // one stage: [wave][ks]
+  static constexpr int OFF_DSX = OFF_TR + 4 * TR_T;  // two buffers
+  static constexpr int STAT_T = 1024;       // b1, b2, KL (fp32) and sign (16 bit) of 64 queries
+  static constexpr int OFF_STAT = OFF_DSX + 2 * DSX_T;
+  static constexpr int LDS_BYTES = OFF_STAT + (KEYS_RES ? 2 * STAT_T : 0);
+  static constexpr int ROW_LOADS = 2 * ROW_T / 16 / NT;  // 16-byte loads per thread per stage
+  static constexpr int TR_LOADS = 2 * TR_T / 16 / NT;
+  static_assert(BR == 4 * 32 && BX == 64, "tiles");
+  static_assert(ROW_LOADS * 16 * NT == 2 * ROW_T && TR_LOADS * 16 * NT == 2 * TR_T, "load split");
+  static_assert(ROW_T % (16 * NT) == 0 && TR_T % (16 * NT) == 0, "one tensor per load instruction");
+  static_assert((4 * TR_T + 2 * DSX_T) % (16 * NT) == 0, "clear split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(STAGE_BYTES % 16 == 0, "LDS alignment");
 };
 
+// XOR swizzles of the 16-byte chunks within a row, chosen so that the 16 lanes
+// reading one logical chunk of 16 consecutive rows hit 16 distinct slots of a
+// 256-byte bank row.
+template <int D> __device__ __forceinline__ int swz_row(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);  // 256- or 128-byte rows
+}
+__device__ __forceinline__ int swz_tr(int d) { return (d >> 1) & 7; }  // 128-byte rows
+
 template <int D, bool KEYS_RES>
-__global__ __launch_bounds__(512, 1) void bwd2_kernel(BwdParams p) {
-  using Tr = Bwd2Traits<D, KEYS_RES>;
-  using CG = f16x8;
+__global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
+  using Tr = Bwd4Traits<D, KEYS_RES>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  typedef __attribute__((address_space(3))) void lds_void;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int pr = wave & 3;   // pair: resident rows
-  const int e = wave >> 2;   // streamed block for dS, half of D for the gradient
+  const int pr = wave & 3;  // pair: resident rows
+  const int e = wave >> 2;  // streamed block for dS; distribution whose gradient this wave accumulates
   const int h = lane >> 5, c32 = lane & 31;
 
   const int NQ = (int)p.NQ, NK = (int)p.NK;
@@ -544,9 +561,9 @@ __global__ __launch_bounds__(512, 1) void bwd2_kernel(BwdParams p) {
   const int NR = KEYS_RES ? NK : NQ;
   const int NX = KEYS_RES ? NQ : NK;
   const int nrt = (NR + Tr::BR - 1) / Tr::BR;
+  const int nxt = (NX + Tr::BX - 1) / Tr::BX;  // transposed tiles per head
 
-  // Same workgroup order as the one-wave kernel: head-major per XCD, heaviest
-  // resident tiles of a head first.
+  // Head-major order per XCD, heaviest resident tiles of a head first.
   const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t bh = L / (uint32_t)nrt;
   const int rt = KEYS_RES ? (int)(L % (uint32_t)nrt) : nrt - 1 - (int)(L % (uint32_t)nrt);
@@ -557,6 +574,8 @@ __global__ __launch_bounds__(512, 1) void bwd2_kernel(BwdParams p) {
                                                   bh * (int64_t)NX * D);
   const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q2 : p.k2) +
                                                   bh * (int64_t)NX * D);
+  const char *T1 = reinterpret_cast<const char *>(KEYS_RES ? p.tq1 : p.tk1) + bh * (int64_t)nxt * Tr::TR_T;
+  const char *T2 = reinterpret_cast<const char *>(KEYS_RES ? p.tq2 : p.tk2) + bh * (int64_t)nxt * Tr::TR_T;
   const float *KLr = p.kl + bh * (int64_t)NQ;
   const float *LS1 = p.lse1 + bh * (int64_t)NQ;
   const float *LS2 = p.lse2 + bh * (int64_t)NQ;
@@ -581,69 +600,97 @@ __global__ __launch_bounds__(512, 1) void bwd2_kernel(BwdParams p) {
     }
   }
   const int ntiles = x_hi > x_lo ? (x_hi - x_lo + Tr::BX - 1) / Tr::BX : 0;
+  // Streamed tiles start at multiples of 64 rows; the key-resident pass walks
+  // them downward so that all workgroups of a head share their first tiles.
   auto x_of = [&](int t) { return x_lo + (KEYS_RES ? ntiles - 1 - t : t) * Tr::BX; };
 
-  // Resident fragments (B operand of the logits product), converted to fp16.
-  CG rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
+  // Resident fragments (B operand of the logits product): lane's row, elements [16s + 8h, +8).
+  bf16x8 rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
 #pragma unroll
   for (int s = 0; s < Tr::KSTEPS; ++s) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 w1 = r_ok ? *reinterpret_cast<const u32x4 *>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : z;
-    const u32x4 w2 = r_ok ? *reinterpret_cast<const u32x4 *>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : z;
-    rf1[s] = __builtin_bit_cast(CG, bf16x8_to_f16x8(w1));
-    rf2[s] = __builtin_bit_cast(CG, bf16x8_to_f16x8(w2));
+    rf1[s] = r_ok ? *reinterpret_cast<const bf16x8 *>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : bf16x8{};
+    rf2[s] = r_ok ? *reinterpret_cast<const bf16x8 *>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : bf16x8{};
   }
 
   const float c = p.scale * kLog2e;
   float qb1 = kNoGrad, qb2 = kNoGrad, qkl = 0.f, qsg = 1.f;
   if (!KEYS_RES && r_ok) query_stats(LS1[my_r], LS2[my_r], KLr[my_r], Gr[my_r], sigma, qb1, qb2, qkl, qsg);
 
-  // ---- staging: global -> registers -> LDS (fp16 rows) ----
-  u32x4 st[2][Tr::CPT];
-  float sv[Tr::NSTAT];
-  uint32_t sgn = 0;
-  auto gload = [&](int t) {
-    const int xb0 = x_of(t);
+  // ---- staging: global -> LDS without registers ----
+  // Row tile: tensor-major, row r at r * RB, logical chunk c in slot c ^ swz_row(r).
+  auto load_rows = [&](int t) {
+    const int x0 = x_of(t);
+#pragma unroll
+    for (int i = 0; i < Tr::ROW_LOADS; ++i) {
+      const int C = i * Tr::NT + tid;
+      const int tn = C / (Tr::BX * Tr::CPROW);
+      const int rem = C % (Tr::BX * Tr::CPROW);
+      const int row = rem / Tr::CPROW;
+      const int lch = (rem % Tr::CPROW) ^ swz_row<D>(row);
+      const int grow = min(x0 + row, NX - 1);  // rows past the end only feed masked pairs
+      const char *src = (tn ? X2 : X1) + (int64_t)grow * Tr::RB + lch * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(smem + (i * Tr::NT + wave * 64) * 16), 16, 0, 0);
+    }
+  };
+  // Transposed tile into buffer `buf`: tensor-major, column d at d * 128,
+  // logical chunk c in slot c ^ swz_tr(d).
+  auto load_tr = [&](int t, int buf) {
+    const int64_t tile = x_of(t) / Tr::BX;
+#pragma unroll
+    for (int i = 0; i < Tr::TR_LOADS; ++i) {
+      const int C = i * Tr::NT + tid;
+      const int tn = C / (D * 8);
+      const int rem = C % (D * 8);
+      const int d = rem / 8;
+      const int lch = (rem % 8) ^ swz_tr(d);
+      const char *src = (tn ? T2 : T1) + tile * Tr::TR_T + d * 128 + lch * 16;
+      __builtin_amdgcn_global_load_lds(
+          src, (lds_void *)(smem + Tr::OFF_TR + buf * 2 * Tr::TR_T + (i * Tr::NT + wave * 64) * 16), 16, 0, 0);
+    }
+  };
+  // Key-resident pass: statistics of the 64 streamed queries of a stage,
+  // gathered by the first wave into stat buffer `buf`.
+  float sl1 = 0.f, sl2 = 0.f, skl_ = 0.f, sg_ = 0.f;
+  auto stats_load = [&](int t) {
+    if (KEYS_RES && tid < Tr::BX) {
+      const int q = x_of(t) + tid;
+      if (q < NQ) {
+        sl1 = LS1[q];
+        sl2 = LS2[q];
+        skl_ = KLr[q];
+        sg_ = Gr[q];
+      }
+    }
+  };
+  auto stats_store = [&](int t, int buf) {
+    if (KEYS_RES && tid < Tr::BX) {
+      float b1 = kNoGrad, b2 = kNoGrad, kv = 0.f, sg = 1.f;
+      if (x_of(t) + tid < NQ) query_stats(sl1, sl2, skl_, sg_, sigma, b1, b2, kv, sg);
+      float *sb = reinterpret_cast<float *>(smem + Tr::OFF_STAT + buf * Tr::STAT_T);
+      sb[tid] = b1;
+      sb[Tr::BX + tid] = b2;
+      sb[2 * Tr::BX + tid] = kv;
+      reinterpret_cast<uint16_t *>(sb + 3 * Tr::BX)[tid] = sg < 0.f ? 0x8000u : 0u;
+    }
+  };
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // Workgroup barrier that waits for this wave's LDS operations but leaves
+  // global loads in flight (the direct LDS loads are waited for explicitly).
+  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // The pipeline's first step multiplies the second transposed buffer and the
+  // second dS buffer by zero operands: clear them so that they hold no NaN.
+  {
+    constexpr int NCLR = (4 * Tr::TR_T + 2 * Tr::DSX_T) / 16 / Tr::NT;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < Tr::CPT; ++i) {
-      const int cidx = tid + Tr::NT * i;
-      const int row = xb0 + cidx / Tr::CPR, col = cidx % Tr::CPR;
-      const int64_t o = (int64_t)row * Tr::ROW_BYTES + col * 16;
-      st[0][i] = row < NX ? *reinterpret_cast<const u32x4 *>(X1 + o) : z;
-      st[1][i] = row < NX ? *reinterpret_cast<const u32x4 *>(X2 + o) : z;
-    }
-    if (KEYS_RES && tid < Tr::BX) {
-      const int q = xb0 + tid;
-      sv[0] = sv[1] = kNoGrad;
-      sv[2] = 0.f;
-      float sg = 1.f;
-      if (q < NQ) query_stats(LS1[q], LS2[q], KLr[q], Gr[q], sigma, sv[0], sv[1], sv[2], sg);
-      sgn = sg < 0.f ? 0x8000u : 0u;
-    }
-  };
-  auto sstore = [&](int buf) {
-    char *base = smem + buf * Tr::STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < Tr::CPT; ++i) {
-      const int cidx = tid + Tr::NT * i;
-      const int row = cidx / Tr::CPR, col = cidx % Tr::CPR;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-        *reinterpret_cast<u32x4 *>(base + t2 * Tr::XROW_BYTES + row * Tr::XROW + col * 16) =
-            bf16x8_to_f16x8(st[t2][i]);
-    }
-    if (KEYS_RES && tid < Tr::BX) {
-      float *sb = reinterpret_cast<float *>(base + Tr::OFF_STAT);
-#pragma unroll
-      for (int f = 0; f < Tr::NSTAT; ++f) sb[f * Tr::BX + tid] = sv[f];
-      reinterpret_cast<uint16_t *>(sb + Tr::NSTAT * Tr::BX)[tid] = (uint16_t)sgn;
-    }
-  };
-
+    for (int i = 0; i < NCLR; ++i) *reinterpret_cast<u32x4 *>(smem + Tr::OFF_TR + (i * Tr::NT + tid) * 16) = z;
+  }
   if (ntiles > 0) {
-    gload(0);
-    sstore(0);
+    load_rows(0);
+    stats_load(0);
+    stats_store(0, 0);
+    wait_loads();
   }
   __syncthreads();
 
@@ -663,174 +710,226 @@ __global__ __launch_bounds__(512, 1) void bwd2_kernel(BwdParams p) {
     t_b = b;
   }
 
-  // dS operand slots of this wave and of its partner (lane-ordered, conflict-free).
-  char *own_slot = smem + Tr::OFF_DSX + (pr * 2 + e) * 4 * Tr::DSX_SLOT + lane * 16;
-  const char *par_slot = smem + Tr::OFF_DSX + (pr * 2 + (1 - e)) * 4 * Tr::DSX_SLOT + lane * 16;
+  f32x16 acc[Tr::NDB];
+#pragma unroll
+  for (int db = 0; db < Tr::NDB; ++db) acc[db] = f32x16{};
 
-  {
-    f32x16 acc1[Tr::NDH], acc2[Tr::NDH];
+  auto empty_blk = [&](int xa) -> bool {
+    if (KEYS_RES) return xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
+    return ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
+  };
+  // Logits of streamed block e of the row tile.
+  auto logits = [&](f32x16 &x1, f32x16 &x2) {
+    const int row = e * 32 + c32;
+    const int sw = swz_row<D>(row);
+    const char *a1p = smem + row * Tr::RB;
+    const char *a2p = a1p + Tr::ROW_T;
+    x1 = f32x16{};
+    x2 = f32x16{};
 #pragma unroll
-    for (int db = 0; db < Tr::NDH; ++db) {
-      acc1[db] = f32x16{};
-      acc2[db] = f32x16{};
+    for (int s = 0; s < Tr::KSTEPS; ++s) {
+      const int pc = ((2 * s + h) ^ sw) * 16;
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(a1p + pc);
+      const bf16x8 a2 = *reinterpret_cast<const bf16x8 *>(a2p + pc);
+      x1 = mma16(a1, rf1[s], x1);
+      x2 = mma16(a2, rf2[s], x2);
     }
-    // No visible pair between this pair's resident rows and streamed rows [xa, xa + 32).
-    auto empty_blk = [&](int xa) -> bool {
-      if (KEYS_RES) return xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
-      return ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
-    };
-    // Logits and dS of streamed block xb (rows xa..xa+31) -> gradient-product B
-    // operands: bo[ks] (teacher), bo[2 + ks] (student).
-    auto dsblock = [&](const char *base, int xb, int xa, auto mask_tag, CG(&bo)[4]) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      f32x16 x1 = f32x16{}, x2 = f32x16{};
-      {
-        const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 16 * h;
-        const char *a2p = a1p + Tr::XROW_BYTES;
-#pragma unroll
-        for (int s = 0; s < Tr::KSTEPS; ++s) {
-          const CG a1 = *reinterpret_cast<const CG *>(a1p + 32 * s);
-          const CG a2 = *reinterpret_cast<const CG *>(a2p + 32 * s);
-          x1 = mma16(a1, rf1[s], x1);
-          x2 = mma16(a2, rf2[s], x2);
-        }
+  };
+  // dS of the own block (rows xa..xa+31) as gradient-product B operands:
+  // mine[ks] for this wave's distribution, other[ks] for the partner's.
+  auto dsblock = [&](const f32x16 &x1, const f32x16 &x2, int xa, const float *sb, auto mask_tag, f16x8(&mine)[2],
+                     f16x8(&other)[2]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // Visibility in masked blocks: element r is streamed row xa + 4h + cr(r),
+    // cr(r) = 8(r/4) + r%4, and visible exactly when lo <= cr(r) < hi.
+    int lo = 0, hi = 0;
+    if (MASK) {
+      const int base = xa + 4 * h;
+      if (KEYS_RES) {  // streamed query q, resident key my_r: q < NQ, my_r < NK, my_r <= q + off
+        hi = NQ - base;
+        lo = !r_ok ? 1 << 30 : (p.causal ? my_r - off - base : -(1 << 30));
+      } else {  // resident query my_r, streamed key k: my_r < NQ, k < NK, k <= my_r + off
+        hi = min(NK - base, p.causal ? my_r + off - base + 1 : 1 << 30);
+        lo = r_ok ? -(1 << 30) : 1 << 30;
       }
-      const float *sb = reinterpret_cast<const float *>(base + Tr::OFF_STAT);
-      f32x16 d1, d2;
+    }
+    f16x8 b1[2], b2[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 B1, B2, KV;
+      if (KEYS_RES) {
+        const int q = e * 32 + 8 * j + 4 * h;
+        B1 = *reinterpret_cast<const f32x4 *>(sb + q);
+        B2 = *reinterpret_cast<const f32x4 *>(sb + Tr::BX + q);
+        KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
+      } else {
+        B1 = f32x4{qb1, qb1, qb1, qb1};
+        B2 = f32x4{qb2, qb2, qb2, qb2};
+        KV = f32x4{qkl, qkl, qkl, qkl};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * j + u;
+        const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
+        const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
+        const float p1 = fast_exp2(y1);
+        const float p2 = fast_exp2(y2);
+        const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
+        float v2 = p2 - p1;
+        float v1 = p1 * dl;
+        if (MASK) {
+          const int cr = 8 * (r >> 2) + (r & 3);
+          const bool vis = cr >= lo && cr < hi;
+          v1 = vis ? v1 : 0.f;
+          v2 = vis ? v2 : 0.f;
+        }
+        b1[r >> 3][r & 7] = (f16)v1;
+        b2[r >> 3][r & 7] = (f16)v2;
+      }
+    }
+    // Key-resident pass with some g < 0: dS of query q carries sign(g_q).
+    // Slot pair (2m, 2m+1) of k-step ks holds queries 16ks + 4h + {0,2,8,10}[m] + (0, 1).
+    if (KEYS_RES && any_neg) {
+      const char *sgp = reinterpret_cast<const char *>(sb + 3 * Tr::BX) + (e * 32 + 4 * h) * 2;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint2 lo2 = *reinterpret_cast<const uint2 *>(sgp + 32 * ks);
+        const uint2 hi2 = *reinterpret_cast<const uint2 *>(sgp + 32 * ks + 16);
+        const u32x4 m = {lo2.x, lo2.y, hi2.x, hi2.y};
+        b1[ks] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, b1[ks]) ^ m);
+        b2[ks] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, b2[ks]) ^ m);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      mine[ks] = e ? b2[ks] : b1[ks];
+      other[ks] = e ? b1[ks] : b2[ks];
+    }
+  };
+  // Gradient product of this wave's distribution over streamed block xb of
+  // the transposed tile at `trb`: dR^T[d, resident] += X^T[d, streamed] * dS.
+  // The copy stores the 16 rows of a k-step in the dS operands' slot order,
+  // so lane half h reads 8 consecutive positions 32xb + 16ks + 8h.
+  auto grad = [&](int xb, const char *trb, const f16x8(&bo)[2]) {
+    const int sw = swz_tr(c32);
+    const char *tb = trb + e * Tr::TR_T + c32 * 128;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int pc = ((4 * xb + 2 * ks + h) ^ sw) * 16;
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+        const f16x8 a = *reinterpret_cast<const f16x8 *>(tb + db * 32 * 128 + pc);
+        acc[db] = mma16(a, bo[ks], acc[db]);
+      }
+    }
+  };
+
+  // Stage t: the transposed tile of stage t starts loading (second buffer);
+  // logits of stage t; barrier (row tile free); the next row tile starts
+  // loading; dS of stage t interleaved with the gradient products of stage
+  // t - 1; the partner's dS posted; all loads land; barrier.
+  f16x8 prev[2] = {f16x8{}, f16x8{}};  // own block's dS (this wave's distribution) of stage t - 1
+  auto run_tiles = [&](int t0, int t1, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    for (int t = t0; t < t1; ++t) {
+      const bool more = t + 1 < ntiles;
+      const int xt = x_of(t);
+      const bool own_live = !MASK || !empty_blk(xt + 32 * e);
+      const float *sb = reinterpret_cast<const float *>(smem + Tr::OFF_STAT + (t & 1) * Tr::STAT_T);
+      load_tr(t, t & 1);
+      if (more) stats_load(t + 1);
+      f32x16 x1, x2;
+      if (own_live) logits(x1, x2);
+      lds_barrier();
+      if (more) load_rows(t + 1);
+      f16x8 mine[2] = {f16x8{}, f16x8{}}, other[2] = {f16x8{}, f16x8{}};
+      if (own_live) dsblock(x1, x2, xt + 32 * e, sb, mask_tag, mine, other);
+      {
+        // Stage t - 1: own block from registers, partner's block from LDS.
+        const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * 2 * Tr::TR_T;
+        const char *dsp = smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::DSX_SLOT +
+                          lane * 16;
+        f16x8 pb[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
+        grad(e, trp, prev);
+        grad(1 - e, trp, pb);
+      }
+      {
+        char *dsw = smem + Tr::OFF_DSX + (t & 1) * Tr::DSX_T + (wave * 2) * Tr::DSX_SLOT + lane * 16;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<f16x8 *>(dsw + ks * Tr::DSX_SLOT) = other[ks];
+      }
+      prev[0] = mine[0];
+      prev[1] = mine[1];
+      if (more) stats_store(t + 1, (t + 1) & 1);
+      wait_loads();
+      lds_barrier();
+    }
+  };
+  run_tiles(0, t_a, std::true_type{});
+  run_tiles(t_a, t_b, std::false_type{});
+  run_tiles(t_b, ntiles, std::true_type{});
+  if (ntiles > 0) {
+    // Drain: gradient products of the last stage.
+    const int t = ntiles;
+    const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * 2 * Tr::TR_T;
+    const char *dsp =
+        smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::DSX_SLOT + lane * 16;
+    f16x8 pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
+    grad(e, trp, prev);
+    grad(1 - e, trp, pb);
+  }
+
+  // Epilogue: lane writes its resident row of this wave's distribution, d = db*32 + 8j + 4h + (0..3).
+  if (r_ok && (e ? p.want2 : p.want1)) {
+    const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
+    float *O = e ? (KEYS_RES ? p.dk2 : p.dq2) : (KEYS_RES ? p.dk1 : p.dq1);
+    const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f32x4 B1, B2, KV;
-        if (KEYS_RES) {
-          const int q = xb * 32 + 8 * j + 4 * h;
-          B1 = *reinterpret_cast<const f32x4 *>(sb + 0 * Tr::BX + q);
-          B2 = *reinterpret_cast<const f32x4 *>(sb + 1 * Tr::BX + q);
-          KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
-        } else {
-          B1 = f32x4{qb1, qb1, qb1, qb1};
-          B2 = f32x4{qb2, qb2, qb2, qb2};
-          KV = f32x4{qkl, qkl, qkl, qkl};
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * j + u;
-          const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
-          const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
-          const float p1 = fast_exp2(y1);
-          const float p2 = fast_exp2(y2);
-          const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
-          float v2 = p2 - p1;
-          float v1 = p1 * dl;
-          if (MASK) {
-            const int srow = xa + acc_row(r, h);
-            const int qi = KEYS_RES ? srow : my_r;
-            const int kj = KEYS_RES ? my_r : srow;
-            const bool vis = qi < NQ && kj < NK && (!p.causal || kj <= qi + off);
-            v1 = vis ? v1 : 0.f;
-            v2 = vis ? v2 : 0.f;
-          }
-          d1[r] = v1;
-          d2[r] = v2;
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          bo[ks][u] = (f16)d1[8 * ks + u];
-          bo[2 + ks][u] = (f16)d2[8 * ks + u];
-        }
-      }
-      // Key-resident pass with some g < 0: dS of query q carries sign(g_q).
-      // Slot pair (2m, 2m+1) of k-step ks holds queries 16ks + 4h + {0,2,8,10}[m] + (0, 1).
-      if (KEYS_RES && any_neg) {
-        const char *sgp = reinterpret_cast<const char *>(sb + Tr::NSTAT * Tr::BX) + (xb * 32 + 4 * h) * 2;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const uint2 lo = *reinterpret_cast<const uint2 *>(sgp + 32 * ks);
-          const uint2 hi = *reinterpret_cast<const uint2 *>(sgp + 32 * ks + 16);
-          const u32x4 m = {lo.x, lo.y, hi.x, hi.y};
-          bo[ks] = __builtin_bit_cast(CG, __builtin_bit_cast(u32x4, bo[ks]) ^ m);
-          bo[2 + ks] = __builtin_bit_cast(CG, __builtin_bit_cast(u32x4, bo[2 + ks]) ^ m);
-        }
-      }
-    };
-    // Gradient product over streamed block xb for this wave's half of D:
-    // dR^T[d, resident] += X^T[d, streamed] * dS[streamed, resident].
-    auto grad = [&](const char *base, int xb, const CG(&bo)[4]) {
-      const int j16 = lane & 15, grp = lane >> 4;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int db = 0; db < Tr::NDH; ++db) {
-          const int rb = xb * 32 + 16 * ks + 4 * (grp >> 1) + (j16 >> 2);
-          const int d0 = (e * Tr::NDH + db) * 32 + 16 * (grp & 1) + 4 * (j16 & 3);
-          const char *t1 = base + rb * Tr::XROW + d0 * 2;
-          const char *t2 = t1 + Tr::XROW_BYTES;
-          const f16x4 l1 = lds_read_tr16(t1), h1 = lds_read_tr16(t1 + 8 * Tr::XROW);
-          const f16x4 l2 = lds_read_tr16(t2), h2 = lds_read_tr16(t2 + 8 * Tr::XROW);
-          const CG a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-          const CG a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc1[db] = mma16(a1, bo[ks], acc1[db]);
-          acc2[db] = mma16(a2, bo[2 + ks], acc2[db]);
-        }
-      }
-    };
-
-    auto run_tiles = [&](int t0, int t1, auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      for (int t = t0; t < t1; ++t) {
-        const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
-        const int xt = x_of(t);
-        const bool own_live = !MASK || !empty_blk(xt + 32 * e);
-        const bool par_live = !MASK || !empty_blk(xt + 32 * (1 - e));
-        CG bo[4];
-        if (own_live) {
-          dsblock(base, e, xt + 32 * e, mask_tag, bo);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) *reinterpret_cast<CG *>(own_slot + i * Tr::DSX_SLOT) = bo[i];
-        }
-        __syncthreads();
-        // The next stage's global loads overlap the gradient products.
-        if (t + 1 < ntiles) gload(t + 1);
-        if (own_live) grad(base, e, bo);
-        if (par_live) {
-          CG pb[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pb[i] = *reinterpret_cast<const CG *>(par_slot + i * Tr::DSX_SLOT);
-          grad(base, 1 - e, pb);
-        }
-        if (t + 1 < ntiles) sstore((t + 1) & 1);
-        __syncthreads();
-      }
-    };
-    run_tiles(0, t_a, std::true_type{});
-    run_tiles(t_a, t_b, std::false_type{});
-    run_tiles(t_b, ntiles, std::true_type{});
-
-    // Epilogue: lane writes its resident row, d = (e*NDH + db)*32 + 8j + 4h + (0..3).
-    if (r_ok) {
-      const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
-      float *O1 = KEYS_RES ? p.dk1 : p.dq1;
-      float *O2 = KEYS_RES ? p.dk2 : p.dq2;
-      const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
-#pragma unroll
-      for (int db = 0; db < Tr::NDH; ++db) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = (e * Tr::NDH + db) * 32 + 8 * j + 4 * h;
-          if (p.want1) {
-            const f32x4 v = {acc1[db][4 * j] * f, acc1[db][4 * j + 1] * f, acc1[db][4 * j + 2] * f,
-                             acc1[db][4 * j + 3] * f};
-            *reinterpret_cast<f32x4 *>(O1 + rowoff + d) = v;
-          }
-          if (p.want2) {
-            const f32x4 v = {acc2[db][4 * j] * f, acc2[db][4 * j + 1] * f, acc2[db][4 * j + 2] * f,
-                             acc2[db][4 * j + 3] * f};
-            *reinterpret_cast<f32x4 *>(O2 + rowoff + d) = v;
-          }
-        }
+        const int d = db * 32 + 8 * j + 4 * h;
+        const f32x4 v = {acc[db][4 * j] * f, acc[db][4 * j + 1] * f, acc[db][4 * j + 2] * f, acc[db][4 * j + 3] * f};
+        *reinterpret_cast<f32x4 *>(O + rowoff + d) = v;
       }
     }
+  }
+}
+
+// Transposed fp16 copy of one bf16 operand for the gradient product: for each
+// 64-row tile T of each (b, h), out[T][d][pos] = x[64T + row(pos)][d] with
+// row(pos) swapping bits 2 and 3 of pos (the slot order of the dS operands in
+// a 16-row k-step); rows past the end are zero.  One workgroup per (b, h, tile).
+template <int D>
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16 *x, int64_t N, int64_t ntile, f16 *out) {
+  constexpr int CPR = D * 2 / 16;
+  constexpr int LROW = D + 8;  // fp16 elements per LDS row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) f16 tile[kBwdTile * LROW];
+  const int64_t T = blockIdx.x % ntile, bh = blockIdx.x / ntile;
+  const bf16 *xs = x + (bh * N + T * kBwdTile) * D;
+  const int nrow = (int)min<int64_t>(kBwdTile, N - T * kBwdTile);
+  for (int cidx = threadIdx.x; cidx < kBwdTile * CPR; cidx += 256) {
+    const int r = cidx / CPR, cc = cidx % CPR;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (r < nrow) w = *reinterpret_cast<const u32x4 *>(xs + (int64_t)r * D + cc * 8);
+    *reinterpret_cast<u32x4 *>(&tile[r * LROW + cc * 8]) = bf16x8_to_f16x8(w);
+  }
+  __syncthreads();
+  f16 *o = out + (bh * ntile + T) * (int64_t)(D * kBwdTile);
+  for (int cidx = threadIdx.x; cidx < D * (kBwdTile / 8); cidx += 256) {
+    const int d = cidx / (kBwdTile / 8), pc = cidx % (kBwdTile / 8);
+    f16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pos = 8 * pc + i;
+      const int row = (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1);
+      v[i] = tile[row * LROW + d];
+    }
+    *reinterpret_cast<f16x8 *>(o + (int64_t)d * kBwdTile + 8 * pc) = v;
   }
 }
 
@@ -903,22 +1002,35 @@ hipError_t launch_grad_scale(int dtype, const float *g, int64_t BH, int64_t NQ, 
 }
 
 template <int D, bool KEYS_RES>
-static hipError_t launch_pass2(const BwdParams &p, hipStream_t s) {
-  using Tr = Bwd2Traits<D, KEYS_RES>;
+static hipError_t launch_pass4(const BwdParams &p, hipStream_t s) {
+  using Tr = Bwd4Traits<D, KEYS_RES>;
   const int64_t NR = KEYS_RES ? p.NK : p.NQ;
   if (NR == 0) return hipSuccess;
-  const void *fn = reinterpret_cast<const void *>(&bwd2_kernel<D, KEYS_RES>);
+  const void *fn = reinterpret_cast<const void *>(&bwd4_kernel<D, KEYS_RES>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR);
-  hipLaunchKernelGGL((bwd2_kernel<D, KEYS_RES>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  hipLaunchKernelGGL((bwd4_kernel<D, KEYS_RES>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_transpose(int D, const void *x, int64_t BH, int64_t N, void *out, hipStream_t s) {
+  if (BH == 0 || N == 0) return hipSuccess;
+  const int64_t ntile = (N + kBwdTile - 1) / kBwdTile;
+  const dim3 grid((uint32_t)(ntile * BH));
+  if (D == 128)
+    hipLaunchKernelGGL(transpose_kernel<128>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), N, ntile,
+                       reinterpret_cast<f16 *>(out));
+  else
+    hipLaunchKernelGGL(transpose_kernel<64>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), N, ntile,
+                       reinterpret_cast<f16 *>(out));
   return hipGetLastError();
 }
 
 #ifdef SKL_BWD_ONE_WAVE
 #define SKL_BF16_PASS(D, KR) launch_pass<bf16, D, KR>(p, s)
 #else
-#define SKL_BF16_PASS(D, KR) launch_pass2<D, KR>(p, s)
+#define SKL_BF16_PASS(D, KR) launch_pass4<D, KR>(p, s)
 #endif
 
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s) {

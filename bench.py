@@ -236,7 +236,7 @@ def main():
         skl.streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal, out=(kl, l1, l2))
         if ev is not None:
             ev[1].record()
-        skl.streamkl_bwd_prepare(q1, k1, g, w.scale, w.causal, workspace=ws)
+        skl.streamkl_bwd_prepare(q1, k1, q2, k2, g, w.scale, w.causal, workspace=ws)
         if ev is not None:
             ev[2].record()
         skl.streamkl_bwd_dk(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws,

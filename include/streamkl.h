@@ -108,8 +108,10 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p,
                                     void *stream);
 
 /*
- * Bytes of device workspace streamkl_bwd needs (one fp32 per (batch, head)).
- * Returns 0 if the problem is invalid.
+ * Bytes of device workspace streamkl_bwd needs: one fp32 per (batch, head)
+ * and, for bf16 inputs, transposed fp16 copies of q1, q2, k1 and k2
+ * (2 * D * 64 * ceil(N / 64) bytes per (batch, head) and tensor, N = NQ for
+ * the queries, NK for the keys).  Returns 0 if the problem is invalid.
  */
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p);
 
@@ -151,13 +153,19 @@ streamkl_status streamkl_bwd(const streamkl_problem *p,
  * streamkl_bwd_prepare writes into `workspace` one fp32 per (batch, head): the
  * power of two sigma with max_i |g_i| * sigma in [2^7, 2^8), by which the
  * passes scale dS before rounding it to fp16 (1 for fp32 inputs), negated
- * when some g of that head is negative.
+ * when some g of that head is negative; with bf16 inputs it also writes the
+ * transposed fp16 copies of q1, q2, k1, k2 that the gradient products read.
+ * It reads q1, k1, q2, k2 (bf16 inputs only) and g, with the layouts and
+ * alignment rules of streamkl_bwd.
  * streamkl_bwd_dk writes dK1, dK2 (one pass over key tiles, queries streamed);
  * streamkl_bwd_dq writes dQ1, dQ2 (one pass over query tiles, keys streamed).
  * NULL-pair rules, layouts and errors are those of streamkl_bwd; the pass
  * calls read `workspace` and never write it.
  */
-streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const float *g,
+streamkl_status streamkl_bwd_prepare(const streamkl_problem *p,
+                                     const void *q1, const void *k1,
+                                     const void *q2, const void *k2,
+                                     const float *g,
                                      void *workspace, size_t workspace_bytes, void *stream);
 
 streamkl_status streamkl_bwd_dk(const streamkl_problem *p,

@@ -113,10 +113,22 @@ def bwd(L, p, dq1=A, dk1=A, dq2=A, dk2=A, ws=A, wsb=1 << 20, g=A, kl=A):
     return L.streamkl_bwd(ctypes.byref(p), A, A, A, A, kl, A, A, g, dq1, dk1, dq2, dk2, ws, wsb, None)
 
 
+def bf16_workspace(B, H, NQ, NK, D):
+    # sigma (256-byte slot), then transposed fp16 copies of q1, q2 (64-row tiles) and k1, k2.
+    up = lambda n, a: (n + a - 1) // a * a
+    tiles = lambda n: (n + 63) // 64
+    qt, kt = B * H * tiles(NQ) * 64 * D * 2, B * H * tiles(NK) * 64 * D * 2
+    return up(max(16, 4 * B * H), 256) + 2 * up(qt, 256) + 2 * up(kt, 256)
+
+
 def test_backward_validation(L):
     p = P()
-    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == 16
-    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7))) == 96
+    f32 = _lib.STREAMKL_FP32
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(dtype=f32))) == 16
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, dtype=f32))) == 96
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == bf16_workspace(1, 2, 8, 8, 64)
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, NQ=65, NK=200, D=128))) == \
+        bf16_workspace(3, 7, 65, 200, 128)
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(D=32))) == 0
     assert bwd(L, p, dq1=None) == _lib.STREAMKL_ERR_NULL       # half pair
     assert bwd(L, p, dk2=None) == _lib.STREAMKL_ERR_NULL
@@ -132,8 +144,11 @@ def test_backward_validation(L):
 
 def test_backward_step_validation(L):
     p = P()
-    prep = lambda g=A, ws=A, wsb=1 << 20, pp=p: L.streamkl_bwd_prepare(ctypes.byref(pp), g, ws, wsb, None)
+    prep = lambda g=A, ws=A, wsb=1 << 20, pp=p, q1=A, k2=A: L.streamkl_bwd_prepare(ctypes.byref(pp), q1, A, A, k2,
+                                                                                   g, ws, wsb, None)
     assert prep(g=None) == _lib.STREAMKL_ERR_NULL
+    assert prep(q1=None) == _lib.STREAMKL_ERR_NULL
+    assert prep(k2=MIS) == _lib.STREAMKL_ERR_ALIGN
     assert prep(ws=None) == _lib.STREAMKL_ERR_WORKSPACE
     assert prep(wsb=4) == _lib.STREAMKL_ERR_WORKSPACE
     assert prep(ws=MIS) == _lib.STREAMKL_ERR_ALIGN

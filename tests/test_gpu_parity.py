@@ -91,7 +91,7 @@ def test_backward_steps_equal_combined_call():
     kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, True)
     g = torch.rand(2, 2, 300, device=DEV) * 1e-3
     full = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True)
-    ws = streamkl_bwd_prepare(q1, k1, g, None, True)
+    ws = streamkl_bwd_prepare(q1, k1, q2, k2, g, None, True)
     dk1, dk2 = streamkl_bwd_dk(q1, k1, q2, k2, kl, l1, l2, g, None, True, workspace=ws)
     dq1, dq2 = streamkl_bwd_dq(q1, k1, q2, k2, kl, l1, l2, g, None, True, workspace=ws)
     torch.cuda.synchronize()
