@@ -48,9 +48,12 @@ streamkl_status check_problem(const streamkl_problem *p) {
   // A row with no visible key has no distribution to compare.
   if (p->B > 0 && p->H > 0 && p->NQ > 0 && p->NK == 0) return STREAMKL_ERR_SHAPE;
   if (p->causal && p->NQ > p->NK) return STREAMKL_ERR_SHAPE;
-  // In-head offsets are 32-bit; whole tensors use 64-bit bases.
+  // In-head byte offsets are 32-bit (buffer resources, per-head bases);
+  // whole tensors use 64-bit bases.  The largest per-head object is an fp32
+  // gradient tensor; the transposed copies round rows up to 64.
   const int64_t lim = (int64_t)1 << 31;
-  if (p->NQ * p->D >= lim || p->NK * p->D >= lim) return STREAMKL_ERR_SHAPE;
+  const int64_t nmax = (p->NQ > p->NK ? p->NQ : p->NK);
+  if (nmax >= lim || (nmax + 63) / 64 * 64 * p->D * 4 >= lim) return STREAMKL_ERR_SHAPE;
   if (p->B * p->H >= lim || rows < 0) return STREAMKL_ERR_SHAPE;
   if (!(p->scale == p->scale)) return STREAMKL_ERR_SHAPE;  // NaN scale
   return STREAMKL_OK;

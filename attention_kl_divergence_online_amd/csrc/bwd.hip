@@ -520,11 +520,15 @@ struct Bwd4Traits {
   static constexpr int CPROW = RB / 16;     // 16-byte chunks per row
   static constexpr int ROW_T = BX * RB;     // one tensor's row tile
   static constexpr int TR_T = D * BX * 2;   // one tensor's transposed tile: D rows of 64 fp16
-  static constexpr int OFF_TR = 2 * ROW_T;  // two buffers of 2 * TR_T
   static constexpr int DSX_SLOT = 64 * 16;  // one lane-ordered 16-byte operand
   static constexpr int DSX_T = 8 * 2 * DSX_SLOT;  // one stage: [wave][ks]
-  static constexpr int OFF_DSX = OFF_TR + 4 * TR_T;  // two buffers
   static constexpr int STAT_T = 1024;       // b1, b2, KL (fp32) and sign (16 bit) of 64 queries
+  static constexpr int REST = 4 * TR_T + 2 * DSX_T + (KEYS_RES ? 2 * STAT_T : 0);
+  // Two row-tile buffers when they fit (one barrier per stage), else one
+  // (a second barrier per stage releases it for the next tile).
+  static constexpr int ROWBUF = 4 * ROW_T + REST <= 160 * 1024 ? 2 : 1;
+  static constexpr int OFF_TR = ROWBUF * 2 * ROW_T;  // two buffers of 2 * TR_T
+  static constexpr int OFF_DSX = OFF_TR + 4 * TR_T;  // two buffers
   static constexpr int OFF_STAT = OFF_DSX + 2 * DSX_T;
   static constexpr int LDS_BYTES = OFF_STAT + (KEYS_RES ? 2 * STAT_T : 0);
   static constexpr int ROW_LOADS = 2 * ROW_T / 16 / NT;  // 16-byte loads per thread per stage
@@ -535,6 +539,24 @@ struct Bwd4Traits {
   static_assert((4 * TR_T + 2 * DSX_T) % (16 * NT) == 0, "clear split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
+
+// Word 3 of a raw buffer resource (no stride, no swizzle, dword data format):
+// reads past num_records return zero.
+constexpr int kRawBuffer = 0x00020000;
+
+// A byte range read through a raw buffer resource.
+struct BufRange {
+  const void *base;
+  int bytes;
+};
+// 16 bytes per lane from range `r` at byte voff + soff into LDS at
+// lds + 16 * lane (lds must be the same for the whole wave); bytes past the
+// range read as zero.
+__device__ __forceinline__ void buffer_load_lds16(BufRange r, char *lds, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(r.base), 0, r.bytes,
+                                                                      kRawBuffer);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
 
 // XOR swizzles of the 16-byte chunks within a row, chosen so that the 16 lanes
 // reading one logical chunk of 16 consecutive rows hit 16 distinct slots of a
@@ -553,7 +575,7 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int pr = wave & 3;  // pair: resident rows
-  const int e = wave >> 2;  // streamed block for dS; distribution whose gradient this wave accumulates
+  const int e_rt = wave >> 2;  // streamed block for dS; distribution whose gradient this wave accumulates
   const int h = lane >> 5, c32 = lane & 31;
 
   const int NQ = (int)p.NQ, NK = (int)p.NK;
@@ -617,36 +639,45 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   if (!KEYS_RES && r_ok) query_stats(LS1[my_r], LS2[my_r], KLr[my_r], Gr[my_r], sigma, qb1, qb2, qkl, qsg);
 
   // ---- staging: global -> LDS without registers ----
-  // Row tile: tensor-major, row r at r * RB, logical chunk c in slot c ^ swz_row(r).
-  auto load_rows = [&](int t) {
-    const int x0 = x_of(t);
+  // Buffer resources over this head's streamed rows and transposed tiles:
+  // 32-bit offsets, and rows past the end of the streamed operand read as
+  // zero (they only feed masked pairs).
+  const BufRange rx1{X1, NX * Tr::RB}, rx2{X2, NX * Tr::RB};
+  const BufRange rt1{T1, nxt * Tr::TR_T}, rt2{T2, nxt * Tr::TR_T};
+  // Per-lane source offsets within a tile (the same for both tensors).  Row
+  // tile: tensor-major, row r at r * RB, logical chunk c in slot c ^ swz_row(r).
+  // Transposed tile: tensor-major, column d at d * 128, chunk c in slot c ^ swz_tr(d).
+  constexpr int RL = Tr::ROW_LOADS / 2, TL = Tr::TR_LOADS / 2;
+  uint32_t vrow[RL], vtr[TL];
 #pragma unroll
-    for (int i = 0; i < Tr::ROW_LOADS; ++i) {
-      const int C = i * Tr::NT + tid;
-      const int tn = C / (Tr::BX * Tr::CPROW);
-      const int rem = C % (Tr::BX * Tr::CPROW);
-      const int row = rem / Tr::CPROW;
-      const int lch = (rem % Tr::CPROW) ^ swz_row<D>(row);
-      const int grow = min(x0 + row, NX - 1);  // rows past the end only feed masked pairs
-      const char *src = (tn ? X2 : X1) + (int64_t)grow * Tr::RB + lch * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(smem + (i * Tr::NT + wave * 64) * 16), 16, 0, 0);
-    }
+  for (int i = 0; i < RL; ++i) {
+    const int C = i * Tr::NT + tid;
+    const int row = C / Tr::CPROW;
+    vrow[i] = row * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(row)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < TL; ++i) {
+    const int C = i * Tr::NT + tid;
+    const int d = C / 8;
+    vtr[i] = d * 128 + ((C % 8) ^ swz_tr(d)) * 16;
+  }
+  auto load_rows = [&](int t, int buf) {
+    const uint32_t soff = (uint32_t)x_of(t) * Tr::RB;
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int i = 0; i < RL; ++i)
+        buffer_load_lds16(tn ? rx2 : rx1, smem + (buf * 2 + tn) * Tr::ROW_T + (i * Tr::NT + wave * 64) * 16,
+                          vrow[i], soff);
   };
-  // Transposed tile into buffer `buf`: tensor-major, column d at d * 128,
-  // logical chunk c in slot c ^ swz_tr(d).
   auto load_tr = [&](int t, int buf) {
-    const int64_t tile = x_of(t) / Tr::BX;
+    const uint32_t soff = (uint32_t)(x_of(t) / Tr::BX) * Tr::TR_T;
 #pragma unroll
-    for (int i = 0; i < Tr::TR_LOADS; ++i) {
-      const int C = i * Tr::NT + tid;
-      const int tn = C / (D * 8);
-      const int rem = C % (D * 8);
-      const int d = rem / 8;
-      const int lch = (rem % 8) ^ swz_tr(d);
-      const char *src = (tn ? T2 : T1) + tile * Tr::TR_T + d * 128 + lch * 16;
-      __builtin_amdgcn_global_load_lds(
-          src, (lds_void *)(smem + Tr::OFF_TR + buf * 2 * Tr::TR_T + (i * Tr::NT + wave * 64) * 16), 16, 0, 0);
-    }
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int i = 0; i < TL; ++i)
+        buffer_load_lds16(tn ? rt2 : rt1, smem + Tr::OFF_TR + (buf * 2 + tn) * Tr::TR_T + (i * Tr::NT + wave * 64) * 16,
+                          vtr[i], soff);
   };
   // Key-resident pass: statistics of the 64 streamed queries of a stage,
   // gathered by the first wave into stat buffer `buf`.
@@ -687,7 +718,7 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
     for (int i = 0; i < NCLR; ++i) *reinterpret_cast<u32x4 *>(smem + Tr::OFF_TR + (i * Tr::NT + tid) * 16) = z;
   }
   if (ntiles > 0) {
-    load_rows(0);
+    load_rows(0, 0);
     stats_load(0);
     stats_store(0, 0);
     wait_loads();
@@ -710,193 +741,216 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
     t_b = b;
   }
 
-  f32x16 acc[Tr::NDB];
-#pragma unroll
-  for (int db = 0; db < Tr::NDB; ++db) acc[db] = f32x16{};
+  // Specialised per wave role and, in the key-resident pass, per presence of
+  // negative upstream gradients in the head (branch-free stage bodies).
+  auto body = [&](auto e_tag, auto neg_tag) {
+    constexpr int e = decltype(e_tag)::value;
+    constexpr bool NEG = decltype(neg_tag)::value;
+    f32x16 acc[Tr::NDB];
+  #pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) acc[db] = f32x16{};
 
-  auto empty_blk = [&](int xa) -> bool {
-    if (KEYS_RES) return xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
-    return ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
-  };
-  // Logits of streamed block e of the row tile.
-  auto logits = [&](f32x16 &x1, f32x16 &x2) {
-    const int row = e * 32 + c32;
-    const int sw = swz_row<D>(row);
-    const char *a1p = smem + row * Tr::RB;
-    const char *a2p = a1p + Tr::ROW_T;
-    x1 = f32x16{};
-    x2 = f32x16{};
-#pragma unroll
-    for (int s = 0; s < Tr::KSTEPS; ++s) {
-      const int pc = ((2 * s + h) ^ sw) * 16;
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(a1p + pc);
-      const bf16x8 a2 = *reinterpret_cast<const bf16x8 *>(a2p + pc);
-      x1 = mma16(a1, rf1[s], x1);
-      x2 = mma16(a2, rf2[s], x2);
-    }
-  };
-  // dS of the own block (rows xa..xa+31) as gradient-product B operands:
-  // mine[ks] for this wave's distribution, other[ks] for the partner's.
-  auto dsblock = [&](const f32x16 &x1, const f32x16 &x2, int xa, const float *sb, auto mask_tag, f16x8(&mine)[2],
-                     f16x8(&other)[2]) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    // Visibility in masked blocks: element r is streamed row xa + 4h + cr(r),
-    // cr(r) = 8(r/4) + r%4, and visible exactly when lo <= cr(r) < hi.
-    int lo = 0, hi = 0;
-    if (MASK) {
-      const int base = xa + 4 * h;
-      if (KEYS_RES) {  // streamed query q, resident key my_r: q < NQ, my_r < NK, my_r <= q + off
-        hi = NQ - base;
-        lo = !r_ok ? 1 << 30 : (p.causal ? my_r - off - base : -(1 << 30));
-      } else {  // resident query my_r, streamed key k: my_r < NQ, k < NK, k <= my_r + off
-        hi = min(NK - base, p.causal ? my_r + off - base + 1 : 1 << 30);
-        lo = r_ok ? -(1 << 30) : 1 << 30;
+    auto empty_blk = [&](int xa) -> bool {
+      if (KEYS_RES) return xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
+      return ra >= NQ || xa >= NK || (p.causal && xa > ra + 31 + off);
+    };
+    // Logits of streamed block e of the row tile at `rowb`.
+    auto logits = [&](const char *rowb, f32x16 &x1, f32x16 &x2) {
+      const int row = e * 32 + c32;
+      const int sw = swz_row<D>(row);
+      const char *a1p = rowb + row * Tr::RB;
+      const char *a2p = a1p + Tr::ROW_T;
+      x1 = f32x16{};
+      x2 = f32x16{};
+  #pragma unroll
+      for (int s = 0; s < Tr::KSTEPS; ++s) {
+        const int pc = ((2 * s + h) ^ sw) * 16;
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(a1p + pc);
+        const bf16x8 a2 = *reinterpret_cast<const bf16x8 *>(a2p + pc);
+        x1 = mma16(a1, rf1[s], x1);
+        x2 = mma16(a2, rf2[s], x2);
       }
-    }
-    f16x8 b1[2], b2[2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4 B1, B2, KV;
-      if (KEYS_RES) {
-        const int q = e * 32 + 8 * j + 4 * h;
-        B1 = *reinterpret_cast<const f32x4 *>(sb + q);
-        B2 = *reinterpret_cast<const f32x4 *>(sb + Tr::BX + q);
-        KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
-      } else {
-        B1 = f32x4{qb1, qb1, qb1, qb1};
-        B2 = f32x4{qb2, qb2, qb2, qb2};
-        KV = f32x4{qkl, qkl, qkl, qkl};
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * j + u;
-        const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
-        const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
-        const float p1 = fast_exp2(y1);
-        const float p2 = fast_exp2(y2);
-        const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
-        float v2 = p2 - p1;
-        float v1 = p1 * dl;
-        if (MASK) {
-          const int cr = 8 * (r >> 2) + (r & 3);
-          const bool vis = cr >= lo && cr < hi;
-          v1 = vis ? v1 : 0.f;
-          v2 = vis ? v2 : 0.f;
+    };
+    // dS of the own block (rows xa..xa+31) as gradient-product B operands:
+    // mine[ks] for this wave's distribution, other[ks] for the partner's.
+    auto dsblock = [&](const f32x16 &x1, const f32x16 &x2, int xa, const float *sb, auto mask_tag, f16x8(&mine)[2],
+                       f16x8(&other)[2]) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // Visibility in masked blocks: element r is streamed row xa + 4h + cr(r),
+      // cr(r) = 8(r/4) + r%4, and visible exactly when lo <= cr(r) < hi.
+      int lo = 0, hi = 0;
+      if (MASK) {
+        const int base = xa + 4 * h;
+        if (KEYS_RES) {  // streamed query q, resident key my_r: q < NQ, my_r < NK, my_r <= q + off
+          hi = NQ - base;
+          lo = !r_ok ? 1 << 30 : (p.causal ? my_r - off - base : -(1 << 30));
+        } else {  // resident query my_r, streamed key k: my_r < NQ, k < NK, k <= my_r + off
+          hi = min(NK - base, p.causal ? my_r + off - base + 1 : 1 << 30);
+          lo = r_ok ? -(1 << 30) : 1 << 30;
         }
-        b1[r >> 3][r & 7] = (f16)v1;
-        b2[r >> 3][r & 7] = (f16)v2;
       }
-    }
-    // Key-resident pass with some g < 0: dS of query q carries sign(g_q).
-    // Slot pair (2m, 2m+1) of k-step ks holds queries 16ks + 4h + {0,2,8,10}[m] + (0, 1).
-    if (KEYS_RES && any_neg) {
-      const char *sgp = reinterpret_cast<const char *>(sb + 3 * Tr::BX) + (e * 32 + 4 * h) * 2;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint2 lo2 = *reinterpret_cast<const uint2 *>(sgp + 32 * ks);
-        const uint2 hi2 = *reinterpret_cast<const uint2 *>(sgp + 32 * ks + 16);
-        const u32x4 m = {lo2.x, lo2.y, hi2.x, hi2.y};
-        b1[ks] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, b1[ks]) ^ m);
-        b2[ks] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, b2[ks]) ^ m);
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      mine[ks] = e ? b2[ks] : b1[ks];
-      other[ks] = e ? b1[ks] : b2[ks];
-    }
-  };
-  // Gradient product of this wave's distribution over streamed block xb of
-  // the transposed tile at `trb`: dR^T[d, resident] += X^T[d, streamed] * dS.
-  // The copy stores the 16 rows of a k-step in the dS operands' slot order,
-  // so lane half h reads 8 consecutive positions 32xb + 16ks + 8h.
-  auto grad = [&](int xb, const char *trb, const f16x8(&bo)[2]) {
-    const int sw = swz_tr(c32);
-    const char *tb = trb + e * Tr::TR_T + c32 * 128;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int pc = ((4 * xb + 2 * ks + h) ^ sw) * 16;
-#pragma unroll
-      for (int db = 0; db < Tr::NDB; ++db) {
-        const f16x8 a = *reinterpret_cast<const f16x8 *>(tb + db * 32 * 128 + pc);
-        acc[db] = mma16(a, bo[ks], acc[db]);
-      }
-    }
-  };
-
-  // Stage t: the transposed tile of stage t starts loading (second buffer);
-  // logits of stage t; barrier (row tile free); the next row tile starts
-  // loading; dS of stage t interleaved with the gradient products of stage
-  // t - 1; the partner's dS posted; all loads land; barrier.
-  f16x8 prev[2] = {f16x8{}, f16x8{}};  // own block's dS (this wave's distribution) of stage t - 1
-  auto run_tiles = [&](int t0, int t1, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    for (int t = t0; t < t1; ++t) {
-      const bool more = t + 1 < ntiles;
-      const int xt = x_of(t);
-      const bool own_live = !MASK || !empty_blk(xt + 32 * e);
-      const float *sb = reinterpret_cast<const float *>(smem + Tr::OFF_STAT + (t & 1) * Tr::STAT_T);
-      load_tr(t, t & 1);
-      if (more) stats_load(t + 1);
-      f32x16 x1, x2;
-      if (own_live) logits(x1, x2);
-      lds_barrier();
-      if (more) load_rows(t + 1);
-      f16x8 mine[2] = {f16x8{}, f16x8{}}, other[2] = {f16x8{}, f16x8{}};
-      if (own_live) dsblock(x1, x2, xt + 32 * e, sb, mask_tag, mine, other);
-      {
-        // Stage t - 1: own block from registers, partner's block from LDS.
-        const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * 2 * Tr::TR_T;
-        const char *dsp = smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::DSX_SLOT +
-                          lane * 16;
-        f16x8 pb[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
-        grad(e, trp, prev);
-        grad(1 - e, trp, pb);
-      }
-      {
-        char *dsw = smem + Tr::OFF_DSX + (t & 1) * Tr::DSX_T + (wave * 2) * Tr::DSX_SLOT + lane * 16;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<f16x8 *>(dsw + ks * Tr::DSX_SLOT) = other[ks];
-      }
-      prev[0] = mine[0];
-      prev[1] = mine[1];
-      if (more) stats_store(t + 1, (t + 1) & 1);
-      wait_loads();
-      lds_barrier();
-    }
-  };
-  run_tiles(0, t_a, std::true_type{});
-  run_tiles(t_a, t_b, std::false_type{});
-  run_tiles(t_b, ntiles, std::true_type{});
-  if (ntiles > 0) {
-    // Drain: gradient products of the last stage.
-    const int t = ntiles;
-    const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * 2 * Tr::TR_T;
-    const char *dsp =
-        smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::DSX_SLOT + lane * 16;
-    f16x8 pb[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
-    grad(e, trp, prev);
-    grad(1 - e, trp, pb);
-  }
-
-  // Epilogue: lane writes its resident row of this wave's distribution, d = db*32 + 8j + 4h + (0..3).
-  if (r_ok && (e ? p.want2 : p.want1)) {
-    const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
-    float *O = e ? (KEYS_RES ? p.dk2 : p.dq2) : (KEYS_RES ? p.dk1 : p.dq1);
-    const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
-#pragma unroll
-    for (int db = 0; db < Tr::NDB; ++db) {
-#pragma unroll
+      f16x8 b1[2], b2[2];
+  #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + 8 * j + 4 * h;
-        const f32x4 v = {acc[db][4 * j] * f, acc[db][4 * j + 1] * f, acc[db][4 * j + 2] * f, acc[db][4 * j + 3] * f};
-        *reinterpret_cast<f32x4 *>(O + rowoff + d) = v;
+        f32x4 B1, B2, KV;
+        if (KEYS_RES) {
+          const int q = e * 32 + 8 * j + 4 * h;
+          B1 = *reinterpret_cast<const f32x4 *>(sb + q);
+          B2 = *reinterpret_cast<const f32x4 *>(sb + Tr::BX + q);
+          KV = *reinterpret_cast<const f32x4 *>(sb + 2 * Tr::BX + q);
+        } else {
+          B1 = f32x4{qb1, qb1, qb1, qb1};
+          B2 = f32x4{qb2, qb2, qb2, qb2};
+          KV = f32x4{qkl, qkl, qkl, qkl};
+        }
+  #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * j + u;
+          const float y1 = __builtin_fmaf(x1[r], c, -B1[u]);
+          const float y2 = __builtin_fmaf(x2[r], c, -B2[u]);
+          const float p1 = fast_exp2(y1);
+          const float p2 = fast_exp2(y2);
+          const float dl = __builtin_fmaf(y1 - y2, kLn2, -KV[u]);
+          float v2 = p2 - p1;
+          float v1 = p1 * dl;
+          if (MASK) {
+            const int cr = 8 * (r >> 2) + (r & 3);
+            const bool vis = cr >= lo && cr < hi;
+            v1 = vis ? v1 : 0.f;
+            v2 = vis ? v2 : 0.f;
+          }
+          b1[r >> 3][r & 7] = (f16)v1;
+          b2[r >> 3][r & 7] = (f16)v2;
+        }
+      }
+      // Key-resident pass with some g < 0: dS of query q carries sign(g_q).
+      // Slot pair (2m, 2m+1) of k-step ks holds queries 16ks + 4h + {0,2,8,10}[m] + (0, 1).
+      if (KEYS_RES && NEG) {
+        const char *sgp = reinterpret_cast<const char *>(sb + 3 * Tr::BX) + (e * 32 + 4 * h) * 2;
+  #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint2 lo2 = *reinterpret_cast<const uint2 *>(sgp + 32 * ks);
+          const uint2 hi2 = *reinterpret_cast<const uint2 *>(sgp + 32 * ks + 16);
+          const u32x4 m = {lo2.x, lo2.y, hi2.x, hi2.y};
+          b1[ks] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, b1[ks]) ^ m);
+          b2[ks] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, b2[ks]) ^ m);
+        }
+      }
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        mine[ks] = e ? b2[ks] : b1[ks];
+        other[ks] = e ? b1[ks] : b2[ks];
+      }
+    };
+    // Gradient product of this wave's distribution over streamed block xb of
+    // the transposed tile at `trb`: dR^T[d, resident] += X^T[d, streamed] * dS.
+    // The copy stores the 16 rows of a k-step in the dS operands' slot order,
+    // so lane half h reads 8 consecutive positions 32xb + 16ks + 8h.
+    auto grad = [&](int xb, const char *trb, const f16x8(&bo)[2]) {
+      const int sw = swz_tr(c32);
+      const char *tb = trb + e * Tr::TR_T + c32 * 128;
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int pc = ((4 * xb + 2 * ks + h) ^ sw) * 16;
+  #pragma unroll
+        for (int db = 0; db < Tr::NDB; ++db) {
+          const f16x8 a = *reinterpret_cast<const f16x8 *>(tb + db * 32 * 128 + pc);
+          acc[db] = mma16(a, bo[ks], acc[db]);
+        }
+      }
+    };
+
+    // Stage t: the transposed tile of stage t starts loading (second buffer),
+    // with two row buffers the next row tile too; logits of stage t; with one
+    // row buffer a barrier (row tile free) and then the next row tile starts
+    // loading; dS of stage t interleaved with the gradient products of stage
+    // t - 1; the partner's dS posted; all loads land; barrier.
+    f16x8 prev[2] = {f16x8{}, f16x8{}};  // own block's dS (this wave's distribution) of stage t - 1
+    auto run_tiles = [&](int t0, int t1, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      for (int t = t0; t < t1; ++t) {
+        const bool more = t + 1 < ntiles;
+        const int xt = x_of(t);
+        const bool own_live = !MASK || !empty_blk(xt + 32 * e);
+        const float *sb = reinterpret_cast<const float *>(smem + Tr::OFF_STAT + (t & 1) * Tr::STAT_T);
+        load_tr(t, t & 1);
+        if (Tr::ROWBUF == 2 && more) load_rows(t + 1, (t + 1) & 1);
+        if (more) stats_load(t + 1);
+        f32x16 x1, x2;
+        if (own_live) logits(smem + (Tr::ROWBUF == 2 ? (t & 1) * 2 * Tr::ROW_T : 0), x1, x2);
+        if (Tr::ROWBUF == 1) {
+          lds_barrier();
+          if (more) load_rows(t + 1, 0);
+        }
+        f16x8 mine[2] = {f16x8{}, f16x8{}}, other[2] = {f16x8{}, f16x8{}};
+        if (own_live) dsblock(x1, x2, xt + 32 * e, sb, mask_tag, mine, other);
+        {
+          // Stage t - 1: own block from registers, partner's block from LDS.
+          const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * 2 * Tr::TR_T;
+          const char *dsp = smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::DSX_SLOT +
+                            lane * 16;
+          f16x8 pb[2];
+  #pragma unroll
+          for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
+          grad(e, trp, prev);
+          grad(1 - e, trp, pb);
+        }
+        {
+          char *dsw = smem + Tr::OFF_DSX + (t & 1) * Tr::DSX_T + (wave * 2) * Tr::DSX_SLOT + lane * 16;
+  #pragma unroll
+          for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<f16x8 *>(dsw + ks * Tr::DSX_SLOT) = other[ks];
+        }
+        prev[0] = mine[0];
+        prev[1] = mine[1];
+        if (more) stats_store(t + 1, (t + 1) & 1);
+        wait_loads();
+        lds_barrier();
+      }
+    };
+    run_tiles(0, t_a, std::true_type{});
+    run_tiles(t_a, t_b, std::false_type{});
+    run_tiles(t_b, ntiles, std::true_type{});
+    if (ntiles > 0) {
+      // Drain: gradient products of the last stage.
+      const int t = ntiles;
+      const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * 2 * Tr::TR_T;
+      const char *dsp =
+          smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::DSX_SLOT + lane * 16;
+      f16x8 pb[2];
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
+      grad(e, trp, prev);
+      grad(1 - e, trp, pb);
+    }
+
+    // Epilogue: lane writes its resident row of this wave's distribution, d = db*32 + 8j + 4h + (0..3).
+    if (r_ok && (e ? p.want2 : p.want1)) {
+      const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
+      float *O = e ? (KEYS_RES ? p.dk2 : p.dq2) : (KEYS_RES ? p.dk1 : p.dq1);
+      const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
+  #pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = db * 32 + 8 * j + 4 * h;
+          const f32x4 v = {acc[db][4 * j] * f, acc[db][4 * j + 1] * f, acc[db][4 * j + 2] * f, acc[db][4 * j + 3] * f};
+          *reinterpret_cast<f32x4 *>(O + rowoff + d) = v;
+        }
       }
     }
+  };
+  using E0 = std::integral_constant<int, 0>;
+  using E1 = std::integral_constant<int, 1>;
+  if (KEYS_RES && any_neg) {
+    if (e_rt)
+      body(E1{}, std::true_type{});
+    else
+      body(E0{}, std::true_type{});
+  } else {
+    if (e_rt)
+      body(E1{}, std::false_type{});
+    else
+      body(E0{}, std::false_type{});
   }
 }
 
