@@ -27,10 +27,10 @@ sys.path.insert(0, ROOT)
 METRIC = "attn-KL fwd and fwd+bwd TFLOP/s + ms at 64K ctx, 32 heads, d=128 bf16"
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_kl_causal_64k_hbm_traffic.json")
 COPY_BYTES = 1 << 30
-KERNELS = {  # bench key -> mangled kernel symbol
-    "fwd": "_ZN3skl10fwd_kernelIDF16bLi128ELb0EEEvNS_9FwdParamsE",
-    "bwd_dk": "_ZN3skl10bwd_kernelIDF16bLi128ELb1EEEvNS_9BwdParamsE",
-    "bwd_dq": "_ZN3skl10bwd_kernelIDF16bLi128ELb0EEEvNS_9BwdParamsE",
+KERNELS = {  # bench key -> kernel names as rocprofv3 reports them (mangled or demangled)
+    "fwd": ("_ZN3skl10fwd_kernelIDF16bLi128ELb0EEEvNS_9FwdParamsE", "void skl::fwd_kernel<__bf16, 128, false>"),
+    "bwd_dk": ("_ZN3skl11bwd4_kernelILi128ELb1EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, true>"),
+    "bwd_dq": ("_ZN3skl11bwd4_kernelILi128ELb0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, false>"),
 }
 
 
@@ -61,8 +61,8 @@ def summarize_traffic(fetch_csv: str, write_csv: str) -> None:
                 continue
             v = float(r["Counter_Value"]) * 1024.0
             name = r["Kernel_Name"]
-            for key, sym in KERNELS.items():
-                if name.startswith(sym):
+            for key, syms in KERNELS.items():
+                if name.startswith(syms):
                     per.setdefault(key, []).append(v)
             if "copy" in name.lower() or "elementwise" in name.lower():
                 copy_vals.append(v)
@@ -110,11 +110,11 @@ def summarize_counters(csvs, out_path: str) -> None:
     vals = {}
     for path in csvs:
         for r in csv.DictReader(open(path)):
-            for key, sym in KERNELS.items():
-                if r["Kernel_Name"].startswith(sym):
+            for key, syms in KERNELS.items():
+                if r["Kernel_Name"].startswith(syms):
                     vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     simds, xcds = 1024, 8
-    lines = [f"{'kernel':8s} {'ms':>7s} {'MFMA busy':>10s} {'VALU/wave':>10s} {'wait/wave':>10s} "
+    lines = [f"{'kernel':8s} {'ms@2.4G':>7s} {'MFMA busy':>10s} {'VALU/wave':>10s} {'wait/wave':>10s} "
              f"{'LDS conflict':>13s} {'VALU lane-op/pair':>18s} {'exp/pair':>9s}"]
     import synth
     pairs = synth.get("causal_64k").visible_pairs()
@@ -286,8 +286,8 @@ def main():
     kern_flop = {"fwd": fwd_flop, "bwd_dk": 8 * w.D * pairs, "bwd_dq": 8 * w.D * pairs}
     dom = max(kern_flop, key=lambda k: per[k])
     achieved = kern_flop[dom] / (per[dom] * 1e-3) / 1e12
-    kernel_names = {"fwd": "fwd_kernel<bf16,128,false>", "bwd_dk": "bwd_kernel<bf16,128,true>",
-                    "bwd_dq": "bwd_kernel<bf16,128,false>"}
+    kernel_names = {"fwd": "fwd_kernel<bf16,128,unsplit>", "bwd_dk": "bwd4_kernel<128,keys resident>",
+                    "bwd_dq": "bwd4_kernel<128,queries resident>"}
 
     out = {
         "metric": METRIC,
