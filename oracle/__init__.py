@@ -42,23 +42,27 @@ def build(force: bool = True) -> str:
     return LIB_PATH
 
 
+def configure(lib):
+    """Declare the C oracle's signatures on a loaded library and return it."""
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int64)
+    i64, dbl, cint = ctypes.c_int64, ctypes.c_double, ctypes.c_int
+    lib.skl_oracle_fwd.argtypes = [i64, i64, i64, dbl, cint, dp, dp, dp, dp, ip, i64, dp, dp, dp]
+    lib.skl_oracle_fwd.restype = cint
+    lib.skl_oracle_bwd.argtypes = [i64, i64, i64, dbl, cint, dp, dp, dp, dp, ip, i64, dp,
+                                   dp, dp, dp, dp, dp, dp, dp]
+    lib.skl_oracle_bwd.restype = cint
+    lib.skl_oracle_threads.argtypes = []
+    lib.skl_oracle_threads.restype = cint
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             build(force=False)
-        lib = ctypes.CDLL(LIB_PATH)
-        dp = ctypes.POINTER(ctypes.c_double)
-        ip = ctypes.POINTER(ctypes.c_int64)
-        i64, dbl, cint = ctypes.c_int64, ctypes.c_double, ctypes.c_int
-        lib.skl_oracle_fwd.argtypes = [i64, i64, i64, dbl, cint, dp, dp, dp, dp, ip, i64, dp, dp, dp]
-        lib.skl_oracle_fwd.restype = cint
-        lib.skl_oracle_bwd.argtypes = [i64, i64, i64, dbl, cint, dp, dp, dp, dp, ip, i64, dp,
-                                       dp, dp, dp, dp, dp, dp, dp]
-        lib.skl_oracle_bwd.restype = cint
-        lib.skl_oracle_threads.argtypes = []
-        lib.skl_oracle_threads.restype = cint
-        _lib = lib
+        _lib = configure(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

@@ -7,7 +7,8 @@ independent route: a high-precision brute force through probabilities
 autograd), closed forms, invariants, finite differences, and the pages' own
 online recurrence (gist.science "Formulacion Online").  Any of a dropped term,
 a sign error, a transposed operand, an off-by-one causal mask or a wrong scale
-fails at least one of them (see test_mutants_are_caught).
+fails at least one of them (tests/test_oracle_mutants.py plants such mistakes in a
+copy of the oracle and checks that they are caught).
 """
 import math
 
