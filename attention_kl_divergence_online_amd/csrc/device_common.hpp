@@ -77,4 +77,29 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
   return (w & 7u) * (n >> 3) + (w >> 3);
 }
 
+// Word 3 of a raw buffer resource (no stride, no swizzle, dword data format):
+// reads past num_records return zero.
+constexpr int kRawBuffer = 0x00020000;
+
+// A byte range read through a raw buffer resource.
+struct BufRange {
+  const void *base;
+  int bytes;
+};
+// 16 bytes per lane from range `r` at byte voff + soff into LDS at
+// lds + 16 * lane (lds must be the same for the whole wave); bytes past the
+// range read as zero.
+__device__ __forceinline__ void buffer_load_lds16(BufRange r, char *lds, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(r.base), 0, r.bytes,
+                                                                      kRawBuffer);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
+// XOR swizzles of the 16-byte chunks within a row, chosen so that the 16 lanes
+// reading one logical chunk of 16 consecutive rows hit 16 distinct slots of a
+// 256-byte bank row.
+template <int D> __device__ __forceinline__ int swz_row(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);  // 256- or 128-byte rows
+}
+
 }  // namespace skl

@@ -421,6 +421,209 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(FwdParams p) {
   finish_row(M1, L1, M2, L2, A, p.scale, p.kl + idx, p.lse1 + idx, p.lse2 + idx);
 }
 
+// ---- bf16 inputs: direct LDS staging, pipelined key blocks ----
+//
+// Eight waves (two per SIMD), each owning 32 queries; 64-key tiles of K1 and
+// K2 reach LDS through buffer loads (no staging registers, rows past NK read
+// as zero) into double buffers with XOR-swizzled 16-byte chunks, one barrier
+// per tile.  A wave walks its 32-key blocks as a pipeline: the logits of block
+// b + 1 are computed while the online update of block b runs, in one
+// instruction stream whenever both blocks are fully visible (no mask code).
+template <int D>
+struct Fwd2Traits {
+  static constexpr int NT = 512;
+  static constexpr int BQ = 256;        // 8 waves x 32 queries
+  static constexpr int BK = kFwdBK;     // keys per tile
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int RB = D * 2;      // bf16 row bytes
+  static constexpr int CPROW = RB / 16;
+  static constexpr int ROW_T = BK * RB;  // one tensor's key tile
+  static constexpr int LDS_BYTES = 2 * 2 * ROW_T;
+  static constexpr int LOADS = ROW_T / 16 / NT;  // per tensor per thread
+  static_assert(BK == 64 && LOADS * 16 * NT == ROW_T, "tiles");
+};
+
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
+  using Tr = Fwd2Traits<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c32 = lane & 31;
+
+  int qt, sp;
+  int64_t bh;
+  if (SPLIT) {
+    // Workgroups that share a key chunk are adjacent logical ids on one XCD.
+    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    qt = (int)(L % (uint32_t)p.nqt);
+    const uint32_t rest = L / (uint32_t)p.nqt;
+    sp = (int)(rest % (uint32_t)p.splits);
+    bh = rest / (uint32_t)p.splits;
+  } else {
+    // Head-major with each XCD on a contiguous run of heads; within a head
+    // the longest (last) query tiles go first.
+    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    bh = L / (uint32_t)p.nqt;
+    qt = p.nqt - 1 - (int)(L % (uint32_t)p.nqt);
+    sp = 0;
+  }
+
+  const int NQ = (int)p.NQ, NK = (int)p.NK;
+  const int off = NK - NQ;
+  const bf16 *Q1 = reinterpret_cast<const bf16 *>(p.q1) + bh * (int64_t)NQ * D;
+  const bf16 *Q2 = reinterpret_cast<const bf16 *>(p.q2) + bh * (int64_t)NQ * D;
+  const BufRange rk1{reinterpret_cast<const bf16 *>(p.k1) + bh * (int64_t)NK * D, NK * Tr::RB};
+  const BufRange rk2{reinterpret_cast<const bf16 *>(p.k2) + bh * (int64_t)NK * D, NK * Tr::RB};
+
+  const int q0 = qt * Tr::BQ;
+  const int qend = min(q0 + Tr::BQ, NQ);
+  const int qw0 = q0 + wave * 32;
+  const int qw_last = min(qw0 + 31, qend - 1);
+  const bool wave_live = qw0 <= qw_last;
+
+  const int kwg_end = p.causal ? min(NK, qend - 1 + off + 1) : NK;
+  const int k_lo = SPLIT ? sp * p.chunk : 0;
+  const int k_hi = SPLIT ? min(k_lo + p.chunk, kwg_end) : kwg_end;
+  const int ntiles = k_hi > k_lo ? (k_hi - k_lo + Tr::BK - 1) / Tr::BK : 0;
+
+  // This wave's 32-key blocks from k_lo: [0, nfull) are visible to all its
+  // queries, [nfull, nlive) to some, the rest to none.
+  const int vis_all = min(k_hi, p.causal ? qw0 + off + 1 : NK);
+  const int vis_any = min(k_hi, p.causal ? qw_last + off + 1 : NK);
+  const int nfull = wave_live ? max(0, vis_all - k_lo) / 32 : 0;
+  const int nlive = wave_live ? (max(0, vis_any - k_lo) + 31) / 32 : 0;
+
+  // Resident query fragments: lane owns query qw0 + c32, elements [16s + 8h, +8).
+  const int row = qw0 + c32;
+  const bool row_ok = row < qend;
+  const int klim = min(k_hi, p.causal ? row + off + 1 : NK);
+  bf16x8 qf1[Tr::KSTEPS], qf2[Tr::KSTEPS];
+#pragma unroll
+  for (int s = 0; s < Tr::KSTEPS; ++s) {
+    qf1[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(Q1 + (int64_t)row * D + 16 * s + 8 * h) : bf16x8{};
+    qf2[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(Q2 + (int64_t)row * D + 16 * s + 8 * h) : bf16x8{};
+  }
+
+  const float c = p.scale * kLog2e;
+  RowState st{kNegBig, 0.f, kNegBig, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+  // Key tile t into buffer t & 1: tensor-major, key r at r * RB, logical
+  // chunk c in slot c ^ swz_row(r).
+  uint32_t voff[Tr::LOADS];
+#pragma unroll
+  for (int i = 0; i < Tr::LOADS; ++i) {
+    const int C = i * Tr::NT + tid;
+    const int r = C / Tr::CPROW;
+    voff[i] = r * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(r)) * 16;
+  }
+  auto load_tile = [&](int t) {
+    const uint32_t soff = (uint32_t)(k_lo + t * Tr::BK) * Tr::RB;
+    char *buf = smem + (t & 1) * 2 * Tr::ROW_T;
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int i = 0; i < Tr::LOADS; ++i)
+        buffer_load_lds16(tn ? rk2 : rk1, buf + tn * Tr::ROW_T + (i * Tr::NT + wave * 64) * 16, voff[i], soff);
+  };
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // Logits of block b (key block b % 2 of tile b / 2).
+  auto scores = [&](int b, f32x16 &s1, f32x16 &s2) {
+    const int kr = (b & 1) * 32 + c32;
+    const int sw = swz_row<D>(kr);
+    const char *r1 = smem + ((b >> 1) & 1) * 2 * Tr::ROW_T + kr * Tr::RB;
+    const char *r2 = r1 + Tr::ROW_T;
+    s1 = f32x16{};
+    s2 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < Tr::KSTEPS; ++s) {
+      const int pc = ((2 * s + h) ^ sw) * 16;
+      s1 = mma16(*reinterpret_cast<const bf16x8 *>(r1 + pc), qf1[s], s1);
+      s2 = mma16(*reinterpret_cast<const bf16x8 *>(r2 + pc), qf2[s], s2);
+    }
+  };
+  auto update = [&](int b, const f32x16 &s1, const f32x16 &s2) {
+    const int kbase = k_lo + b * 32;
+    if (b < nfull)
+      online_update<false, false>(s1, s2, st, c, kbase, h, 0);
+    else
+      online_update<true, false>(s1, s2, st, c, kbase, h, klim);
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    wait_loads();
+  }
+  __syncthreads();
+
+  // Step b: logits of block b and the update of block b - 1.  Both blocks of
+  // a tile are fully visible in the steady state, which runs without branches.
+  f32x16 p1 = f32x16{}, p2 = f32x16{};
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) load_tile(t + 1);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int b = 2 * t + kb;
+      f32x16 n1, n2;
+      if (b < nfull && b > 0) {
+        scores(b, n1, n2);
+        online_update<false, false>(p1, p2, st, c, k_lo + (b - 1) * 32, h, 0);
+      } else {
+        if (b < nlive) scores(b, n1, n2);
+        if (b > 0 && b - 1 < nlive) update(b - 1, p1, p2);
+      }
+      p1 = n1;
+      p2 = n2;
+    }
+    wait_loads();
+    lds_barrier();
+  }
+  if (2 * ntiles - 1 < nlive && ntiles > 0) update(2 * ntiles - 1, p1, p2);
+
+  // Merge the two lane halves that hold disjoint keys of the same query.
+  {
+    const float m1 = st.m1, m2 = st.m2, l1 = st.l1, l2 = st.l2, acc = st.acc;
+    const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32);
+    const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
+    const float oacc = __shfl_xor(acc, 32);
+    const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
+    const float wa = fast_exp2((m1 - M1) * c), wb = fast_exp2((om1 - M1) * c);
+    const float va = fast_exp2((m2 - M2) * c), vb = fast_exp2((om2 - M2) * c);
+    const float L1 = __builtin_fmaf(l1, wa, ol1 * wb);
+    const float A = __builtin_fmaf(acc, wa, oacc * wb);
+    const float L2 = __builtin_fmaf(l2, va, ol2 * vb);
+    if (h == 0 && row_ok) {
+      const int64_t idx = bh * (int64_t)NQ + row;
+      if (SPLIT) {
+        const int64_t rows = p.BH * (int64_t)NQ;
+        float *w = p.ws + (int64_t)sp * rows + idx;
+        const int64_t fstride = (int64_t)p.splits * rows;
+        w[0] = M1;
+        w[fstride] = L1;
+        w[2 * fstride] = M2;
+        w[3 * fstride] = L2;
+        w[4 * fstride] = A;
+      } else {
+        finish_row(M1, L1, M2, L2, A, p.scale, p.kl + idx, p.lse1 + idx, p.lse2 + idx);
+      }
+    }
+  }
+}
+
+template <int D, bool SPLIT>
+static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
+  using Tr = Fwd2Traits<D>;
+  const void *fn = reinterpret_cast<const void *>(&fwd2_kernel<D, SPLIT>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const int64_t nblk = p.BH * (int64_t)p.nqt * p.splits;
+  hipLaunchKernelGGL((fwd2_kernel<D, SPLIT>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool SPLIT>
 static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s) {
   using Tr = FwdTraits<T, D>;
@@ -433,15 +636,15 @@ static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s) {
 }
 
 int fwd_block_queries(int dtype, int D) {
-  if (dtype == 0) return D == 128 ? FwdTraits<bf16, 128>::BQ : FwdTraits<bf16, 64>::BQ;
+  if (dtype == 0) return D == 128 ? Fwd2Traits<128>::BQ : Fwd2Traits<64>::BQ;
   return D == 128 ? FwdTraits<float, 128>::BQ : FwdTraits<float, 64>::BQ;
 }
 
 hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s) {
   const bool split = p.splits > 1;
   if (dtype == 0) {
-    if (D == 128) return split ? launch_fwd_t<bf16, 128, true>(p, s) : launch_fwd_t<bf16, 128, false>(p, s);
-    return split ? launch_fwd_t<bf16, 64, true>(p, s) : launch_fwd_t<bf16, 64, false>(p, s);
+    if (D == 128) return split ? launch_fwd2<128, true>(p, s) : launch_fwd2<128, false>(p, s);
+    return split ? launch_fwd2<64, true>(p, s) : launch_fwd2<64, false>(p, s);
   }
   if (D == 128) return split ? launch_fwd_t<float, 128, true>(p, s) : launch_fwd_t<float, 128, false>(p, s);
   return split ? launch_fwd_t<float, 64, true>(p, s) : launch_fwd_t<float, 64, false>(p, s);
