@@ -542,7 +542,11 @@ struct Bwd4Traits {
 
 __device__ __forceinline__ int swz_tr(int d) { return (d >> 1) & 7; }  // 128-byte rows
 
-template <int D, bool KEYS_RES>
+// MODE 0 computes both distributions' gradients; MODE 1 only the teacher's
+// (Configuration 2), MODE 2 only the student's (Configuration 1).  With one
+// distribution the pair splits D instead: each wave accumulates its half of
+// D over both blocks, and the dS that is not needed is never formed.
+template <int D, bool KEYS_RES, int MODE>
 __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   using Tr = Bwd4Traits<D, KEYS_RES>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -722,9 +726,12 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   auto body = [&](auto e_tag, auto neg_tag) {
     constexpr int e = decltype(e_tag)::value;
     constexpr bool NEG = decltype(neg_tag)::value;
-    f32x16 acc[Tr::NDB];
+    constexpr int NACC = MODE == 0 ? Tr::NDB : Tr::NDB / 2;  // 32-column accumulator blocks
+    constexpr int TEN = MODE == 0 ? e : MODE - 1;            // distribution accumulated
+    constexpr int DB0 = MODE == 0 ? 0 : e * NACC;            // first 32-column block
+    f32x16 acc[NACC];
   #pragma unroll
-    for (int db = 0; db < Tr::NDB; ++db) acc[db] = f32x16{};
+    for (int db = 0; db < NACC; ++db) acc[db] = f32x16{};
 
     auto empty_blk = [&](int xa) -> bool {
       if (KEYS_RES) return xa >= NQ || ra >= NK || (p.causal && ra > xa + 31 + off);
@@ -814,8 +821,12 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
       }
   #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        mine[ks] = e ? b2[ks] : b1[ks];
-        other[ks] = e ? b1[ks] : b2[ks];
+        if (MODE == 0) {
+          mine[ks] = e ? b2[ks] : b1[ks];
+          other[ks] = e ? b1[ks] : b2[ks];
+        } else {
+          mine[ks] = other[ks] = MODE == 1 ? b1[ks] : b2[ks];
+        }
       }
     };
     // Gradient product of this wave's distribution over streamed block xb of
@@ -824,15 +835,28 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
     // so lane half h reads 8 consecutive positions 32xb + 16ks + 8h.
     auto grad = [&](int xb, const char *trb, const f16x8(&bo)[2]) {
       const int sw = swz_tr(c32);
-      const char *tb = trb + e * Tr::TR_T + c32 * 128;
+      const char *tb = trb + TEN * Tr::TR_T + (DB0 * 32 + c32) * 128;
   #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int pc = ((4 * xb + 2 * ks + h) ^ sw) * 16;
   #pragma unroll
-        for (int db = 0; db < Tr::NDB; ++db) {
+        for (int db = 0; db < NACC; ++db) {
           const f16x8 a = *reinterpret_cast<const f16x8 *>(tb + db * 32 * 128 + pc);
           acc[db] = mma16(a, bo[ks], acc[db]);
         }
+      }
+    };
+
+    // Both blocks of a stage, own dS from registers and the partner's from LDS,
+    // block TEN first: every distribution's accumulation order is the same in
+    // every mode, so results do not depend on which gradients are requested.
+    auto grad2 = [&](const char *trp, const f16x8(&own)[2], const f16x8(&par)[2]) {
+      if (e == TEN) {
+        grad(e, trp, own);
+        grad(1 - e, trp, par);
+      } else {
+        grad(1 - e, trp, par);
+        grad(e, trp, own);
       }
     };
 
@@ -868,8 +892,7 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
           f16x8 pb[2];
   #pragma unroll
           for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
-          grad(e, trp, prev);
-          grad(1 - e, trp, pb);
+          grad2(trp, prev, pb);
         }
         {
           char *dsw = smem + Tr::OFF_DSX + (t & 1) * Tr::DSX_T + (wave * 2) * Tr::DSX_SLOT + lane * 16;
@@ -895,20 +918,20 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
       f16x8 pb[2];
   #pragma unroll
       for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
-      grad(e, trp, prev);
-      grad(1 - e, trp, pb);
+      grad2(trp, prev, pb);
     }
 
-    // Epilogue: lane writes its resident row of this wave's distribution, d = db*32 + 8j + 4h + (0..3).
-    if (r_ok && (e ? p.want2 : p.want1)) {
+    // Epilogue: lane writes its resident row of the accumulated distribution,
+    // d = (DB0 + db)*32 + 8j + 4h + (0..3).
+    if (r_ok && (TEN ? p.want2 : p.want1)) {
       const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
-      float *O = e ? (KEYS_RES ? p.dk2 : p.dq2) : (KEYS_RES ? p.dk1 : p.dq1);
+      float *O = TEN ? (KEYS_RES ? p.dk2 : p.dq2) : (KEYS_RES ? p.dk1 : p.dq1);
       const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
   #pragma unroll
-      for (int db = 0; db < Tr::NDB; ++db) {
+      for (int db = 0; db < NACC; ++db) {
   #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int d = db * 32 + 8 * j + 4 * h;
+          const int d = (DB0 + db) * 32 + 8 * j + 4 * h;
           const f32x4 v = {acc[db][4 * j] * f, acc[db][4 * j + 1] * f, acc[db][4 * j + 2] * f, acc[db][4 * j + 3] * f};
           *reinterpret_cast<f32x4 *>(O + rowoff + d) = v;
         }
@@ -1031,17 +1054,26 @@ hipError_t launch_grad_scale(int dtype, const float *g, int64_t BH, int64_t NQ, 
   return hipGetLastError();
 }
 
-template <int D, bool KEYS_RES>
+template <int D, bool KEYS_RES, int MODE>
 static hipError_t launch_pass4(const BwdParams &p, hipStream_t s) {
   using Tr = Bwd4Traits<D, KEYS_RES>;
   const int64_t NR = KEYS_RES ? p.NK : p.NQ;
   if (NR == 0) return hipSuccess;
-  const void *fn = reinterpret_cast<const void *>(&bwd4_kernel<D, KEYS_RES>);
+  const void *fn = reinterpret_cast<const void *>(&bwd4_kernel<D, KEYS_RES, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR);
-  hipLaunchKernelGGL((bwd4_kernel<D, KEYS_RES>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  hipLaunchKernelGGL((bwd4_kernel<D, KEYS_RES, MODE>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
   return hipGetLastError();
+}
+
+// Both distributions, the teacher's only or the student's only.
+template <int D, bool KEYS_RES>
+static hipError_t launch_bf16_pass(const BwdParams &p, hipStream_t s) {
+  if (p.want1 && p.want2) return launch_pass4<D, KEYS_RES, 0>(p, s);
+  if (p.want1) return launch_pass4<D, KEYS_RES, 1>(p, s);
+  if (p.want2) return launch_pass4<D, KEYS_RES, 2>(p, s);
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_transpose(int D, const void *x, int64_t BH, int64_t N, void *out, hipStream_t s) {
@@ -1057,19 +1089,13 @@ hipError_t launch_bwd_transpose(int D, const void *x, int64_t BH, int64_t N, voi
   return hipGetLastError();
 }
 
-#ifdef SKL_BWD_ONE_WAVE
-#define SKL_BF16_PASS(D, KR) launch_pass<bf16, D, KR>(p, s)
-#else
-#define SKL_BF16_PASS(D, KR) launch_pass4<D, KR>(p, s)
-#endif
-
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s) {
-  if (dtype == 0) return D == 128 ? SKL_BF16_PASS(128, true) : SKL_BF16_PASS(64, true);
+  if (dtype == 0) return D == 128 ? launch_bf16_pass<128, true>(p, s) : launch_bf16_pass<64, true>(p, s);
   return D == 128 ? launch_pass<float, 128, true>(p, s) : launch_pass<float, 64, true>(p, s);
 }
 
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s) {
-  if (dtype == 0) return D == 128 ? SKL_BF16_PASS(128, false) : SKL_BF16_PASS(64, false);
+  if (dtype == 0) return D == 128 ? launch_bf16_pass<128, false>(p, s) : launch_bf16_pass<64, false>(p, s);
   return D == 128 ? launch_pass<float, 128, false>(p, s) : launch_pass<float, 64, false>(p, s);
 }
 

@@ -429,22 +429,30 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(FwdParams p) {
 // per tile.  A wave walks its 32-key blocks as a pipeline: the logits of block
 // b + 1 are computed while the online update of block b runs, in one
 // instruction stream whenever both blocks are fully visible (no mask code).
+#ifndef SKL_FWD2_WAVES
+#define SKL_FWD2_WAVES 8
+#endif
+#ifndef SKL_FWD2_PIPE
+#define SKL_FWD2_PIPE 1
+#endif
 template <int D>
 struct Fwd2Traits {
-  static constexpr int NT = 512;
-  static constexpr int BQ = 256;        // 8 waves x 32 queries
+  static constexpr int WAVES = SKL_FWD2_WAVES;
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int BQ = 32 * WAVES;  // 32 queries per wave
   static constexpr int BK = kFwdBK;     // keys per tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int RB = D * 2;      // bf16 row bytes
   static constexpr int CPROW = RB / 16;
   static constexpr int ROW_T = BK * RB;  // one tensor's key tile
   static constexpr int LDS_BYTES = 2 * 2 * ROW_T;
-  static constexpr int LOADS = ROW_T / 16 / NT;  // per tensor per thread
-  static_assert(BK == 64 && LOADS * 16 * NT == ROW_T, "tiles");
+  static constexpr int CHUNKS = ROW_T / 16;            // 16-byte loads per tensor per tile
+  static constexpr int LOADS = (CHUNKS + NT - 1) / NT;  // per tensor per thread (the last may be partial)
+  static_assert(BK == 64 && NT % 64 == 0, "tiles");
 };
 
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * SKL_FWD2_WAVES, 1) void fwd2_kernel(FwdParams p) {
   using Tr = Fwd2Traits<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -525,7 +533,8 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
     for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
       for (int i = 0; i < Tr::LOADS; ++i)
-        buffer_load_lds16(tn ? rk2 : rk1, buf + tn * Tr::ROW_T + (i * Tr::NT + wave * 64) * 16, voff[i], soff);
+        if (Tr::CHUNKS % Tr::NT == 0 || i * Tr::NT + wave * 64 < Tr::CHUNKS)  // whole waves only
+          buffer_load_lds16(tn ? rk2 : rk1, buf + tn * Tr::ROW_T + (i * Tr::NT + wave * 64) * 16, voff[i], soff);
   };
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
@@ -568,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       const int b = 2 * t + kb;
       f32x16 n1, n2;
-      if (b < nfull && b > 0) {
+      if (SKL_FWD2_PIPE && b < nfull && b > 0) {
         scores(b, n1, n2);
         online_update<false, false>(p1, p2, st, c, k_lo + (b - 1) * 32, h, 0);
       } else {

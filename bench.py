@@ -28,9 +28,9 @@ METRIC = "attn-KL fwd and fwd+bwd TFLOP/s + ms at 64K ctx, 32 heads, d=128 bf16"
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_kl_causal_64k_hbm_traffic.json")
 COPY_BYTES = 1 << 30
 KERNELS = {  # bench key -> kernel names as rocprofv3 reports them (mangled or demangled)
-    "fwd": ("_ZN3skl10fwd_kernelIDF16bLi128ELb0EEEvNS_9FwdParamsE", "void skl::fwd_kernel<__bf16, 128, false>"),
-    "bwd_dk": ("_ZN3skl11bwd4_kernelILi128ELb1EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, true>"),
-    "bwd_dq": ("_ZN3skl11bwd4_kernelILi128ELb0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, false>"),
+    "fwd": ("_ZN3skl11fwd2_kernelILi128ELb0EEEvNS_9FwdParamsE", "void skl::fwd2_kernel<128, false>"),
+    "bwd_dk": ("_ZN3skl11bwd4_kernelILi128ELb1ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, true, 0>"),
+    "bwd_dq": ("_ZN3skl11bwd4_kernelILi128ELb0ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, false, 0>"),
 }
 
 
@@ -286,8 +286,8 @@ def main():
     kern_flop = {"fwd": fwd_flop, "bwd_dk": 8 * w.D * pairs, "bwd_dq": 8 * w.D * pairs}
     dom = max(kern_flop, key=lambda k: per[k])
     achieved = kern_flop[dom] / (per[dom] * 1e-3) / 1e12
-    kernel_names = {"fwd": "fwd_kernel<bf16,128,unsplit>", "bwd_dk": "bwd4_kernel<128,keys resident>",
-                    "bwd_dq": "bwd4_kernel<128,queries resident>"}
+    kernel_names = {"fwd": "fwd2_kernel<128,unsplit>", "bwd_dk": "bwd4_kernel<128,keys resident,both>",
+                    "bwd_dq": "bwd4_kernel<128,queries resident,both>"}
 
     out = {
         "metric": METRIC,

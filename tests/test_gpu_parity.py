@@ -166,6 +166,25 @@ def test_gradient_pairs_can_be_skipped():
     assert torch.equal(s_only[2], full[2]) and torch.equal(s_only[3], full[3])
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_single_configuration_passes_match_oracle(D):
+    # Teacher-only (Configuration 2) and student-only (Configuration 1) passes
+    # form only the dS they need; causal, NQ < NK, signed g.
+    q1, k1, q2, k2 = _rand(1, 2, 300, 517, D, torch.bfloat16, seed=12)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, True)
+    g = (torch.rand((1, 2, 300), generator=torch.Generator().manual_seed(13)) - 0.4).to(DEV)
+    full = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True)
+    t_only = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True, student=False)
+    s_only = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True, teacher=False)
+    torch.cuda.synchronize()
+    for a, b in ((t_only[0], full[0]), (t_only[1], full[1]), (s_only[2], full[2]), (s_only[3], full[3])):
+        assert torch.equal(a, b)
+    scale = 1.0 / math.sqrt(D)
+    grads = (t_only[0], t_only[1], s_only[2], s_only[3])
+    errs = compare_backward(q1, k1, q2, k2, scale, True, g, grads, heads=[(0, 0), (0, 1)])
+    assert_within(errs, TOL["bf16"], f"single-configuration passes D={D}")
+
+
 def test_autograd_function():
     q1, k1, q2, k2 = _rand(1, 2, 130, 260, 64, torch.float32, seed=9)
     ts = [t.clone().requires_grad_(True) for t in (q1, k1, q2, k2)]
