@@ -13,12 +13,10 @@
 // The pages fuse both products into one kernel with dQ atomics and fall back
 // to separate kernels under contention.  Here the separate, atomic-free form
 // is the design: one pass keeps a tile of keys resident and streams queries
-// (dK), the other keeps queries resident and streams keys (dQ).  Both are the
-// same kernel template: a wave owns 32 resident rows, whose fragments stay in
-// registers, and 64-row tiles of the streamed operand pass through LDS.  With
-// bf16 inputs the tile is staged once, as fp16 rows: the logits product reads
-// rows of it and the gradient product reads columns of it through the
-// transposing LDS loads.  fp32 inputs stage a row-major and a transposed copy.
+// (dK), the other keeps queries resident and streams keys (dQ).  bf16 inputs
+// run bwd4_kernel (eight waves, direct LDS staging, pipelined stages); fp32
+// inputs run bwd_fp32_kernel (four waves, register staging of a row-major and
+// a transposed fp32 copy of the streamed tile).
 //
 // Logits come out as (streamed x resident) accumulator blocks, so a lane holds
 // one resident row and 16 streamed rows; that accumulator is, element for
@@ -36,47 +34,33 @@
 
 namespace skl {
 
-template <typename T> struct GradOp { using type = f16; };
-template <> struct GradOp<float> { using type = float; };
-
-template <typename T, int D, bool KEYS_RES>
-struct BwdTraits {
-  // bf16 inputs run both products on fp16 operands converted (exactly, within
-  // the fp16 range) from one fp16 row-major copy of the streamed tile; the
-  // gradient product reads it through the transposing LDS loads.  fp32 inputs
-  // keep an fp32 row-major copy plus an fp32 transposed copy.
-  static constexpr bool F16 = sizeof(T) == 2;
-  using G = typename GradOp<T>::type;
+// fp32 inputs: four waves, each owning 32 resident rows; the streamed tile is
+// staged through registers as a row-major copy (logits product) and a
+// transposed copy (gradient product).
+template <int D, bool KEYS_RES>
+struct BwdF32Traits {
   static constexpr int WAVES = 4;
-  static constexpr int BR = kBwdBR;                        // resident rows per workgroup
-#ifndef SKL_BWD_BX
-#define SKL_BWD_BX 64
-#endif
-  static constexpr int BX = (!F16 && D == 128) ? 32 : (F16 ? SKL_BWD_BX : 64);  // streamed rows per stage
+  static constexpr int BR = kBwdBR;             // resident rows per workgroup
+  static constexpr int BX = D == 128 ? 32 : 64;  // streamed rows per stage
   static constexpr int XB = BX / 32;
   static constexpr int KSTEPS = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int ROW_BYTES = D * (int)sizeof(T);  // one row in HBM
-  static constexpr int CPR = ROW_BYTES / 16;            // 16-byte chunks per HBM row
-  static constexpr int ES = (int)sizeof(G);             // element size of the LDS copy
-  // fp16 row stride D*2 + 48 B: the 16 rows of a logits-operand read and the
-  // 4 rows x 32 B of a transposing read both fall in distinct banks.
-  static constexpr int XROW = F16 ? D * 2 + 48 : ROW_BYTES + 16;
-  static constexpr int XT_STRIDE = F16 ? 0 : BX * 4 + 16;
+  static constexpr int ROW_BYTES = D * 4;       // one row in HBM
+  static constexpr int CPR = ROW_BYTES / 16;    // 16-byte chunks per HBM row
+  static constexpr int XROW = ROW_BYTES + 16;
+  static constexpr int XT_STRIDE = BX * 4 + 16;
   static constexpr int XROW_BYTES = BX * XROW;
-  static constexpr int XT_BYTES = F16 ? 0 : D * XT_STRIDE;
+  static constexpr int XT_BYTES = D * XT_STRIDE;
   static constexpr int NSTAT = 4;  // b1, b2, KL, sign(g) of each streamed query
   static constexpr int STAT_BYTES = KEYS_RES ? NSTAT * BX * 4 : 0;
   static constexpr int OFF_XT = 2 * XROW_BYTES;
   static constexpr int OFF_STAT = OFF_XT + 2 * XT_BYTES;
   static constexpr int STAGE_BYTES = OFF_STAT + STAT_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  // Staging work per thread: bf16 -> 16-byte chunks; fp32 -> items of 4 rows x 1 chunk.
-  static constexpr int CPT = F16 ? BX * CPR / 256 : 1;
+  // Staging work per thread: items of 4 rows x 1 chunk.
   static constexpr int ITEMS = (BX / 4) * CPR;
-  static constexpr int IPT = F16 ? 1 : (ITEMS + 255) / 256;
+  static constexpr int IPT = (ITEMS + 255) / 256;
   static_assert(BR == WAVES * 32, "resident tile");
-  static_assert(!F16 || CPT * 256 == BX * CPR, "staging split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(XROW_BYTES % 16 == 0 && XT_BYTES % 16 == 0, "LDS alignment");
 };
@@ -93,16 +77,6 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = pack_f16(bf16lo_to_f32(w[i]), bf16hi_to_f32(w[i]));
   return o;
-}
-
-// Four consecutive-row fp16 elements of one column, gathered by the
-// transposing LDS load: within each 16-lane group, lane 4k + q reads 8 bytes
-// at `p` and lane i receives element i%4 of the reads of lanes 4k + i/4.
-typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
-__device__ __forceinline__ f16x4 lds_read_tr16(const char *p) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
-  return __builtin_bit_cast(f16x4, v);
 }
 
 // Exponent offset for rows with g = 0: every exp2 underflows to 0 and the
@@ -126,11 +100,11 @@ __device__ __forceinline__ void query_stats(float lse1, float lse2, float kl, fl
   }
 }
 
-template <typename T, int D, bool KEYS_RES>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
-  using Tr = BwdTraits<T, D, KEYS_RES>;
-  using G = typename Tr::G;
-  using CG = chunk_t<G>;
+template <int D, bool KEYS_RES>
+__global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p) {
+  using Tr = BwdF32Traits<D, KEYS_RES>;
+  using T = float;
+  using CG = f32x8;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -193,16 +167,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   CG rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
 #pragma unroll
   for (int s = 0; s < Tr::KSTEPS; ++s) {
-    if constexpr (Tr::F16) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const u32x4 w1 = r_ok ? *reinterpret_cast<const u32x4 *>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : z;
-      const u32x4 w2 = r_ok ? *reinterpret_cast<const u32x4 *>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : z;
-      rf1[s] = __builtin_bit_cast(CG, bf16x8_to_f16x8(w1));
-      rf2[s] = __builtin_bit_cast(CG, bf16x8_to_f16x8(w2));
-    } else {
-      rf1[s] = r_ok ? load_chunk<T>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : CG{};
-      rf2[s] = r_ok ? load_chunk<T>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : CG{};
-    }
+    rf1[s] = r_ok ? load_chunk<T>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : CG{};
+    rf2[s] = r_ok ? load_chunk<T>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : CG{};
   }
 
   const float c = p.scale * kLog2e;
@@ -211,21 +177,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   if (!KEYS_RES && r_ok) query_stats(LS1[my_r], LS2[my_r], KLr[my_r], Gr[my_r], sigma, qb1, qb2, qkl, qsg);
 
   // ---- staging: global -> registers -> LDS ----
-  u32x4 st[2][Tr::F16 ? Tr::CPT : 4 * Tr::IPT];
+  u32x4 st[2][4 * Tr::IPT];
   float sv[Tr::NSTAT];
   auto gload = [&](int t) {
     const int xb0 = x_of(t);
     const u32x4 z = {0u, 0u, 0u, 0u};
-    if constexpr (Tr::F16) {
-#pragma unroll
-      for (int i = 0; i < Tr::CPT; ++i) {
-        const int cidx = tid + 256 * i;
-        const int row = xb0 + cidx / Tr::CPR, col = cidx % Tr::CPR;
-        const int64_t o = (int64_t)row * Tr::ROW_BYTES + col * 16;
-        st[0][i] = row < NX ? *reinterpret_cast<const u32x4 *>(X1 + o) : z;
-        st[1][i] = row < NX ? *reinterpret_cast<const u32x4 *>(X2 + o) : z;
-      }
-    } else {
+    {
 #pragma unroll
       for (int k = 0; k < Tr::IPT; ++k) {
         const int item = tid + 256 * k;
@@ -250,17 +207,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
   };
   auto sstore = [&](int buf) {
     char *base = smem + buf * Tr::STAGE_BYTES;
-    if constexpr (Tr::F16) {
-#pragma unroll
-      for (int i = 0; i < Tr::CPT; ++i) {
-        const int cidx = tid + 256 * i;
-        const int row = cidx / Tr::CPR, col = cidx % Tr::CPR;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-          *reinterpret_cast<u32x4 *>(base + t2 * Tr::XROW_BYTES + row * Tr::XROW + col * 16) =
-              bf16x8_to_f16x8(st[t2][i]);
-      }
-    } else {
+    {
 #pragma unroll
       for (int k = 0; k < Tr::IPT; ++k) {
         const int item = tid + 256 * k;
@@ -335,12 +282,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
       // Logits block: lane = resident row, element r = streamed row xa + acc_row(r, h).
       f32x16 x1 = f32x16{}, x2 = f32x16{};
       {
-        const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 8 * h * Tr::ES;
+        const char *a1p = base + (xb * 32 + c32) * Tr::XROW + 8 * h * 4;
         const char *a2p = a1p + Tr::XROW_BYTES;
 #pragma unroll
         for (int s = 0; s < Tr::KSTEPS; ++s) {
-          const CG a1 = *reinterpret_cast<const CG *>(a1p + 16 * s * Tr::ES);
-          const CG a2 = *reinterpret_cast<const CG *>(a2p + 16 * s * Tr::ES);
+          const CG a1 = *reinterpret_cast<const CG *>(a1p + 16 * s * 4);
+          const CG a2 = *reinterpret_cast<const CG *>(a2p + 16 * s * 4);
           x1 = mma16(a1, rf1[s], x1);
           x2 = mma16(a2, rf2[s], x2);
         }
@@ -396,24 +343,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdParams p) {
         CG b1, b2;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          b1[u] = (G)d1[8 * ks + u];
-          b2[u] = (G)d2[8 * ks + u];
+          b1[u] = d1[8 * ks + u];
+          b2[u] = d2[8 * ks + u];
         }
 #pragma unroll
         for (int db = 0; db < Tr::NDB; ++db) {
           CG a1, a2;
-          if constexpr (Tr::F16) {
-            // 16-lane group g: columns db*32 + 16(g&1) + (0..15), rows 16ks + 4(g>>1) + (0..3) (+8).
-            const int j16 = lane & 15, grp = lane >> 4;
-            const int rb = xb * 32 + 16 * ks + 4 * (grp >> 1) + (j16 >> 2);
-            const int d0 = db * 32 + 16 * (grp & 1) + 4 * (j16 & 3);
-            const char *t1 = base + rb * Tr::XROW + d0 * 2;
-            const char *t2 = t1 + Tr::XROW_BYTES;
-            const f16x4 l1 = lds_read_tr16(t1), h1 = lds_read_tr16(t1 + 8 * Tr::XROW);
-            const f16x4 l2 = lds_read_tr16(t2), h2 = lds_read_tr16(t2 + 8 * Tr::XROW);
-            a1 = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-            a2 = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
-          } else {
+          {
             const int so = xb * 32 + 16 * ks + 4 * h;
             const char *t1 = base + Tr::OFF_XT + (db * 32 + c32) * Tr::XT_STRIDE + so * 4;
             const char *t2 = t1 + Tr::XT_BYTES;
@@ -1036,16 +972,16 @@ __global__ __launch_bounds__(256) void zero_kernel(float *dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = 0.f;
 }
 
-template <typename T, int D, bool KEYS_RES>
-static hipError_t launch_pass(const BwdParams &p, hipStream_t s) {
-  using Tr = BwdTraits<T, D, KEYS_RES>;
+template <int D, bool KEYS_RES>
+static hipError_t launch_fp32_pass(const BwdParams &p, hipStream_t s) {
+  using Tr = BwdF32Traits<D, KEYS_RES>;
   const int64_t NR = KEYS_RES ? p.NK : p.NQ;
   if (NR == 0) return hipSuccess;
-  const void *fn = reinterpret_cast<const void *>(&bwd_kernel<T, D, KEYS_RES>);
+  const void *fn = reinterpret_cast<const void *>(&bwd_fp32_kernel<D, KEYS_RES>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR);
-  hipLaunchKernelGGL((bwd_kernel<T, D, KEYS_RES>), dim3((uint32_t)nblk), dim3(256), Tr::LDS_BYTES, s, p);
+  hipLaunchKernelGGL((bwd_fp32_kernel<D, KEYS_RES>), dim3((uint32_t)nblk), dim3(256), Tr::LDS_BYTES, s, p);
   return hipGetLastError();
 }
 
@@ -1091,12 +1027,12 @@ hipError_t launch_bwd_transpose(int D, const void *x, int64_t BH, int64_t N, voi
 
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s) {
   if (dtype == 0) return D == 128 ? launch_bf16_pass<128, true>(p, s) : launch_bf16_pass<64, true>(p, s);
-  return D == 128 ? launch_pass<float, 128, true>(p, s) : launch_pass<float, 64, true>(p, s);
+  return D == 128 ? launch_fp32_pass<128, true>(p, s) : launch_fp32_pass<64, true>(p, s);
 }
 
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s) {
   if (dtype == 0) return D == 128 ? launch_bf16_pass<128, false>(p, s) : launch_bf16_pass<64, false>(p, s);
-  return D == 128 ? launch_pass<float, 128, false>(p, s) : launch_pass<float, 64, false>(p, s);
+  return D == 128 ? launch_fp32_pass<128, false>(p, s) : launch_fp32_pass<64, false>(p, s);
 }
 
 hipError_t launch_zero(float *dst, int64_t n, hipStream_t s) {

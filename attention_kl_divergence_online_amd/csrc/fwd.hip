@@ -24,34 +24,17 @@
 
 namespace skl {
 
-#ifndef SKL_FWD_WAVES
-#define SKL_FWD_WAVES 8
-#endif
-#ifndef SKL_FWD_QB
-#define SKL_FWD_QB 1
-#endif
-#ifndef SKL_FWD_BK
-#define SKL_FWD_BK 64
-#endif
-#ifndef SKL_FWD_PP
-#define SKL_FWD_PP 0
-#endif
-#ifndef SKL_FWD_PRIO
-#define SKL_FWD_PRIO 0
-#endif
-
-
-constexpr int kFwdThreads = SKL_FWD_WAVES * 64;
+constexpr int kFwdThreads = 8 * 64;
 
 template <typename T, int D>
 struct FwdTraits {
-  static constexpr int WAVES = SKL_FWD_WAVES;
+  static constexpr int WAVES = 8;
   // 32-query blocks per wave (fp32 at D=128 keeps one so its fragments fit in registers)
-  static constexpr int QB = (sizeof(T) == 4 && D == 128) ? 1 : SKL_FWD_QB;
+  static constexpr int QB = 1;
   static constexpr int NT = WAVES * 64;
   static constexpr int BQ = WAVES * QB * 32;
   // Keys per LDS stage (fp32 at D=128 keeps 64 to fit two stages in LDS).
-  static constexpr int BK = (sizeof(T) == 4 && D == 128) ? 64 : SKL_FWD_BK;
+  static constexpr int BK = kFwdBK;
   static constexpr int NB = BK / 32;  // 32-key blocks per stage
   static constexpr int KSTEPS = D / 16;
   static constexpr int ROW_BYTES = D * (int)sizeof(T);
@@ -269,65 +252,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
     }
   };
 
-#if SKL_FWD_PP
-  // Ping-pong: waves w and w + WAVES/2 share a SIMD.  Group A issues block j's
-  // matrix products while group B runs the online update of block j - 1, then
-  // they swap; a workgroup barrier separates the phases.  A block's scores
-  // stay in s1/s2 from its product phase to its update phase.  Tile t + 1 is
-  // stored during the update of block t*NB (by each group) and tile t + 2 is
-  // fetched right after, so every LDS buffer is rewritten only after both
-  // groups finished reading it and is complete before either group reads it.
-  const bool grp_b = wave >= Tr::WAVES / 2;
-  const int nblk = ntiles * Tr::NB;
-  f32x16 s1[Tr::QB], s2[Tr::QB];
-  auto mphase = [&](int j) {
-    const int t = j / Tr::NB, kb = j % Tr::NB;
-    const int kbase = k_lo + j * 32;
-    if (wave_live && kbase < vis_any) {
-#if SKL_FWD_PRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
-      block_scores(smem + (t & 1) * Tr::STAGE_BYTES, kb, s1, s2);
-#if SKL_FWD_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
-    }
-  };
-  auto vphase = [&](int j) {
-    const int kbase = k_lo + j * 32;
-    if (wave_live && kbase < vis_any) {
-      if (kbase + 32 <= vis_all) {
-#pragma unroll
-        for (int qb = 0; qb < Tr::QB; ++qb) online_update<false, COMP>(s1[qb], s2[qb], st[qb], c, kbase, h, 0);
-      } else {
-#pragma unroll
-        for (int qb = 0; qb < Tr::QB; ++qb)
-          online_update<true, COMP>(s1[qb], s2[qb], st[qb], c, kbase, h, klim[qb]);
-      }
-    }
-    if (j % Tr::NB == 0) {
-      const int t = j / Tr::NB;
-      if (t + 1 < ntiles) {
-        sstore((t + 1) & 1);
-        if (t + 2 < ntiles) gload(t + 2);
-      }
-    }
-  };
-  if (ntiles > 1) gload(1);
-  for (int j = 0; j < nblk; ++j) {
-    if (!grp_b)
-      mphase(j);
-    else if (j > 0)
-      vphase(j - 1);
-    __syncthreads();
-    if (!grp_b)
-      vphase(j);
-    else
-      mphase(j);
-    __syncthreads();
-  }
-  if (grp_b && nblk > 0) vphase(nblk - 1);
-#else
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) gload(t + 1);
     const char *base = smem + (t & 1) * Tr::STAGE_BYTES;
@@ -353,7 +277,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
     __syncthreads();
   }
 
-#endif
 
   // Merge the two lane halves that hold disjoint keys of the same query.
 #pragma unroll
@@ -429,15 +352,9 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(FwdParams p) {
 // per tile.  A wave walks its 32-key blocks as a pipeline: the logits of block
 // b + 1 are computed while the online update of block b runs, in one
 // instruction stream whenever both blocks are fully visible (no mask code).
-#ifndef SKL_FWD2_WAVES
-#define SKL_FWD2_WAVES 8
-#endif
-#ifndef SKL_FWD2_PIPE
-#define SKL_FWD2_PIPE 1
-#endif
 template <int D>
 struct Fwd2Traits {
-  static constexpr int WAVES = SKL_FWD2_WAVES;
+  static constexpr int WAVES = 8;
   static constexpr int NT = 64 * WAVES;
   static constexpr int BQ = 32 * WAVES;  // 32 queries per wave
   static constexpr int BK = kFwdBK;     // keys per tile
@@ -452,7 +369,7 @@ struct Fwd2Traits {
 };
 
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(64 * SKL_FWD2_WAVES, 1) void fwd2_kernel(FwdParams p) {
+__global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
   using Tr = Fwd2Traits<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -577,7 +494,7 @@ __global__ __launch_bounds__(64 * SKL_FWD2_WAVES, 1) void fwd2_kernel(FwdParams 
     for (int kb = 0; kb < 2; ++kb) {
       const int b = 2 * t + kb;
       f32x16 n1, n2;
-      if (SKL_FWD2_PIPE && b < nfull && b > 0) {
+      if (b < nfull && b > 0) {
         scores(b, n1, n2);
         online_update<false, false>(p1, p2, st, c, k_lo + (b - 1) * 32, h, 0);
       } else {
