@@ -681,14 +681,26 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
       const char *a2p = a1p + Tr::ROW_T;
       x1 = f32x16{};
       x2 = f32x16{};
+      bf16x8 a1[Tr::KSTEPS], a2[Tr::KSTEPS];
   #pragma unroll
       for (int s = 0; s < Tr::KSTEPS; ++s) {
         const int pc = ((2 * s + h) ^ sw) * 16;
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(a1p + pc);
-        const bf16x8 a2 = *reinterpret_cast<const bf16x8 *>(a2p + pc);
-        x1 = mma16(a1, rf1[s], x1);
-        x2 = mma16(a2, rf2[s], x2);
+        a1[s] = *reinterpret_cast<const bf16x8 *>(a1p + pc);
+        a2[s] = *reinterpret_cast<const bf16x8 *>(a2p + pc);
       }
+  #pragma unroll
+      for (int s = 0; s < Tr::KSTEPS; ++s) {
+        x1 = mma16(a1[s], rf1[s], x1);
+        x2 = mma16(a2[s], rf2[s], x2);
+      }
+      // Keep four k-steps of operand reads in flight ahead of the products.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  #pragma unroll
+      for (int s = 0; s < Tr::KSTEPS - 4; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
     // dS of the own block (rows xa..xa+31) as gradient-product B operands:
     // mine[ks] for this wave's distribution, other[ks] for the partner's.
