@@ -105,6 +105,11 @@ def bwd_workspace_size(q1, k1, scale=None, causal=False) -> int:
     return int(_lib.lib().streamkl_bwd_workspace_size(problem_for(q1, k1, scale, causal)))
 
 
+def bwd_workspace_size_min(q1, k1, scale=None, causal=False) -> int:
+    """Smallest workspace streamkl_bwd accepts (copies for one head at a time)."""
+    return int(_lib.lib().streamkl_bwd_workspace_size_min(problem_for(q1, k1, scale, causal)))
+
+
 def streamkl_bwd(q1, k1, q2, k2, kl, lse1, lse2, g, scale: Optional[float] = None, causal: bool = False,
                  teacher: bool = True, student: bool = True, workspace: Optional[torch.Tensor] = None,
                  out=None):

@@ -29,6 +29,7 @@ EXPORTS = (
     "streamkl_fwd_splitk_workspace_size",
     "streamkl_fwd_splitk",
     "streamkl_bwd_workspace_size",
+    "streamkl_bwd_workspace_size_min",
     "streamkl_bwd",
     "streamkl_bwd_prepare",
     "streamkl_bwd_dk",
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.streamkl_fwd_splitk.restype = ctypes.c_int
         L.streamkl_bwd_workspace_size.argtypes = [pp]
         L.streamkl_bwd_workspace_size.restype = sz
+        L.streamkl_bwd_workspace_size_min.argtypes = [pp]
+        L.streamkl_bwd_workspace_size_min.restype = sz
         L.streamkl_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.streamkl_bwd.restype = ctypes.c_int
         L.streamkl_bwd_prepare.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]

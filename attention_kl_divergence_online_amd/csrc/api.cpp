@@ -15,7 +15,9 @@ struct BwdLayout {
   size_t tq1, tq2, tk1, tk2, total;
 };
 inline size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
-BwdLayout bwd_layout(const streamkl_problem *p) {
+// Layout with transposed copies for `heads` heads after a sigma area for all
+// B*H heads.
+BwdLayout bwd_layout_heads(const streamkl_problem *p, size_t heads) {
   BwdLayout l{};
   const size_t bh = (size_t)(p->B * p->H);
   size_t o = round_up(bh * sizeof(float) > 16 ? bh * sizeof(float) : 16, 256);
@@ -24,8 +26,8 @@ BwdLayout bwd_layout(const streamkl_problem *p) {
     return l;
   }
   const size_t tile = (size_t)skl::kBwdTile;
-  const size_t qt = bh * (((size_t)p->NQ + tile - 1) / tile) * tile * (size_t)p->D * 2;
-  const size_t kt = bh * (((size_t)p->NK + tile - 1) / tile) * tile * (size_t)p->D * 2;
+  const size_t qt = heads * (((size_t)p->NQ + tile - 1) / tile) * tile * (size_t)p->D * 2;
+  const size_t kt = heads * (((size_t)p->NK + tile - 1) / tile) * tile * (size_t)p->D * 2;
   l.tq1 = o;
   l.tq2 = l.tq1 + round_up(qt, 256);
   l.tk1 = l.tq2 + round_up(qt, 256);
@@ -33,6 +35,7 @@ BwdLayout bwd_layout(const streamkl_problem *p) {
   l.total = l.tk2 + round_up(kt, 256);
   return l;
 }
+BwdLayout bwd_layout(const streamkl_problem *p) { return bwd_layout_heads(p, (size_t)(p->B * p->H)); }
 
 constexpr int kVersion = 100;  // 0.1.0
 
@@ -174,6 +177,12 @@ size_t streamkl_bwd_workspace_size(const streamkl_problem *p) {
   return bwd_layout(p).total;
 }
 
+size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p) {
+  if (check_problem(p) != STREAMKL_OK) return 0;
+  const int64_t bh = p->B * p->H;
+  return bwd_layout_heads(p, (size_t)(bh > 0 ? 1 : 0)).total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -183,7 +192,7 @@ namespace {
 streamkl_status check_bwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
                           const void *k2, const float *kl, const float *lse1, const float *lse2,
                           const float *g, float *const *outs, int nouts, const void *workspace,
-                          size_t workspace_bytes) {
+                          size_t workspace_bytes, size_t need) {
   streamkl_status st = check_inputs(p, q1, k1, q2, k2);
   if (st != STREAMKL_OK) return st;
   for (int i = 0; i < nouts; ++i)
@@ -191,7 +200,7 @@ streamkl_status check_bwd(const streamkl_problem *p, const void *q1, const void 
   if (p->NQ == 0) return STREAMKL_OK;
   if (!kl || !lse1 || !lse2 || !g) return STREAMKL_ERR_NULL;
   if (!aligned16(kl) || !aligned16(lse1) || !aligned16(lse2) || !aligned16(g)) return STREAMKL_ERR_ALIGN;
-  if (!workspace || workspace_bytes < streamkl_bwd_workspace_size(p)) return STREAMKL_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < need) return STREAMKL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
   return STREAMKL_OK;
 }
@@ -229,6 +238,38 @@ skl::BwdParams make_bwd(const streamkl_problem *p, const void *q1, const void *k
   return b;
 }
 
+// The same parameters restricted to heads [h0, h0 + n) of the flattened
+// B*H range, with that group's transposed copies at layout `l` of `workspace`.
+skl::BwdParams head_group(const streamkl_problem *p, skl::BwdParams b, int64_t h0, int64_t n, const BwdLayout &l,
+                          void *workspace) {
+  const size_t es = p->dtype == STREAMKL_BF16 ? 2 : 4;
+  auto adv = [](const void *ptr, int64_t bytes) -> const void * {
+    return ptr ? reinterpret_cast<const char *>(ptr) + bytes : nullptr;
+  };
+  auto advf = [](float *ptr, int64_t elems) -> float * { return ptr ? ptr + elems : nullptr; };
+  const int64_t q = h0 * p->NQ * p->D, k = h0 * p->NK * p->D;
+  b.q1 = adv(b.q1, q * (int64_t)es);
+  b.q2 = adv(b.q2, q * (int64_t)es);
+  b.k1 = adv(b.k1, k * (int64_t)es);
+  b.k2 = adv(b.k2, k * (int64_t)es);
+  b.kl += h0 * p->NQ;
+  b.lse1 += h0 * p->NQ;
+  b.lse2 += h0 * p->NQ;
+  b.g += h0 * p->NQ;
+  b.sigma += h0;
+  b.dq1 = advf(b.dq1, q);
+  b.dq2 = advf(b.dq2, q);
+  b.dk1 = advf(b.dk1, k);
+  b.dk2 = advf(b.dk2, k);
+  const char *w = reinterpret_cast<const char *>(workspace);
+  b.tq1 = w + l.tq1;
+  b.tq2 = w + l.tq2;
+  b.tk1 = w + l.tk1;
+  b.tk2 = w + l.tk2;
+  b.BH = n;
+  return b;
+}
+
 // dK pass; with no query rows every key gradient is zero.
 streamkl_status run_dk(const streamkl_problem *p, skl::BwdParams b, hipStream_t s) {
   if (p->NQ == 0) {
@@ -249,22 +290,34 @@ streamkl_status run_dq(const streamkl_problem *p, skl::BwdParams b, hipStream_t 
   return skl::launch_bwd_dq(p->dtype, (int)p->D, b, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
 }
 
+streamkl_status run_sigma(const streamkl_problem *p, const float *g, void *workspace, hipStream_t s) {
+  return skl::launch_grad_scale(p->dtype, g, p->B * p->H, p->NQ, reinterpret_cast<float *>(workspace), s) ==
+                 hipSuccess
+             ? STREAMKL_OK
+             : STREAMKL_ERR_HIP;
+}
+
+// Transposed fp16 copies of the group's heads (bf16 inputs).
+streamkl_status run_transposes(const streamkl_problem *p, const skl::BwdParams &b, hipStream_t s) {
+  const int D = (int)p->D;
+  void *tq1 = const_cast<void *>(b.tq1), *tq2 = const_cast<void *>(b.tq2);
+  void *tk1 = const_cast<void *>(b.tk1), *tk2 = const_cast<void *>(b.tk2);
+  if (skl::launch_bwd_transpose(D, b.q1, b.BH, p->NQ, tq1, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, b.q2, b.BH, p->NQ, tq2, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, b.k1, b.BH, p->NK, tk1, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, b.k2, b.BH, p->NK, tk2, s) != hipSuccess)
+    return STREAMKL_ERR_HIP;
+  return STREAMKL_OK;
+}
+
 streamkl_status run_prepare(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
                             const void *k2, const float *g, void *workspace, hipStream_t s) {
   if (p->NQ == 0) return STREAMKL_OK;
-  const int64_t bh = p->B * p->H;
-  if (skl::launch_grad_scale(p->dtype, g, bh, p->NQ, reinterpret_cast<float *>(workspace), s) != hipSuccess)
-    return STREAMKL_ERR_HIP;
-  if (p->dtype != STREAMKL_BF16) return STREAMKL_OK;
-  const BwdLayout l = bwd_layout(p);
-  char *w = reinterpret_cast<char *>(workspace);
-  const int D = (int)p->D;
-  if (skl::launch_bwd_transpose(D, q1, bh, p->NQ, w + l.tq1, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, q2, bh, p->NQ, w + l.tq2, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, k1, bh, p->NK, w + l.tk1, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, k2, bh, p->NK, w + l.tk2, s) != hipSuccess)
-    return STREAMKL_ERR_HIP;
-  return STREAMKL_OK;
+  streamkl_status st = run_sigma(p, g, workspace, s);
+  if (st != STREAMKL_OK || p->dtype != STREAMKL_BF16) return st;
+  const skl::BwdParams b =
+      make_bwd(p, q1, k1, q2, k2, nullptr, nullptr, nullptr, g, nullptr, nullptr, nullptr, nullptr, workspace);
+  return run_transposes(p, b, s);
 }
 
 }  // namespace
@@ -281,13 +334,33 @@ streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const vo
   if (p->B * p->H == 0 || (p->NQ == 0 && p->NK == 0)) return STREAMKL_OK;
   if (!dq1 && !dq2) return STREAMKL_OK;
   float *outs[4] = {dq1, dk1, dq2, dk2};
-  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 4, workspace, workspace_bytes);
+  const bool grouped = p->dtype == STREAMKL_BF16 && p->NQ > 0 && workspace_bytes < streamkl_bwd_workspace_size(p);
+  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 4, workspace, workspace_bytes,
+                 streamkl_bwd_workspace_size_min(p));
   if (st != STREAMKL_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, dk1, dq2, dk2, workspace);
-  if ((st = run_prepare(p, q1, k1, q2, k2, g, workspace, s)) != STREAMKL_OK) return st;
-  if ((st = run_dk(p, b, s)) != STREAMKL_OK) return st;
-  return run_dq(p, b, s);
+  if (!grouped) {
+    if ((st = run_prepare(p, q1, k1, q2, k2, g, workspace, s)) != STREAMKL_OK) return st;
+    if ((st = run_dk(p, b, s)) != STREAMKL_OK) return st;
+    return run_dq(p, b, s);
+  }
+  // A smaller workspace: the transposed copies are made and used for as many
+  // heads at a time as fit (at least one, as the minimum-size query states).
+  const int64_t bh = p->B * p->H;
+  int64_t n = 1;
+  while (n < bh && bwd_layout_heads(p, (size_t)(2 * n)).total <= workspace_bytes) n *= 2;
+  while (n < bh && bwd_layout_heads(p, (size_t)(n + 1)).total <= workspace_bytes) ++n;
+  const BwdLayout l = bwd_layout_heads(p, (size_t)n);
+  if ((st = run_sigma(p, g, workspace, s)) != STREAMKL_OK) return st;
+  for (int64_t h0 = 0; h0 < bh; h0 += n) {
+    const int64_t cnt = h0 + n <= bh ? n : bh - h0;
+    skl::BwdParams bg = head_group(p, b, h0, cnt, l, workspace);
+    if ((st = run_transposes(p, bg, s)) != STREAMKL_OK) return st;
+    if ((st = run_dk(p, bg, s)) != STREAMKL_OK) return st;
+    if ((st = run_dq(p, bg, s)) != STREAMKL_OK) return st;
+  }
+  return STREAMKL_OK;
 }
 
 streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
@@ -312,7 +385,8 @@ streamkl_status streamkl_bwd_dk(const streamkl_problem *p, const void *q1, const
   if (st != STREAMKL_OK) return st;
   if (p->B * p->H == 0 || p->NK == 0 || (!dk1 && !dk2)) return STREAMKL_OK;
   float *outs[2] = {dk1, dk2};
-  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 2, workspace, workspace_bytes);
+  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 2, workspace, workspace_bytes,
+                 streamkl_bwd_workspace_size(p));
   if (st != STREAMKL_OK) return st;
   skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, nullptr, dk1, nullptr, dk2, workspace);
   return run_dk(p, b, reinterpret_cast<hipStream_t>(stream));
@@ -326,7 +400,8 @@ streamkl_status streamkl_bwd_dq(const streamkl_problem *p, const void *q1, const
   if (st != STREAMKL_OK) return st;
   if (p->B * p->H == 0 || p->NQ == 0 || (!dq1 && !dq2)) return STREAMKL_OK;
   float *outs[2] = {dq1, dq2};
-  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 2, workspace, workspace_bytes);
+  st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 2, workspace, workspace_bytes,
+                 streamkl_bwd_workspace_size(p));
   if (st != STREAMKL_OK) return st;
   skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, nullptr, dq2, nullptr, workspace);
   return run_dq(p, b, reinterpret_cast<hipStream_t>(stream));

@@ -117,6 +117,16 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p,
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p);
 
 /*
+ * Smallest workspace streamkl_bwd accepts: the sigma factors of every head
+ * plus, for bf16 inputs, the transposed copies of one (batch, head).  Given
+ * less than streamkl_bwd_workspace_size, streamkl_bwd makes and consumes the
+ * copies for as many heads at a time as fit, in more, smaller launches; the
+ * results are bitwise the same.  The step-wise entry points below need the
+ * full size.  Returns 0 if the problem is invalid.
+ */
+size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p);
+
+/*
  * Backward of L = sum_{b,h,i} g[b,h,i] * KL[b,h,i] (gist.science, "Estrategia
  * de Recomputacion"): probabilities are recomputed tile by tile as
  * P_t = exp(s_t - LSE_t) from Q, K and the saved LSE vectors, and

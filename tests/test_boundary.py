@@ -113,11 +113,13 @@ def bwd(L, p, dq1=A, dk1=A, dq2=A, dk2=A, ws=A, wsb=1 << 20, g=A, kl=A):
     return L.streamkl_bwd(ctypes.byref(p), A, A, A, A, kl, A, A, g, dq1, dk1, dq2, dk2, ws, wsb, None)
 
 
-def bf16_workspace(B, H, NQ, NK, D):
-    # sigma (256-byte slot), then transposed fp16 copies of q1, q2 (64-row tiles) and k1, k2.
+def bf16_workspace(B, H, NQ, NK, D, heads=None):
+    # sigma of every head (256-byte slot), then transposed fp16 copies of q1, q2
+    # (64-row tiles) and k1, k2 for `heads` heads (default: all).
     up = lambda n, a: (n + a - 1) // a * a
     tiles = lambda n: (n + 63) // 64
-    qt, kt = B * H * tiles(NQ) * 64 * D * 2, B * H * tiles(NK) * 64 * D * 2
+    heads = B * H if heads is None else heads
+    qt, kt = heads * tiles(NQ) * 64 * D * 2, heads * tiles(NK) * 64 * D * 2
     return up(max(16, 4 * B * H), 256) + 2 * up(qt, 256) + 2 * up(kt, 256)
 
 
@@ -130,6 +132,14 @@ def test_backward_validation(L):
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, NQ=65, NK=200, D=128))) == \
         bf16_workspace(3, 7, 65, 200, 128)
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(D=32))) == 0
+    # Minimum: sigma for every head, transposed copies of one head.
+    assert L.streamkl_bwd_workspace_size_min(ctypes.byref(P(B=3, H=7, NQ=65, NK=200, D=128))) == \
+        bf16_workspace(3, 7, 65, 200, 128, heads=1)
+    assert L.streamkl_bwd_workspace_size_min(ctypes.byref(P(B=3, H=7, dtype=f32))) == 96
+    # Below the minimum the combined call refuses; between minimum and full it accepts (not run here).
+    pm = P(B=4, H=8)
+    mn = L.streamkl_bwd_workspace_size_min(ctypes.byref(pm))
+    assert bwd(L, pm, wsb=mn - 1) == _lib.STREAMKL_ERR_WORKSPACE
     assert bwd(L, p, dq1=None) == _lib.STREAMKL_ERR_NULL       # half pair
     assert bwd(L, p, dk2=None) == _lib.STREAMKL_ERR_NULL
     assert bwd(L, p, ws=None) == _lib.STREAMKL_ERR_WORKSPACE

@@ -185,6 +185,24 @@ def test_single_configuration_passes_match_oracle(D):
     assert_within(errs, TOL["bf16"], f"single-configuration passes D={D}")
 
 
+def test_small_workspace_runs_in_head_groups():
+    # A workspace below the full size makes the transposed copies a few heads
+    # at a time; the gradients are bitwise those of the full workspace.
+    from attention_kl_divergence_online_amd import bwd_workspace_size, bwd_workspace_size_min
+    q1, k1, q2, k2 = _rand(2, 3, 200, 333, 128, torch.bfloat16, seed=14)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, True)
+    g = (torch.rand((2, 3, 200), generator=torch.Generator().manual_seed(15)) - 0.3).to(DEV)
+    full = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True)
+    lo, hi = bwd_workspace_size_min(q1, k1, None, True), bwd_workspace_size(q1, k1, None, True)
+    assert 0 < lo < hi
+    for nbytes in (lo, lo + (hi - lo) // 3, hi - 256):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        got = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True, workspace=ws)
+        torch.cuda.synchronize()
+        for a, b in zip(got, full):
+            assert torch.equal(a, b), nbytes
+
+
 def test_autograd_function():
     q1, k1, q2, k2 = _rand(1, 2, 130, 260, 64, torch.float32, seed=9)
     ts = [t.clone().requires_grad_(True) for t in (q1, k1, q2, k2)]
