@@ -31,6 +31,7 @@ KERNELS = {  # bench key -> kernel names as rocprofv3 reports them (mangled or d
     "fwd": ("_ZN3skl11fwd2_kernelILi128ELb0EEEvNS_9FwdParamsE", "void skl::fwd2_kernel<128, false>"),
     "bwd_dk": ("_ZN3skl11bwd4_kernelILi128ELb1ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, true, 0>"),
     "bwd_dq": ("_ZN3skl11bwd4_kernelILi128ELb0ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, false, 0>"),
+    "fwd_split": ("_ZN3skl11fwd2_kernelILi128ELb1EEEvNS_9FwdParamsE", "void skl::fwd2_kernel<128, true>"),
 }
 
 
@@ -114,11 +115,12 @@ def summarize_counters(csvs, out_path: str) -> None:
                 if r["Kernel_Name"].startswith(syms):
                     vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     simds, xcds = 1024, 8
-    lines = [f"{'kernel':8s} {'ms@2.4G':>7s} {'MFMA busy':>10s} {'VALU/wave':>10s} {'wait/wave':>10s} "
+    lines = [f"{'kernel':9s} {'ms@2.4G':>7s} {'MFMA busy':>10s} {'VALU/wave':>10s} {'wait/wave':>10s} "
              f"{'LDS conflict':>13s} {'VALU lane-op/pair':>18s} {'exp/pair':>9s}"]
     import synth
-    pairs = synth.get("causal_64k").visible_pairs()
+    workload_of = {"fwd_split": "splitk_512k"}  # per-pair figures use the kernel's own workload
     for key in KERNELS:
+        pairs = synth.get(workload_of.get(key, "causal_64k")).visible_pairs()
         d = {k: sum(v) / len(v) for k, v in vals.get(key, {}).items()}
         if "GRBM_GUI_ACTIVE" not in d:
             continue
@@ -126,7 +128,7 @@ def summarize_counters(csvs, out_path: str) -> None:
         wc = d.get("SQ_WAVE_CYCLES", float("nan"))
         g = lambda name: d.get(name, float("nan"))
         lines.append(
-            f"{key:8s} {cyc / 2.4e6:7.1f} {g('SQ_VALU_MFMA_BUSY_CYCLES') / (simds * cyc):10.1%} "
+            f"{key:9s} {cyc / 2.4e6:7.1f} {g('SQ_VALU_MFMA_BUSY_CYCLES') / (simds * cyc):10.1%} "
             f"{g('SQ_ACTIVE_INST_VALU') / wc:10.1%} {g('SQ_WAIT_INST_ANY') / wc:10.1%} "
             f"{g('SQ_LDS_BANK_CONFLICT') / g('SQ_LDS_IDX_ACTIVE'):13.1%} "
             f"{(g('SQ_INSTS_VALU') - g('SQ_INSTS_MFMA')) * 64 / pairs:18.2f} "
@@ -330,6 +332,7 @@ def main():
     if args.other_configs:
         out["other_configs"] = {n: config_bench(skl, synth, torch, args, n)
                                 for n in ("causal_4k", "noncausal_16k", "splitk_bwd_128k")}
+        out["other_configs"]["decode_128k"] = splitk_bench(skl, synth, torch, args, "decode_128k")
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q1, k1, q2, k2, args.cpu_seconds)
@@ -367,9 +370,9 @@ def config_bench(skl, synth, torch, args, name):
     return res
 
 
-def splitk_bench(skl, synth, torch, args):
-    """Split-K forward on the 512K-key, 1024-query workload (64 chunks)."""
-    w = synth.get("splitk_512k")
+def splitk_bench(skl, synth, torch, args, name="splitk_512k"):
+    """Split-K forward (splits from the workload); also the HBM rate of reading the keys once."""
+    w = synth.get(name)
     q1, k1, q2, k2 = synth.make_inputs(w, device="cuda")
     out = tuple(torch.empty((w.B, w.H, w.NQ), dtype=torch.float32, device="cuda") for _ in range(3))
     ws = torch.empty(skl.fwd_splitk_workspace_size(q1, k1, w.splits, w.scale, w.causal), dtype=torch.uint8,
@@ -385,8 +388,10 @@ def splitk_bench(skl, synth, torch, args):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
     flop = 4 * w.D * w.visible_pairs()
+    key_bytes = 2 * w.B * w.H * w.NK * w.D * 2  # K1 and K2, bf16, read once
     res = {"workload": w.name, "splits": w.splits, "ms": round(ms, 3),
-           "tflops": round(flop / (ms * 1e-3) / 1e12, 2)}
+           "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+           "key_read_gbs": round(key_bytes / (ms * 1e-3) / 1e9, 1)}
     del q1, k1, q2, k2, ws
     torch.cuda.empty_cache()
     return res

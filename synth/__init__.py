@@ -74,6 +74,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload(3, "causal_64k", 1, 32, 65536, 65536, 128, "bf16", True, noise=0.1),
         Workload(4, "splitk_512k", 1, 32, 1024, 524288, 128, "bf16", False, noise=0.2, splits=64),
         Workload(5, "splitk_bwd_128k", 1, 32, 1024, 131072, 128, "bf16", False, noise=0.2),
+        # Decode step: 16 new queries per sequence against a 128K-key cache, split-K forward.
+        Workload(6, "decode_128k", 4, 32, 16, 131072, 128, "bf16", True, noise=0.2, splits=64),
     ]
 }
 

@@ -39,7 +39,9 @@ def head(t: torch.Tensor, b: int, h: int) -> np.ndarray:
 
 
 def sample_rows(n: int, count: int, seed: int, tile: int = 256) -> List[int]:
-    """First and last rows, rows around tile edges, and random rows."""
+    """First and last rows, rows around tile edges, and random rows (all rows if count >= n)."""
+    if count >= n:
+        return list(range(n))
     rng = np.random.default_rng(seed)
     rows = {0, 1, n - 1, n - 2}
     for e in (tile - 1, tile, 2 * tile - 1, n // 2):

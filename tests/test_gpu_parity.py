@@ -114,6 +114,19 @@ def test_splitk_small(splits, causal):
         assert d <= 1e-4, d  # both sides are also held to the oracle bound above
 
 
+@pytest.mark.parametrize("NQ", [1, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_splitk(NQ, causal):
+    # Few queries against a long key range: the decode use of the split-K forward.
+    B, H, NK, D = 2, 2, 5000, 128
+    q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, torch.bfloat16, seed=21 + NQ)
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd_splitk(q1, k1, q2, k2, 16, scale, causal)
+    torch.cuda.synchronize()
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, _heads(B, H)), TOL["bf16"],
+                  f"decode NQ={NQ} causal={causal}")
+
+
 def test_identical_teacher_student_is_exact_zero():
     q1, k1, _, _ = _rand(1, 2, 300, 300, 128, torch.bfloat16, seed=5)
     for causal in (False, True):
@@ -278,3 +291,8 @@ def test_splitk_512k_forward_full_size():
 
 def test_splitk_bwd_128k_full_size():
     _full_size("splitk_bwd_128k", rows_per_head=24)
+
+
+def test_decode_128k_full_size():
+    # Every one of the 16 rows of two heads, and the backward of the decode shape.
+    _full_size("decode_128k", rows_per_head=16)
