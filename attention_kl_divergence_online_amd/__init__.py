@@ -10,6 +10,13 @@ the library.  All arithmetic runs in the library's HIP kernels.
 
 Q tensors are [B, H, NQ, D] and K tensors [B, H, NK, D], contiguous, bf16 or
 fp32, on a HIP device; D is 64 or 128.
+
+Packed variable-length batches use head-major tensors, Q [H, TQ, D] and
+K [H, TK, D], with cumulative sequence offsets cu_seqlens_q / cu_seqlens_k
+(B + 1 int32 values from 0):
+
+    kl, lse1, lse2 = streamkl_fwd_varlen(q1, k1, q2, k2, cu_q, cu_k, causal=True)
+    dq1, dk1, dq2, dk2 = streamkl_bwd_varlen(q1, k1, q2, k2, cu_q, cu_k, kl, lse1, lse2, g, causal=True)
 """
 from __future__ import annotations
 
@@ -23,6 +30,7 @@ from ._lib import StreamKLError
 
 __all__ = ["streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd", "streamkl_bwd_prepare", "streamkl_bwd_dk",
            "streamkl_bwd_dq", "attention_kl",
+           "streamkl_fwd_varlen", "streamkl_bwd_varlen", "varlen_problem_for", "bwd_varlen_workspace_size",
            "StreamKLError", "problem_for", "fwd_splitk_workspace_size", "bwd_workspace_size"]
 
 _DTYPES = {torch.bfloat16: _lib.STREAMKL_BF16, torch.float32: _lib.STREAMKL_FP32}
@@ -215,3 +223,86 @@ class _AttentionKL(torch.autograd.Function):
 def attention_kl(q1, k1, q2, k2, scale: Optional[float] = None, causal: bool = False) -> torch.Tensor:
     """Differentiable per-row KL(P1||P2), [B, H, NQ] fp32."""
     return _AttentionKL.apply(q1, k1, q2, k2, scale, causal)
+
+
+class _Varlen:
+    """A streamkl_varlen_problem together with the host offset arrays it points at."""
+
+    def __init__(self, q1, k1, cu_seqlens_q, cu_seqlens_k, scale, causal):
+        if q1.dim() != 3 or k1.dim() != 3:
+            raise ValueError("packed tensors are [H, T, D]")
+        if q1.dtype not in _DTYPES:
+            raise TypeError(f"unsupported dtype {q1.dtype}")
+        H, TQ, D = q1.shape
+        # The offsets are read on the host (a device tensor is copied, which synchronises).
+        self.cu_q = torch.as_tensor(cu_seqlens_q, dtype=torch.int32).to("cpu").contiguous()
+        self.cu_k = torch.as_tensor(cu_seqlens_k, dtype=torch.int32).to("cpu").contiguous()
+        if self.cu_q.dim() != 1 or self.cu_q.shape != self.cu_k.shape or self.cu_q.numel() < 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D with B + 1 entries each")
+        if int(self.cu_q[-1]) != TQ or int(self.cu_k[-1]) != k1.shape[1]:
+            raise ValueError("the last offsets must equal the packed lengths TQ and TK")
+        self.p = _lib.VarlenProblem(self.cu_q.numel() - 1, H, D, self.cu_q.data_ptr(), self.cu_k.data_ptr(),
+                                    float(1.0 / math.sqrt(D) if scale is None else scale),
+                                    1 if causal else 0, _DTYPES[q1.dtype])
+
+
+def varlen_problem_for(q1, k1, cu_seqlens_q, cu_seqlens_k, scale=None, causal=False) -> _Varlen:
+    return _Varlen(q1, k1, cu_seqlens_q, cu_seqlens_k, scale, causal)
+
+
+def _check_packed(q1, k1, q2, k2):
+    for t in (q1, k1, q2, k2):
+        if not t.is_cuda:
+            raise ValueError("inputs must live on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+        if t.dtype != q1.dtype:
+            raise TypeError("all inputs must share one dtype")
+    if q2.shape != q1.shape or k2.shape != k1.shape:
+        raise ValueError("teacher and student shapes differ")
+    if k1.shape[0] != q1.shape[0] or k1.shape[2] != q1.shape[2]:
+        raise ValueError("Q and K disagree on heads or head dim")
+
+
+def streamkl_fwd_varlen(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, scale: Optional[float] = None,
+                        causal: bool = False, out=None):
+    """Per-row KL, LSE1, LSE2 (fp32 [H, TQ]) of a packed batch of sequences."""
+    _check_packed(q1, k1, q2, k2)
+    v = _Varlen(q1, k1, cu_seqlens_q, cu_seqlens_k, scale, causal)
+    if out is None:
+        out = tuple(torch.empty(q1.shape[:2], dtype=torch.float32, device=q1.device) for _ in range(3))
+    kl, lse1, lse2 = out
+    st = _lib.lib().streamkl_fwd_varlen(v.p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
+                                        _ptr(lse2), _stream_handle(q1.device))
+    _lib.check(st, "streamkl_fwd_varlen")
+    return kl, lse1, lse2
+
+
+def bwd_varlen_workspace_size(q1, k1, cu_seqlens_q, cu_seqlens_k, scale=None, causal=False) -> int:
+    v = _Varlen(q1, k1, cu_seqlens_q, cu_seqlens_k, scale, causal)
+    return int(_lib.lib().streamkl_bwd_varlen_workspace_size(v.p))
+
+
+def streamkl_bwd_varlen(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, kl, lse1, lse2, g,
+                        scale: Optional[float] = None, causal: bool = False, teacher: bool = True,
+                        student: bool = True, workspace: Optional[torch.Tensor] = None, out=None):
+    """Gradients (dq1, dk1, dq2, dk2) of sum(g * KL) over a packed batch; a skipped pair is None."""
+    _check_packed(q1, k1, q2, k2)
+    v = _Varlen(q1, k1, cu_seqlens_q, cu_seqlens_k, scale, causal)
+    for t in (kl, lse1, lse2, g):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != q1.shape[:2]:
+            raise ValueError("kl, lse1, lse2, g must be contiguous fp32 [H, TQ]")
+    if out is None:
+        def mk(ref, on):
+            return torch.empty(ref.shape, dtype=torch.float32, device=ref.device) if on else None
+        out = (mk(q1, teacher), mk(k1, teacher), mk(q2, student), mk(k2, student))
+    dq1, dk1, dq2, dk2 = out
+    if workspace is None:
+        need = int(_lib.lib().streamkl_bwd_varlen_workspace_size(v.p))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.lib().streamkl_bwd_varlen(v.p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
+                                        _ptr(lse2), _ptr(g), _ptr(dq1), _ptr(dk1), _ptr(dq2), _ptr(dk2),
+                                        _ptr(workspace), nbytes, _stream_handle(q1.device))
+    _lib.check(st, "streamkl_bwd_varlen")
+    return dq1, dk1, dq2, dk2

@@ -34,6 +34,9 @@ EXPORTS = (
     "streamkl_bwd_prepare",
     "streamkl_bwd_dk",
     "streamkl_bwd_dq",
+    "streamkl_fwd_varlen",
+    "streamkl_bwd_varlen_workspace_size",
+    "streamkl_bwd_varlen",
     "streamkl_status_string",
     "streamkl_version",
 )
@@ -47,6 +50,20 @@ class Problem(ctypes.Structure):
         ("NQ", ctypes.c_int64),
         ("NK", ctypes.c_int64),
         ("D", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class VarlenProblem(ctypes.Structure):
+    """Mirror of streamkl_varlen_problem (offset arrays are host pointers)."""
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_k", ctypes.c_void_p),
         ("scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
@@ -91,6 +108,13 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
             fn.restype = ctypes.c_int
+        vpp = ctypes.POINTER(VarlenProblem)
+        L.streamkl_fwd_varlen.argtypes = [vpp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.streamkl_fwd_varlen.restype = ctypes.c_int
+        L.streamkl_bwd_varlen_workspace_size.argtypes = [vpp]
+        L.streamkl_bwd_varlen_workspace_size.restype = sz
+        L.streamkl_bwd_varlen.argtypes = [vpp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.streamkl_bwd_varlen.restype = ctypes.c_int
         L.streamkl_status_string.argtypes = [ctypes.c_int]
         L.streamkl_status_string.restype = ctypes.c_char_p
         L.streamkl_version.argtypes = []

@@ -93,6 +93,8 @@ skl::FwdParams make_fwd(const streamkl_problem *p, const void *q1, const void *k
   f.lse1 = lse1;
   f.lse2 = lse2;
   f.ws = nullptr;
+  f.qmap = skl::RowMap::dense(p->NQ);
+  f.kmap = skl::RowMap::dense(p->NK);
   f.BH = p->B * p->H;
   f.NQ = p->NQ;
   f.NK = p->NK;
@@ -230,6 +232,8 @@ skl::BwdParams make_bwd(const streamkl_problem *p, const void *q1, const void *k
   b.dk1 = dk1;
   b.dq2 = dq2;
   b.dk2 = dk2;
+  b.qmap = skl::RowMap::dense(p->NQ);
+  b.kmap = skl::RowMap::dense(p->NK);
   b.BH = p->B * p->H;
   b.NQ = p->NQ;
   b.NK = p->NK;
@@ -290,9 +294,9 @@ streamkl_status run_dq(const streamkl_problem *p, skl::BwdParams b, hipStream_t 
   return skl::launch_bwd_dq(p->dtype, (int)p->D, b, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
 }
 
-streamkl_status run_sigma(const streamkl_problem *p, const float *g, void *workspace, hipStream_t s) {
-  return skl::launch_grad_scale(p->dtype, g, p->B * p->H, p->NQ, reinterpret_cast<float *>(workspace), s) ==
-                 hipSuccess
+// sigma of every unit of `b` into the front of its workspace.
+streamkl_status run_sigma(const streamkl_problem *p, const skl::BwdParams &b, hipStream_t s) {
+  return skl::launch_grad_scale(p->dtype, b.g, b.qmap, b.BH, p->NQ, const_cast<float *>(b.sigma), s) == hipSuccess
              ? STREAMKL_OK
              : STREAMKL_ERR_HIP;
 }
@@ -302,10 +306,10 @@ streamkl_status run_transposes(const streamkl_problem *p, const skl::BwdParams &
   const int D = (int)p->D;
   void *tq1 = const_cast<void *>(b.tq1), *tq2 = const_cast<void *>(b.tq2);
   void *tk1 = const_cast<void *>(b.tk1), *tk2 = const_cast<void *>(b.tk2);
-  if (skl::launch_bwd_transpose(D, b.q1, b.BH, p->NQ, tq1, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, b.q2, b.BH, p->NQ, tq2, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, b.k1, b.BH, p->NK, tk1, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, b.k2, b.BH, p->NK, tk2, s) != hipSuccess)
+  if (skl::launch_bwd_transpose(D, b.q1, b.qmap, b.BH, p->NQ, tq1, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, b.q2, b.qmap, b.BH, p->NQ, tq2, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, b.k1, b.kmap, b.BH, p->NK, tk1, s) != hipSuccess ||
+      skl::launch_bwd_transpose(D, b.k2, b.kmap, b.BH, p->NK, tk2, s) != hipSuccess)
     return STREAMKL_ERR_HIP;
   return STREAMKL_OK;
 }
@@ -313,10 +317,10 @@ streamkl_status run_transposes(const streamkl_problem *p, const skl::BwdParams &
 streamkl_status run_prepare(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
                             const void *k2, const float *g, void *workspace, hipStream_t s) {
   if (p->NQ == 0) return STREAMKL_OK;
-  streamkl_status st = run_sigma(p, g, workspace, s);
-  if (st != STREAMKL_OK || p->dtype != STREAMKL_BF16) return st;
   const skl::BwdParams b =
       make_bwd(p, q1, k1, q2, k2, nullptr, nullptr, nullptr, g, nullptr, nullptr, nullptr, nullptr, workspace);
+  streamkl_status st = run_sigma(p, b, s);
+  if (st != STREAMKL_OK || p->dtype != STREAMKL_BF16) return st;
   return run_transposes(p, b, s);
 }
 
@@ -352,7 +356,7 @@ streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const vo
   while (n < bh && bwd_layout_heads(p, (size_t)(2 * n)).total <= workspace_bytes) n *= 2;
   while (n < bh && bwd_layout_heads(p, (size_t)(n + 1)).total <= workspace_bytes) ++n;
   const BwdLayout l = bwd_layout_heads(p, (size_t)n);
-  if ((st = run_sigma(p, g, workspace, s)) != STREAMKL_OK) return st;
+  if ((st = run_sigma(p, b, s)) != STREAMKL_OK) return st;
   for (int64_t h0 = 0; h0 < bh; h0 += n) {
     const int64_t cnt = h0 + n <= bh ? n : bh - h0;
     skl::BwdParams bg = head_group(p, b, h0, cnt, l, workspace);
@@ -405,6 +409,171 @@ streamkl_status streamkl_bwd_dq(const streamkl_problem *p, const void *q1, const
   if (st != STREAMKL_OK) return st;
   skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, nullptr, dq2, nullptr, workspace);
   return run_dq(p, b, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Packed variable-length batches.  Each run of consecutive sequences with the
+// same (query, key) lengths is one launchable problem whose units are
+// (sequence, head) pairs addressed through row maps (b * L + h * T rows from
+// the run's first row); runs are launched one after another on the stream.
+
+namespace {
+
+struct Run {
+  int64_t b0, b1, nq, nk;
+};
+
+int64_t seq_len(const int32_t *cu, int64_t b) { return (int64_t)cu[b + 1] - (int64_t)cu[b]; }
+
+// The problem a run stands for (B = its sequence count).
+streamkl_problem run_problem(const streamkl_varlen_problem *v, const Run &r) {
+  streamkl_problem p{};
+  p.B = r.b1 - r.b0;
+  p.H = v->H;
+  p.NQ = r.nq;
+  p.NK = r.nk;
+  p.D = v->D;
+  p.scale = v->scale;
+  p.causal = v->causal;
+  p.dtype = v->dtype;
+  return p;
+}
+
+// Calls f(run) for the maximal runs of equal-length sequences, in order;
+// stops at the first status other than OK.
+template <class F>
+streamkl_status for_each_run(const streamkl_varlen_problem *v, F f) {
+  const int32_t *cq = v->cu_seqlens_q, *ck = v->cu_seqlens_k;
+  int64_t b = 0;
+  while (b < v->B) {
+    const int64_t nq = seq_len(cq, b), nk = seq_len(ck, b);
+    int64_t e = b + 1;
+    while (e < v->B && seq_len(cq, e) == nq && seq_len(ck, e) == nk) ++e;
+    const streamkl_status st = f(Run{b, e, nq, nk});
+    if (st != STREAMKL_OK) return st;
+    b = e;
+  }
+  return STREAMKL_OK;
+}
+
+streamkl_status check_varlen(const streamkl_varlen_problem *v) {
+  if (!v) return STREAMKL_ERR_NULL;
+  if (v->dtype != STREAMKL_BF16 && v->dtype != STREAMKL_FP32) return STREAMKL_ERR_DTYPE;
+  if (v->B < 0 || v->H < 0) return STREAMKL_ERR_SHAPE;
+  if (v->D != 64 && v->D != 128) return STREAMKL_ERR_SHAPE;
+  if (!v->cu_seqlens_q || !v->cu_seqlens_k) return STREAMKL_ERR_NULL;
+  const int32_t *cq = v->cu_seqlens_q, *ck = v->cu_seqlens_k;
+  if (cq[0] != 0 || ck[0] != 0) return STREAMKL_ERR_SHAPE;
+  for (int64_t b = 0; b < v->B; ++b)
+    if (seq_len(cq, b) < 0 || seq_len(ck, b) < 0) return STREAMKL_ERR_SHAPE;
+  if (v->H >= ((int64_t)1 << 31)) return STREAMKL_ERR_SHAPE;
+  // Every run must be a valid problem on its own (lengths, causal shape,
+  // per-sequence 32-bit offsets).
+  return for_each_run(v, [&](const Run &r) {
+    const streamkl_problem p = run_problem(v, r);
+    return check_problem(&p);
+  });
+}
+
+int64_t total_rows(const int32_t *cu, int64_t B) { return (int64_t)cu[B]; }
+
+const void *adv_rows(const void *ptr, int64_t rows, int64_t D, int64_t es) {
+  return ptr ? reinterpret_cast<const char *>(ptr) + rows * D * es : nullptr;
+}
+float *adv_rowsf(float *ptr, int64_t rows, int64_t D) { return ptr ? ptr + rows * D : nullptr; }
+
+}  // namespace
+
+extern "C" {
+
+streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v, const void *q1, const void *k1,
+                                    const void *q2, const void *k2, float *kl, float *lse1, float *lse2,
+                                    void *stream) {
+  streamkl_status st = check_varlen(v);
+  if (st != STREAMKL_OK) return st;
+  const int64_t TQ = total_rows(v->cu_seqlens_q, v->B), TK = total_rows(v->cu_seqlens_k, v->B);
+  if (v->B == 0 || v->H == 0 || TQ == 0) return STREAMKL_OK;
+  if (!q1 || !k1 || !q2 || !k2) return STREAMKL_ERR_NULL;
+  if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2)) return STREAMKL_ERR_ALIGN;
+  if ((st = check_rowvecs(kl, lse1, lse2)) != STREAMKL_OK) return st;
+  const int64_t es = v->dtype == STREAMKL_BF16 ? 2 : 4;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return for_each_run(v, [&](const Run &r) {
+    if (r.nq == 0) return STREAMKL_OK;
+    const streamkl_problem p = run_problem(v, r);
+    const int64_t oq = v->cu_seqlens_q[r.b0], ok = v->cu_seqlens_k[r.b0];
+    skl::FwdParams f = make_fwd(&p, adv_rows(q1, oq, v->D, es), adv_rows(k1, ok, v->D, es),
+                                adv_rows(q2, oq, v->D, es), adv_rows(k2, ok, v->D, es), kl + oq, lse1 + oq,
+                                lse2 + oq);
+    f.qmap = skl::RowMap{r.nq, TQ, (int)v->H};
+    f.kmap = skl::RowMap{r.nk, TK, (int)v->H};
+    return skl::launch_fwd(v->dtype, (int)v->D, f, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+  });
+}
+
+size_t streamkl_bwd_varlen_workspace_size(const streamkl_varlen_problem *v) {
+  if (check_varlen(v) != STREAMKL_OK) return 0;
+  size_t need = 16;
+  for_each_run(v, [&](const Run &r) {
+    if (r.nq > 0) {
+      const streamkl_problem p = run_problem(v, r);
+      const size_t n = bwd_layout(&p).total;
+      if (n > need) need = n;
+    }
+    return STREAMKL_OK;
+  });
+  return need;
+}
+
+streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void *q1, const void *k1,
+                                    const void *q2, const void *k2, const float *kl, const float *lse1,
+                                    const float *lse2, const float *g, float *dq1, float *dk1, float *dq2,
+                                    float *dk2, void *workspace, size_t workspace_bytes, void *stream) {
+  streamkl_status st = check_varlen(v);
+  if (st != STREAMKL_OK) return st;
+  if ((dq1 == nullptr) != (dk1 == nullptr) || (dq2 == nullptr) != (dk2 == nullptr)) return STREAMKL_ERR_NULL;
+  const int64_t TQ = total_rows(v->cu_seqlens_q, v->B), TK = total_rows(v->cu_seqlens_k, v->B);
+  if (v->B == 0 || v->H == 0 || (TQ == 0 && TK == 0)) return STREAMKL_OK;
+  if (!dq1 && !dq2) return STREAMKL_OK;
+  if (!q1 || !k1 || !q2 || !k2) return STREAMKL_ERR_NULL;
+  if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2)) return STREAMKL_ERR_ALIGN;
+  for (float *o : {dq1, dk1, dq2, dk2})
+    if (o && !aligned16(o)) return STREAMKL_ERR_ALIGN;
+  if (TQ > 0) {
+    if (!kl || !lse1 || !lse2 || !g) return STREAMKL_ERR_NULL;
+    if (!aligned16(kl) || !aligned16(lse1) || !aligned16(lse2) || !aligned16(g)) return STREAMKL_ERR_ALIGN;
+    if (!workspace || workspace_bytes < streamkl_bwd_varlen_workspace_size(v)) return STREAMKL_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
+  }
+  const int64_t es = v->dtype == STREAMKL_BF16 ? 2 : 4, D = v->D, H = v->H;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return for_each_run(v, [&](const Run &r) {
+    const int64_t oq = v->cu_seqlens_q[r.b0], ok = v->cu_seqlens_k[r.b0];
+    if (r.nq == 0) {
+      // No query rows: the key gradients of these sequences are zero.
+      const int64_t n = (r.b1 - r.b0) * r.nk * D;
+      for (int64_t h = 0; h < H && n > 0; ++h)
+        for (float *dk : {dk1, dk2})
+          if (dk && skl::launch_zero(dk + (h * TK + ok) * D, n, s) != hipSuccess) return STREAMKL_ERR_HIP;
+      return STREAMKL_OK;
+    }
+    const streamkl_problem p = run_problem(v, r);
+    skl::BwdParams b = make_bwd(&p, adv_rows(q1, oq, D, es), adv_rows(k1, ok, D, es), adv_rows(q2, oq, D, es),
+                                adv_rows(k2, ok, D, es), kl + oq, lse1 + oq, lse2 + oq, g + oq,
+                                adv_rowsf(dq1, oq, D), adv_rowsf(dk1, ok, D), adv_rowsf(dq2, oq, D),
+                                adv_rowsf(dk2, ok, D), workspace);
+    b.qmap = skl::RowMap{r.nq, TQ, (int)H};
+    b.kmap = skl::RowMap{r.nk, TK, (int)H};
+    // The run's sigma and transposed copies reuse the front of the workspace;
+    // stream order keeps the runs apart.
+    streamkl_status rs = run_sigma(&p, b, s);
+    if (rs == STREAMKL_OK && v->dtype == STREAMKL_BF16) rs = run_transposes(&p, b, s);
+    if (rs == STREAMKL_OK) rs = run_dk(&p, b, s);
+    if (rs == STREAMKL_OK) rs = run_dq(&p, b, s);
+    return rs;
+  });
 }
 
 }  // extern "C"

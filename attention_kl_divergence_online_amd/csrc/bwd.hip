@@ -125,16 +125,16 @@ __global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p) {
   const int64_t bh = L / (uint32_t)nrt;
   const int rt = KEYS_RES ? (int)(L % (uint32_t)nrt) : nrt - 1 - (int)(L % (uint32_t)nrt);
 
-  const T *R1 = reinterpret_cast<const T *>(KEYS_RES ? p.k1 : p.q1) + bh * (int64_t)NR * D;
-  const T *R2 = reinterpret_cast<const T *>(KEYS_RES ? p.k2 : p.q2) + bh * (int64_t)NR * D;
-  const char *X1 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(KEYS_RES ? p.q1 : p.k1) +
-                                                  bh * (int64_t)NX * D);
-  const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(KEYS_RES ? p.q2 : p.k2) +
-                                                  bh * (int64_t)NX * D);
-  const float *KLr = p.kl + bh * (int64_t)NQ;
-  const float *LS1 = p.lse1 + bh * (int64_t)NQ;
-  const float *LS2 = p.lse2 + bh * (int64_t)NQ;
-  const float *Gr = p.g + bh * (int64_t)NQ;
+  const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
+  const int64_t rr = KEYS_RES ? rk : rq, rx = KEYS_RES ? rq : rk;  // resident / streamed row bases
+  const T *R1 = reinterpret_cast<const T *>(KEYS_RES ? p.k1 : p.q1) + rr * D;
+  const T *R2 = reinterpret_cast<const T *>(KEYS_RES ? p.k2 : p.q2) + rr * D;
+  const char *X1 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(KEYS_RES ? p.q1 : p.k1) + rx * D);
+  const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(KEYS_RES ? p.q2 : p.k2) + rx * D);
+  const float *KLr = p.kl + rq;
+  const float *LS1 = p.lse1 + rq;
+  const float *LS2 = p.lse2 + rq;
+  const float *Gr = p.g + rq;
   // Prepared per-head factor; stored negated when some g of the head is negative.
   const float sigma_raw = p.sigma[bh];
   const float sigma = fabsf(sigma_raw);
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p) {
       const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
       float *O1 = KEYS_RES ? p.dk1 : p.dq1;
       float *O2 = KEYS_RES ? p.dk2 : p.dq2;
-      const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
+      const int64_t rowoff = (rr + my_r) * D;
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
@@ -506,18 +506,18 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   const int64_t bh = L / (uint32_t)nrt;
   const int rt = KEYS_RES ? (int)(L % (uint32_t)nrt) : nrt - 1 - (int)(L % (uint32_t)nrt);
 
-  const bf16 *R1 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k1 : p.q1) + bh * (int64_t)NR * D;
-  const bf16 *R2 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k2 : p.q2) + bh * (int64_t)NR * D;
-  const char *X1 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q1 : p.k1) +
-                                                  bh * (int64_t)NX * D);
-  const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q2 : p.k2) +
-                                                  bh * (int64_t)NX * D);
+  const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
+  const int64_t rr = KEYS_RES ? rk : rq, rx = KEYS_RES ? rq : rk;  // resident / streamed row bases
+  const bf16 *R1 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k1 : p.q1) + rr * D;
+  const bf16 *R2 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k2 : p.q2) + rr * D;
+  const char *X1 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q1 : p.k1) + rx * D);
+  const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q2 : p.k2) + rx * D);
   const char *T1 = reinterpret_cast<const char *>(KEYS_RES ? p.tq1 : p.tk1) + bh * (int64_t)nxt * Tr::TR_T;
   const char *T2 = reinterpret_cast<const char *>(KEYS_RES ? p.tq2 : p.tk2) + bh * (int64_t)nxt * Tr::TR_T;
-  const float *KLr = p.kl + bh * (int64_t)NQ;
-  const float *LS1 = p.lse1 + bh * (int64_t)NQ;
-  const float *LS2 = p.lse2 + bh * (int64_t)NQ;
-  const float *Gr = p.g + bh * (int64_t)NQ;
+  const float *KLr = p.kl + rq;
+  const float *LS1 = p.lse1 + rq;
+  const float *LS2 = p.lse2 + rq;
+  const float *Gr = p.g + rq;
   const float sigma_raw = p.sigma[bh];
   const float sigma = fabsf(sigma_raw);
   const bool any_neg = sigma_raw < 0.f;
@@ -874,7 +874,7 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
     if (r_ok && (TEN ? p.want2 : p.want1)) {
       const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
       float *O = TEN ? (KEYS_RES ? p.dk2 : p.dq2) : (KEYS_RES ? p.dk1 : p.dq1);
-      const int64_t rowoff = (bh * (int64_t)NR + my_r) * D;
+      const int64_t rowoff = (rr + my_r) * D;
   #pragma unroll
       for (int db = 0; db < NACC; ++db) {
   #pragma unroll
@@ -906,12 +906,13 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
 // row(pos) swapping bits 2 and 3 of pos (the slot order of the dS operands in
 // a 16-row k-step); rows past the end are zero.  One workgroup per (b, h, tile).
 template <int D>
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16 *x, int64_t N, int64_t ntile, f16 *out) {
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16 *x, RowMap map, int64_t N, int64_t ntile,
+                                                        f16 *out) {
   constexpr int CPR = D * 2 / 16;
   constexpr int LROW = D + 8;  // fp16 elements per LDS row (16-byte pad)
   __shared__ __attribute__((aligned(16))) f16 tile[kBwdTile * LROW];
   const int64_t T = blockIdx.x % ntile, bh = blockIdx.x / ntile;
-  const bf16 *xs = x + (bh * N + T * kBwdTile) * D;
+  const bf16 *xs = x + (map.row0(bh) + T * kBwdTile) * D;
   const int nrow = (int)min<int64_t>(kBwdTile, N - T * kBwdTile);
   for (int cidx = threadIdx.x; cidx < kBwdTile * CPR; cidx += 256) {
     const int r = cidx / CPR, cc = cidx % CPR;
@@ -937,18 +938,19 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16 *x, int64_t N
 // sigma[b,h] = 2^(kGradExp - e) with 2^(e-1) <= max_i |g[b,h,i]| < 2^e (1 if g is all zero,
 // and 1 everywhere when `unit` is set: fp32 inputs need no scaling), stored
 // negated when some g[b,h,:] is negative.
-__global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, int64_t NQ, float *sigma, int unit) {
+__global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap qmap, int64_t NQ, float *sigma,
+                                                         int unit) {
   const int64_t bh = blockIdx.x;
   if (unit) {
     // fp32 inputs: no dS scaling, but the sign flag is still needed.
-    const float *gu = g + bh * NQ;
+    const float *gu = g + qmap.row0(bh);
     int neg = 0;
     for (int64_t i = threadIdx.x; i < NQ; i += 256) neg |= gu[i] < 0.f;
     neg = __syncthreads_or(neg);
     if (threadIdx.x == 0) sigma[bh] = neg ? -1.f : 1.f;
     return;
   }
-  const float *gp = g + bh * NQ;
+  const float *gp = g + qmap.row0(bh);
   float m = 0.f;
   int neg = 0;
   for (int64_t i = threadIdx.x; i < NQ; i += 256) {
@@ -997,8 +999,10 @@ static hipError_t launch_fp32_pass(const BwdParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_grad_scale(int dtype, const float *g, int64_t BH, int64_t NQ, float *sigma, hipStream_t s) {
-  hipLaunchKernelGGL(grad_scale_kernel, dim3((uint32_t)BH), dim3(256), 0, s, g, NQ, sigma, dtype == 1 ? 1 : 0);
+hipError_t launch_grad_scale(int dtype, const float *g, RowMap qmap, int64_t BH, int64_t NQ, float *sigma,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(grad_scale_kernel, dim3((uint32_t)BH), dim3(256), 0, s, g, qmap, NQ, sigma,
+                     dtype == 1 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1024,16 +1028,16 @@ static hipError_t launch_bf16_pass(const BwdParams &p, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_bwd_transpose(int D, const void *x, int64_t BH, int64_t N, void *out, hipStream_t s) {
+hipError_t launch_bwd_transpose(int D, const void *x, RowMap map, int64_t BH, int64_t N, void *out, hipStream_t s) {
   if (BH == 0 || N == 0) return hipSuccess;
   const int64_t ntile = (N + kBwdTile - 1) / kBwdTile;
   const dim3 grid((uint32_t)(ntile * BH));
   if (D == 128)
-    hipLaunchKernelGGL(transpose_kernel<128>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), N, ntile,
-                       reinterpret_cast<f16 *>(out));
+    hipLaunchKernelGGL(transpose_kernel<128>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map, N,
+                       ntile, reinterpret_cast<f16 *>(out));
   else
-    hipLaunchKernelGGL(transpose_kernel<64>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), N, ntile,
-                       reinterpret_cast<f16 *>(out));
+    hipLaunchKernelGGL(transpose_kernel<64>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map, N,
+                       ntile, reinterpret_cast<f16 *>(out));
   return hipGetLastError();
 }
 

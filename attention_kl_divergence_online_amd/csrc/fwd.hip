@@ -155,10 +155,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
 
   const int NQ = (int)p.NQ, NK = (int)p.NK;
   const int off = NK - NQ;
-  const T *Q1 = reinterpret_cast<const T *>(p.q1) + bh * (int64_t)NQ * D;
-  const T *Q2 = reinterpret_cast<const T *>(p.q2) + bh * (int64_t)NQ * D;
-  const char *K1 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(p.k1) + bh * (int64_t)NK * D);
-  const char *K2 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(p.k2) + bh * (int64_t)NK * D);
+  const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
+  const T *Q1 = reinterpret_cast<const T *>(p.q1) + rq * D;
+  const T *Q2 = reinterpret_cast<const T *>(p.q2) + rq * D;
+  const char *K1 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(p.k1) + rk * D);
+  const char *K2 = reinterpret_cast<const char *>(reinterpret_cast<const T *>(p.k2) + rk * D);
 
   const int q0 = qt * Tr::BQ;
   const int qend = min(q0 + Tr::BQ, NQ);
@@ -296,10 +297,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
     const float L2 = __builtin_fmaf(l2, va, ol2 * vb);
     const int row = qw0 + qb * 32 + c32;
     if (h == 0 && row < qend) {
-      const int64_t idx = bh * (int64_t)NQ + row;
       if (SPLIT) {
+        // Partial states are indexed densely by (unit, row).
         const int64_t rows = p.BH * (int64_t)NQ;
-        float *w = p.ws + (int64_t)sp * rows + idx;
+        float *w = p.ws + (int64_t)sp * rows + bh * (int64_t)NQ + row;
         const int64_t fstride = (int64_t)p.splits * rows;
         w[0] = M1;
         w[fstride] = L1;
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
         w[3 * fstride] = L2;
         w[4 * fstride] = A;
       } else {
+        const int64_t idx = rq + row;
         finish_row(M1, L1, M2, L2, A, p.scale, p.kl + idx, p.lse1 + idx, p.lse2 + idx);
       }
     }
@@ -341,7 +343,8 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(FwdParams p) {
       L2 = __builtin_fmaf(w2, ws[3 * fstride], L2);
     }
   }
-  finish_row(M1, L1, M2, L2, A, p.scale, p.kl + idx, p.lse1 + idx, p.lse2 + idx);
+  const int64_t u = idx / p.NQ, o = p.qmap.row0(u) + (idx - u * p.NQ);
+  finish_row(M1, L1, M2, L2, A, p.scale, p.kl + o, p.lse1 + o, p.lse2 + o);
 }
 
 // ---- bf16 inputs: direct LDS staging, pipelined key blocks ----
@@ -397,10 +400,11 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
 
   const int NQ = (int)p.NQ, NK = (int)p.NK;
   const int off = NK - NQ;
-  const bf16 *Q1 = reinterpret_cast<const bf16 *>(p.q1) + bh * (int64_t)NQ * D;
-  const bf16 *Q2 = reinterpret_cast<const bf16 *>(p.q2) + bh * (int64_t)NQ * D;
-  const BufRange rk1{reinterpret_cast<const bf16 *>(p.k1) + bh * (int64_t)NK * D, NK * Tr::RB};
-  const BufRange rk2{reinterpret_cast<const bf16 *>(p.k2) + bh * (int64_t)NK * D, NK * Tr::RB};
+  const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
+  const bf16 *Q1 = reinterpret_cast<const bf16 *>(p.q1) + rq * D;
+  const bf16 *Q2 = reinterpret_cast<const bf16 *>(p.q2) + rq * D;
+  const BufRange rk1{reinterpret_cast<const bf16 *>(p.k1) + rk * D, NK * Tr::RB};
+  const BufRange rk2{reinterpret_cast<const bf16 *>(p.k2) + rk * D, NK * Tr::RB};
 
   const int q0 = qt * Tr::BQ;
   const int qend = min(q0 + Tr::BQ, NQ);
@@ -522,10 +526,10 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
     const float A = __builtin_fmaf(acc, wa, oacc * wb);
     const float L2 = __builtin_fmaf(l2, va, ol2 * vb);
     if (h == 0 && row_ok) {
-      const int64_t idx = bh * (int64_t)NQ + row;
       if (SPLIT) {
+        // Partial states are indexed densely by (unit, row).
         const int64_t rows = p.BH * (int64_t)NQ;
-        float *w = p.ws + (int64_t)sp * rows + idx;
+        float *w = p.ws + (int64_t)sp * rows + bh * (int64_t)NQ + row;
         const int64_t fstride = (int64_t)p.splits * rows;
         w[0] = M1;
         w[fstride] = L1;
@@ -533,6 +537,7 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
         w[3 * fstride] = L2;
         w[4 * fstride] = A;
       } else {
+        const int64_t idx = rq + row;
         finish_row(M1, L1, M2, L2, A, p.scale, p.kl + idx, p.lse1 + idx, p.lse2 + idx);
       }
     }

@@ -7,9 +7,26 @@
 
 namespace skl {
 
+// Row addressing of one family of per-unit tensors.  A launch runs BH units
+// (one sequence of one head each); unit u starts at row
+// (u / H) * sb + (u % H) * sh of its tensors, rows of D elements (row
+// vectors: one element).  [B, H, N, D] tensors are unit after unit (row0 =
+// u * N: `dense`); a run of equal-length sequences packed per head
+// ([H, T, D], sequence length L, u = b * H + h) has sb = L and sh = T.
+struct RowMap {
+  int64_t sb, sh;
+  int H;  // >= 1
+  __host__ __device__ int64_t row0(int64_t u) const {
+    const uint32_t uu = (uint32_t)u, hh = (uint32_t)H;
+    return (int64_t)(uu / hh) * sb + (int64_t)(uu % hh) * sh;
+  }
+  static RowMap dense(int64_t N) { return RowMap{N, 0, 1}; }
+};
+
 struct FwdParams {
-  const void *q1, *k1, *q2, *k2;  // [BH, NQ|NK, D] in the input dtype
-  float *kl, *lse1, *lse2;         // [BH, NQ]
+  const void *q1, *k1, *q2, *k2;  // unit rows of NQ|NK x D in the input dtype (qmap / kmap)
+  float *kl, *lse1, *lse2;         // unit rows of NQ (qmap)
+  RowMap qmap, kmap;
   float *ws;                       // split-K partial states [5][splits][BH*NQ], else null
   int64_t BH, NQ, NK;
   float scale;
@@ -20,12 +37,13 @@ struct FwdParams {
 };
 
 struct BwdParams {
-  const void *q1, *k1, *q2, *k2;
-  const float *kl, *lse1, *lse2, *g;
-  const float *sigma;  // per (b,h) power-of-two factor applied to g (null: 1)
+  const void *q1, *k1, *q2, *k2;      // qmap / kmap rows
+  const float *kl, *lse1, *lse2, *g;  // qmap rows
+  RowMap qmap, kmap;
+  const float *sigma;  // per unit power-of-two factor applied to g (null: 1)
   // bf16 inputs: prepared transposed fp16 copies [BH][ceil(N/64)][D][64] (null for fp32)
   const void *tq1, *tq2, *tk1, *tk2;
-  float *dq1, *dk1, *dq2, *dk2;
+  float *dq1, *dk1, *dq2, *dk2;  // like the inputs (qmap / kmap rows), fp32
   int64_t BH, NQ, NK;
   float scale;
   int causal;
@@ -45,11 +63,13 @@ int fwd_block_queries(int dtype, int D);
 hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s);
 hipError_t launch_splitk_merge(const FwdParams &p, hipStream_t s);
 // Backward pieces; `p.sigma` must point at the prepared per-(b,h) factors.
-hipError_t launch_grad_scale(int dtype, const float *g, int64_t BH, int64_t NQ, float *sigma, hipStream_t s);
+hipError_t launch_grad_scale(int dtype, const float *g, RowMap qmap, int64_t BH, int64_t NQ, float *sigma,
+                             hipStream_t s);
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s);
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s);
 hipError_t launch_zero(float *dst, int64_t n, hipStream_t s);
-// bf16 inputs: transposed fp16 copy of x [BH, N, D] into out [BH][ceil(N/64)][D][64].
-hipError_t launch_bwd_transpose(int D, const void *x, int64_t BH, int64_t N, void *out, hipStream_t s);
+// bf16 inputs: transposed fp16 copy of x (BH units of N rows, addressed by `map`)
+// into out [BH][ceil(N/64)][D][64].
+hipError_t launch_bwd_transpose(int D, const void *x, RowMap map, int64_t BH, int64_t N, void *out, hipStream_t s);
 
 }  // namespace skl

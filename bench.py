@@ -153,7 +153,8 @@ def parse():
     ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--other-configs", action="store_true",
                     help="also time forward and backward on the other bf16 workloads (causal_4k, "
-                         "noncausal_16k, splitk_bwd_128k) and report them under \"other_configs\"")
+                         "noncausal_16k, splitk_bwd_128k), the decode split-K forward and the packed "
+                         "variable-length batch, and report them under \"other_configs\"")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (scale reference for HBM byte counters)")
@@ -333,6 +334,7 @@ def main():
         out["other_configs"] = {n: config_bench(skl, synth, torch, args, n)
                                 for n in ("causal_4k", "noncausal_16k", "splitk_bwd_128k")}
         out["other_configs"]["decode_128k"] = splitk_bench(skl, synth, torch, args, "decode_128k")
+        out["other_configs"]["varlen_mix"] = varlen_bench(skl, synth, torch, args, "varlen_mix")
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q1, k1, q2, k2, args.cpu_seconds)
@@ -365,6 +367,38 @@ def config_bench(skl, synth, torch, args, name):
            "fwd_tflops": round(4 * w.D * pairs / (fwd_ms * 1e-3) / 1e12, 2),
            "bwd_tflops": round(12 * w.D * pairs / (bwd_ms * 1e-3) / 1e12, 2),
            "step_tflops": round(16 * w.D * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2)}
+    del q1, k1, q2, k2, grads, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def varlen_bench(skl, synth, torch, args, name):
+    """Forward and full backward of a packed variable-length batch; HIP-event ms per step."""
+    pb = synth.PACKED[name]
+    q1, k1, q2, k2 = synth.make_packed(pb, "cuda")
+    cq, ck = pb.cu_q, pb.cu_k
+    g = synth.packed_grad(pb, "cuda")
+    out = tuple(torch.empty(q1.shape[:2], dtype=torch.float32, device="cuda") for _ in range(3))
+    grads = tuple(torch.empty_like(t, dtype=torch.float32) for t in (q1, k1, q2, k2))
+    ws = torch.empty(skl.bwd_varlen_workspace_size(q1, k1, cq, ck, pb.scale, pb.causal), dtype=torch.uint8,
+                     device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd_ms = bwd_ms = 0.0
+    for it in range(args.warmup + args.steps):
+        ev[0].record()
+        skl.streamkl_fwd_varlen(q1, k1, q2, k2, cq, ck, pb.scale, pb.causal, out=out)
+        ev[1].record()
+        skl.streamkl_bwd_varlen(q1, k1, q2, k2, cq, ck, *out, g, pb.scale, pb.causal, workspace=ws, out=grads)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            fwd_ms += ev[0].elapsed_time(ev[1]) / args.steps
+            bwd_ms += ev[1].elapsed_time(ev[2]) / args.steps
+    pairs = pb.visible_pairs()
+    res = {"sequences": len(pb.lens_q), "rows": cq[-1], "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+           "fwd_tflops": round(4 * pb.D * pairs / (fwd_ms * 1e-3) / 1e12, 2),
+           "bwd_tflops": round(12 * pb.D * pairs / (bwd_ms * 1e-3) / 1e12, 2),
+           "step_tflops": round(16 * pb.D * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2)}
     del q1, k1, q2, k2, grads, ws
     torch.cuda.empty_cache()
     return res

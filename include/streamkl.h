@@ -193,6 +193,75 @@ streamkl_status streamkl_bwd_dq(const streamkl_problem *p,
                                 const float *g, float *dq1, float *dq2,
                                 const void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Packed variable-length batches.  The pages list variable-length queries and
+ * keys as future work (arxivlens.com paper view of StreamKL, future
+ * directions).  Here each sequence is an independent problem of the kind
+ * above, and a batch of them is packed without padding.
+ *
+ * Sequence b owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key
+ * rows [cu_seqlens_k[b], cu_seqlens_k[b+1]) of every head, with
+ * TQ = cu_seqlens_q[B] and TK = cu_seqlens_k[B]:
+ *  - Q1, Q2 are [H, TQ, D] and K1, K2 are [H, TK, D], contiguous, in `dtype`
+ *    (head-major: each head's sequences follow one another);
+ *  - KL, LSE1, LSE2 and g are fp32 [H, TQ];
+ *  - gradients are fp32 with the shape of their tensor.
+ * Within a sequence, the visible set, the scale and the causal rule are
+ * those of streamkl_problem with NQ, NK the sequence's own lengths (causal
+ * masks are bottom-right aligned per sequence).  Results are those of a
+ * separate streamkl_fwd / streamkl_bwd call per sequence.
+ *
+ * cu_seqlens_q and cu_seqlens_k are HOST arrays of B + 1 int32 offsets
+ * starting at 0.  They are read during the call only and never kept.
+ * Errors (STREAMKL_ERR_SHAPE) are:
+ *  - a nonzero first offset or a decreasing offset;
+ *  - any sequence that would be rejected as a streamkl_problem: keys == 0
+ *    with queries > 0, causal with more queries than keys, or per-sequence
+ *    sizes past the 32-bit limits.
+ * Sequences with no query rows produce nothing in the forward and zero key
+ * gradients in the backward.  Consecutive sequences of equal lengths run in
+ * one launch per kernel; runs follow one another on `stream`.
+ */
+typedef struct {
+    int64_t B, H;                  /* sequences, heads */
+    int64_t D;                     /* head dimension: 64 or 128 */
+    const int32_t *cu_seqlens_q;   /* host, B + 1 query-row offsets */
+    const int32_t *cu_seqlens_k;   /* host, B + 1 key-row offsets */
+    float scale;                   /* logit scale, as in streamkl_problem */
+    int32_t causal;                /* nonzero: per-sequence bottom-right causal mask */
+    int32_t dtype;                 /* streamkl_dtype of Q1, K1, Q2, K2 */
+} streamkl_varlen_problem;
+
+/* Forward of every sequence (as streamkl_fwd).  Extra device memory: none. */
+streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v,
+                                    const void *q1, const void *k1,
+                                    const void *q2, const void *k2,
+                                    float *kl, float *lse1, float *lse2,
+                                    void *stream);
+
+/*
+ * Workspace bytes for streamkl_bwd_varlen: the largest full-size
+ * streamkl_bwd workspace among the runs of equal-length sequences, since the
+ * runs reuse it one after another.  Returns 0 if `v` is invalid.
+ */
+size_t streamkl_bwd_varlen_workspace_size(const streamkl_varlen_problem *v);
+
+/*
+ * Backward of every sequence (as streamkl_bwd, same NULL-pair rules and
+ * fp16 range condition).  kl, lse1 and lse2 must come from
+ * streamkl_fwd_varlen on the same inputs.  `workspace` must hold at least
+ * streamkl_bwd_varlen_workspace_size bytes (STREAMKL_ERR_WORKSPACE
+ * otherwise) and is overwritten.
+ */
+streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v,
+                                    const void *q1, const void *k1,
+                                    const void *q2, const void *k2,
+                                    const float *kl, const float *lse1, const float *lse2,
+                                    const float *g,
+                                    float *dq1, float *dk1, float *dq2, float *dk2,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *streamkl_status_string(int status);
 

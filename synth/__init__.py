@@ -24,7 +24,8 @@ from typing import Dict, Iterable, Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_head", "make_inputs", "upstream_grad"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_head", "make_inputs", "upstream_grad",
+           "PackedBatch", "PACKED", "make_packed", "packed_grad"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -136,3 +137,92 @@ def make_inputs(w: Workload, device: str = "cpu", heads: Optional[Iterable] = No
 def upstream_grad(w: Workload, device: str = "cpu") -> torch.Tensor:
     """Per-row upstream gradient g of a mean-reduced loss: 1/(B*H*NQ) everywhere."""
     return torch.full((w.B, w.H, w.NQ), 1.0 / (w.B * w.H * w.NQ), dtype=torch.float32, device=device)
+
+
+@dataclasses.dataclass(frozen=True)
+class PackedBatch:
+    """Variable-length sequences packed per head: sequence b has lens_q[b] query
+    rows and lens_k[b] key rows; tensors are [H, sum(lens), D] (head-major)."""
+    cfg_id: int
+    name: str
+    H: int
+    lens_q: tuple
+    lens_k: tuple
+    D: int
+    dtype: str
+    causal: bool
+    noise: float = 0.1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    @staticmethod
+    def _cu(lens):
+        out = [0]
+        for n in lens:
+            out.append(out[-1] + n)
+        return out
+
+    @property
+    def cu_q(self):
+        return self._cu(self.lens_q)
+
+    @property
+    def cu_k(self):
+        return self._cu(self.lens_k)
+
+    def sequence(self, b: int) -> Workload:
+        """Sequence b as a one-sequence workload (its seeds depend on b)."""
+        return Workload(self.cfg_id, f"{self.name}[{b}]", len(self.lens_q), self.H, self.lens_q[b],
+                        self.lens_k[b], self.D, self.dtype, self.causal, noise=self.noise)
+
+    def visible_pairs(self) -> int:
+        return sum(self.sequence(b).visible_pairs() // len(self.lens_q) for b in range(len(self.lens_q)))
+
+
+def _mixed_lengths(n: int, lo: int, hi: int, seed: int) -> tuple:
+    gen = torch.Generator()
+    gen.manual_seed(seed)
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (n,), generator=gen))
+
+
+_MIX = _mixed_lengths(16, 1024, 7168, 77)
+
+PACKED: Dict[str, PackedBatch] = {
+    pb.name: pb for pb in [
+        # 16 causal sequences of 1K-7K tokens (seeded uniform lengths), 32 heads: a
+        # packed long-context batch without padding.
+        PackedBatch(20, "varlen_mix", 32, _MIX, _MIX, 128, "bf16", True),
+    ]
+}
+
+
+def make_packed(pb: PackedBatch, device: str = "cpu"):
+    """(q1, k1, q2, k2): [H, TQ, D] and [H, TK, D]; sequence b of head h is
+    make_head(pb.sequence(b), b, h)."""
+    dt = pb.torch_dtype
+    cq, ck = pb.cu_q, pb.cu_k
+    q1 = torch.empty((pb.H, cq[-1], pb.D), dtype=dt, device=device)
+    k1 = torch.empty((pb.H, ck[-1], pb.D), dtype=dt, device=device)
+    q2 = torch.empty_like(q1)
+    k2 = torch.empty_like(k1)
+    for b in range(len(pb.lens_q)):
+        w = pb.sequence(b)
+        for h in range(pb.H):
+            a, bb, c, d = make_head(w, b, h, device)
+            q1[h, cq[b]:cq[b + 1]].copy_(a)
+            q2[h, cq[b]:cq[b + 1]].copy_(c)
+            k1[h, ck[b]:ck[b + 1]].copy_(bb)
+            k2[h, ck[b]:ck[b + 1]].copy_(d)
+    return q1, k1, q2, k2
+
+
+def packed_grad(pb: PackedBatch, device: str = "cpu") -> torch.Tensor:
+    """Upstream gradient of a mean over all packed rows: 1/(H*TQ) everywhere, [H, TQ]."""
+    tq = pb.cu_q[-1]
+    return torch.full((pb.H, tq), 1.0 / (pb.H * tq), dtype=torch.float32, device=device)

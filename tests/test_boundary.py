@@ -174,3 +174,68 @@ def test_backward_step_validation(L):
         assert call(kl=None) == _lib.STREAMKL_ERR_NULL, name
         assert call(a=None, b=None, ws=None) == _lib.STREAMKL_OK, name
         assert fn(ctypes.byref(P(dtype=5)), A, A, A, A, A, A, A, A, A, A, A, 64, None) == _lib.STREAMKL_ERR_DTYPE
+
+
+class VP:
+    """streamkl_varlen_problem with its host offset arrays kept alive."""
+
+    def __init__(self, cu_q, cu_k, H=2, D=64, causal=0, dtype=_lib.STREAMKL_BF16, null_cu=False):
+        self.cq = (ctypes.c_int32 * len(cu_q))(*cu_q)
+        self.ck = (ctypes.c_int32 * len(cu_k))(*cu_k)
+        self.p = _lib.VarlenProblem(len(cu_q) - 1, H, D, None if null_cu else ctypes.addressof(self.cq),
+                                    ctypes.addressof(self.ck), 0.125, causal, dtype)
+
+    def ref(self):
+        return ctypes.byref(self.p)
+
+
+def vfwd(L, v, q1=A, kl=A):
+    return L.streamkl_fwd_varlen(v.ref(), q1, A, A, A, kl, A, A, None)
+
+
+def vbwd(L, v, ws=A, wsb=1 << 30, dq1=A, dk1=A, g=A, q2=A):
+    return L.streamkl_bwd_varlen(v.ref(), A, A, q2, A, A, A, A, g, dq1, dk1, A, A, ws, wsb, None)
+
+
+def test_varlen_validation(L):
+    assert L.streamkl_fwd_varlen(None, A, A, A, A, A, A, A, None) == _lib.STREAMKL_ERR_NULL
+    assert vfwd(L, VP([0, 5], [0, 5], null_cu=True)) == _lib.STREAMKL_ERR_NULL
+    assert vfwd(L, VP([1, 5], [0, 5])) == _lib.STREAMKL_ERR_SHAPE              # first offset not 0
+    assert vfwd(L, VP([0, 5, 3], [0, 5, 9])) == _lib.STREAMKL_ERR_SHAPE        # decreasing
+    assert vfwd(L, VP([0, 5, 9], [0, 5, 5])) == _lib.STREAMKL_ERR_SHAPE        # queries without keys
+    assert vfwd(L, VP([0, 5, 9], [0, 5, 8], causal=1)) == _lib.STREAMKL_ERR_SHAPE  # 4 queries > 3 keys
+    assert vfwd(L, VP([0, 5], [0, 5], D=96)) == _lib.STREAMKL_ERR_SHAPE
+    assert vfwd(L, VP([0, 5], [0, 5], dtype=9)) == _lib.STREAMKL_ERR_DTYPE
+    assert vfwd(L, VP([0, 5], [0, 5]), q1=None) == _lib.STREAMKL_ERR_NULL
+    assert vfwd(L, VP([0, 5], [0, 5]), q1=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert vfwd(L, VP([0, 5], [0, 5]), kl=MIS) == _lib.STREAMKL_ERR_ALIGN
+    # Nothing to compute: no sequences, no heads, or no query rows at all.
+    assert vfwd(L, VP([0], [0]), q1=None, kl=None) == _lib.STREAMKL_OK
+    assert vfwd(L, VP([0, 5], [0, 5], H=0), q1=None, kl=None) == _lib.STREAMKL_OK
+    assert vfwd(L, VP([0, 0, 0], [0, 4, 9]), q1=None, kl=None) == _lib.STREAMKL_OK
+
+
+def test_varlen_backward_validation(L):
+    # Runs of equal lengths: (3,3) x2, (64,200), (0,7), (65,65).  The workspace is the
+    # largest run's full-size streamkl_bwd workspace.
+    cu_q = [0, 3, 6, 70, 70, 135]
+    cu_k = [0, 3, 6, 206, 213, 278]
+    v = VP(cu_q, cu_k, H=3, D=128)
+    need = L.streamkl_bwd_varlen_workspace_size(v.ref())
+    runs = [(2, 3, 3), (1, 64, 200), (1, 65, 65)]
+    assert need == max(bf16_workspace(b, 3, nq, nk, 128) for b, nq, nk in runs)
+    f32 = VP(cu_q, cu_k, H=3, D=128, dtype=_lib.STREAMKL_FP32)
+    # fp32: sigma only, for the largest run (2 sequences x 3 heads, rounded to 16 bytes).
+    assert L.streamkl_bwd_varlen_workspace_size(f32.ref()) == 32
+    assert L.streamkl_bwd_varlen_workspace_size(VP([2, 3], [0, 3]).ref()) == 0
+    assert vbwd(L, v, wsb=need - 1) == _lib.STREAMKL_ERR_WORKSPACE
+    assert vbwd(L, v, ws=None) == _lib.STREAMKL_ERR_WORKSPACE
+    assert vbwd(L, v, ws=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert vbwd(L, v, dq1=None) == _lib.STREAMKL_ERR_NULL     # half pair
+    assert vbwd(L, v, g=None) == _lib.STREAMKL_ERR_NULL
+    assert vbwd(L, v, q2=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert vbwd(L, v, dk1=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert vbwd(L, VP([0, 4], [0, 3], causal=1)) == _lib.STREAMKL_ERR_SHAPE
+    # Both pairs skipped: nothing to do.
+    assert L.streamkl_bwd_varlen(v.ref(), A, A, A, A, A, A, A, A, None, None, None, None, None, 0,
+                                 None) == _lib.STREAMKL_OK
