@@ -100,7 +100,7 @@ skl::FwdParams make_fwd(const streamkl_problem *p, const void *q1, const void *k
   f.NK = p->NK;
   f.scale = p->scale;
   f.causal = p->causal ? 1 : 0;
-  const int bq = skl::fwd_block_queries(p->dtype, (int)p->D);
+  const int bq = skl::fwd_block_queries(p->dtype, (int)p->D, p->NQ);
   f.nqt = (int)((p->NQ + bq - 1) / bq);
   f.splits = 1;
   f.chunk = (int)p->NK;

@@ -349,18 +349,26 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(FwdParams p) {
 
 // ---- bf16 inputs: direct LDS staging, pipelined key blocks ----
 //
-// Eight waves (two per SIMD), each owning 32 queries; 64-key tiles of K1 and
-// K2 reach LDS through buffer loads (no staging registers, rows past NK read
-// as zero) into double buffers with XOR-swizzled 16-byte chunks, one barrier
-// per tile.  A wave walks its 32-key blocks as a pipeline: the logits of block
-// b + 1 are computed while the online update of block b runs, in one
-// instruction stream whenever both blocks are fully visible (no mask code).
-template <int D>
+// Each wave owns 32 queries; key tiles of K1 and K2 reach LDS through buffer
+// loads (no staging registers, rows past NK read as zero) into double buffers
+// with XOR-swizzled 16-byte chunks, one barrier per tile.  A wave walks its
+// 32-key blocks as a pipeline: the logits of block b + 1 are computed while
+// the online update of block b runs, in one instruction stream whenever both
+// blocks are fully visible (no mask code).
+//
+// Two shapes: 8 waves (two per SIMD) over 64-key tiles for query tiles of
+// 256, and, for at most 32 queries per head (decode), one wave over 32-key
+// tiles.  The small shape's 32 KB of LDS lets about five workgroups share a
+// CU, so every resident wave has live queries and several tiles of keys are
+// in flight per CU; the large shape at 32 queries would leave seven of eight
+// waves idle and one tile in flight.
+template <int D, int WAVES_ = 8, int BK_ = kFwdBK>
 struct Fwd2Traits {
-  static constexpr int WAVES = 8;
+  static constexpr int WAVES = WAVES_;
   static constexpr int NT = 64 * WAVES;
   static constexpr int BQ = 32 * WAVES;  // 32 queries per wave
-  static constexpr int BK = kFwdBK;     // keys per tile
+  static constexpr int BK = BK_;         // keys per tile
+  static constexpr int BPT = BK / 32;    // 32-key blocks per tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int RB = D * 2;      // bf16 row bytes
   static constexpr int CPROW = RB / 16;
@@ -368,12 +376,16 @@ struct Fwd2Traits {
   static constexpr int LDS_BYTES = 2 * 2 * ROW_T;
   static constexpr int CHUNKS = ROW_T / 16;            // 16-byte loads per tensor per tile
   static constexpr int LOADS = (CHUNKS + NT - 1) / NT;  // per tensor per thread (the last may be partial)
-  static_assert(BK == 64 && NT % 64 == 0, "tiles");
+  static_assert((BK == 64 || BK == 32) && kFwdBK % BK == 0 && NT % 64 == 0, "tiles");
 };
 
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
-  using Tr = Fwd2Traits<D>;
+// Queries per head at or below which bf16 inputs take the one-wave shape.
+constexpr int kDecodeRows = 32;
+inline bool fwd_decode_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <= kDecodeRows; }
+
+template <int D, bool SPLIT, int WAVES, int BK>
+__global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p) {
+  using Tr = Fwd2Traits<D, WAVES, BK>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -439,7 +451,8 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
   RowState st{kNegBig, 0.f, kNegBig, 0.f, 0.f, 0.f, 0.f, 0.f};
 
   // Key tile t into buffer t & 1: tensor-major, key r at r * RB, logical
-  // chunk c in slot c ^ swz_row(r).
+  // chunk c in slot c ^ swz_row(r) (the swizzle repeats every 16 rows, so a
+  // 32-key block reads the same slots in either tile shape).
   uint32_t voff[Tr::LOADS];
 #pragma unroll
   for (int i = 0; i < Tr::LOADS; ++i) {
@@ -460,11 +473,11 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  // Logits of block b (key block b % 2 of tile b / 2).
+  // Logits of block b (key block b % BPT of tile b / BPT).
   auto scores = [&](int b, f32x16 &s1, f32x16 &s2) {
-    const int kr = (b & 1) * 32 + c32;
+    const int kr = (b % Tr::BPT) * 32 + c32;
     const int sw = swz_row<D>(kr);
-    const char *r1 = smem + ((b >> 1) & 1) * 2 * Tr::ROW_T + kr * Tr::RB;
+    const char *r1 = smem + ((b / Tr::BPT) & 1) * 2 * Tr::ROW_T + kr * Tr::RB;
     const char *r2 = r1 + Tr::ROW_T;
     s1 = f32x16{};
     s2 = f32x16{};
@@ -495,8 +508,8 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) load_tile(t + 1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int b = 2 * t + kb;
+    for (int kb = 0; kb < Tr::BPT; ++kb) {
+      const int b = Tr::BPT * t + kb;
       f32x16 n1, n2;
       if (b < nfull && b > 0) {
         scores(b, n1, n2);
@@ -511,7 +524,7 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
     wait_loads();
     lds_barrier();
   }
-  if (2 * ntiles - 1 < nlive && ntiles > 0) update(2 * ntiles - 1, p1, p2);
+  if (Tr::BPT * ntiles - 1 < nlive && ntiles > 0) update(Tr::BPT * ntiles - 1, p1, p2);
 
   // Merge the two lane halves that hold disjoint keys of the same query.
   {
@@ -544,15 +557,22 @@ __global__ __launch_bounds__(512, 1) void fwd2_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool SPLIT>
-static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
-  using Tr = Fwd2Traits<D>;
-  const void *fn = reinterpret_cast<const void *>(&fwd2_kernel<D, SPLIT>);
+template <int D, bool SPLIT, int WAVES, int BK>
+static hipError_t launch_fwd2_shape(const FwdParams &p, hipStream_t s) {
+  using Tr = Fwd2Traits<D, WAVES, BK>;
+  const void *fn = reinterpret_cast<const void *>(&fwd2_kernel<D, SPLIT, WAVES, BK>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int64_t nblk = p.BH * (int64_t)p.nqt * p.splits;
-  hipLaunchKernelGGL((fwd2_kernel<D, SPLIT>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  hipLaunchKernelGGL((fwd2_kernel<D, SPLIT, WAVES, BK>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
   return hipGetLastError();
+}
+
+// The grid's query tiles (p.nqt) were sized by fwd_block_queries for the same NQ.
+template <int D, bool SPLIT>
+static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
+  if (fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, s);
+  return launch_fwd2_shape<D, SPLIT, 8, kFwdBK>(p, s);
 }
 
 template <typename T, int D, bool SPLIT>
@@ -566,7 +586,8 @@ static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-int fwd_block_queries(int dtype, int D) {
+int fwd_block_queries(int dtype, int D, int64_t NQ) {
+  if (fwd_decode_shape(dtype, NQ)) return Fwd2Traits<128, 1, 32>::BQ;
   if (dtype == 0) return D == 128 ? Fwd2Traits<128>::BQ : Fwd2Traits<64>::BQ;
   return D == 128 ? FwdTraits<float, 128>::BQ : FwdTraits<float, 64>::BQ;
 }

@@ -56,8 +56,9 @@ constexpr int kBwdBR = 128;   // resident rows per backward workgroup
 constexpr int kBwdTile = 64;  // streamed rows per backward stage (tile of the transposed copies)
 constexpr int kGradExp = 8;   // |g| * sigma <= 2^kGradExp before fp16 rounding of dS
 
-// Queries per forward workgroup for an input type (dtype: 0 = bf16, 1 = fp32).
-int fwd_block_queries(int dtype, int D);
+// Queries per forward workgroup for an input type (dtype: 0 = bf16, 1 = fp32)
+// and query count per head.
+int fwd_block_queries(int dtype, int D, int64_t NQ);
 
 // dtype: 0 = bf16, 1 = fp32.  Return the launch status.
 hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s);
