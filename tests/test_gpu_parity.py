@@ -64,6 +64,8 @@ SMALL = [
     (1, 1, 1, 1, 128, False),
     (1, 1, 5, 5, 128, True),
     (1, 2, 64, 4100, 128, False),
+    (1, 2, 32, 200, 64, True),     # bf16: one-wave forward shape at its 32-query limit
+    (1, 1, 33, 97, 128, False),    # bf16: one query past it (8-wave shape, one live wave)
 ]
 
 
@@ -116,15 +118,16 @@ def test_splitk_small(splits, causal):
 
 @pytest.mark.parametrize("NQ", [1, 16])
 @pytest.mark.parametrize("causal", [False, True])
-def test_decode_splitk(NQ, causal):
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_splitk(NQ, causal, D):
     # Few queries against a long key range: the decode use of the split-K forward.
-    B, H, NK, D = 2, 2, 5000, 128
+    B, H, NK = 2, 2, 5000
     q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, torch.bfloat16, seed=21 + NQ)
     scale = 1.0 / math.sqrt(D)
     kl, l1, l2 = streamkl_fwd_splitk(q1, k1, q2, k2, 16, scale, causal)
     torch.cuda.synchronize()
     assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, _heads(B, H)), TOL["bf16"],
-                  f"decode NQ={NQ} causal={causal}")
+                  f"decode NQ={NQ} causal={causal} D={D}")
 
 
 def test_identical_teacher_student_is_exact_zero():
