@@ -94,6 +94,13 @@ __device__ __forceinline__ void buffer_load_lds16(BufRange r, char *lds, uint32_
                                                                       kRawBuffer);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
+// 16 bytes per lane from range `r` at byte voff + soff into registers; bytes
+// at or past the range end read as zero (the range check counts soff).
+__device__ __forceinline__ u32x4 buffer_load16(BufRange r, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(r.base), 0, r.bytes,
+                                                                      kRawBuffer);
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+}
 
 // XOR swizzles of the 16-byte chunks within a row, chosen so that the 16 lanes
 // reading one logical chunk of 16 consecutive rows hit 16 distinct slots of a

@@ -379,9 +379,12 @@ struct Fwd2Traits {
   static_assert((BK == 64 || BK == 32) && kFwdBK % BK == 0 && NT % 64 == 0, "tiles");
 };
 
-// Queries per head at or below which bf16 inputs take the one-wave shape.
+// Queries per head at or below which bf16 inputs take the one-wave shapes:
+// 16x16 products up to 16 queries, 32x32 products up to 32.
 constexpr int kDecodeRows = 32;
+constexpr int kDecode16Rows = 16;
 inline bool fwd_decode_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <= kDecodeRows; }
+inline bool fwd_decode16_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <= kDecode16Rows; }
 
 template <int D, bool SPLIT, int WAVES, int BK>
 __global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p) {
@@ -557,6 +560,239 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p) {
   }
 }
 
+
+// ---- bf16 inputs, at most 16 queries per head: 16x16 products ----
+//
+// One wave per workgroup computes the logits of 16 keys x 16 queries per
+// v_mfma_f32_16x16x32_bf16 (A = key rows, B = the resident queries), so no
+// product row is spent on absent queries.  Lane l owns query l % 16 and keys
+// 4 (l / 16) + i of each 16-key block; the four lane groups holding one query
+// merge once at the end.  Every key element is used once, by this wave, so
+// the key fragments stream from memory straight into registers (no LDS, no
+// barriers): the next 32-key tile loads while this one is multiplied, and
+// without an LDS footprint about eight such waves share a CU, each with a
+// tile in flight.  The online update folds a whole tile.
+template <int D>
+struct Fwd16Traits {
+  static constexpr int NT = 64;
+  static constexpr int BQ = 16;
+  static constexpr int BK = 32;
+  static constexpr int BPT = BK / 16;  // 16-key blocks per tile
+  static constexpr int KSTEPS = D / 32;
+  static constexpr int RB = D * 2;
+  static_assert(kFwdBK % BK == 0, "tiles");
+};
+
+__device__ __forceinline__ f32x4 mma16x16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Fold one tile (element i of block j is key kbase + 16 j + 4 g + i) into a
+// lane's running state; keys >= klim are masked.
+template <bool MASK, int NB>
+__device__ __forceinline__ void online_update_tile(const f32x4 (&x1)[NB], const f32x4 (&x2)[NB], RowState &st,
+                                                   float c, int kbase, int g, int klim) {
+  float mx1 = st.m1, mx2 = st.m2;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (!MASK || kbase + 16 * j + 4 * g + i < klim) {
+        mx1 = fmaxf(mx1, x1[j][i]);
+        mx2 = fmaxf(mx2, x2[j][i]);
+      }
+  const float a1 = fast_exp2((st.m1 - mx1) * c);
+  const float a2 = fast_exp2((st.m2 - mx2) * c);
+  st.m1 = mx1;
+  st.m2 = mx2;
+  const float b1 = mx1 * c, b2 = mx2 * c;
+  float s1 = 0.f, s2 = 0.f, sa = 0.f;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p1 = fast_exp2(__builtin_fmaf(x1[j][i], c, -b1));
+      float p2 = fast_exp2(__builtin_fmaf(x2[j][i], c, -b2));
+      float d = x1[j][i] - x2[j][i];
+      if (MASK) {
+        const bool v = kbase + 16 * j + 4 * g + i < klim;
+        p1 = v ? p1 : 0.f;
+        p2 = v ? p2 : 0.f;
+        d = v ? d : 0.f;
+      }
+      s1 += p1;
+      s2 += p2;
+      sa = __builtin_fmaf(p1, d, sa);
+    }
+  st.l1 = __builtin_fmaf(st.l1, a1, s1);
+  st.l2 = __builtin_fmaf(st.l2, a2, s2);
+  st.acc = __builtin_fmaf(st.acc, a1, sa);
+}
+
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(64, 1) void fwd16_kernel(FwdParams p) {
+  using Tr = Fwd16Traits<D>;
+  using Frags = bf16x8[Tr::BPT][Tr::KSTEPS][2];  // one tile's key fragments: block, k-step, tensor
+
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, c16 = lane & 15;
+
+  int qt, sp;
+  int64_t bh;
+  if (SPLIT) {
+    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    qt = (int)(L % (uint32_t)p.nqt);
+    const uint32_t rest = L / (uint32_t)p.nqt;
+    sp = (int)(rest % (uint32_t)p.splits);
+    bh = rest / (uint32_t)p.splits;
+  } else {
+    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    bh = L / (uint32_t)p.nqt;
+    qt = p.nqt - 1 - (int)(L % (uint32_t)p.nqt);
+    sp = 0;
+  }
+
+  const int NQ = (int)p.NQ, NK = (int)p.NK;
+  const int off = NK - NQ;
+  const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
+  const bf16 *Q1 = reinterpret_cast<const bf16 *>(p.q1) + rq * D;
+  const bf16 *Q2 = reinterpret_cast<const bf16 *>(p.q2) + rq * D;
+  const BufRange rk1{reinterpret_cast<const bf16 *>(p.k1) + rk * D, NK * Tr::RB};
+  const BufRange rk2{reinterpret_cast<const bf16 *>(p.k2) + rk * D, NK * Tr::RB};
+
+  const int q0 = qt * Tr::BQ;
+  const int qend = min(q0 + Tr::BQ, NQ);
+  const int kwg_end = p.causal ? min(NK, qend - 1 + off + 1) : NK;
+  const int k_lo = SPLIT ? sp * p.chunk : 0;
+  const int k_hi = SPLIT ? min(k_lo + p.chunk, kwg_end) : kwg_end;
+  const int ntiles = k_hi > k_lo ? (k_hi - k_lo + Tr::BK - 1) / Tr::BK : 0;
+  // Tiles [0, nfull) are visible to all the queries, [nfull, nlive) to some.
+  const int vis_all = min(k_hi, p.causal ? q0 + off + 1 : NK);
+  const int vis_any = min(k_hi, p.causal ? qend - 1 + off + 1 : NK);
+  const int nfull = max(0, vis_all - k_lo) / Tr::BK;
+  const int nlive = (max(0, vis_any - k_lo) + Tr::BK - 1) / Tr::BK;
+
+  // Resident queries (B operand): lane owns query q0 + c16, elements [32s + 8g, +8).
+  const int row = q0 + c16;
+  const bool row_ok = row < qend;
+  const int klim = min(k_hi, p.causal ? row + off + 1 : NK);
+  bf16x8 qf1[Tr::KSTEPS], qf2[Tr::KSTEPS];
+#pragma unroll
+  for (int s = 0; s < Tr::KSTEPS; ++s) {
+    qf1[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(Q1 + (int64_t)row * D + 32 * s + 8 * g) : bf16x8{};
+    qf2[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(Q2 + (int64_t)row * D + 32 * s + 8 * g) : bf16x8{};
+  }
+
+  const float c = p.scale * kLog2e;
+  RowState st{kNegBig, 0.f, kNegBig, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+  // Key fragments of tile t: block j, k-step s, tensor tn holds key
+  // 16 j + c16 of the tile, bytes [64 s + 16 g, +16) of its row.
+  auto load_tile = [&](int t, Frags &f) {
+    const uint32_t soff = (uint32_t)(k_lo + t * Tr::BK) * Tr::RB;
+#pragma unroll
+    for (int j = 0; j < Tr::BPT; ++j)
+#pragma unroll
+      for (int s = 0; s < Tr::KSTEPS; ++s) {
+        const uint32_t voff = (uint32_t)((16 * j + c16) * Tr::RB + 64 * s + 16 * g);
+        f[j][s][0] = __builtin_bit_cast(bf16x8, buffer_load16(rk1, voff, soff));
+        f[j][s][1] = __builtin_bit_cast(bf16x8, buffer_load16(rk2, voff, soff));
+      }
+  };
+  // Logits of one tile: block j holds keys 16 j .. 16 j + 15 of the tile.
+  auto scores = [&](const Frags &f, f32x4(&s1)[Tr::BPT], f32x4(&s2)[Tr::BPT]) {
+#pragma unroll
+    for (int j = 0; j < Tr::BPT; ++j) {
+      s1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < Tr::KSTEPS; ++s) {
+        s1[j] = mma16x16(f[j][s][0], qf1[s], s1[j]);
+        s2[j] = mma16x16(f[j][s][1], qf2[s], s2[j]);
+      }
+    }
+  };
+  auto update = [&](int t, const f32x4(&s1)[Tr::BPT], const f32x4(&s2)[Tr::BPT]) {
+    const int kbase = k_lo + t * Tr::BK;
+    if (t < nfull)
+      online_update_tile<false, Tr::BPT>(s1, s2, st, c, kbase, g, 0);
+    else
+      online_update_tile<true, Tr::BPT>(s1, s2, st, c, kbase, g, klim);
+  };
+
+  // Step t: logits of tile t (fragments in `f`) and the update of tile t - 1.
+  f32x4 p1[Tr::BPT], p2[Tr::BPT];
+#pragma unroll
+  for (int j = 0; j < Tr::BPT; ++j) p1[j] = p2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](int t, const Frags &f) {
+    f32x4 n1[Tr::BPT], n2[Tr::BPT];
+    if (t < nfull && t > 0) {
+      scores(f, n1, n2);
+      online_update_tile<false, Tr::BPT>(p1, p2, st, c, k_lo + (t - 1) * Tr::BK, g, 0);
+    } else {
+      if (t < nlive) scores(f, n1, n2);
+      if (t > 0 && t - 1 < nlive) update(t - 1, p1, p2);
+    }
+#pragma unroll
+    for (int j = 0; j < Tr::BPT; ++j) {
+      p1[j] = n1[j];
+      p2[j] = n2[j];
+    }
+  };
+  // Two register slots, alternating: tile t + 1 loads while tile t is used.
+  Frags fa, fb;
+  if (ntiles > 0) load_tile(0, fa);
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) load_tile(t + 1, fb);
+    step(t, fa);
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) load_tile(t + 2, fa);
+    step(t + 1, fb);
+  }
+  if (ntiles > 0 && ntiles - 1 < nlive) update(ntiles - 1, p1, p2);
+
+  // Merge the four lane groups that hold disjoint keys of the same query.
+  float m1 = st.m1, m2 = st.m2, l1 = st.l1, l2 = st.l2, acc = st.acc;
+#pragma unroll
+  for (int o = 16; o <= 32; o *= 2) {
+    const float om1 = __shfl_xor(m1, o), ol1 = __shfl_xor(l1, o);
+    const float om2 = __shfl_xor(m2, o), ol2 = __shfl_xor(l2, o);
+    const float oacc = __shfl_xor(acc, o);
+    const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
+    const float wa = fast_exp2((m1 - M1) * c), wb = fast_exp2((om1 - M1) * c);
+    const float va = fast_exp2((m2 - M2) * c), vb = fast_exp2((om2 - M2) * c);
+    l1 = __builtin_fmaf(l1, wa, ol1 * wb);
+    acc = __builtin_fmaf(acc, wa, oacc * wb);
+    l2 = __builtin_fmaf(l2, va, ol2 * vb);
+    m1 = M1;
+    m2 = M2;
+  }
+  if (g == 0 && row_ok) {
+    if (SPLIT) {
+      // Partial states are indexed densely by (unit, row).
+      const int64_t rows = p.BH * (int64_t)NQ;
+      float *w = p.ws + (int64_t)sp * rows + bh * (int64_t)NQ + row;
+      const int64_t fstride = (int64_t)p.splits * rows;
+      w[0] = m1;
+      w[fstride] = l1;
+      w[2 * fstride] = m2;
+      w[3 * fstride] = l2;
+      w[4 * fstride] = acc;
+    } else {
+      const int64_t idx = rq + row;
+      finish_row(m1, l1, m2, l2, acc, p.scale, p.kl + idx, p.lse1 + idx, p.lse2 + idx);
+    }
+  }
+}
+
+template <int D, bool SPLIT>
+static hipError_t launch_fwd16(const FwdParams &p, hipStream_t s) {
+  using Tr = Fwd16Traits<D>;
+  const int64_t nblk = p.BH * (int64_t)p.nqt * p.splits;
+  hipLaunchKernelGGL((fwd16_kernel<D, SPLIT>), dim3((uint32_t)nblk), dim3(Tr::NT), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D, bool SPLIT, int WAVES, int BK>
 static hipError_t launch_fwd2_shape(const FwdParams &p, hipStream_t s) {
   using Tr = Fwd2Traits<D, WAVES, BK>;
@@ -571,6 +807,7 @@ static hipError_t launch_fwd2_shape(const FwdParams &p, hipStream_t s) {
 // The grid's query tiles (p.nqt) were sized by fwd_block_queries for the same NQ.
 template <int D, bool SPLIT>
 static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
+  if (fwd_decode16_shape(0, p.NQ)) return launch_fwd16<D, SPLIT>(p, s);
   if (fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, s);
   return launch_fwd2_shape<D, SPLIT, 8, kFwdBK>(p, s);
 }
@@ -587,6 +824,7 @@ static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s) {
 }
 
 int fwd_block_queries(int dtype, int D, int64_t NQ) {
+  if (fwd_decode16_shape(dtype, NQ)) return Fwd16Traits<128>::BQ;
   if (fwd_decode_shape(dtype, NQ)) return Fwd2Traits<128, 1, 32>::BQ;
   if (dtype == 0) return D == 128 ? Fwd2Traits<128>::BQ : Fwd2Traits<64>::BQ;
   return D == 128 ? FwdTraits<float, 128>::BQ : FwdTraits<float, 64>::BQ;

@@ -64,6 +64,7 @@ SMALL = [
     (1, 1, 1, 1, 128, False),
     (1, 1, 5, 5, 128, True),
     (1, 2, 64, 4100, 128, False),
+    (2, 1, 16, 77, 64, True),      # bf16: 16x16-product forward shape at its 16-query limit
     (1, 2, 32, 200, 64, True),     # bf16: one-wave forward shape at its 32-query limit
     (1, 1, 33, 97, 128, False),    # bf16: one query past it (8-wave shape, one live wave)
 ]
