@@ -23,7 +23,7 @@
 // element, the B operand of the gradient product dR^T += X^T dS, which needs
 // no shuffle.  bf16 inputs use fp16 for the gradient product: dS in bf16
 // loses too much (8-bit significand) for the 2e-3 relative bound, fp16 keeps
-// 11 bits.  dS is scaled by a per-(b,h) power of two sigma with
+// 11 bits.  dS is scaled by a power of two sigma per (sequence, head) with
 // max|g| * sigma in [2^7, 2^8) so it sits in fp16's normal range; the factor
 // is divided out exactly at the end.  Q and K themselves convert to fp16
 // exactly as long as they lie within the fp16 range.

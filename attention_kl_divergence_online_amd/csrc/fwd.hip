@@ -9,14 +9,17 @@
 // states with log-sum-exp rescaling.
 //
 // gfx950 mapping
-//  * workgroup = 4 waves x 64 queries (two 32-query blocks per wave); the
-//    wave's Q1/Q2 fragments stay in registers for the whole pass;
-//  * K1/K2 tiles of 64 keys are double-buffered in LDS (rows padded by 16 B so
-//    the 32 rows a matrix-core operand read touches fall in distinct banks);
 //  * logits are produced transposed (keys x queries) so that every lane owns
-//    one query: each lane keeps its own online state over its 16 keys of a
-//    block, no cross-lane reduction happens inside the loop, and the two lane
-//    halves sharing a query are merged once at the end;
+//    one query: each lane keeps its own online state over its keys of a
+//    block, no cross-lane reduction happens inside the loop, and the lanes
+//    sharing a query are merged once at the end;
+//  * the resident queries' Q1/Q2 fragments stay in registers for the whole
+//    pass; key tiles stream through double-buffered LDS (or, for at most 16
+//    queries, straight into registers);
+//  * bf16 inputs: 8 waves x 32 queries over 64-key tiles (fwd2_kernel), one
+//    wave x 32 queries over 32-key tiles for at most 32 queries per head, and
+//    16x16 products for at most 16 (fwd16_kernel); fp32 inputs: fwd_kernel
+//    with register-staged tiles and compensated sums;
 //  * scores stay in raw dot-product units x = q.k; exponentials are
 //    exp2((x - m) * scale * log2 e).
 #include "device_common.hpp"
