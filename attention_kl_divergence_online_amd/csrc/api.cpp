@@ -41,13 +41,32 @@ constexpr int kVersion = 100;  // 0.1.0
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// A dispatch's grid is at most 2^32 - 1 work-items.  The forward's largest
+// grids are its query tiles x key chunks and the split-K merge (one thread
+// per row); the backward's, its passes (resident tiles of 128 rows) and the
+// transposes (64-row tiles).
+constexpr __int128 kGridLimit = ((__int128)1 << 32) - 1;
+bool fwd_grids_fit(const streamkl_problem *p, int64_t splits) {
+  const __int128 bh = (__int128)p->B * p->H;
+  const int64_t bq = skl::fwd_block_queries(p->dtype, (int)p->D, p->NQ);
+  const __int128 fwd = bh * ((p->NQ + bq - 1) / bq) * splits * (bq <= 32 ? 64 : 512);
+  const __int128 merge = bh * ((p->NQ + 255) / 256 * 256);
+  return fwd <= kGridLimit && merge <= kGridLimit;
+}
+bool bwd_grids_fit(const streamkl_problem *p) {
+  const __int128 bh = (__int128)p->B * p->H;
+  const int64_t nmax = p->NQ > p->NK ? p->NQ : p->NK;
+  const __int128 bwd = bh * ((nmax + skl::kBwdBR - 1) / skl::kBwdBR) * 512;
+  const __int128 tr = bh * ((nmax + skl::kBwdTile - 1) / skl::kBwdTile) * 256;
+  return bwd <= kGridLimit && tr <= kGridLimit;
+}
+
 // Shape / dtype checks common to every entry point.
 streamkl_status check_problem(const streamkl_problem *p) {
   if (!p) return STREAMKL_ERR_NULL;
   if (p->dtype != STREAMKL_BF16 && p->dtype != STREAMKL_FP32) return STREAMKL_ERR_DTYPE;
   if (p->B < 0 || p->H < 0 || p->NQ < 0 || p->NK < 0) return STREAMKL_ERR_SHAPE;
   if (p->D != 64 && p->D != 128) return STREAMKL_ERR_SHAPE;
-  const int64_t rows = p->B * p->H * p->NQ;
   // A row with no visible key has no distribution to compare.
   if (p->B > 0 && p->H > 0 && p->NQ > 0 && p->NK == 0) return STREAMKL_ERR_SHAPE;
   if (p->causal && p->NQ > p->NK) return STREAMKL_ERR_SHAPE;
@@ -57,9 +76,22 @@ streamkl_status check_problem(const streamkl_problem *p) {
   const int64_t lim = (int64_t)1 << 31;
   const int64_t nmax = (p->NQ > p->NK ? p->NQ : p->NK);
   if (nmax >= lim || (nmax + 63) / 64 * 64 * p->D * 4 >= lim) return STREAMKL_ERR_SHAPE;
-  if (p->B * p->H >= lim || rows < 0) return STREAMKL_ERR_SHAPE;
+  if ((__int128)p->B * p->H >= lim) return STREAMKL_ERR_SHAPE;
   if (!(p->scale == p->scale)) return STREAMKL_ERR_SHAPE;  // NaN scale
   return STREAMKL_OK;
+}
+
+// check_problem plus the grid limit of the forward (`splits` key chunks) or
+// of the backward.
+streamkl_status check_fwd_problem(const streamkl_problem *p, int64_t splits) {
+  const streamkl_status st = check_problem(p);
+  if (st != STREAMKL_OK) return st;
+  return fwd_grids_fit(p, splits) ? STREAMKL_OK : STREAMKL_ERR_SHAPE;
+}
+streamkl_status check_bwd_problem(const streamkl_problem *p) {
+  const streamkl_status st = check_problem(p);
+  if (st != STREAMKL_OK) return st;
+  return bwd_grids_fit(p) ? STREAMKL_OK : STREAMKL_ERR_SHAPE;
 }
 
 bool empty_rows(const streamkl_problem *p) { return p->B == 0 || p->H == 0 || p->NQ == 0; }
@@ -128,7 +160,7 @@ int streamkl_version(void) { return kVersion; }
 
 streamkl_status streamkl_fwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
                              const void *k2, float *kl, float *lse1, float *lse2, void *stream) {
-  streamkl_status st = check_problem(p);
+  streamkl_status st = check_fwd_problem(p, 1);
   if (st != STREAMKL_OK) return st;
   if (empty_rows(p)) return STREAMKL_OK;
   if ((st = check_inputs(p, q1, k1, q2, k2)) != STREAMKL_OK) return st;
@@ -141,7 +173,7 @@ streamkl_status streamkl_fwd(const streamkl_problem *p, const void *q1, const vo
 
 size_t streamkl_fwd_splitk_workspace_size(const streamkl_problem *p, int num_splits) {
   if (check_problem(p) != STREAMKL_OK) return 0;
-  if (num_splits < 1 || (p->NK > 0 && num_splits > fwd_splits_max(p))) return 0;
+  if (num_splits < 1 || (p->NK > 0 && num_splits > fwd_splits_max(p)) || !fwd_grids_fit(p, num_splits)) return 0;
   return (size_t)5 * (size_t)num_splits * (size_t)(p->B * p->H * p->NQ) * sizeof(float);
 }
 
@@ -152,7 +184,7 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, c
   if (st != STREAMKL_OK) return st;
   if (num_splits < 1) return STREAMKL_ERR_SHAPE;
   if (empty_rows(p)) return STREAMKL_OK;
-  if (num_splits > fwd_splits_max(p)) return STREAMKL_ERR_SHAPE;
+  if (num_splits > fwd_splits_max(p) || !fwd_grids_fit(p, num_splits)) return STREAMKL_ERR_SHAPE;
   if ((st = check_inputs(p, q1, k1, q2, k2)) != STREAMKL_OK) return st;
   if ((st = check_rowvecs(kl, lse1, lse2)) != STREAMKL_OK) return st;
   skl::FwdParams f = make_fwd(p, q1, k1, q2, k2, kl, lse1, lse2);
@@ -175,12 +207,12 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, c
 }
 
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p) {
-  if (check_problem(p) != STREAMKL_OK) return 0;
+  if (check_bwd_problem(p) != STREAMKL_OK) return 0;
   return bwd_layout(p).total;
 }
 
 size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p) {
-  if (check_problem(p) != STREAMKL_OK) return 0;
+  if (check_bwd_problem(p) != STREAMKL_OK) return 0;
   const int64_t bh = p->B * p->H;
   return bwd_layout_heads(p, (size_t)(bh > 0 ? 1 : 0)).total;
 }
@@ -332,7 +364,7 @@ streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const vo
                              const void *k2, const float *kl, const float *lse1, const float *lse2,
                              const float *g, float *dq1, float *dk1, float *dq2, float *dk2, void *workspace,
                              size_t workspace_bytes, void *stream) {
-  streamkl_status st = check_problem(p);
+  streamkl_status st = check_bwd_problem(p);
   if (st != STREAMKL_OK) return st;
   if ((dq1 == nullptr) != (dk1 == nullptr) || (dq2 == nullptr) != (dk2 == nullptr)) return STREAMKL_ERR_NULL;
   if (p->B * p->H == 0 || (p->NQ == 0 && p->NK == 0)) return STREAMKL_OK;
@@ -370,7 +402,7 @@ streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const vo
 streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
                                      const void *k2, const float *g, void *workspace, size_t workspace_bytes,
                                      void *stream) {
-  streamkl_status st = check_problem(p);
+  streamkl_status st = check_bwd_problem(p);
   if (st != STREAMKL_OK) return st;
   if (p->B * p->H == 0 || p->NQ == 0) return STREAMKL_OK;
   if ((st = check_inputs(p, q1, k1, q2, k2)) != STREAMKL_OK) return st;
@@ -385,7 +417,7 @@ streamkl_status streamkl_bwd_dk(const streamkl_problem *p, const void *q1, const
                                 const void *k2, const float *kl, const float *lse1, const float *lse2,
                                 const float *g, float *dk1, float *dk2, const void *workspace,
                                 size_t workspace_bytes, void *stream) {
-  streamkl_status st = check_problem(p);
+  streamkl_status st = check_bwd_problem(p);
   if (st != STREAMKL_OK) return st;
   if (p->B * p->H == 0 || p->NK == 0 || (!dk1 && !dk2)) return STREAMKL_OK;
   float *outs[2] = {dk1, dk2};
@@ -400,7 +432,7 @@ streamkl_status streamkl_bwd_dq(const streamkl_problem *p, const void *q1, const
                                 const void *k2, const float *kl, const float *lse1, const float *lse2,
                                 const float *g, float *dq1, float *dq2, const void *workspace,
                                 size_t workspace_bytes, void *stream) {
-  streamkl_status st = check_problem(p);
+  streamkl_status st = check_bwd_problem(p);
   if (st != STREAMKL_OK) return st;
   if (p->B * p->H == 0 || p->NQ == 0 || (!dq1 && !dq2)) return STREAMKL_OK;
   float *outs[2] = {dq1, dq2};
@@ -458,7 +490,7 @@ streamkl_status for_each_run(const streamkl_varlen_problem *v, F f) {
   return STREAMKL_OK;
 }
 
-streamkl_status check_varlen(const streamkl_varlen_problem *v) {
+streamkl_status check_varlen(const streamkl_varlen_problem *v, bool backward) {
   if (!v) return STREAMKL_ERR_NULL;
   if (v->dtype != STREAMKL_BF16 && v->dtype != STREAMKL_FP32) return STREAMKL_ERR_DTYPE;
   if (v->B < 0 || v->H < 0) return STREAMKL_ERR_SHAPE;
@@ -473,7 +505,7 @@ streamkl_status check_varlen(const streamkl_varlen_problem *v) {
   // per-sequence 32-bit offsets).
   return for_each_run(v, [&](const Run &r) {
     const streamkl_problem p = run_problem(v, r);
-    return check_problem(&p);
+    return backward ? check_bwd_problem(&p) : check_fwd_problem(&p, 1);
   });
 }
 
@@ -491,7 +523,7 @@ extern "C" {
 streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v, const void *q1, const void *k1,
                                     const void *q2, const void *k2, float *kl, float *lse1, float *lse2,
                                     void *stream) {
-  streamkl_status st = check_varlen(v);
+  streamkl_status st = check_varlen(v, false);
   if (st != STREAMKL_OK) return st;
   const int64_t TQ = total_rows(v->cu_seqlens_q, v->B), TK = total_rows(v->cu_seqlens_k, v->B);
   if (v->B == 0 || v->H == 0 || TQ == 0) return STREAMKL_OK;
@@ -514,7 +546,7 @@ streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v, const void
 }
 
 size_t streamkl_bwd_varlen_workspace_size(const streamkl_varlen_problem *v) {
-  if (check_varlen(v) != STREAMKL_OK) return 0;
+  if (check_varlen(v, true) != STREAMKL_OK) return 0;
   size_t need = 16;
   for_each_run(v, [&](const Run &r) {
     if (r.nq > 0) {
@@ -531,7 +563,7 @@ streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void
                                     const void *q2, const void *k2, const float *kl, const float *lse1,
                                     const float *lse2, const float *g, float *dq1, float *dk1, float *dq2,
                                     float *dk2, void *workspace, size_t workspace_bytes, void *stream) {
-  streamkl_status st = check_varlen(v);
+  streamkl_status st = check_varlen(v, true);
   if (st != STREAMKL_OK) return st;
   if ((dq1 == nullptr) != (dk1 == nullptr) || (dq2 == nullptr) != (dk2 == nullptr)) return STREAMKL_ERR_NULL;
   const int64_t TQ = total_rows(v->cu_seqlens_q, v->B), TK = total_rows(v->cu_seqlens_k, v->B);

@@ -51,7 +51,8 @@ typedef enum {
     STREAMKL_ERR_SHAPE = 2,     /* bad sizes: negative, D not 64/128, NK == 0 with rows,
                                    causal with NQ > NK, a per-head fp32 tensor of
                                    ceil(N / 64) * 64 rows of D reaching 2^31 bytes,
-                                   split count out of range */
+                                   B * H reaching 2^31, a kernel grid past the GPU's
+                                   2^32 - 1 work-items, split count out of range */
     STREAMKL_ERR_DTYPE = 3,     /* dtype is not STREAMKL_BF16 / STREAMKL_FP32 */
     STREAMKL_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
     STREAMKL_ERR_WORKSPACE = 5, /* workspace missing or smaller than the size query */

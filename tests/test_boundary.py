@@ -87,6 +87,20 @@ def test_forward_validation(L):
     assert fwd(L, P(), l2=MIS) == _lib.STREAMKL_ERR_ALIGN
 
 
+def test_grid_limit_is_rejected_on_the_host(L):
+    # 2^30 heads of 1024 queries: every size is legal on its own, but the forward
+    # grid (4 query tiles x 512 threads per head) passes 2^32 work-items.
+    big = P(B=1 << 20, H=1 << 10, NQ=1024, NK=1024)
+    assert fwd(L, big) == _lib.STREAMKL_ERR_SHAPE
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(big)) == 0
+    # Split-K multiplies the forward grid by the split count.
+    p = P(B=1, H=1 << 14, NQ=1024, NK=1 << 20)
+    assert L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 1) > 0
+    assert L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 1 << 14) == 0
+    assert L.streamkl_fwd_splitk(ctypes.byref(p), A, A, A, A, A, A, A, 1 << 14, A, 1 << 40,
+                                 None) == _lib.STREAMKL_ERR_SHAPE
+
+
 def test_empty_problems_are_no_ops(L):
     # Nothing to compute: success without touching any pointer.
     assert fwd(L, P(B=0), q1=None, kl=None) == _lib.STREAMKL_OK
