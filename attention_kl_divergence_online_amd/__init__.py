@@ -31,6 +31,7 @@ from ._lib import StreamKLError
 __all__ = ["streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd", "streamkl_bwd_prepare", "streamkl_bwd_dk",
            "streamkl_bwd_dq", "attention_kl",
            "streamkl_fwd_varlen", "streamkl_bwd_varlen", "varlen_problem_for", "bwd_varlen_workspace_size",
+           "attention_kl_varlen",
            "StreamKLError", "problem_for", "fwd_splitk_workspace_size", "bwd_workspace_size"]
 
 _DTYPES = {torch.bfloat16: _lib.STREAMKL_BF16, torch.float32: _lib.STREAMKL_FP32}
@@ -306,3 +307,35 @@ def streamkl_bwd_varlen(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, kl, lse1, ls
                                         _ptr(workspace), nbytes, _stream_handle(q1.device))
     _lib.check(st, "streamkl_bwd_varlen")
     return dq1, dk1, dq2, dk2
+
+
+class _AttentionKLVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, scale, causal):
+        q1, k1, q2, k2 = (t.contiguous() for t in (q1, k1, q2, k2))
+        cu_q = torch.as_tensor(cu_seqlens_q, dtype=torch.int32).to("cpu")
+        cu_k = torch.as_tensor(cu_seqlens_k, dtype=torch.int32).to("cpu")
+        kl, lse1, lse2 = streamkl_fwd_varlen(q1, k1, q2, k2, cu_q, cu_k, scale, causal)
+        ctx.save_for_backward(q1, k1, q2, k2, kl, lse1, lse2)
+        ctx.cu, ctx.scale, ctx.causal = (cu_q, cu_k), scale, causal
+        return kl
+
+    @staticmethod
+    def backward(ctx, g):
+        q1, k1, q2, k2, kl, lse1, lse2 = ctx.saved_tensors
+        need1 = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+        need2 = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
+        none = (None,) * 4
+        if not (need1 or need2):
+            return (None,) * 8
+        dq1, dk1, dq2, dk2 = streamkl_bwd_varlen(q1, k1, q2, k2, *ctx.cu, kl, lse1, lse2,
+                                                 g.to(torch.float32).contiguous(), ctx.scale, ctx.causal,
+                                                 teacher=need1, student=need2)
+        cast = lambda d, ref: None if d is None else d.to(ref.dtype)
+        return (cast(dq1, q1), cast(dk1, k1), cast(dq2, q2), cast(dk2, k2)) + none
+
+
+def attention_kl_varlen(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, scale: Optional[float] = None,
+                        causal: bool = False) -> torch.Tensor:
+    """Differentiable per-row KL(P1||P2) of a packed batch ([H, T, D] inputs), [H, TQ] fp32."""
+    return _AttentionKLVarlen.apply(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, scale, causal)

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 import synth
-from attention_kl_divergence_online_amd import (streamkl_bwd, streamkl_bwd_varlen, streamkl_fwd,
-                                                streamkl_fwd_varlen)
+from attention_kl_divergence_online_amd import (attention_kl_varlen, streamkl_bwd, streamkl_bwd_varlen,
+                                                streamkl_fwd, streamkl_fwd_varlen)
 from parity_util import TOL, assert_within, compare_backward, compare_forward, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -128,6 +128,25 @@ def test_varlen_teacher_or_student_only():
         assert torch.equal(teacher[i], both[i])
     for i in (2, 3):
         assert torch.equal(student[i], both[i])
+
+
+def test_varlen_autograd_matches_direct_calls():
+    lens_q, lens_k = [70, 0, 129], [70, 5, 300]
+    H, D = 2, 64
+    print("varlen autograd", flush=True)
+    q1, k1, q2, k2 = _packed(lens_q, lens_k, H, D, torch.float32, seed=9)
+    cq, ck = _cu(lens_q), _cu(lens_k)
+    leaves = [t.clone().requires_grad_(True) for t in (q1, k1, q2, k2)]
+    kl = attention_kl_varlen(*leaves, cq, ck, None, True)
+    gen = torch.Generator(device="cpu").manual_seed(4)
+    w = torch.randn(kl.shape, generator=gen).to(DEV)
+    (kl * w).sum().backward()
+    out = streamkl_fwd_varlen(q1, k1, q2, k2, cq, ck, None, True)
+    grads = streamkl_bwd_varlen(q1, k1, q2, k2, cq, ck, *out, w.contiguous(), None, True)
+    torch.cuda.synchronize()
+    assert torch.equal(kl.detach(), out[0])
+    for leaf, gr in zip(leaves, grads):
+        assert torch.equal(leaf.grad, gr)
 
 
 def test_varlen_mix_full_size():
