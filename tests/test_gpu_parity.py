@@ -220,6 +220,47 @@ def test_small_workspace_runs_in_head_groups():
             assert torch.equal(a, b), nbytes
 
 
+def test_no_device_memory_beyond_the_callers_buffers():
+    # The library allocates nothing: with inputs, outputs and workspaces allocated
+    # up front, the calls raise neither torch's peak allocation nor the device's
+    # used memory (after one warm-up call, which lets the runtime set up).
+    from attention_kl_divergence_online_amd import (bwd_workspace_size, fwd_splitk_workspace_size,
+                                                    streamkl_fwd_varlen, streamkl_bwd_varlen,
+                                                    bwd_varlen_workspace_size)
+    B, H, N, D = 2, 8, 4096, 128
+    print(f"memory B={B} H={H} N={N}", flush=True)
+    q1, k1, q2, k2 = _rand(B, H, N, N, D, torch.bfloat16, seed=17)
+    outs = tuple(torch.empty(B, H, N, device=DEV) for _ in range(3))
+    g = torch.full((B, H, N), 1e-3, device=DEV)
+    grads = tuple(torch.empty(B, H, N, D, device=DEV) for _ in range(4))
+    ws = torch.empty(bwd_workspace_size(q1, k1, None, True), dtype=torch.uint8, device=DEV)
+    splits = 8
+    wsk = torch.empty(fwd_splitk_workspace_size(q1, k1, splits, None, True), dtype=torch.uint8, device=DEV)
+    cu = [0, 1000, 4096, 8192]  # three packed sequences of 1000, 3096 and 4096 rows
+    packed = [t.transpose(0, 1).reshape(H, B * N, D).contiguous() for t in (q1, k1, q2, k2)]
+    pouts = tuple(torch.empty(H, B * N, device=DEV) for _ in range(3))
+    pg = torch.full((H, B * N), 1e-3, device=DEV)
+    pgrads = tuple(torch.empty(H, B * N, D, device=DEV) for _ in range(4))
+    pws = torch.empty(bwd_varlen_workspace_size(packed[0], packed[1], cu, cu, None, True), dtype=torch.uint8,
+                      device=DEV)
+
+    def calls():
+        streamkl_fwd(q1, k1, q2, k2, None, True, out=outs)
+        streamkl_fwd_splitk(q1, k1, q2, k2, splits, None, True, workspace=wsk, out=outs)
+        streamkl_bwd(q1, k1, q2, k2, *outs, g, None, True, workspace=ws, out=grads)
+        streamkl_fwd_varlen(*packed, cu, cu, None, True, out=pouts)
+        streamkl_bwd_varlen(*packed, cu, cu, *pouts, pg, None, True, workspace=pws, out=pgrads)
+        torch.cuda.synchronize()
+
+    calls()
+    torch.cuda.reset_peak_memory_stats()
+    held = torch.cuda.memory_allocated()
+    free_before = torch.cuda.mem_get_info()[0]
+    calls()
+    assert torch.cuda.max_memory_allocated() == held
+    assert torch.cuda.mem_get_info()[0] >= free_before
+
+
 def test_autograd_function():
     q1, k1, q2, k2 = _rand(1, 2, 130, 260, 64, torch.float32, seed=9)
     ts = [t.clone().requires_grad_(True) for t in (q1, k1, q2, k2)]
