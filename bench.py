@@ -258,6 +258,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Device memory: everything the step touches is allocated above; the step
+    # itself must add nothing (peak allocation during the timed steps minus
+    # what is held before them).
+    torch.cuda.reset_peak_memory_stats()
+    held = torch.cuda.memory_allocated()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
@@ -270,6 +275,16 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    extra_bytes = torch.cuda.max_memory_allocated() - held
+    nbytes = lambda *ts: sum(t.numel() * t.element_size() for t in ts)
+    memory = {
+        "inputs_bytes": nbytes(q1, k1, q2, k2, g),
+        "outputs_bytes": nbytes(kl, l1, l2, *grads),
+        "workspace_bytes": nbytes(ws),
+        "extra_during_step_bytes": extra_bytes,
+        # P1 and P2 as full NQ x NK bf16 matrices, which the fused path never forms.
+        "materialised_p_bytes": 2 * 2 * w.B * w.H * w.NQ * w.NK,
+    }
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     per = {"fwd": 0.0, "bwd_prepare": 0.0, "bwd_dk": 0.0, "bwd_dq": 0.0}
@@ -326,6 +341,7 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": recorded_traffic(dom),
         },
+        "memory": memory,
     }
 
     if not args.no_splitk:
