@@ -77,6 +77,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload(5, "splitk_bwd_128k", 1, 32, 1024, 131072, 128, "bf16", False, noise=0.2),
         # Decode step: 16 new queries per sequence against a 128K-key cache, split-K forward.
         Workload(6, "decode_128k", 4, 32, 16, 131072, 128, "bf16", True, noise=0.2, splits=64),
+        # The D = 64 kernels at long context: 64 heads of 16K, causal.
+        Workload(7, "causal_16k_d64", 1, 64, 16384, 16384, 64, "bf16", True, noise=0.1),
     ]
 }
 
