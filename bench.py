@@ -153,8 +153,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--other-configs", action="store_true",
-                    help="also time forward and backward on the other bf16 workloads (causal_4k, "
-                         "noncausal_16k, splitk_bwd_128k, causal_16k_d64), the decode split-K forward and the packed "
+                    help="also time forward and backward on the other workloads (causal_4k, noncausal_16k, "
+                         "splitk_bwd_128k, causal_16k_d64, causal_4k_fp32), the decode split-K forward and the packed "
                          "variable-length batch, and report them under \"other_configs\"")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -349,7 +349,8 @@ def main():
 
     if args.other_configs:
         out["other_configs"] = {n: config_bench(skl, synth, torch, args, n)
-                                for n in ("causal_4k", "noncausal_16k", "splitk_bwd_128k", "causal_16k_d64")}
+                                for n in ("causal_4k", "noncausal_16k", "splitk_bwd_128k", "causal_16k_d64",
+                                          "causal_4k_fp32")}
         out["other_configs"]["decode_128k"] = splitk_bench(skl, synth, torch, args, "decode_128k")
         out["other_configs"]["varlen_mix"] = varlen_bench(skl, synth, torch, args, "varlen_mix")
 

@@ -79,6 +79,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload(6, "decode_128k", 4, 32, 16, 131072, 128, "bf16", True, noise=0.2, splits=64),
         # The D = 64 kernels at long context: 64 heads of 16K, causal.
         Workload(7, "causal_16k_d64", 1, 64, 16384, 16384, 64, "bf16", True, noise=0.1),
+        # fp32 inputs (the 1e-5 path) at a moderate causal context.
+        Workload(8, "causal_4k_fp32", 2, 16, 4096, 4096, 128, "fp32", True, noise=0.3),
     ]
 }
 

@@ -342,6 +342,10 @@ def test_causal_16k_d64_full_size():
     _full_size("causal_16k_d64")
 
 
+def test_causal_4k_fp32_full_size():
+    _full_size("causal_4k_fp32")
+
+
 def test_decode_128k_full_size():
     # Every one of the 16 rows of two heads, and the backward of the decode shape.
     _full_size("decode_128k", rows_per_head=16)
