@@ -10,11 +10,37 @@
 namespace {
 
 // Backward workspace: the per-(b,h) factors sigma, then for bf16 inputs the
-// transposed fp16 copies of q1, q2, k1, k2 ([BH][ceil(N/64)][D][64] each).
+// transposed fp16 copies of q1, q2, k1, k2 ([BH][ceil(N/64)][D][64] each),
+// then, when the query-resident pass is split over key chunks, its partial dQ
+// ([splits][2][BH * NQ][D] fp32).
 struct BwdLayout {
-  size_t tq1, tq2, tk1, tk2, total;
+  size_t tq1, tq2, tk1, tk2, dqp, total;
 };
 inline size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+// The bf16 query-resident pass runs one workgroup per CU (its LDS use); with
+// fewer query tiles than CUs its key range is split into chunks so that the
+// grid still covers the GPU.  fp32 inputs never split.
+constexpr int64_t kDqSplitTarget = 256;  // workgroups to aim for (the CU count)
+constexpr int64_t kDqSplitMax = 64;
+struct DqSplit {
+  int splits, kchunk;
+};
+DqSplit dq_split(const streamkl_problem *p) {
+  DqSplit r{1, 0};
+  if (p->dtype != STREAMKL_BF16 || p->NQ == 0 || p->NK == 0) return r;
+  const int64_t wgs = p->B * p->H * ((p->NQ + skl::kBwdBR - 1) / skl::kBwdBR);
+  if (wgs >= kDqSplitTarget) return r;
+  const int64_t ktiles = (p->NK + skl::kBwdTile - 1) / skl::kBwdTile;
+  int64_t sp = (kDqSplitTarget + wgs - 1) / wgs;
+  if (sp > kDqSplitMax) sp = kDqSplitMax;
+  if (sp > ktiles) sp = ktiles;
+  if (sp <= 1) return r;
+  const int64_t per = (ktiles + sp - 1) / sp;  // tiles per chunk
+  r.splits = (int)((ktiles + per - 1) / per);  // no empty trailing chunk
+  r.kchunk = (int)(per * skl::kBwdTile);
+  return r.splits > 1 ? r : DqSplit{1, 0};
+}
 // Layout with transposed copies for `heads` heads after a sigma area for all
 // B*H heads.
 BwdLayout bwd_layout_heads(const streamkl_problem *p, size_t heads) {
@@ -32,7 +58,10 @@ BwdLayout bwd_layout_heads(const streamkl_problem *p, size_t heads) {
   l.tq2 = l.tq1 + round_up(qt, 256);
   l.tk1 = l.tq2 + round_up(qt, 256);
   l.tk2 = l.tk1 + round_up(kt, 256);
-  l.total = l.tk2 + round_up(kt, 256);
+  l.dqp = l.tk2 + round_up(kt, 256);
+  const DqSplit ds = dq_split(p);
+  const size_t dqp = ds.splits > 1 ? (size_t)ds.splits * 2 * heads * (size_t)p->NQ * (size_t)p->D * 4 : 0;
+  l.total = l.dqp + round_up(dqp, 256);
   return l;
 }
 BwdLayout bwd_layout(const streamkl_problem *p) { return bwd_layout_heads(p, (size_t)(p->B * p->H)); }
@@ -56,7 +85,7 @@ bool fwd_grids_fit(const streamkl_problem *p, int64_t splits) {
 bool bwd_grids_fit(const streamkl_problem *p) {
   const __int128 bh = (__int128)p->B * p->H;
   const int64_t nmax = p->NQ > p->NK ? p->NQ : p->NK;
-  const __int128 bwd = bh * ((nmax + skl::kBwdBR - 1) / skl::kBwdBR) * 512;
+  const __int128 bwd = bh * ((nmax + skl::kBwdBR - 1) / skl::kBwdBR) * 512 * dq_split(p).splits;
   const __int128 tr = bh * ((nmax + skl::kBwdTile - 1) / skl::kBwdTile) * 256;
   return bwd <= kGridLimit && tr <= kGridLimit;
 }
@@ -259,6 +288,12 @@ skl::BwdParams make_bwd(const streamkl_problem *p, const void *q1, const void *k
     b.tq2 = w + l.tq2;
     b.tk1 = w + l.tk1;
     b.tk2 = w + l.tk2;
+    const DqSplit ds = dq_split(p);
+    b.splits = ds.splits;
+    b.kchunk = ds.kchunk;
+    b.dqp = ds.splits > 1 ? const_cast<float *>(reinterpret_cast<const float *>(w + l.dqp)) : nullptr;
+  } else {
+    b.splits = 1;
   }
   b.dq1 = dq1;
   b.dk1 = dk1;
@@ -302,6 +337,7 @@ skl::BwdParams head_group(const streamkl_problem *p, skl::BwdParams b, int64_t h
   b.tq2 = w + l.tq2;
   b.tk1 = w + l.tk1;
   b.tk2 = w + l.tk2;
+  if (b.splits > 1) b.dqp = const_cast<float *>(reinterpret_cast<const float *>(w + l.dqp));
   b.BH = n;
   return b;
 }
@@ -323,7 +359,9 @@ streamkl_status run_dq(const streamkl_problem *p, skl::BwdParams b, hipStream_t 
   if (p->NQ == 0) return STREAMKL_OK;
   b.want1 = b.dq1 != nullptr;
   b.want2 = b.dq2 != nullptr;
-  return skl::launch_bwd_dq(p->dtype, (int)p->D, b, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+  if (skl::launch_bwd_dq(p->dtype, (int)p->D, b, s) != hipSuccess) return STREAMKL_ERR_HIP;
+  if (b.splits > 1 && skl::launch_dq_reduce((int)p->D, b, s) != hipSuccess) return STREAMKL_ERR_HIP;
+  return STREAMKL_OK;
 }
 
 // sigma of every unit of `b` into the front of its workspace.

@@ -501,10 +501,16 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   const int nrt = (NR + Tr::BR - 1) / Tr::BR;
   const int nxt = (NX + Tr::BX - 1) / Tr::BX;  // transposed tiles per head
 
-  // Head-major order per XCD, heaviest resident tiles of a head first.
+  // Head-major order per XCD, heaviest resident tiles of a head first; in a
+  // query-resident pass split over key chunks, the chunks of one query tile
+  // are adjacent.
   const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t bh = L / (uint32_t)nrt;
-  const int rt = KEYS_RES ? (int)(L % (uint32_t)nrt) : nrt - 1 - (int)(L % (uint32_t)nrt);
+  const int S = KEYS_RES ? 1 : p.splits;
+  const uint32_t per_bh = (uint32_t)nrt * (uint32_t)S;
+  const int64_t bh = L / per_bh;
+  const uint32_t jj = L % per_bh;
+  const int rt = KEYS_RES ? (int)jj : nrt - 1 - (int)(jj / (uint32_t)S);
+  const int sp = KEYS_RES ? 0 : (int)(jj % (uint32_t)S);
 
   const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
   const int64_t rr = KEYS_RES ? rk : rq, rx = KEYS_RES ? rq : rk;  // resident / streamed row bases
@@ -536,6 +542,10 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
     } else {
       x_hi = min(NK, rlast_wg + off + 1);
     }
+  }
+  if (S > 1) {  // this workgroup's key chunk (chunks are whole 64-key tiles)
+    x_lo = max(x_lo, sp * p.kchunk);
+    x_hi = min(x_hi, (sp + 1) * p.kchunk);
   }
   const int ntiles = x_hi > x_lo ? (x_hi - x_lo + Tr::BX - 1) / Tr::BX : 0;
   // Streamed tiles start at multiples of 64 rows; the key-resident pass walks
@@ -871,10 +881,16 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
 
     // Epilogue: lane writes its resident row of the accumulated distribution,
     // d = (DB0 + db)*32 + 8j + 4h + (0..3).
+    // A key chunk of a split pass writes its partial (zeros if the chunk is
+    // empty) in the dense [split][distribution][unit, row] layout instead.
     if (r_ok && (TEN ? p.want2 : p.want1)) {
       const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
       float *O = TEN ? (KEYS_RES ? p.dk2 : p.dq2) : (KEYS_RES ? p.dk1 : p.dq1);
-      const int64_t rowoff = (rr + my_r) * D;
+      int64_t rowoff = (rr + my_r) * D;
+      if (S > 1) {
+        O = p.dqp + ((int64_t)sp * 2 + TEN) * (p.BH * (int64_t)NQ * D);
+        rowoff = (bh * (int64_t)NQ + my_r) * D;
+      }
   #pragma unroll
       for (int db = 0; db < NACC; ++db) {
   #pragma unroll
@@ -1014,7 +1030,7 @@ static hipError_t launch_pass4(const BwdParams &p, hipStream_t s) {
   const void *fn = reinterpret_cast<const void *>(&bwd4_kernel<D, KEYS_RES, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
-  const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR);
+  const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR) * (KEYS_RES ? 1 : p.splits);
   hipLaunchKernelGGL((bwd4_kernel<D, KEYS_RES, MODE>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
   return hipGetLastError();
 }
@@ -1049,6 +1065,31 @@ hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s) {
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s) {
   if (dtype == 0) return D == 128 ? launch_bf16_pass<128, false>(p, s) : launch_bf16_pass<64, false>(p, s);
   return D == 128 ? launch_fp32_pass<128, false>(p, s) : launch_fp32_pass<64, false>(p, s);
+}
+
+// dQ_t = sum of the key chunks' partials, in chunk order (deterministic); one
+// thread per 4 consecutive elements of the dense [unit, row][D] layout.
+__global__ __launch_bounds__(256) void dq_reduce_kernel(BwdParams p, int D) {
+  const int64_t per_t = p.BH * p.NQ * D;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= per_t) return;
+  const int64_t urow = e / D, d = e - urow * D;
+  const int64_t u = urow / p.NQ, row = urow - u * p.NQ;
+  const int64_t o = (p.qmap.row0(u) + row) * D + d;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (!(t ? p.want2 : p.want1)) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < p.splits; ++sp) acc += *reinterpret_cast<const f32x4 *>(p.dqp + (sp * 2 + t) * per_t + e);
+    *reinterpret_cast<f32x4 *>((t ? p.dq2 : p.dq1) + o) = acc;
+  }
+}
+
+hipError_t launch_dq_reduce(int D, const BwdParams &p, hipStream_t s) {
+  const int64_t n4 = p.BH * p.NQ * D / 4;
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(dq_reduce_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, s, p, D);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero(float *dst, int64_t n, hipStream_t s) {

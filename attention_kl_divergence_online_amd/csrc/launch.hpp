@@ -44,6 +44,11 @@ struct BwdParams {
   // bf16 inputs: prepared transposed fp16 copies [BH][ceil(N/64)][D][64] (null for fp32)
   const void *tq1, *tq2, *tk1, *tk2;
   float *dq1, *dk1, *dq2, *dk2;  // like the inputs (qmap / kmap rows), fp32
+  // bf16 query-resident pass over `splits` key chunks of `kchunk` keys: each
+  // chunk writes a partial dQ into dqp ([split][distribution][BH * NQ][D],
+  // dense), and launch_dq_reduce sums them.  splits == 1: no partials.
+  float *dqp;
+  int splits, kchunk;
   int64_t BH, NQ, NK;
   float scale;
   int causal;
@@ -69,6 +74,8 @@ hipError_t launch_grad_scale(int dtype, const float *g, RowMap qmap, int64_t BH,
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s);
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s);
 hipError_t launch_zero(float *dst, int64_t n, hipStream_t s);
+// dQ1 / dQ2 (the requested ones) = sum over the key chunks of p.dqp, in chunk order.
+hipError_t launch_dq_reduce(int D, const BwdParams &p, hipStream_t s);
 // bf16 inputs: transposed fp16 copy of x (BH units of N rows, addressed by `map`)
 // into out [BH][ceil(N/64)][D][64].
 hipError_t launch_bwd_transpose(int D, const void *x, RowMap map, int64_t BH, int64_t N, void *out, hipStream_t s);

@@ -154,7 +154,8 @@ def parse():
     ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--other-configs", action="store_true",
                     help="also time forward and backward on the other workloads (causal_4k, noncausal_16k, "
-                         "splitk_bwd_128k, causal_16k_d64, causal_4k_fp32), the decode split-K forward and the packed "
+                         "splitk_bwd_128k, shortq_bwd_64k, causal_16k_d64, causal_4k_fp32), the decode split-K "
+                         "forward and the packed "
                          "variable-length batch, and report them under \"other_configs\"")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -349,8 +350,8 @@ def main():
 
     if args.other_configs:
         out["other_configs"] = {n: config_bench(skl, synth, torch, args, n)
-                                for n in ("causal_4k", "noncausal_16k", "splitk_bwd_128k", "causal_16k_d64",
-                                          "causal_4k_fp32")}
+                                for n in ("causal_4k", "noncausal_16k", "splitk_bwd_128k", "shortq_bwd_64k",
+                                          "causal_16k_d64", "causal_4k_fp32")}
         out["other_configs"]["decode_128k"] = splitk_bench(skl, synth, torch, args, "decode_128k")
         out["other_configs"]["varlen_mix"] = varlen_bench(skl, synth, torch, args, "varlen_mix")
 
@@ -361,18 +362,26 @@ def main():
 
 
 def config_bench(skl, synth, torch, args, name):
-    """Forward and full backward (prepare + both passes) of one workload; HIP-event ms per step."""
+    """Forward (split-K when the workload sets a split count) and full backward
+    (prepare + both passes) of one workload; HIP-event ms per step."""
     w = synth.get(name)
     q1, k1, q2, k2 = synth.make_inputs(w, device="cuda")
     g = synth.upstream_grad(w, "cuda")
     kl, l1, l2 = (torch.empty((w.B, w.H, w.NQ), dtype=torch.float32, device="cuda") for _ in range(3))
     grads = tuple(torch.empty_like(t, dtype=torch.float32) for t in (q1, k1, q2, k2))
     ws = torch.empty(max(16, skl.bwd_workspace_size(q1, k1, w.scale, w.causal)), dtype=torch.uint8, device="cuda")
+    wsk = None
+    if w.splits > 1:
+        wsk = torch.empty(skl.fwd_splitk_workspace_size(q1, k1, w.splits, w.scale, w.causal), dtype=torch.uint8,
+                          device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     fwd_ms = bwd_ms = 0.0
     for it in range(args.warmup + args.steps):
         ev[0].record()
-        skl.streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal, out=(kl, l1, l2))
+        if wsk is None:
+            skl.streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal, out=(kl, l1, l2))
+        else:
+            skl.streamkl_fwd_splitk(q1, k1, q2, k2, w.splits, w.scale, w.causal, workspace=wsk, out=(kl, l1, l2))
         ev[1].record()
         skl.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws, out=grads)
         ev[2].record()
@@ -381,11 +390,11 @@ def config_bench(skl, synth, torch, args, name):
             fwd_ms += ev[0].elapsed_time(ev[1]) / args.steps
             bwd_ms += ev[1].elapsed_time(ev[2]) / args.steps
     pairs = w.visible_pairs()
-    res = {"fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+    res = {"fwd_splits": w.splits, "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
            "fwd_tflops": round(4 * w.D * pairs / (fwd_ms * 1e-3) / 1e12, 2),
            "bwd_tflops": round(12 * w.D * pairs / (bwd_ms * 1e-3) / 1e12, 2),
            "step_tflops": round(16 * w.D * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2)}
-    del q1, k1, q2, k2, grads, ws
+    del q1, k1, q2, k2, grads, ws, wsk
     torch.cuda.empty_cache()
     return res
 

@@ -113,7 +113,12 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p,
  * Bytes of device workspace streamkl_bwd needs: one fp32 per (batch, head)
  * and, for bf16 inputs, transposed fp16 copies of q1, q2, k1 and k2
  * (2 * D * 64 * ceil(N / 64) bytes per (batch, head) and tensor, N = NQ for
- * the queries, NK for the keys).  Returns 0 if the problem is invalid.
+ * the queries, NK for the keys).  With bf16 inputs and fewer than 256 query
+ * tiles of 128 rows in all (B * H * ceil(NQ / 128) < 256), the query-gradient
+ * pass splits the keys into S chunks, S = min(ceil(256 / tiles), 64,
+ * ceil(NK / 64)) (then as many chunks as whole 64-key tiles fill), and the
+ * workspace also holds S partial dQ1, dQ2 in fp32 (S * 2 * B * H * NQ * D * 4
+ * bytes), summed in chunk order.  Returns 0 if the problem is invalid.
  */
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p);
 
@@ -171,8 +176,10 @@ streamkl_status streamkl_bwd(const streamkl_problem *p,
  * alignment rules of streamkl_bwd.
  * streamkl_bwd_dk writes dK1, dK2 (one pass over key tiles, queries streamed);
  * streamkl_bwd_dq writes dQ1, dQ2 (one pass over query tiles, keys streamed).
- * NULL-pair rules, layouts and errors are those of streamkl_bwd; the pass
- * calls read `workspace` and never write it.
+ * NULL-pair rules, layouts and errors are those of streamkl_bwd.  The dK
+ * pass only reads `workspace`; the dQ pass also writes the partial dQ area
+ * when its keys are split, so two dQ passes must not share a workspace
+ * concurrently.
  */
 streamkl_status streamkl_bwd_prepare(const streamkl_problem *p,
                                      const void *q1, const void *k1,

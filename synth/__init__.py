@@ -74,11 +74,14 @@ WORKLOADS: Dict[str, Workload] = {
                  teacher_std=1.5, student="independent"),
         Workload(3, "causal_64k", 1, 32, 65536, 65536, 128, "bf16", True, noise=0.1),
         Workload(4, "splitk_512k", 1, 32, 1024, 524288, 128, "bf16", False, noise=0.2, splits=64),
-        Workload(5, "splitk_bwd_128k", 1, 32, 1024, 131072, 128, "bf16", False, noise=0.2),
+        Workload(5, "splitk_bwd_128k", 1, 32, 1024, 131072, 128, "bf16", False, noise=0.2, splits=16),
         # Decode step: 16 new queries per sequence against a 128K-key cache, split-K forward.
         Workload(6, "decode_128k", 4, 32, 16, 131072, 128, "bf16", True, noise=0.2, splits=64),
         # The D = 64 kernels at long context: 64 heads of 16K, causal.
         Workload(7, "causal_16k_d64", 1, 64, 16384, 16384, 64, "bf16", True, noise=0.1),
+        # Few queries against a long key range, backward: 2 query tiles per head,
+        # so the query-gradient pass splits its keys.
+        Workload(9, "shortq_bwd_64k", 1, 32, 256, 65536, 128, "bf16", False, noise=0.2, splits=32),
         # fp32 inputs (the 1e-5 path) at a moderate causal context.
         Workload(8, "causal_4k_fp32", 2, 16, 4096, 4096, 128, "fp32", True, noise=0.3),
     ]

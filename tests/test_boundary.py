@@ -127,14 +127,31 @@ def bwd(L, p, dq1=A, dk1=A, dq2=A, dk2=A, ws=A, wsb=1 << 20, g=A, kl=A):
     return L.streamkl_bwd(ctypes.byref(p), A, A, A, A, kl, A, A, g, dq1, dk1, dq2, dk2, ws, wsb, None)
 
 
+def dq_splits(B, H, NQ, NK):
+    # The header's rule: fewer than 256 query tiles of 128 rows in all split the
+    # keys into S chunks of whole 64-key tiles.
+    tiles = B * H * ((NQ + 127) // 128)
+    ktiles = (NK + 63) // 64
+    if NQ == 0 or NK == 0 or tiles >= 256:
+        return 1
+    sp = min((256 + tiles - 1) // tiles, 64, ktiles)
+    if sp <= 1:
+        return 1
+    per = (ktiles + sp - 1) // sp
+    return (ktiles + per - 1) // per
+
+
 def bf16_workspace(B, H, NQ, NK, D, heads=None):
     # sigma of every head (256-byte slot), then transposed fp16 copies of q1, q2
-    # (64-row tiles) and k1, k2 for `heads` heads (default: all).
+    # (64-row tiles) and k1, k2 for `heads` heads (default: all), then the split
+    # query pass's partial dQ1, dQ2 (fp32) for those heads.
     up = lambda n, a: (n + a - 1) // a * a
     tiles = lambda n: (n + 63) // 64
     heads = B * H if heads is None else heads
     qt, kt = heads * tiles(NQ) * 64 * D * 2, heads * tiles(NK) * 64 * D * 2
-    return up(max(16, 4 * B * H), 256) + 2 * up(qt, 256) + 2 * up(kt, 256)
+    S = dq_splits(B, H, NQ, NK)
+    dqp = S * 2 * heads * NQ * D * 4 if S > 1 else 0
+    return up(max(16, 4 * B * H), 256) + 2 * up(qt, 256) + 2 * up(kt, 256) + up(dqp, 256)
 
 
 def test_backward_validation(L):

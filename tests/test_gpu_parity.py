@@ -342,6 +342,11 @@ def test_causal_16k_d64_full_size():
     _full_size("causal_16k_d64")
 
 
+def test_shortq_bwd_64k_full_size():
+    # 2 query tiles per head: the query-gradient pass runs split over key chunks.
+    _full_size("shortq_bwd_64k")
+
+
 def test_causal_4k_fp32_full_size():
     _full_size("causal_4k_fp32")
 
