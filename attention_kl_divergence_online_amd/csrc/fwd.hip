@@ -16,7 +16,8 @@
 //  * the resident queries' Q1/Q2 fragments stay in registers for the whole
 //    pass; key tiles stream through double-buffered LDS (or, for at most 16
 //    queries, straight into registers);
-//  * bf16 inputs: 8 waves x 32 queries over 64-key tiles (fwd2_kernel), one
+//  * bf16 inputs: 8 waves x 32 queries over 128-key tiles (64 when split
+//    over key chunks; fwd2_kernel), one
 //    wave x 32 queries over 32-key tiles for at most 32 queries per head, and
 //    16x16 products for at most 16 (fwd16_kernel); fp32 inputs: fwd_kernel
 //    with register-staged tiles and compensated sums;
@@ -379,7 +380,7 @@ struct Fwd2Traits {
   static constexpr int LDS_BYTES = 2 * 2 * ROW_T;
   static constexpr int CHUNKS = ROW_T / 16;            // 16-byte loads per tensor per tile
   static constexpr int LOADS = (CHUNKS + NT - 1) / NT;  // per tensor per thread (the last may be partial)
-  static_assert((BK == 64 || BK == 32) && kFwdBK % BK == 0 && NT % 64 == 0, "tiles");
+  static_assert((BK == 128 || BK == 64 || BK == 32) && NT % 64 == 0, "tiles");
 };
 
 // Queries per head at or below which bf16 inputs take the one-wave shapes:
@@ -807,11 +808,15 @@ static hipError_t launch_fwd2_shape(const FwdParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The grid's query tiles (p.nqt) were sized by fwd_block_queries for the same NQ.
+// The grid's query tiles (p.nqt) were sized by fwd_block_queries for the same
+// NQ.  The unsplit 8-wave shape stages 128-key tiles (half the barriers per
+// key of 64-key tiles); split chunks are whole 64-key tiles, so the split-K
+// shape keeps 64.
 template <int D, bool SPLIT>
 static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
   if (fwd_decode16_shape(0, p.NQ)) return launch_fwd16<D, SPLIT>(p, s);
   if (fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, s);
+  if (!SPLIT) return launch_fwd2_shape<D, SPLIT, 8, 2 * kFwdBK>(p, s);
   return launch_fwd2_shape<D, SPLIT, 8, kFwdBK>(p, s);
 }
 

@@ -28,7 +28,8 @@ METRIC = "attn-KL fwd and fwd+bwd TFLOP/s + ms at 64K ctx, 32 heads, d=128 bf16"
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_kl_causal_64k_hbm_traffic.json")
 COPY_BYTES = 1 << 30
 KERNELS = {  # bench key -> kernel names as rocprofv3 reports them (mangled or demangled)
-    "fwd": ("_ZN3skl11fwd2_kernelILi128ELb0ELi8ELi64EEEvNS_9FwdParamsE", "void skl::fwd2_kernel<128, false, 8, 64>"),
+    "fwd": ("_ZN3skl11fwd2_kernelILi128ELb0ELi8ELi128EEEvNS_9FwdParamsE",
+            "void skl::fwd2_kernel<128, false, 8, 128>"),
     "bwd_dk": ("_ZN3skl11bwd4_kernelILi128ELb1ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, true, 0>"),
     "bwd_dq": ("_ZN3skl11bwd4_kernelILi128ELb0ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, false, 0>"),
     "fwd_split": ("_ZN3skl11fwd2_kernelILi128ELb1ELi8ELi64EEEvNS_9FwdParamsE",
