@@ -224,11 +224,11 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, c
   const size_t need = streamkl_fwd_splitk_workspace_size(p, num_splits);
   if (!workspace || workspace_bytes < need) return STREAMKL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
-  // Whole 64-key tiles per chunk; trailing chunks past NK are empty.
-  const int64_t tiles = (p->NK + skl::kFwdBK - 1) / skl::kFwdBK;
+  // Whole 128-key tiles per chunk; trailing chunks past NK are empty.
+  const int64_t tiles = (p->NK + skl::kFwdChunkTile - 1) / skl::kFwdChunkTile;
   const int64_t tiles_per = (tiles + num_splits - 1) / num_splits;
   f.splits = num_splits;
-  f.chunk = (int)(tiles_per * skl::kFwdBK);
+  f.chunk = (int)(tiles_per * skl::kFwdChunkTile);
   f.ws = reinterpret_cast<float *>(workspace);
   if (skl::launch_fwd(p->dtype, (int)p->D, f, s) != hipSuccess) return STREAMKL_ERR_HIP;
   if (skl::launch_splitk_merge(f, s) != hipSuccess) return STREAMKL_ERR_HIP;

@@ -56,7 +56,8 @@ struct BwdParams {
 };
 
 // Tile sizes the host needs for grids and validation.
-constexpr int kFwdBK = 64;    // keys per forward stage (split chunks are multiples)
+constexpr int kFwdBK = 64;    // keys per forward stage of the split and fp32 shapes
+constexpr int kFwdChunkTile = 128;  // split-K chunks are whole multiples of this (and of every forward tile)
 constexpr int kBwdBR = 128;   // resident rows per backward workgroup
 constexpr int kBwdTile = 64;  // streamed rows per backward stage (tile of the transposed copies)
 constexpr int kGradExp = 8;   // |g| * sigma <= 2^kGradExp before fp16 rounding of dS

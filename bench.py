@@ -32,8 +32,8 @@ KERNELS = {  # bench key -> kernel names as rocprofv3 reports them (mangled or d
             "void skl::fwd2_kernel<128, false, 8, 128>"),
     "bwd_dk": ("_ZN3skl11bwd4_kernelILi128ELb1ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, true, 0>"),
     "bwd_dq": ("_ZN3skl11bwd4_kernelILi128ELb0ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, false, 0>"),
-    "fwd_split": ("_ZN3skl11fwd2_kernelILi128ELb1ELi8ELi64EEEvNS_9FwdParamsE",
-                  "void skl::fwd2_kernel<128, true, 8, 64>"),
+    "fwd_split": ("_ZN3skl11fwd2_kernelILi128ELb1ELi8ELi128EEEvNS_9FwdParamsE",
+                  "void skl::fwd2_kernel<128, true, 8, 128>"),
 }
 
 

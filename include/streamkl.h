@@ -98,7 +98,9 @@ size_t streamkl_fwd_splitk_workspace_size(const streamkl_problem *p, int num_spl
  * into `num_splits` contiguous chunks processed by separate workgroups, each
  * producing a partial row state; a second kernel merges the states with
  * log-sum-exp rescaling and writes KL, LSE1, LSE2 exactly as streamkl_fwd
- * does.  1 <= num_splits <= ceil(NK / 64); chunks are whole 64-key tiles.
+ * does.  1 <= num_splits <= ceil(NK / 64).  Chunks are whole 128-key tiles
+ * of ceil(ceil(NK / 128) / num_splits) tiles each, so past ceil(NK / 128)
+ * splits the trailing chunks are empty (correct, but idle workgroups).
  * `workspace` (device, caller-owned, >= the size query) is scratch between
  * the two kernels; its contents on return are unspecified.
  */
