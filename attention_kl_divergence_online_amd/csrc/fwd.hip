@@ -16,7 +16,8 @@
 //  * the resident queries' Q1/Q2 fragments stay in registers for the whole
 //    pass; key tiles stream through double-buffered LDS (or, for at most 16
 //    queries, straight into registers);
-//  * bf16 inputs: 8 waves x 32 queries over 128-key tiles (fwd2_kernel), one
+//  * bf16 inputs: 8 waves x 32 queries over 128-key tiles (64 at D = 64;
+//    fwd2_kernel), one
 //    wave x 32 queries over 32-key tiles for at most 32 queries per head, and
 //    16x16 products for at most 16 (fwd16_kernel); fp32 inputs: fwd_kernel
 //    with register-staged tiles and compensated sums;
@@ -808,14 +809,16 @@ static hipError_t launch_fwd2_shape(const FwdParams &p, hipStream_t s) {
 }
 
 // The grid's query tiles (p.nqt) were sized by fwd_block_queries for the same
-// NQ.  The 8-wave shape stages 128-key tiles (half the barriers per key of
-// 64-key tiles); split-K chunks are whole 128-key tiles.
+// NQ.  At D = 128 the 8-wave shape stages 128-key tiles (half the barriers
+// per key of 64-key tiles: 2-4% faster); at D = 64, where a tile carries half
+// the work, 64-key tiles measure faster.  Split-K chunks are whole 128-key
+// tiles, a whole number of either.
 template <int D, bool SPLIT>
 static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
   static_assert(kFwdChunkTile % 128 == 0, "split chunks must hold whole 128-key tiles");
   if (fwd_decode16_shape(0, p.NQ)) return launch_fwd16<D, SPLIT>(p, s);
   if (fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, s);
-  return launch_fwd2_shape<D, SPLIT, 8, 128>(p, s);
+  return launch_fwd2_shape<D, SPLIT, 8, D == 128 ? 128 : 64>(p, s);
 }
 
 template <typename T, int D, bool SPLIT>
