@@ -104,14 +104,19 @@ def test_backward_steps_equal_combined_call():
 
 @pytest.mark.parametrize("splits", [2, 3, 7, 16])
 @pytest.mark.parametrize("causal", [False, True])
-def test_splitk_small(splits, causal):
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_splitk_small(splits, causal, dtype):
+    # 1000 keys are 8 chunk tiles of 128: at 16 splits the last 8 chunks are empty.
     B, H, NQ, NK, D = 1, 2, 300, 1000, 128
-    q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, torch.bfloat16, seed=11 + splits)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    print(f"split-K {dtype} splits={splits} causal={causal}", flush=True)
+    q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, tdt, seed=11 + splits)
     scale = 1.0 / math.sqrt(D)
     kl, l1, l2 = streamkl_fwd_splitk(q1, k1, q2, k2, splits, scale, causal)
     ukl, ul1, ul2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
     torch.cuda.synchronize()
-    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, _heads(B, H)), TOL["bf16"], "split")
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, _heads(B, H)), TOL[dtype],
+                  f"split {dtype} {splits}")
     for a, b in ((kl, ukl), (l1, ul1), (l2, ul2)):
         d = (a - b).abs().max().item() / max(b.abs().max().item(), 1e-30)
         assert d <= 1e-4, d  # both sides are also held to the oracle bound above
