@@ -18,6 +18,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -170,6 +171,18 @@ def parse():
     return ap.parse_args()
 
 
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w, q1, k1, q2, k2, target_s: float):
     """Time the fp64 oracle (fwd + bwd) on evenly spaced rows of head (0, 0)."""
     import numpy as np
@@ -196,6 +209,8 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s: float):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.threads(),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"fp64 oracle fwd+bwd on {nrows} evenly spaced query rows of head (0,0) of {w.name} "
                   f"({pairs} visible pairs, {dt:.1f} s; flops counted as 16*D per pair)",
@@ -289,13 +304,11 @@ def main():
     }
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    per = {"fwd": 0.0, "bwd_prepare": 0.0, "bwd_dk": 0.0, "bwd_dq": 0.0}
+    samples = {"fwd": [], "bwd_prepare": [], "bwd_dk": [], "bwd_dq": []}
     for e in evs:
-        per["fwd"] += e[0].elapsed_time(e[1])
-        per["bwd_prepare"] += e[1].elapsed_time(e[2])
-        per["bwd_dk"] += e[2].elapsed_time(e[3])
-        per["bwd_dq"] += e[3].elapsed_time(e[4])
-    per = {k: v / args.steps for k, v in per.items()}
+        for i, k in enumerate(samples):
+            samples[k].append(e[i].elapsed_time(e[i + 1]))
+    per = {k: sum(v) / len(v) for k, v in samples.items()}
     fwd_ms = per["fwd"]
     bwd_ms = per["bwd_prepare"] + per["bwd_dk"] + per["bwd_dq"]
 
@@ -333,6 +346,8 @@ def main():
         "bwd_ms": round(bwd_ms, 3),
         "bwd_tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
         "kernel_ms": {k: round(v, 3) for k, v in per.items()},
+        "kernel_ms_median": {k: round(statistics.median(v), 3) for k, v in samples.items()},
+        "kernel_ms_min": {k: round(min(v), 3) for k, v in samples.items()},
         "wall_s_timed": round(wall, 3),
         "roofline": {
             "bound": "mfma",
