@@ -152,7 +152,10 @@ size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p);
  * With bf16 inputs the two gradient products run on fp16 matrix cores with
  * fp32 accumulation (dS in bf16 would exceed a 2e-3 relative error): entries
  * of Q and K must lie within the fp16 range, |x| <= 65504; larger entries give
- * non-finite gradients.
+ * non-finite gradients.  The fp16 dS operands are scaled so that the largest
+ * |g| maps to [2^7, 2^8), so P1 * |log(P1/P2) - KL| must stay below about 255
+ * at every pair; it exceeds that only where the teacher gives a key real mass
+ * and the student a log-probability hundreds of nats lower.
  */
 streamkl_status streamkl_bwd(const streamkl_problem *p,
                              const void *q1, const void *k1,

@@ -88,6 +88,41 @@ def test_small_shapes_full(dtype, B, H, NQ, NK, D, causal):
     assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, grads, heads), TOL[dtype], f"bwd {case}")
 
 
+PEAKED = [
+    # D, scale, causal: raw logit ranges of about 130 and 270 per row, row KL up to
+    # about 100 and 190 (teacher and student independent), so nearly one-hot rows,
+    # rescaling by large max jumps, and dS1 terms with large log-ratios.
+    (64, 2.0, False),
+    (64, 4.0, True),
+    (128, 2.0, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D,scale,causal", PEAKED)
+def test_peaked_rows_large_kl(dtype, D, scale, causal):
+    B, H, NQ, NK = 1, 2, 200, 333
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    print(f"peaked {dtype} D={D} scale={scale} causal={causal}", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(int(D + 10 * scale + causal))
+    q1, k1, q2, k2 = (torch.randn(B, H, n, D, generator=gen).to(tdt).to(DEV).contiguous()
+                      for n in (NQ, NK, NQ, NK))
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    g = (torch.rand(B, H, NQ, generator=gen) - 0.3).to(DEV)
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal)
+    kls, l1s, l2s = streamkl_fwd_splitk(q1, k1, q2, k2, 3, scale, causal)
+    torch.cuda.synchronize()
+    assert kl.max().item() > 30.0  # the regime this case is for
+    heads = _heads(B, H)
+    case = f"peaked {dtype} D{D} scale={scale} causal={causal}"
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL[dtype], f"fwd {case}")
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kls, l1s, l2s, heads), TOL[dtype],
+                  f"split fwd {case}")
+    assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, grads, heads), TOL[dtype], f"bwd {case}")
+    for t in grads:
+        assert torch.isfinite(t).all()
+
+
 def test_backward_steps_equal_combined_call():
     from attention_kl_divergence_online_amd import streamkl_bwd_dk, streamkl_bwd_dq, streamkl_bwd_prepare
     q1, k1, q2, k2 = _rand(2, 2, 300, 400, 128, torch.bfloat16, seed=12)
