@@ -100,6 +100,37 @@ __device__ __forceinline__ void query_stats(float lse1, float lse2, float kl, fl
   }
 }
 
+// Head, resident tile and key chunk of workgroup w in a backward pass of n =
+// BH * nrt * S workgroups (S key chunks per resident tile, the query-resident
+// pass only).  Each XCD runs a contiguous run of logical ids on its own heads.
+// Causal resident tiles differ in length (low keys see the most queries, high
+// queries the most keys).  By default the run is head-major, heaviest resident
+// tiles first, with the chunks of one tile adjacent, so that the workgroups
+// running at once share one head's streamed tiles through one L2.  With few
+// tiles per head (up to kLongestFirstTiles, unsplit) that order leaves the
+// XCD's CUs unevenly loaded at the end; then, when the heads divide evenly
+// over the XCDs, the run holds whole heads and goes heaviest tile first across
+// all of them.  Measured at 32 resident tiles per head: 5-8% faster.
+template <bool KEYS_RES>
+__device__ __forceinline__ void resident_tile(const BwdParams &p, int nrt, int S, uint32_t w, uint32_t n,
+                                              int64_t &bh, int &rt, int &sp) {
+  const uint32_t L = xcd_remap(w, n);
+  if (p.causal && S == 1 && nrt <= kLongestFirstTiles && p.BH % kXcds == 0) {
+    const uint32_t hx = (uint32_t)(p.BH / kXcds), per = hx * (uint32_t)nrt;
+    const uint32_t i = L % per;
+    bh = (int64_t)(L / per) * hx + i % hx;
+    const int j = (int)(i / hx);
+    rt = KEYS_RES ? j : nrt - 1 - j;
+    sp = 0;
+  } else {
+    const uint32_t per_bh = (uint32_t)nrt * (uint32_t)S;
+    bh = L / per_bh;
+    const uint32_t jj = L % per_bh;
+    rt = KEYS_RES ? (int)jj : nrt - 1 - (int)(jj / (uint32_t)S);
+    sp = KEYS_RES ? 0 : (int)(jj % (uint32_t)S);
+  }
+}
+
 template <int D, bool KEYS_RES>
 __global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p) {
   using Tr = BwdF32Traits<D, KEYS_RES>;
@@ -117,13 +148,9 @@ __global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p) {
   const int NX = KEYS_RES ? NQ : NK;  // streamed row count
   const int nrt = (NR + Tr::BR - 1) / Tr::BR;
 
-  // Head-major order, each XCD taking a contiguous run of heads (so one
-  // head's streamed tiles are shared through one L2); within a head the
-  // heaviest resident tiles go first: under the causal mask low keys see the
-  // most queries, high queries see the most keys.
-  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t bh = L / (uint32_t)nrt;
-  const int rt = KEYS_RES ? (int)(L % (uint32_t)nrt) : nrt - 1 - (int)(L % (uint32_t)nrt);
+  int64_t bh;
+  int rt, sp_unused;
+  resident_tile<KEYS_RES>(p, nrt, 1, blockIdx.x, gridDim.x, bh, rt, sp_unused);
 
   const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
   const int64_t rr = KEYS_RES ? rk : rq, rx = KEYS_RES ? rq : rk;  // resident / streamed row bases
@@ -501,16 +528,10 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   const int nrt = (NR + Tr::BR - 1) / Tr::BR;
   const int nxt = (NX + Tr::BX - 1) / Tr::BX;  // transposed tiles per head
 
-  // Head-major order per XCD, heaviest resident tiles of a head first; in a
-  // query-resident pass split over key chunks, the chunks of one query tile
-  // are adjacent.
-  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
   const int S = KEYS_RES ? 1 : p.splits;
-  const uint32_t per_bh = (uint32_t)nrt * (uint32_t)S;
-  const int64_t bh = L / per_bh;
-  const uint32_t jj = L % per_bh;
-  const int rt = KEYS_RES ? (int)jj : nrt - 1 - (int)(jj / (uint32_t)S);
-  const int sp = KEYS_RES ? 0 : (int)(jj % (uint32_t)S);
+  int64_t bh;
+  int rt, sp;
+  resident_tile<KEYS_RES>(p, nrt, S, blockIdx.x, gridDim.x, bh, rt, sp);
 
   const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
   const int64_t rr = KEYS_RES ? rk : rq, rx = KEYS_RES ? rq : rk;  // resident / streamed row bases

@@ -72,6 +72,11 @@ __device__ __forceinline__ chunk_t<T> load_chunk(const T* p) {
 // the dispatcher hands workgroup w to XCD w % 8, so logical id
 // (w % 8) * (n / 8) + w / 8 gives each XCD a contiguous run of logical ids.
 // Only applied when n is a multiple of 8 (otherwise identity).
+constexpr int kXcds = 8;
+// Causal launches with at most this many query (forward) or resident
+// (backward) tiles per head order their workgroups longest first across the
+// heads of an XCD rather than head by head.
+constexpr int kLongestFirstTiles = 64;
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
   if ((n & 7u) != 0u) return w;
   return (w & 7u) * (n >> 3) + (w >> 3);
