@@ -5,6 +5,10 @@
 
 #include <stdint.h>
 
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 #include "launch.hpp"
 
 namespace {
@@ -554,6 +558,120 @@ const void *adv_rows(const void *ptr, int64_t rows, int64_t D, int64_t es) {
 }
 float *adv_rowsf(float *ptr, int64_t rows, int64_t D) { return ptr ? ptr + rows * D : nullptr; }
 
+// Runs launched together: each run becomes one segment of a segmented launch
+// (its workgroups follow the previous run's in one grid), so that short
+// sequences share the GPU instead of each leaving most of it idle.  Segments
+// go heaviest workgroups first (longest streamed range), and a launch holds at
+// most kMaxSegs segments and kSegMaxWorkgroups workgroups of 512 work-items.
+constexpr int64_t kSegMaxWorkgroups = (((int64_t)1 << 32) - 1) / 512;
+
+struct SegItem {
+  skl::Seg seg;     // start unused: assigned per launch
+  int64_t count;    // workgroups of the segment
+  int64_t weight;   // order key, larger first
+};
+
+template <class F>
+streamkl_status launch_segments(std::vector<SegItem> items, F launch) {
+  std::stable_sort(items.begin(), items.end(),
+                   [](const SegItem &a, const SegItem &b) { return a.weight > b.weight; });
+  skl::SegTable t{};
+  int64_t end = 0;
+  auto flush = [&]() -> streamkl_status {
+    if (t.n == 0) return STREAMKL_OK;
+    t.end = (uint32_t)end;
+    const streamkl_status st = launch(t);
+    t = skl::SegTable{};
+    end = 0;
+    return st;
+  };
+  for (const SegItem &it : items) {
+    if (it.count == 0) continue;
+    if (t.n == skl::kMaxSegs || end + it.count > kSegMaxWorkgroups) {
+      const streamkl_status st = flush();
+      if (st != STREAMKL_OK) return st;
+    }
+    t.seg[t.n] = it.seg;
+    t.seg[t.n].start = (uint32_t)end;
+    ++t.n;
+    end += it.count;
+  }
+  return flush();
+}
+
+skl::Seg run_seg(const streamkl_varlen_problem *v, const Run &r) {
+  skl::Seg g{};
+  g.units = (r.b1 - r.b0) * v->H;
+  g.nq = r.nq;
+  g.nk = r.nk;
+  g.oq = v->cu_seqlens_q[r.b0];
+  g.ok = v->cu_seqlens_k[r.b0];
+  g.u0 = r.b0 * v->H;
+  return g;
+}
+
+// Backward workspace of a packed batch: sigma for every (sequence, head),
+// then the transposed copies of every run that the segmented passes take
+// (bf16 inputs; each of the four tensors' copies contiguous over the runs, a
+// run's at the same offset in the two query or the two key regions).  A run
+// whose query-gradient pass splits its keys runs on its own afterwards, with
+// the plain layout of its problem at the front of the workspace.
+struct VarlenLayout {
+  size_t tq1, tq2, tk1, tk2, total;
+};
+
+// The query-gradient pass splits keys only to fill the GPU: with at least
+// kDqSplitTarget query tiles over the whole batch every run joins the
+// segmented passes; otherwise a run whose own problem would split its keys
+// runs on its own.
+bool batch_fills_gpu(const streamkl_varlen_problem *v) {
+  int64_t tiles = 0;
+  for_each_run(v, [&](const Run &r) {
+    tiles += (r.b1 - r.b0) * v->H * ((r.nq + skl::kBwdBR - 1) / skl::kBwdBR);
+    return STREAMKL_OK;
+  });
+  return tiles >= kDqSplitTarget;
+}
+
+bool run_segmented_bwd(const streamkl_varlen_problem *v, const Run &r, bool fills) {
+  if (r.nq == 0) return false;
+  if (fills) return true;
+  const streamkl_problem p = run_problem(v, r);
+  return dq_split(&p).splits == 1;
+}
+
+size_t run_copy_bytes(const streamkl_varlen_problem *v, const Run &r, int64_t n) {
+  const size_t tile = (size_t)skl::kBwdTile;
+  const size_t units = (size_t)((r.b1 - r.b0) * v->H);
+  return round_up(units * (((size_t)n + tile - 1) / tile) * tile * (size_t)v->D * 2, 256);
+}
+
+VarlenLayout varlen_layout(const streamkl_varlen_problem *v) {
+  VarlenLayout l{};
+  const size_t units = (size_t)(v->B * v->H);
+  const size_t sig = round_up(units * sizeof(float) > 16 ? units * sizeof(float) : 16, 256);
+  size_t qb = 0, kb = 0, solo = 16;
+  const bool fills = batch_fills_gpu(v);
+  for_each_run(v, [&](const Run &r) {
+    if (run_segmented_bwd(v, r, fills)) {
+      if (v->dtype == STREAMKL_BF16) {
+        qb += run_copy_bytes(v, r, r.nq);
+        kb += run_copy_bytes(v, r, r.nk);
+      }
+    } else if (r.nq > 0) {
+      const streamkl_problem p = run_problem(v, r);
+      solo = std::max(solo, bwd_layout(&p).total);
+    }
+    return STREAMKL_OK;
+  });
+  l.tq1 = sig;
+  l.tq2 = l.tq1 + qb;
+  l.tk1 = l.tq2 + qb;
+  l.tk2 = l.tk1 + kb;
+  l.total = std::max(l.tk2 + kb, solo);
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -569,32 +687,43 @@ streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v, const void
   if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2)) return STREAMKL_ERR_ALIGN;
   if ((st = check_rowvecs(kl, lse1, lse2)) != STREAMKL_OK) return st;
   const int64_t es = v->dtype == STREAMKL_BF16 ? 2 : 4;
+  const int D = (int)v->D;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return for_each_run(v, [&](const Run &r) {
+  // Runs of the main kernel shape: segmented launches.  Decode-shaped runs
+  // (few queries per sequence) launch on their own.
+  std::vector<SegItem> items;
+  st = for_each_run(v, [&](const Run &r) {
     if (r.nq == 0) return STREAMKL_OK;
+    if (skl::fwd_segment_shape(v->dtype, r.nq)) {
+      SegItem it{run_seg(v, r), 0, r.nk};
+      const int bq = skl::fwd_block_queries(v->dtype, D, r.nq);
+      it.seg.tiles = (int32_t)((r.nq + bq - 1) / bq);
+      it.count = it.seg.units * it.seg.tiles;
+      items.push_back(it);
+      return STREAMKL_OK;
+    }
     const streamkl_problem p = run_problem(v, r);
     const int64_t oq = v->cu_seqlens_q[r.b0], ok = v->cu_seqlens_k[r.b0];
     skl::FwdParams f = make_fwd(&p, adv_rows(q1, oq, v->D, es), adv_rows(k1, ok, v->D, es),
                                 adv_rows(q2, oq, v->D, es), adv_rows(k2, ok, v->D, es), kl + oq, lse1 + oq,
                                 lse2 + oq);
-    f.qmap = skl::RowMap{r.nq, TQ, (int)v->H};
-    f.kmap = skl::RowMap{r.nk, TK, (int)v->H};
-    return skl::launch_fwd(v->dtype, (int)v->D, f, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+    f.qmap = skl::RowMap{r.nq, TQ, (int)v->H, 0};
+    f.kmap = skl::RowMap{r.nk, TK, (int)v->H, 0};
+    return skl::launch_fwd(v->dtype, D, f, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+  });
+  if (st != STREAMKL_OK || items.empty()) return st;
+  const streamkl_problem p0 = run_problem(v, Run{0, 1, 0, 0});
+  skl::FwdParams f = make_fwd(&p0, q1, k1, q2, k2, kl, lse1, lse2);
+  f.qmap = skl::RowMap{0, TQ, (int)v->H, 0};
+  f.kmap = skl::RowMap{0, TK, (int)v->H, 0};
+  return launch_segments(items, [&](const skl::SegTable &t) {
+    return skl::launch_fwd_segs(v->dtype, D, f, t, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
   });
 }
 
 size_t streamkl_bwd_varlen_workspace_size(const streamkl_varlen_problem *v) {
   if (check_varlen(v, true) != STREAMKL_OK) return 0;
-  size_t need = 16;
-  for_each_run(v, [&](const Run &r) {
-    if (r.nq > 0) {
-      const streamkl_problem p = run_problem(v, r);
-      const size_t n = bwd_layout(&p).total;
-      if (n > need) need = n;
-    }
-    return STREAMKL_OK;
-  });
-  return need;
+  return varlen_layout(v).total;
 }
 
 streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void *q1, const void *k1,
@@ -617,29 +746,135 @@ streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void
     if (!workspace || workspace_bytes < streamkl_bwd_varlen_workspace_size(v)) return STREAMKL_ERR_WORKSPACE;
     if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
   }
-  const int64_t es = v->dtype == STREAMKL_BF16 ? 2 : 4, D = v->D, H = v->H;
+  const int64_t D = v->D, H = v->H;
+  const bool bf16 = v->dtype == STREAMKL_BF16;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return for_each_run(v, [&](const Run &r) {
-    const int64_t oq = v->cu_seqlens_q[r.b0], ok = v->cu_seqlens_k[r.b0];
+  const VarlenLayout l = varlen_layout(v);
+  char *w = reinterpret_cast<char *>(workspace);
+  float *sigma = reinterpret_cast<float *>(workspace);
+
+  // Query-less runs: their key gradients are zero.  Segmented runs: sigma and
+  // transposed copies into their places, then one pass of each kind over all.
+  std::vector<SegItem> sig_items, tq_items, tk_items, dk_items, dq_items;
+  size_t qoff = 0, koff = 0;
+  const bool fills = batch_fills_gpu(v);
+  st = for_each_run(v, [&](const Run &r) {
+    const int64_t ok = v->cu_seqlens_k[r.b0];
     if (r.nq == 0) {
-      // No query rows: the key gradients of these sequences are zero.
       const int64_t n = (r.b1 - r.b0) * r.nk * D;
       for (int64_t h = 0; h < H && n > 0; ++h)
         for (float *dk : {dk1, dk2})
           if (dk && skl::launch_zero(dk + (h * TK + ok) * D, n, s) != hipSuccess) return STREAMKL_ERR_HIP;
       return STREAMKL_OK;
     }
+    if (!run_segmented_bwd(v, r, fills)) return STREAMKL_OK;
+    SegItem it{run_seg(v, r), 0, 0};
+    if (bf16) {
+      it.seg.tq = (int64_t)qoff;
+      it.seg.tk = (int64_t)koff;
+      qoff += run_copy_bytes(v, r, r.nq);
+      koff += run_copy_bytes(v, r, r.nk);
+    }
+    const int64_t tile = skl::kBwdTile, br = skl::kBwdBR;
+    SegItem us = it, tq = it, tk = it;
+    us.count = it.seg.units;  // sigma: one workgroup per unit
+    tq.count = it.seg.units * ((r.nq + tile - 1) / tile);
+    tk.count = it.seg.units * ((r.nk + tile - 1) / tile);
+    sig_items.push_back(us);
+    tq_items.push_back(tq);
+    tk_items.push_back(tk);
+    SegItem a = it, b = it;
+    a.count = it.seg.units * ((r.nk + br - 1) / br);  // dK pass: key tiles, streaming the queries
+    a.weight = r.nq;
+    b.count = it.seg.units * ((r.nq + br - 1) / br);  // dQ pass: query tiles, streaming the keys
+    b.weight = r.nk;
+    dk_items.push_back(a);
+    dq_items.push_back(b);
+    return STREAMKL_OK;
+  });
+  if (st != STREAMKL_OK) return st;
+  if (!dk_items.empty()) {
+    // Prepare step of all segmented runs: sigma, then the transposed copies.
+    const skl::RowMap qm{0, TQ, (int)H, 0}, km{0, TK, (int)H, 0};
+    st = launch_segments(sig_items, [&](const skl::SegTable &t) {
+      return skl::launch_grad_scale_segs(v->dtype, g, qm, t, sigma, s) == hipSuccess ? STREAMKL_OK
+                                                                                      : STREAMKL_ERR_HIP;
+    });
+    if (st != STREAMKL_OK) return st;
+    if (bf16) {
+      const std::pair<const void *, size_t> qs[2] = {{q1, l.tq1}, {q2, l.tq2}}, ks[2] = {{k1, l.tk1}, {k2, l.tk2}};
+      for (int i = 0; i < 2 && st == STREAMKL_OK; ++i) {
+        st = launch_segments(tq_items, [&](const skl::SegTable &t) {
+          return skl::launch_bwd_transpose_segs((int)D, qs[i].first, qm, 0, t, w + qs[i].second, s) == hipSuccess
+                     ? STREAMKL_OK
+                     : STREAMKL_ERR_HIP;
+        });
+        if (st == STREAMKL_OK)
+          st = launch_segments(tk_items, [&](const skl::SegTable &t) {
+            return skl::launch_bwd_transpose_segs((int)D, ks[i].first, km, 1, t, w + ks[i].second, s) ==
+                           hipSuccess
+                       ? STREAMKL_OK
+                       : STREAMKL_ERR_HIP;
+          });
+      }
+      if (st != STREAMKL_OK) return st;
+    }
+    skl::BwdParams b{};
+    b.q1 = q1;
+    b.k1 = k1;
+    b.q2 = q2;
+    b.k2 = k2;
+    b.kl = kl;
+    b.lse1 = lse1;
+    b.lse2 = lse2;
+    b.g = g;
+    b.sigma = sigma;
+    if (bf16) {
+      b.tq1 = w + l.tq1;
+      b.tq2 = w + l.tq2;
+      b.tk1 = w + l.tk1;
+      b.tk2 = w + l.tk2;
+    }
+    b.splits = 1;
+    b.qmap = skl::RowMap{0, TQ, (int)H, 0};
+    b.kmap = skl::RowMap{0, TK, (int)H, 0};
+    b.scale = v->scale;
+    b.causal = v->causal ? 1 : 0;
+    b.dk1 = dk1;
+    b.dk2 = dk2;
+    b.want1 = dk1 != nullptr;
+    b.want2 = dk2 != nullptr;
+    st = launch_segments(dk_items, [&](const skl::SegTable &t) {
+      return skl::launch_bwd_dk_segs(v->dtype, (int)D, b, t, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+    });
+    if (st != STREAMKL_OK) return st;
+    b.dk1 = b.dk2 = nullptr;
+    b.dq1 = dq1;
+    b.dq2 = dq2;
+    b.want1 = dq1 != nullptr;
+    b.want2 = dq2 != nullptr;
+    st = launch_segments(dq_items, [&](const skl::SegTable &t) {
+      return skl::launch_bwd_dq_segs(v->dtype, (int)D, b, t, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+    });
+    if (st != STREAMKL_OK) return st;
+  }
+
+  // Runs whose query-gradient pass splits its keys, one after another with
+  // their own layout at the front of the workspace (stream order keeps them
+  // after the segmented passes that read it).
+  const int64_t es = bf16 ? 2 : 4;
+  return for_each_run(v, [&](const Run &r) {
+    if (r.nq == 0 || run_segmented_bwd(v, r, fills)) return STREAMKL_OK;
+    const int64_t oq = v->cu_seqlens_q[r.b0], ok = v->cu_seqlens_k[r.b0];
     const streamkl_problem p = run_problem(v, r);
     skl::BwdParams b = make_bwd(&p, adv_rows(q1, oq, D, es), adv_rows(k1, ok, D, es), adv_rows(q2, oq, D, es),
                                 adv_rows(k2, ok, D, es), kl + oq, lse1 + oq, lse2 + oq, g + oq,
                                 adv_rowsf(dq1, oq, D), adv_rowsf(dk1, ok, D), adv_rowsf(dq2, oq, D),
                                 adv_rowsf(dk2, ok, D), workspace);
-    b.qmap = skl::RowMap{r.nq, TQ, (int)H};
-    b.kmap = skl::RowMap{r.nk, TK, (int)H};
-    // The run's sigma and transposed copies reuse the front of the workspace;
-    // stream order keeps the runs apart.
+    b.qmap = skl::RowMap{r.nq, TQ, (int)H, 0};
+    b.kmap = skl::RowMap{r.nk, TK, (int)H, 0};
     streamkl_status rs = run_sigma(&p, b, s);
-    if (rs == STREAMKL_OK && v->dtype == STREAMKL_BF16) rs = run_transposes(&p, b, s);
+    if (rs == STREAMKL_OK && bf16) rs = run_transposes(&p, b, s);
     if (rs == STREAMKL_OK) rs = run_dk(&p, b, s);
     if (rs == STREAMKL_OK) rs = run_dq(&p, b, s);
     return rs;

@@ -131,8 +131,35 @@ __device__ __forceinline__ void resident_tile(const BwdParams &p, int nrt, int S
   }
 }
 
+// Workgroup wg of a segmented launch (t.n > 0, no key split): its segment's
+// parameters replace the run-dependent ones in p (the per-unit sigma and the
+// transposed copies move to the run's own), and wg, nwg become the
+// workgroup's index and count within the segment.  A plain launch (t.n == 0)
+// keeps its parameters.
+__device__ __forceinline__ void select_segment(BwdParams &p, const SegTable &t, uint32_t &wg, uint32_t &nwg) {
+  if (t.n == 0) return;
+  const int lo = seg_index(t, wg);
+  nwg = seg_count(t, lo);
+  wg -= t.seg[lo].start;
+  p.BH = t.seg[lo].units;
+  p.NQ = t.seg[lo].nq;
+  p.NK = t.seg[lo].nk;
+  p.qmap.sb = t.seg[lo].nq;
+  p.qmap.base = t.seg[lo].oq;
+  p.kmap.sb = t.seg[lo].nk;
+  p.kmap.base = t.seg[lo].ok;
+  p.sigma += t.seg[lo].u0;
+  const int64_t tq = t.seg[lo].tq, tk = t.seg[lo].tk;
+  if (p.tq1) {
+    p.tq1 = reinterpret_cast<const char *>(p.tq1) + tq;
+    p.tq2 = reinterpret_cast<const char *>(p.tq2) + tq;
+    p.tk1 = reinterpret_cast<const char *>(p.tk1) + tk;
+    p.tk2 = reinterpret_cast<const char *>(p.tk2) + tk;
+  }
+}
+
 template <int D, bool KEYS_RES>
-__global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p, const SegTable t) {
   using Tr = BwdF32Traits<D, KEYS_RES>;
   using T = float;
   using CG = f32x8;
@@ -142,6 +169,8 @@ __global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
 
+  uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  select_segment(p, t, wg, nwg);
   const int NQ = (int)p.NQ, NK = (int)p.NK;
   const int off = NK - NQ;
   const int NR = KEYS_RES ? NK : NQ;  // resident row count
@@ -150,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p) {
 
   int64_t bh;
   int rt, sp_unused;
-  resident_tile<KEYS_RES>(p, nrt, 1, blockIdx.x, gridDim.x, bh, rt, sp_unused);
+  resident_tile<KEYS_RES>(p, nrt, 1, wg, nwg, bh, rt, sp_unused);
 
   const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
   const int64_t rr = KEYS_RES ? rk : rq, rx = KEYS_RES ? rq : rk;  // resident / streamed row bases
@@ -510,7 +539,7 @@ __device__ __forceinline__ int swz_tr(int d) { return (d >> 1) & 7; }  // 128-by
 // distribution the pair splits D instead: each wave accumulates its half of
 // D over both blocks, and the dS that is not needed is never formed.
 template <int D, bool KEYS_RES, int MODE>
-__global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTable t) {
   using Tr = Bwd4Traits<D, KEYS_RES>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   typedef __attribute__((address_space(3))) void lds_void;
@@ -521,6 +550,8 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   const int e_rt = wave >> 2;  // streamed block for dS; distribution whose gradient this wave accumulates
   const int h = lane >> 5, c32 = lane & 31;
 
+  uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  select_segment(p, t, wg, nwg);
   const int NQ = (int)p.NQ, NK = (int)p.NK;
   const int off = NK - NQ;
   const int NR = KEYS_RES ? NK : NQ;
@@ -531,7 +562,7 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
   const int S = KEYS_RES ? 1 : p.splits;
   int64_t bh;
   int rt, sp;
-  resident_tile<KEYS_RES>(p, nrt, S, blockIdx.x, gridDim.x, bh, rt, sp);
+  resident_tile<KEYS_RES>(p, nrt, S, wg, nwg, bh, rt, sp);
 
   const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
   const int64_t rr = KEYS_RES ? rk : rq, rx = KEYS_RES ? rq : rk;  // resident / streamed row bases
@@ -942,13 +973,25 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p) {
 // 64-row tile T of each (b, h), out[T][d][pos] = x[64T + row(pos)][d] with
 // row(pos) swapping bits 2 and 3 of pos (the slot order of the dS operands in
 // a 16-row k-step); rows past the end are zero.  One workgroup per (b, h, tile).
+// In a segmented launch (t.n > 0) each segment is a run of units with its own
+// row count, rows and copy area (`keys` picks the key fields).
 template <int D>
 __global__ __launch_bounds__(256) void transpose_kernel(const bf16 *x, RowMap map, int64_t N, int64_t ntile,
-                                                        f16 *out) {
+                                                        f16 *out, const SegTable t, int keys) {
   constexpr int CPR = D * 2 / 16;
   constexpr int LROW = D + 8;  // fp16 elements per LDS row (16-byte pad)
   __shared__ __attribute__((aligned(16))) f16 tile[kBwdTile * LROW];
-  const int64_t T = blockIdx.x % ntile, bh = blockIdx.x / ntile;
+  uint32_t wg = blockIdx.x;
+  if (t.n > 0) {
+    const int i = seg_index(t, wg);
+    wg -= t.seg[i].start;
+    N = keys ? t.seg[i].nk : t.seg[i].nq;
+    map.sb = N;
+    map.base = keys ? t.seg[i].ok : t.seg[i].oq;
+    ntile = (N + kBwdTile - 1) / kBwdTile;
+    out = reinterpret_cast<f16 *>(reinterpret_cast<char *>(out) + (keys ? t.seg[i].tk : t.seg[i].tq));
+  }
+  const int64_t T = wg % ntile, bh = wg / ntile;
   const bf16 *xs = x + (map.row0(bh) + T * kBwdTile) * D;
   const int nrow = (int)min<int64_t>(kBwdTile, N - T * kBwdTile);
   for (int cidx = threadIdx.x; cidx < kBwdTile * CPR; cidx += 256) {
@@ -976,8 +1019,16 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16 *x, RowMap ma
 // and 1 everywhere when `unit` is set: fp32 inputs need no scaling), stored
 // negated when some g[b,h,:] is negative.
 __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap qmap, int64_t NQ, float *sigma,
-                                                         int unit) {
-  const int64_t bh = blockIdx.x;
+                                                         int unit, const SegTable t) {
+  int64_t bh = blockIdx.x;
+  if (t.n > 0) {  // a segmented launch: one workgroup per unit of each segment
+    const int i = seg_index(t, (uint32_t)bh);
+    bh -= t.seg[i].start;
+    NQ = t.seg[i].nq;
+    qmap.sb = NQ;
+    qmap.base = t.seg[i].oq;
+    sigma += t.seg[i].u0;
+  }
   if (unit) {
     // fp32 inputs: no dS scaling, but the sign flag is still needed.
     const float *gu = g + qmap.row0(bh);
@@ -1023,45 +1074,57 @@ __global__ __launch_bounds__(256) void zero_kernel(float *dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = 0.f;
 }
 
+// A plain launch passes an empty segment table.
+const SegTable kNoSegs{};
+
 template <int D, bool KEYS_RES>
-static hipError_t launch_fp32_pass(const BwdParams &p, hipStream_t s) {
+static hipError_t launch_fp32_pass(const BwdParams &p, const SegTable &t, hipStream_t s) {
   using Tr = BwdF32Traits<D, KEYS_RES>;
   const int64_t NR = KEYS_RES ? p.NK : p.NQ;
-  if (NR == 0) return hipSuccess;
+  if (t.n == 0 && NR == 0) return hipSuccess;
   const void *fn = reinterpret_cast<const void *>(&bwd_fp32_kernel<D, KEYS_RES>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
-  const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR);
-  hipLaunchKernelGGL((bwd_fp32_kernel<D, KEYS_RES>), dim3((uint32_t)nblk), dim3(256), Tr::LDS_BYTES, s, p);
+  const int64_t nblk = t.n > 0 ? (int64_t)t.end : p.BH * ((NR + Tr::BR - 1) / Tr::BR);
+  hipLaunchKernelGGL((bwd_fp32_kernel<D, KEYS_RES>), dim3((uint32_t)nblk), dim3(256), Tr::LDS_BYTES, s, p, t);
   return hipGetLastError();
 }
 
 hipError_t launch_grad_scale(int dtype, const float *g, RowMap qmap, int64_t BH, int64_t NQ, float *sigma,
                              hipStream_t s) {
   hipLaunchKernelGGL(grad_scale_kernel, dim3((uint32_t)BH), dim3(256), 0, s, g, qmap, NQ, sigma,
-                     dtype == 1 ? 1 : 0);
+                     dtype == 1 ? 1 : 0, kNoSegs);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_scale_segs(int dtype, const float *g, RowMap qmap, const SegTable &t, float *sigma,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(grad_scale_kernel, dim3(t.end), dim3(256), 0, s, g, qmap, (int64_t)0, sigma,
+                     dtype == 1 ? 1 : 0, t);
   return hipGetLastError();
 }
 
 template <int D, bool KEYS_RES, int MODE>
-static hipError_t launch_pass4(const BwdParams &p, hipStream_t s) {
+static hipError_t launch_pass4(const BwdParams &p, const SegTable &t, hipStream_t s) {
   using Tr = Bwd4Traits<D, KEYS_RES>;
   const int64_t NR = KEYS_RES ? p.NK : p.NQ;
-  if (NR == 0) return hipSuccess;
+  if (t.n == 0 && NR == 0) return hipSuccess;
   const void *fn = reinterpret_cast<const void *>(&bwd4_kernel<D, KEYS_RES, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
-  const int64_t nblk = p.BH * ((NR + Tr::BR - 1) / Tr::BR) * (KEYS_RES ? 1 : p.splits);
-  hipLaunchKernelGGL((bwd4_kernel<D, KEYS_RES, MODE>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  const int64_t nblk =
+      t.n > 0 ? (int64_t)t.end : p.BH * ((NR + Tr::BR - 1) / Tr::BR) * (KEYS_RES ? 1 : p.splits);
+  hipLaunchKernelGGL((bwd4_kernel<D, KEYS_RES, MODE>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p,
+                     t);
   return hipGetLastError();
 }
 
 // Both distributions, the teacher's only or the student's only.
 template <int D, bool KEYS_RES>
-static hipError_t launch_bf16_pass(const BwdParams &p, hipStream_t s) {
-  if (p.want1 && p.want2) return launch_pass4<D, KEYS_RES, 0>(p, s);
-  if (p.want1) return launch_pass4<D, KEYS_RES, 1>(p, s);
-  if (p.want2) return launch_pass4<D, KEYS_RES, 2>(p, s);
+static hipError_t launch_bf16_pass(const BwdParams &p, const SegTable &t, hipStream_t s) {
+  if (p.want1 && p.want2) return launch_pass4<D, KEYS_RES, 0>(p, t, s);
+  if (p.want1) return launch_pass4<D, KEYS_RES, 1>(p, t, s);
+  if (p.want2) return launch_pass4<D, KEYS_RES, 2>(p, t, s);
   return hipSuccess;
 }
 
@@ -1071,21 +1134,41 @@ hipError_t launch_bwd_transpose(int D, const void *x, RowMap map, int64_t BH, in
   const dim3 grid((uint32_t)(ntile * BH));
   if (D == 128)
     hipLaunchKernelGGL(transpose_kernel<128>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map, N,
-                       ntile, reinterpret_cast<f16 *>(out));
+                       ntile, reinterpret_cast<f16 *>(out), kNoSegs, 0);
   else
     hipLaunchKernelGGL(transpose_kernel<64>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map, N,
-                       ntile, reinterpret_cast<f16 *>(out));
+                       ntile, reinterpret_cast<f16 *>(out), kNoSegs, 0);
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_transpose_segs(int D, const void *x, RowMap map, int keys, const SegTable &t, void *out,
+                                     hipStream_t s) {
+  const dim3 grid(t.end);
+  if (D == 128)
+    hipLaunchKernelGGL(transpose_kernel<128>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map,
+                       (int64_t)0, (int64_t)1, reinterpret_cast<f16 *>(out), t, keys);
+  else
+    hipLaunchKernelGGL(transpose_kernel<64>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map,
+                       (int64_t)0, (int64_t)1, reinterpret_cast<f16 *>(out), t, keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dk_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s) {
+  if (dtype == 0) return D == 128 ? launch_bf16_pass<128, true>(p, t, s) : launch_bf16_pass<64, true>(p, t, s);
+  return D == 128 ? launch_fp32_pass<128, true>(p, t, s) : launch_fp32_pass<64, true>(p, t, s);
+}
+
+hipError_t launch_bwd_dq_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s) {
+  if (dtype == 0) return D == 128 ? launch_bf16_pass<128, false>(p, t, s) : launch_bf16_pass<64, false>(p, t, s);
+  return D == 128 ? launch_fp32_pass<128, false>(p, t, s) : launch_fp32_pass<64, false>(p, t, s);
+}
+
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s) {
-  if (dtype == 0) return D == 128 ? launch_bf16_pass<128, true>(p, s) : launch_bf16_pass<64, true>(p, s);
-  return D == 128 ? launch_fp32_pass<128, true>(p, s) : launch_fp32_pass<64, true>(p, s);
+  return launch_bwd_dk_segs(dtype, D, p, kNoSegs, s);
 }
 
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s) {
-  if (dtype == 0) return D == 128 ? launch_bf16_pass<128, false>(p, s) : launch_bf16_pass<64, false>(p, s);
-  return D == 128 ? launch_fp32_pass<128, false>(p, s) : launch_fp32_pass<64, false>(p, s);
+  return launch_bwd_dq_segs(dtype, D, p, kNoSegs, s);
 }
 
 // dQ_t = sum of the key chunks' partials, in chunk order (deterministic); one

@@ -152,8 +152,27 @@ __device__ __forceinline__ void unsplit_tile(const FwdParams &p, uint32_t w, uin
   }
 }
 
+// Workgroup wg of a segmented launch (t.n > 0, unsplit): its segment's
+// parameters replace the run-dependent ones in p, and wg, nwg become the
+// workgroup's index and count within the segment.  A plain launch (t.n == 0)
+// keeps its parameters.
+__device__ __forceinline__ void select_segment(FwdParams &p, const SegTable &t, uint32_t &wg, uint32_t &nwg) {
+  if (t.n == 0) return;
+  const int lo = seg_index(t, wg);
+  nwg = seg_count(t, lo);
+  wg -= t.seg[lo].start;
+  p.BH = t.seg[lo].units;
+  p.NQ = t.seg[lo].nq;
+  p.NK = t.seg[lo].nk;
+  p.nqt = t.seg[lo].tiles;
+  p.qmap.sb = t.seg[lo].nq;
+  p.qmap.base = t.seg[lo].oq;
+  p.kmap.sb = t.seg[lo].nk;
+  p.kmap.base = t.seg[lo].ok;
+}
+
 template <typename T, int D, bool SPLIT>
-__global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p, const SegTable t) {
   using Tr = FwdTraits<T, D>;
   using CT = chunk_t<T>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -163,17 +182,19 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdParams p) {
   const int h = lane >> 5, c32 = lane & 31;
 
   // Workgroup -> (head, query tile, key chunk).
+  uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  select_segment(p, t, wg, nwg);
   int qt, sp;
   int64_t bh;
   if (SPLIT) {
     // Workgroups that share a key chunk are adjacent logical ids on one XCD.
-    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t L = xcd_remap(wg, nwg);
     qt = (int)(L % (uint32_t)p.nqt);
     const uint32_t rest = L / (uint32_t)p.nqt;
     sp = (int)(rest % (uint32_t)p.splits);
     bh = rest / (uint32_t)p.splits;
   } else {
-    unsplit_tile(p, blockIdx.x, gridDim.x, bh, qt);
+    unsplit_tile(p, wg, nwg, bh, qt);
     sp = 0;
   }
 
@@ -411,7 +432,7 @@ inline bool fwd_decode_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <=
 inline bool fwd_decode16_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <= kDecode16Rows; }
 
 template <int D, bool SPLIT, int WAVES, int BK>
-__global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p, const SegTable t) {
   using Tr = Fwd2Traits<D, WAVES, BK>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -419,17 +440,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c32 = lane & 31;
 
+  uint32_t wg = blockIdx.x, nwg = gridDim.x;
+  select_segment(p, t, wg, nwg);
   int qt, sp;
   int64_t bh;
   if (SPLIT) {
     // Workgroups that share a key chunk are adjacent logical ids on one XCD.
-    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t L = xcd_remap(wg, nwg);
     qt = (int)(L % (uint32_t)p.nqt);
     const uint32_t rest = L / (uint32_t)p.nqt;
     sp = (int)(rest % (uint32_t)p.splits);
     bh = rest / (uint32_t)p.splits;
   } else {
-    unsplit_tile(p, blockIdx.x, gridDim.x, bh, qt);
+    unsplit_tile(p, wg, nwg, bh, qt);
     sp = 0;
   }
 
@@ -811,14 +834,18 @@ static hipError_t launch_fwd16(const FwdParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// A plain launch passes an empty segment table.
+const SegTable kNoSegs{};
+
 template <int D, bool SPLIT, int WAVES, int BK>
-static hipError_t launch_fwd2_shape(const FwdParams &p, hipStream_t s) {
+static hipError_t launch_fwd2_shape(const FwdParams &p, const SegTable &t, hipStream_t s) {
   using Tr = Fwd2Traits<D, WAVES, BK>;
   const void *fn = reinterpret_cast<const void *>(&fwd2_kernel<D, SPLIT, WAVES, BK>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
-  const int64_t nblk = p.BH * (int64_t)p.nqt * p.splits;
-  hipLaunchKernelGGL((fwd2_kernel<D, SPLIT, WAVES, BK>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  const int64_t nblk = t.n > 0 ? (int64_t)t.end : p.BH * (int64_t)p.nqt * p.splits;
+  hipLaunchKernelGGL((fwd2_kernel<D, SPLIT, WAVES, BK>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p,
+                     t);
   return hipGetLastError();
 }
 
@@ -831,18 +858,18 @@ template <int D, bool SPLIT>
 static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
   static_assert(kFwdChunkTile % 128 == 0, "split chunks must hold whole 128-key tiles");
   if (fwd_decode16_shape(0, p.NQ)) return launch_fwd16<D, SPLIT>(p, s);
-  if (fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, s);
-  return launch_fwd2_shape<D, SPLIT, 8, D == 128 ? 128 : 64>(p, s);
+  if (fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, kNoSegs, s);
+  return launch_fwd2_shape<D, SPLIT, 8, D == 128 ? 128 : 64>(p, kNoSegs, s);
 }
 
 template <typename T, int D, bool SPLIT>
-static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t s) {
+static hipError_t launch_fwd_t(const FwdParams &p, const SegTable &t, hipStream_t s) {
   using Tr = FwdTraits<T, D>;
   const void *fn = reinterpret_cast<const void *>(&fwd_kernel<T, D, SPLIT>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
-  const int64_t nblk = p.BH * (int64_t)p.nqt * p.splits;
-  hipLaunchKernelGGL((fwd_kernel<T, D, SPLIT>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  const int64_t nblk = t.n > 0 ? (int64_t)t.end : p.BH * (int64_t)p.nqt * p.splits;
+  hipLaunchKernelGGL((fwd_kernel<T, D, SPLIT>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p, t);
   return hipGetLastError();
 }
 
@@ -859,8 +886,20 @@ hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s) {
     if (D == 128) return split ? launch_fwd2<128, true>(p, s) : launch_fwd2<128, false>(p, s);
     return split ? launch_fwd2<64, true>(p, s) : launch_fwd2<64, false>(p, s);
   }
-  if (D == 128) return split ? launch_fwd_t<float, 128, true>(p, s) : launch_fwd_t<float, 128, false>(p, s);
-  return split ? launch_fwd_t<float, 64, true>(p, s) : launch_fwd_t<float, 64, false>(p, s);
+  if (D == 128)
+    return split ? launch_fwd_t<float, 128, true>(p, kNoSegs, s) : launch_fwd_t<float, 128, false>(p, kNoSegs, s);
+  return split ? launch_fwd_t<float, 64, true>(p, kNoSegs, s) : launch_fwd_t<float, 64, false>(p, kNoSegs, s);
+}
+
+bool fwd_segment_shape(int dtype, int64_t NQ) { return !fwd_decode_shape(dtype, NQ); }
+
+hipError_t launch_fwd_segs(int dtype, int D, const FwdParams &p, const SegTable &t, hipStream_t s) {
+  if (dtype == 0) {
+    if (D == 128) return launch_fwd2_shape<128, false, 8, 128>(p, t, s);
+    return launch_fwd2_shape<64, false, 8, 64>(p, t, s);
+  }
+  if (D == 128) return launch_fwd_t<float, 128, false>(p, t, s);
+  return launch_fwd_t<float, 64, false>(p, t, s);
 }
 
 hipError_t launch_splitk_merge(const FwdParams &p, hipStream_t s) {

@@ -9,19 +9,55 @@ namespace skl {
 
 // Row addressing of one family of per-unit tensors.  A launch runs BH units
 // (one sequence of one head each); unit u starts at row
-// (u / H) * sb + (u % H) * sh of its tensors, rows of D elements (row
+// base + (u / H) * sb + (u % H) * sh of its tensors, rows of D elements (row
 // vectors: one element).  [B, H, N, D] tensors are unit after unit (row0 =
 // u * N: `dense`); a run of equal-length sequences packed per head
-// ([H, T, D], sequence length L, u = b * H + h) has sb = L and sh = T.
+// ([H, T, D], sequence length L, u = b * H + h, first sequence at packed row
+// R) has sb = L, sh = T and base = R.
 struct RowMap {
   int64_t sb, sh;
   int H;  // >= 1
+  int64_t base;
   __host__ __device__ int64_t row0(int64_t u) const {
     const uint32_t uu = (uint32_t)u, hh = (uint32_t)H;
-    return (int64_t)(uu / hh) * sb + (int64_t)(uu % hh) * sh;
+    return base + (int64_t)(uu / hh) * sb + (int64_t)(uu % hh) * sh;
   }
-  static RowMap dense(int64_t N) { return RowMap{N, 0, 1}; }
+  static RowMap dense(int64_t N) { return RowMap{N, 0, 1, 0}; }
 };
+
+// A launch over several runs of a packed batch.  The runs' workgroups follow
+// one another in the grid, segment i owning workgroups [start_i, start_i+1)
+// (the last up to `end`).  A segment carries the launch parameters that differ
+// between runs; the rest (pointers to the whole packed tensors, the per-head
+// row stride sh of the maps, H, scale, flags) come from the launch's params.
+struct Seg {
+  uint32_t start;  // first workgroup
+  int32_t tiles;   // query tiles (forward) per unit
+  int64_t units;   // sequences x heads
+  int64_t nq, nk;  // rows per sequence
+  int64_t oq, ok;  // packed row of the run's first sequence, queries / keys
+  int64_t u0;      // first unit of the run in the batch (per-unit sigma)
+  int64_t tq, tk;  // byte offset of the run's transposed query / key copies
+};
+constexpr int kMaxSegs = 32;
+struct SegTable {
+  int n;         // segments; 0: a plain launch (its params as given)
+  uint32_t end;  // workgroups of the launch
+  Seg seg[kMaxSegs];
+};
+// Segment of workgroup wg (t.n >= 1): the last one starting at or before wg.
+__host__ __device__ inline int seg_index(const SegTable &t, uint32_t wg) {
+  int lo = 0, hi = t.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.seg[mid].start <= wg) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+__host__ __device__ inline uint32_t seg_count(const SegTable &t, int i) {
+  return (i + 1 < t.n ? t.seg[i + 1].start : t.end) - t.seg[i].start;
+}
 
 struct FwdParams {
   const void *q1, *k1, *q2, *k2;  // unit rows of NQ|NK x D in the input dtype (qmap / kmap)
@@ -68,17 +104,38 @@ int fwd_block_queries(int dtype, int D, int64_t NQ);
 
 // dtype: 0 = bf16, 1 = fp32.  Return the launch status.
 hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s);
+// Unsplit forward over the segments of t (t.n >= 1), in one launch of t.end
+// workgroups.  Every segment must have fwd_segment_shape(dtype, nq) and
+// tiles = ceil(nq / fwd_block_queries(dtype, D, nq)); p supplies the whole
+// packed tensors, the maps' sh and H, scale and causal.
+bool fwd_segment_shape(int dtype, int64_t NQ);
+hipError_t launch_fwd_segs(int dtype, int D, const FwdParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_splitk_merge(const FwdParams &p, hipStream_t s);
 // Backward pieces; `p.sigma` must point at the prepared per-(b,h) factors.
 hipError_t launch_grad_scale(int dtype, const float *g, RowMap qmap, int64_t BH, int64_t NQ, float *sigma,
                              hipStream_t s);
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s);
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s);
+// Either pass over the segments of t (t.n >= 1) in one launch of t.end
+// workgroups, segment i holding units * ceil(resident rows / kBwdBR) of them
+// (resident rows: nk for the dK pass, nq for the dQ pass; p.splits == 1).
+// p supplies the whole packed tensors, the maps' sh and H, sigma and the
+// transposed copies of the whole batch (each run's at its tq / tk offset).
+hipError_t launch_bwd_dk_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s);
+hipError_t launch_bwd_dq_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_zero(float *dst, int64_t n, hipStream_t s);
 // dQ1 / dQ2 (the requested ones) = sum over the key chunks of p.dqp, in chunk order.
 hipError_t launch_dq_reduce(int D, const BwdParams &p, hipStream_t s);
 // bf16 inputs: transposed fp16 copy of x (BH units of N rows, addressed by `map`)
 // into out [BH][ceil(N/64)][D][64].
 hipError_t launch_bwd_transpose(int D, const void *x, RowMap map, int64_t BH, int64_t N, void *out, hipStream_t s);
+// The prepare step over the segments of t: sigma of every segment's units at
+// sigma + u0 (one workgroup per unit), and transposed copies of x (`keys`:
+// the key rows nk / ok, copies at out + tk bytes; else nq / oq / tq) with one
+// workgroup per unit and 64-row tile.  qmap / map supply sh and H.
+hipError_t launch_grad_scale_segs(int dtype, const float *g, RowMap qmap, const SegTable &t, float *sigma,
+                                  hipStream_t s);
+hipError_t launch_bwd_transpose_segs(int D, const void *x, RowMap map, int keys, const SegTable &t, void *out,
+                                     hipStream_t s);
 
 }  // namespace skl

@@ -157,8 +157,8 @@ def parse():
     ap.add_argument("--other-configs", action="store_true",
                     help="also time forward and backward on the other workloads (causal_4k, noncausal_16k, "
                          "splitk_bwd_128k, shortq_bwd_64k, causal_16k_d64, causal_4k_fp32), the decode split-K "
-                         "forward and the packed "
-                         "variable-length batch, and report them under \"other_configs\"")
+                         "forward and the packed variable-length batches (varlen_mix, varlen_short), and "
+                         "report them under \"other_configs\"")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (scale reference for HBM byte counters)")
@@ -370,6 +370,7 @@ def main():
                                           "causal_16k_d64", "causal_4k_fp32")}
         out["other_configs"]["decode_128k"] = splitk_bench(skl, synth, torch, args, "decode_128k")
         out["other_configs"]["varlen_mix"] = varlen_bench(skl, synth, torch, args, "varlen_mix")
+        out["other_configs"]["varlen_short"] = varlen_bench(skl, synth, torch, args, "varlen_short")
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q1, k1, q2, k2, args.cpu_seconds)

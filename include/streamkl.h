@@ -232,8 +232,18 @@ streamkl_status streamkl_bwd_dq(const streamkl_problem *p,
  *    with queries > 0, causal with more queries than keys, or per-sequence
  *    sizes past the 32-bit limits.
  * Sequences with no query rows produce nothing in the forward and zero key
- * gradients in the backward.  Consecutive sequences of equal lengths run in
- * one launch per kernel; runs follow one another on `stream`.
+ * gradients in the backward.  Consecutive sequences of equal lengths form a
+ * run.  The runs share launches: each kernel runs over up to 32 runs at once
+ * (longest first), so that batches of many short sequences still fill the
+ * GPU.  Exceptions launch per run, after the shared launches:
+ *  - bf16 runs of at most 32 queries per sequence (the forward's one-wave
+ *    shapes);
+ *  - in the backward, when the whole batch has fewer than 256 query tiles of
+ *    128 rows, runs whose own problem would split the query-gradient pass's
+ *    keys (see streamkl_bwd_workspace_size).
+ * Each sequence's results are those of streamkl_fwd / streamkl_bwd on that
+ * sequence alone (the same bits, except dQ where the stand-alone call would
+ * split its keys, which changes only the fp32 summation order).
  */
 typedef struct {
     int64_t B, H;                  /* sequences, heads */
@@ -253,9 +263,14 @@ streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v,
                                     void *stream);
 
 /*
- * Workspace bytes for streamkl_bwd_varlen: the largest full-size
- * streamkl_bwd workspace among the runs of equal-length sequences, since the
- * runs reuse it one after another.  Returns 0 if `v` is invalid.
+ * Workspace bytes for streamkl_bwd_varlen.  The workspace holds:
+ *  - sigma for every (sequence, head): B * H fp32 in a slot rounded to 256 bytes;
+ *  - for bf16 inputs, the four tensors' transposed fp16 copies of every run
+ *    in the shared launches (laid out as streamkl_bwd's, one run after
+ *    another, each run's rounded to 256 bytes).
+ * If larger, it is instead the largest full-size streamkl_bwd workspace of a
+ * run launched on its own (those reuse the front of the workspace one after
+ * another).  Returns 0 if `v` is invalid.
  */
 size_t streamkl_bwd_varlen_workspace_size(const streamkl_varlen_problem *v);
 

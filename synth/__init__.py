@@ -199,12 +199,16 @@ def _mixed_lengths(n: int, lo: int, hi: int, seed: int) -> tuple:
 
 
 _MIX = _mixed_lengths(16, 1024, 7168, 77)
+_SHORT = _mixed_lengths(256, 64, 1024, 78)
 
 PACKED: Dict[str, PackedBatch] = {
     pb.name: pb for pb in [
         # 16 causal sequences of 1K-7K tokens (seeded uniform lengths), 32 heads: a
         # packed long-context batch without padding.
         PackedBatch(20, "varlen_mix", 32, _MIX, _MIX, 128, "bf16", True),
+        # 256 causal sequences of 64-1024 tokens, 16 heads: many short sequences,
+        # each far too small to fill the GPU on its own.
+        PackedBatch(21, "varlen_short", 16, _SHORT, _SHORT, 128, "bf16", True),
     ]
 }
 

@@ -246,18 +246,46 @@ def test_varlen_validation(L):
     assert vfwd(L, VP([0, 0, 0], [0, 4, 9]), q1=None, kl=None) == _lib.STREAMKL_OK
 
 
+def varlen_bf16_workspace(B, H, D, runs):
+    # sigma of every (sequence, head) (256-byte slot), then the four tensors'
+    # transposed copies of the runs that join the segmented passes (each run's
+    # copy rounded to 256 bytes), or, if larger, the largest remaining run's own
+    # streamkl_bwd workspace.  All runs join when the batch has at least 256
+    # query tiles of 128 rows; otherwise those whose own query pass would split
+    # its keys run alone.
+    up = lambda n, a: (n + a - 1) // a * a
+    tiles = lambda n: (n + 63) // 64
+    fills = sum(b * H * ((nq + 127) // 128) for b, nq, nk in runs) >= 256
+    seg = up(max(16, 4 * B * H), 256)
+    solo = 16
+    for b, nq, nk in runs:
+        if not fills and dq_splits(b, H, nq, nk) > 1:
+            solo = max(solo, bf16_workspace(b, H, nq, nk, D))
+        else:
+            seg += 2 * up(b * H * tiles(nq) * 64 * D * 2, 256) + 2 * up(b * H * tiles(nk) * 64 * D * 2, 256)
+    return max(seg, solo)
+
+
 def test_varlen_backward_validation(L):
-    # Runs of equal lengths: (3,3) x2, (64,200), (0,7), (65,65).  The workspace is the
-    # largest run's full-size streamkl_bwd workspace.
+    # Runs of equal lengths: (3,3) x2, (64,200), (0,7), (65,65).  The (3,3) run joins
+    # the segmented passes; (64,200) and (65,65) split their query pass's keys
+    # and run on their own.
     cu_q = [0, 3, 6, 70, 70, 135]
     cu_k = [0, 3, 6, 206, 213, 278]
     v = VP(cu_q, cu_k, H=3, D=128)
     need = L.streamkl_bwd_varlen_workspace_size(v.ref())
     runs = [(2, 3, 3), (1, 64, 200), (1, 65, 65)]
-    assert need == max(bf16_workspace(b, 3, nq, nk, 128) for b, nq, nk in runs)
+    assert [dq_splits(b, 3, nq, nk) > 1 for b, nq, nk in runs] == [False, True, True]
+    assert need == varlen_bf16_workspace(5, 3, 128, runs)
+    # A batch of 448 query tiles: every run joins, although the (300, 300) run
+    # alone would split.
+    v2 = VP([0, 300, 600, 1600], [0, 300, 600, 1600], H=32, D=64)
+    runs2 = [(2, 300, 300), (1, 1000, 1000)]
+    assert dq_splits(2, 32, 300, 300) > 1
+    assert L.streamkl_bwd_varlen_workspace_size(v2.ref()) == varlen_bf16_workspace(3, 32, 64, runs2)
     f32 = VP(cu_q, cu_k, H=3, D=128, dtype=_lib.STREAMKL_FP32)
-    # fp32: sigma only, for the largest run (2 sequences x 3 heads, rounded to 16 bytes).
-    assert L.streamkl_bwd_varlen_workspace_size(f32.ref()) == 32
+    # fp32: sigma only, for all 5 x 3 (sequence, head) pairs in a 256-byte slot.
+    assert L.streamkl_bwd_varlen_workspace_size(f32.ref()) == 256
     assert L.streamkl_bwd_varlen_workspace_size(VP([2, 3], [0, 3]).ref()) == 0
     assert vbwd(L, v, wsb=need - 1) == _lib.STREAMKL_ERR_WORKSPACE
     assert vbwd(L, v, ws=None) == _lib.STREAMKL_ERR_WORKSPACE

@@ -111,6 +111,87 @@ def test_varlen_equal_lengths_equal_dense(causal):
         assert torch.equal(a, unpack(b))
 
 
+def test_varlen_segmented_equal_lengths_equal_dense():
+    # 3 x 16 x 6 = 288 query tiles fill the GPU, so the packed batch takes the
+    # segmented passes (one launch over all runs); with equal lengths it is the
+    # dense problem with another layout and must give the same bits.
+    B, H, N, D = 3, 16, 700, 64
+    print(f"segmented varlen vs dense B={B} H={H} N={N}", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(8)
+    dense = [torch.randn(B, H, N, D, generator=gen).to(torch.bfloat16).to(DEV) for _ in range(4)]
+    g = (torch.rand(B, H, N, generator=gen) - 0.3).to(DEV)
+    pack = lambda t: t.transpose(0, 1).reshape(H, B * N, *t.shape[3:]).contiguous()
+    unpack = lambda t: t.reshape(H, B, N, *t.shape[2:]).transpose(0, 1)
+    out_d = streamkl_fwd(*dense, None, True)
+    grads_d = streamkl_bwd(*dense, *out_d, g, None, True)
+    cu = [0, N, 2 * N, 3 * N]
+    packed = [pack(t) for t in dense]
+    out_v = streamkl_fwd_varlen(*packed, cu, cu, None, True)
+    grads_v = streamkl_bwd_varlen(*packed, cu, cu, *out_v, pack(g), None, True)
+    torch.cuda.synchronize()
+    for a, b in zip(out_d, out_v):
+        assert torch.equal(a, unpack(b))
+    for a, b in zip(grads_d, grads_v):
+        assert torch.equal(a, unpack(b))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_varlen_many_runs(dt):
+    # 43 runs: more than one segmented launch holds (32 segments), runs of the
+    # main forward shape mixed with decode-shaped ones (at most 32 queries), a
+    # query-less sequence and a run of two equal sequences; 8 heads give 376
+    # query tiles, so every run joins the segmented backward passes.
+    # (fp32 has no decode shape; its shortest sequence has 6 queries, since the
+    # error measure of a one-row slice is that row's relative KL error, which
+    # fp32 cancellation in a KL near 0.02 takes past 1e-5 in any launch.)
+    H, D, causal = 8, 64, True
+    lens_q = [33 + 3 * i for i in range(36)] + [1 if dt == "bf16" else 6, 16, 32, 0, 5, 20, 90, 90]
+    lens_k = [n + (i % 5) * 7 for i, n in enumerate(lens_q)]
+    lens_k[39] = 11
+    lens_k[43] = lens_k[42]
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    print(f"varlen {len(lens_q)} sequences {dt}", flush=True)
+    q1, k1, q2, k2 = _packed(lens_q, lens_k, H, D, dtype, seed=21)
+    cq, ck = _cu(lens_q), _cu(lens_k)
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd_varlen(q1, k1, q2, k2, cq, ck, scale, causal)
+    gen = torch.Generator(device="cpu").manual_seed(12)
+    g = (torch.randn(H, cq[-1], generator=gen) * 1e-3).to(DEV).contiguous()
+    grads = streamkl_bwd_varlen(q1, k1, q2, k2, cq, ck, kl, l1, l2, g, scale, causal)
+    torch.cuda.synchronize()
+    heads = [(0, h) for h in range(H)]
+    for b in range(len(lens_q)):
+        q0, qe, k0, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if qe == q0:
+            for dk in (grads[1], grads[3]):
+                assert torch.count_nonzero(dk[:, k0:ke]).item() == 0
+            continue
+        S = _seq
+        sq = [S(q1, q0, qe), S(k1, k0, ke), S(q2, q0, qe), S(k2, k0, ke)]
+        errs = compare_forward(*sq, scale, causal, S(kl, q0, qe), S(l1, q0, qe), S(l2, q0, qe), heads)
+        assert_within(errs, TOL[dt], f"varlen many-run fwd seq {b} ({qe - q0}x{ke - k0}) {dt}")
+        sg = [S(grads[0], q0, qe), S(grads[1], k0, ke), S(grads[2], q0, qe), S(grads[3], k0, ke)]
+        errs = compare_backward(*sq, scale, causal, S(g, q0, qe), sg, heads)
+        assert_within(errs, TOL[dt], f"varlen many-run bwd seq {b} ({qe - q0}x{ke - k0}) {dt}")
+        if b in (0, 35, 36, 38, 42):
+            # The same sequence as a dense problem of its own: the same bits
+            # forward and for dK.  The dense dQ pass of so few query tiles
+            # splits its keys and sums the chunks' partials afterwards, so dQ
+            # differs by fp32 summation order only.
+            dq = [t.contiguous() for t in sq]
+            out_d = streamkl_fwd(*dq, scale, causal)
+            gd = S(g, q0, qe).contiguous()
+            grads_d = streamkl_bwd(*dq, *out_d, gd, scale, causal)
+            torch.cuda.synchronize()
+            for a, c in zip(out_d, (S(kl, q0, qe), S(l1, q0, qe), S(l2, q0, qe))):
+                assert torch.equal(a, c), b
+            for i in (1, 3):
+                assert torch.equal(grads_d[i], sg[i]), b
+            for i in (0, 2):
+                d = (grads_d[i] - sg[i]).abs().max().item() / sg[i].abs().max().item()
+                assert d <= 1e-5, (b, i, d)
+
+
 def test_varlen_teacher_or_student_only():
     lens_q, lens_k = [130, 0, 77], [200, 9, 77]
     H, D = 2, 128
