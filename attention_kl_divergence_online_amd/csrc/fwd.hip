@@ -13,6 +13,9 @@
 //    one query: each lane keeps its own online state over its keys of a
 //    block, no cross-lane reduction happens inside the loop, and the lanes
 //    sharing a query are merged once at the end;
+//  * bf16 inputs fold fully visible blocks against the maxima a lane already
+//    holds (no block maximum, no rescale) and fall back to the exact update
+//    only when a block's sums grow past 2^24;
 //  * the resident queries' Q1/Q2 fragments stay in registers for the whole
 //    pass; key tiles stream through double-buffered LDS (or, for at most 16
 //    queries, straight into registers);
@@ -424,6 +427,9 @@ struct Fwd2Traits {
   static_assert((BK == 128 || BK == 64 || BK == 32) && NT % 64 == 0, "tiles");
 };
 
+// Bound on a lane's per-block sum in the forward's lazy update (2^24).
+constexpr float kLazySumMax = 16777216.f;
+
 // Queries per head at or below which bf16 inputs take the one-wave shapes:
 // 16x16 products up to 16 queries, 32x32 products up to 32.
 constexpr int kDecodeRows = 32;
@@ -541,6 +547,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p, const 
     else
       online_update<true, false>(s1, s2, st, c, kbase, h, klim);
   };
+  // Fully visible block after the first: the exponentials are taken against
+  // the maxima the lane holds, with no new maxima and no rescaling.  The
+  // running sums stay sums of exp2((x - m) c) for the held m, which is all
+  // the combine step needs; m only has to keep them finite.  If some lane's
+  // block sum of either distribution exceeds 2^24 (or is not a number) the
+  // whole wave folds the block again with the exact update, which raises the
+  // maxima; otherwise every term of the block is at most 2^24 and the sums
+  // grow by at most that much per block.
+  auto lazy_update = [&](const f32x16 &x1, const f32x16 &x2) {
+    const float b1 = st.m1 * c, b2 = st.m2 * c;
+    float s1 = 0.f, s2 = 0.f, sa = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e1 = fast_exp2(__builtin_fmaf(x1[r], c, -b1));
+      const float e2 = fast_exp2(__builtin_fmaf(x2[r], c, -b2));
+      s1 += e1;
+      s2 += e2;
+      sa = __builtin_fmaf(e1, x1[r] - x2[r], sa);
+    }
+    if (__builtin_expect(__any(!(s1 <= kLazySumMax && s2 <= kLazySumMax)), 0)) {
+      online_update<false, false>(x1, x2, st, c, 0, h, 0);
+    } else {
+      st.l1 += s1;
+      st.l2 += s2;
+      st.acc += sa;
+    }
+  };
 
   if (ntiles > 0) {
     load_tile(0);
@@ -557,9 +590,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p, const 
     for (int kb = 0; kb < Tr::BPT; ++kb) {
       const int b = Tr::BPT * t + kb;
       f32x16 n1, n2;
-      if (b < nfull && b > 0) {
+      if (b < nfull && b > 1) {
         scores(b, n1, n2);
-        online_update<false, false>(p1, p2, st, c, k_lo + (b - 1) * 32, h, 0);
+        lazy_update(p1, p2);
+      } else if (b == 1 && nfull > 1) {
+        scores(b, n1, n2);
+        online_update<false, false>(p1, p2, st, c, k_lo, h, 0);
       } else {
         if (b < nlive) scores(b, n1, n2);
         if (b > 0 && b - 1 < nlive) update(b - 1, p1, p2);

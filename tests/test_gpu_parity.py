@@ -123,6 +123,38 @@ def test_peaked_rows_large_kl(dtype, D, scale, causal):
         assert torch.isfinite(t).all()
 
 
+@pytest.mark.parametrize("slope", [0.2, -0.2])
+@pytest.mark.parametrize("causal", [False, True])
+def test_monotone_logits_held_maxima(slope, causal):
+    # Keys along one direction with a steady rise (or fall) along the key
+    # index: each raw logit differs from the previous key's by about
+    # 2.3 * slope / 0.2, so with rising logits the maxima a lane holds go
+    # stale by far more than 2^24 within a few 32-key blocks (the forward
+    # folds those blocks again exactly), and with falling logits the first
+    # block holds the maxima and later terms underflow.
+    B, H, NQ, NK, D = 1, 2, 260, 1100, 128
+    print(f"monotone logits slope={slope} causal={causal}", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(int(100 * slope) + causal)
+    u = torch.randn(D, generator=gen)
+    u = u / u.norm()
+    j = torch.arange(NK, dtype=torch.float32)[:, None]
+    q1 = 11.3 * u + 0.5 * torch.randn(B, H, NQ, D, generator=gen)
+    q2 = 11.3 * u + 0.5 * torch.randn(B, H, NQ, D, generator=gen)
+    k1 = slope * j * u + 0.3 * torch.randn(B, H, NK, D, generator=gen)
+    k2 = 0.8 * slope * j * u + 0.3 * torch.randn(B, H, NK, D, generator=gen)
+    q1, k1, q2, k2 = (t.to(torch.bfloat16).to(DEV).contiguous() for t in (q1, k1, q2, k2))
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    kls, l1s, l2s = streamkl_fwd_splitk(q1, k1, q2, k2, 3, scale, causal)
+    torch.cuda.synchronize()
+    heads = _heads(B, H)
+    case = f"monotone slope={slope} causal={causal}"
+    assert kl.max().item() > 0.05  # teacher and student spread differently
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"], f"fwd {case}")
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kls, l1s, l2s, heads), TOL["bf16"],
+                  f"split fwd {case}")
+
+
 def test_backward_steps_equal_combined_call():
     from attention_kl_divergence_online_amd import streamkl_bwd_dk, streamkl_bwd_dq, streamkl_bwd_prepare
     q1, k1, q2, k2 = _rand(2, 2, 300, 400, 128, torch.bfloat16, seed=12)
