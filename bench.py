@@ -160,6 +160,9 @@ def parse():
                          "forward and the packed variable-length batches (varlen_mix, varlen_short), and "
                          "report them under \"other_configs\"")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--materialised-heads", type=int, default=2,
+                    help="(b, h) slices on which to time the PyTorch materialise-then-reduce baseline "
+                         "(scaled to the whole batch; 0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (scale reference for HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
@@ -372,10 +375,86 @@ def main():
         out["other_configs"]["varlen_mix"] = varlen_bench(skl, synth, torch, args, "varlen_mix")
         out["other_configs"]["varlen_short"] = varlen_bench(skl, synth, torch, args, "varlen_short")
 
+    if args.materialised_heads > 0:
+        mat = materialised_baseline(torch, w, q1, k1, q2, k2, g, kl, args.materialised_heads)
+        mat["fwd_speedup_fused"] = round(mat["fwd_ms"] / fwd_ms, 1)
+        mat["fwd_bwd_speedup_fused"] = round(mat["fwd_bwd_ms"] / ms_step, 1)
+        out["materialised_baseline"] = mat
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q1, k1, q2, k2, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def materialised_rows(nk: int) -> int:
+    """Query rows per block of the materialised baseline: at most 2^30 logits per matrix."""
+    return max(1, (1 << 30) // max(1, nk))
+
+
+def materialised_baseline(torch, w, q1, k1, q2, k2, g, kl_fused, heads: int):
+    """PyTorch materialise-then-reduce on the GPU, head by head and in blocks
+    of query rows (at most 2^30 logits per matrix): both fp32 logit matrices,
+    log-softmax, KL = sum P1 (log P1 - log P2) per row, and its autograd
+    backward to all four inputs.  Timed on `heads` (b, h) slices after one
+    untimed slice and scaled to the whole batch; the whole problem's P1 and P2
+    would not fit in device memory.  Context for the fused path, not a
+    reference: parity is held against the oracle."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    NQ, NK = w.NQ, w.NK
+    off = NK - NQ
+    rows = min(NQ, materialised_rows(NK))
+
+    def one(b, h, grad):
+        ins = [t[b, h].float().requires_grad_(grad) for t in (q1, k1, q2, k2)]
+        a1, c1, a2, c2 = ins
+        c1t, c2t = c1.t().contiguous(), c2.t().contiguous()
+        parts = []
+        for r0 in range(0, NQ, rows):
+            r1 = min(NQ, r0 + rows)
+            with torch.set_grad_enabled(grad):
+                s1 = (a1[r0:r1] @ c1t) * w.scale
+                s2 = (a2[r0:r1] @ c2t) * w.scale
+                if w.causal:  # a large finite fill keeps 0 * (l1 - l2) at 0 on masked keys
+                    mask = (torch.arange(NK, device=s1.device)[None, :] >
+                            torch.arange(r0, r1, device=s1.device)[:, None] + off)
+                    s1 = s1.masked_fill(mask, -1e30)
+                    s2 = s2.masked_fill(mask, -1e30)
+                l1 = torch.log_softmax(s1, dim=-1)
+                l2 = torch.log_softmax(s2, dim=-1)
+                del s1, s2
+                kl = (l1.exp() * (l1 - l2)).sum(dim=-1)
+                del l1, l2
+                if grad:
+                    (g[b, h, r0:r1] * kl).sum().backward()
+            parts.append(kl.detach())
+        return torch.cat(parts)
+
+    units = [(u // w.H, u % w.H) for u in range(w.B * w.H)]
+    timed = units[:heads]
+    one(*units[-1], False)
+    one(*units[-1], True)
+    torch.cuda.synchronize()
+    worst = 0.0
+    res = {}
+    for grad in (False, True):
+        e0, e1 = ev(), ev()
+        e0.record()
+        outs = [one(b, h, grad) for b, h in timed]
+        e1.record()
+        torch.cuda.synchronize()
+        res["fwd_bwd" if grad else "fwd"] = e0.elapsed_time(e1) * len(units) / len(timed)
+        for (b, h), o in zip(timed, outs):
+            ref = kl_fused[b, h]
+            worst = max(worst, ((o - ref).abs().max() / ref.abs().max().clamp_min(1e-30)).item())
+        del outs
+    torch.cuda.empty_cache()
+    return {"kind": "pytorch materialise-then-reduce (fp32 logits from the bf16 inputs, log_softmax, "
+                    "autograd backward), head by head in blocks of query rows",
+            "heads_timed": len(timed), "scaled_to_heads": len(units),
+            "fwd_ms": round(res["fwd"], 1), "fwd_bwd_ms": round(res["fwd_bwd"], 1),
+            "kl_max_rel_diff_vs_fused": float(f"{worst:.3g}"),
+            "peak_alloc_bytes": torch.cuda.max_memory_allocated()}
 
 
 def config_bench(skl, synth, torch, args, name):
