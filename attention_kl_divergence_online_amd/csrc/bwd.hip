@@ -114,7 +114,12 @@ __device__ __forceinline__ void query_stats(float lse1, float lse2, float kl, fl
 template <bool KEYS_RES>
 __device__ __forceinline__ void resident_tile(const BwdParams &p, int nrt, int S, uint32_t w, uint32_t n,
                                               int64_t &bh, int &rt, int &sp) {
-  const uint32_t L = xcd_remap(w, n);
+  // Causal tiles differ in work: when the heads do not divide evenly over the
+  // XCDs, contiguous runs would give some XCDs only the heavy tiles of a head,
+  // so the tiles are dealt round the XCDs in launch order instead (measured
+  // 37% faster at 4 heads of 64K, 11% at 12 heads of 32K, and a backward in
+  // one-head groups as fast as with every head's copies).
+  const uint32_t L = p.causal && p.BH % kXcds != 0 ? w : xcd_remap(w, n);
   if (p.causal && S == 1 && nrt <= kLongestFirstTiles && p.BH % kXcds == 0) {
     const uint32_t hx = (uint32_t)(p.BH / kXcds), per = hx * (uint32_t)nrt;
     const uint32_t i = L % per;

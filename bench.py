@@ -364,6 +364,32 @@ def main():
         "memory": memory,
     }
 
+    # The same backward through the combined call with smaller workspaces:
+    # sigma plus the operand copies of a group of heads, made and consumed a
+    # group at a time, instead of copies of every head (the smallest accepted
+    # size holds one head's copies; sizes grow linearly with the group).
+    ws_full = nbytes(ws)
+    del ws
+    torch.cuda.empty_cache()
+    ws_lo = skl.bwd_workspace_size_min(q1, k1, w.scale, w.causal)
+    per_head = (ws_full - ws_lo) // max(1, w.B * w.H - 1)
+    small = []
+    for heads in (1, 4, 8):
+        if heads >= w.B * w.H:
+            break
+        ws_small = torch.empty(max(16, ws_lo + (heads - 1) * per_head), dtype=torch.uint8, device=dev)
+        skl.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws_small, out=grads)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(2):
+            skl.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws_small, out=grads)
+        e1.record()
+        torch.cuda.synchronize()
+        small.append({"heads_per_group": heads, "workspace_bytes": nbytes(ws_small),
+                      "bwd_ms": round(e0.elapsed_time(e1) / 2, 3)})
+        del ws_small
+    out["bwd_small_workspace"] = small
+
     if not args.no_splitk:
         out["splitk"] = splitk_bench(skl, synth, torch, args)
 
