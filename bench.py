@@ -154,6 +154,8 @@ def parse():
     ap.add_argument("--workload", default="causal_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-splitk", action="store_true")
+    ap.add_argument("--no-small-workspace", action="store_true",
+                    help="skip timing the backward with one-, four- and eight-head workspaces")
     ap.add_argument("--other-configs", action="store_true",
                     help="also time forward and backward on the other workloads (causal_4k, noncausal_16k, "
                          "splitk_bwd_128k, shortq_bwd_64k, causal_16k_d64, causal_4k_fp32), the decode split-K "
@@ -374,7 +376,7 @@ def main():
     ws_lo = skl.bwd_workspace_size_min(q1, k1, w.scale, w.causal)
     per_head = (ws_full - ws_lo) // max(1, w.B * w.H - 1)
     small = []
-    for heads in (1, 4, 8):
+    for heads in (() if args.no_small_workspace else (1, 4, 8)):
         if heads >= w.B * w.H:
             break
         ws_small = torch.empty(max(16, ws_lo + (heads - 1) * per_head), dtype=torch.uint8, device=dev)
@@ -388,7 +390,8 @@ def main():
         small.append({"heads_per_group": heads, "workspace_bytes": nbytes(ws_small),
                       "bwd_ms": round(e0.elapsed_time(e1) / 2, 3)})
         del ws_small
-    out["bwd_small_workspace"] = small
+    if small:
+        out["bwd_small_workspace"] = small
 
     if not args.no_splitk:
         out["splitk"] = splitk_bench(skl, synth, torch, args)
