@@ -560,19 +560,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p, const 
   // whole wave folds the block again with the exact update, which raises the
   // maxima; otherwise every term of the block is at most 2^24 and the sums
   // grow by at most that much per block.
+  float hb1 = 0.f, hb2 = 0.f;  // held maxima times c, refreshed after every exact update before a lazy one
   auto lazy_update = [&](const f32x16 &x1, const f32x16 &x2) {
-    const float b1 = st.m1 * c, b2 = st.m2 * c;
-    float s1 = 0.f, s2 = 0.f, sa = 0.f;
+    float s1 = fast_exp2(__builtin_fmaf(x1[0], c, -hb1));
+    float s2 = fast_exp2(__builtin_fmaf(x2[0], c, -hb2));
+    float sa = s1 * (x1[0] - x2[0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e1 = fast_exp2(__builtin_fmaf(x1[r], c, -b1));
-      const float e2 = fast_exp2(__builtin_fmaf(x2[r], c, -b2));
+    for (int r = 1; r < 16; ++r) {
+      const float e1 = fast_exp2(__builtin_fmaf(x1[r], c, -hb1));
+      const float e2 = fast_exp2(__builtin_fmaf(x2[r], c, -hb2));
       s1 += e1;
       s2 += e2;
       sa = __builtin_fmaf(e1, x1[r] - x2[r], sa);
     }
     if (__builtin_expect(__any(!(s1 <= kLazySumMax && s2 <= kLazySumMax)), 0)) {
       online_update<false, false>(x1, x2, st, c, 0, h, 0);
+      hb1 = st.m1 * c;
+      hb2 = st.m2 * c;
     } else {
       st.l1 += s1;
       st.l2 += s2;
@@ -601,6 +605,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p, const 
       } else if (b == 1 && nfull > 1) {
         scores(b, n1, n2);
         online_update<false, false>(p1, p2, st, c, k_lo, h, 0);
+        hb1 = st.m1 * c;
+        hb2 = st.m2 * c;
       } else {
         if (b < nlive) scores(b, n1, n2);
         if (b > 0 && b - 1 < nlive) update(b - 1, p1, p2);
