@@ -67,6 +67,8 @@ SMALL = [
     (2, 1, 16, 77, 64, True),      # bf16: 16x16-product forward shape at its 16-query limit
     (1, 2, 32, 200, 64, True),     # bf16: one-wave forward shape at its 32-query limit
     (1, 1, 33, 97, 128, False),    # bf16: one query past it (8-wave shape, one live wave)
+    (3, 4, 300, 520, 128, True),   # 12 heads: causal backward tiles dealt round the XCDs, forward in runs
+    (2, 4, 520, 520, 64, True),    # 8 heads: whole heads per XCD
 ]
 
 
