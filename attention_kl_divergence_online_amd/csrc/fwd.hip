@@ -591,7 +591,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p, const 
   __syncthreads();
 
   // Step b: logits of block b and the update of block b - 1.  Both blocks of
-  // a tile are fully visible in the steady state, which runs without branches.
+  // a tile are fully visible in the steady state, which runs without mask
+  // code; its one branch is the lazy update's rarely taken exact refold.
   f32x16 p1 = f32x16{}, p2 = f32x16{};
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) load_tile(t + 1);
