@@ -428,3 +428,32 @@ def test_causal_4k_fp32_full_size():
 def test_decode_128k_full_size():
     # Every one of the 16 rows of two heads, and the backward of the decode shape.
     _full_size("decode_128k", rows_per_head=16)
+
+
+def _sweep_cases(n=24, seed=2026):
+    # Seeded draws of small problems: ragged lengths on both sides, NQ <= NK
+    # when causal, both head sizes, a few heads and batches.
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        causal = bool(rng.integers(0, 2))
+        nk = int(rng.integers(1, 900))
+        nq = int(rng.integers(1, nk + 1)) if causal else int(rng.integers(1, 900))
+        cases.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), nq, nk, int(rng.choice([64, 128])), causal))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,NQ,NK,D,causal", _sweep_cases())
+def test_seeded_shape_sweep_bf16(B, H, NQ, NK, D, causal):
+    print(f"sweep B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal}", flush=True)
+    q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, torch.bfloat16, seed=NQ * 13 + NK * 7 + D + causal)
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    gen = torch.Generator(device="cpu").manual_seed(NQ + NK)
+    g = torch.rand(B, H, NQ, generator=gen).mul_(2).sub_(0.5).to(DEV)
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal)
+    torch.cuda.synchronize()
+    heads = _heads(B, H)
+    case = f"sweep B{B} H{H} NQ{NQ} NK{NK} D{D} causal={causal}"
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"], f"fwd {case}")
+    assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, grads, heads), TOL["bf16"], f"bwd {case}")
