@@ -32,7 +32,8 @@ __all__ = ["streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd", "streamkl_bwd_
            "streamkl_bwd_dq", "attention_kl",
            "streamkl_fwd_varlen", "streamkl_bwd_varlen", "varlen_problem_for", "bwd_varlen_workspace_size",
            "attention_kl_varlen",
-           "StreamKLError", "problem_for", "fwd_splitk_workspace_size", "bwd_workspace_size"]
+           "StreamKLError", "problem_for", "fwd_splitk_workspace_size", "bwd_workspace_size",
+           "streamkl_probe_mfma_bf16"]
 
 _DTYPES = {torch.bfloat16: _lib.STREAMKL_BF16, torch.float32: _lib.STREAMKL_FP32}
 
@@ -339,3 +340,13 @@ def attention_kl_varlen(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, scale: Optio
                         causal: bool = False) -> torch.Tensor:
     """Differentiable per-row KL(P1||P2) of a packed batch ([H, T, D] inputs), [H, TQ] fp32."""
     return _AttentionKLVarlen.apply(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, scale, causal)
+
+
+def streamkl_probe_mfma_bf16(iters: int, workgroups: int, sink: torch.Tensor) -> None:
+    """Enqueue the matrix-rate probe on the current stream (workgroups * 4 *
+    iters * 4 * 32768 flop); `sink` is a float32 device tensor of at least
+    workgroups * 4 elements.  The caller times it with events."""
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < 4 * int(workgroups):
+        raise ValueError("sink must be a float32 device tensor of at least 4 * workgroups elements")
+    st = _lib.lib().streamkl_probe_mfma_bf16(int(iters), int(workgroups), _ptr(sink), _stream_handle(sink.device))
+    _lib.check(st, "streamkl_probe_mfma_bf16")

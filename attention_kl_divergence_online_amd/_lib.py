@@ -39,6 +39,7 @@ EXPORTS = (
     "streamkl_bwd_varlen",
     "streamkl_status_string",
     "streamkl_version",
+    "streamkl_probe_mfma_bf16",
 )
 
 
@@ -119,6 +120,8 @@ def lib() -> ctypes.CDLL:
         L.streamkl_status_string.restype = ctypes.c_char_p
         L.streamkl_version.argtypes = []
         L.streamkl_version.restype = ctypes.c_int
+        L.streamkl_probe_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int64, vp, vp]
+        L.streamkl_probe_mfma_bf16.restype = ctypes.c_int
         _lib = L
     return _lib
 

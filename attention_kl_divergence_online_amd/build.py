@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libstreamkl.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["fwd.hip", "bwd.hip", "api.cpp"]
+SOURCES = ["fwd.hip", "bwd.hip", "probe.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -191,6 +191,17 @@ const char *streamkl_status_string(int status) {
 
 int streamkl_version(void) { return kVersion; }
 
+streamkl_status streamkl_probe_mfma_bf16(int64_t iters, int64_t workgroups, float *sink, void *stream) {
+  if (iters < 1 || iters > (int64_t{1} << 24) || workgroups < 1 || workgroups > (int64_t{1} << 20))
+    return STREAMKL_ERR_SHAPE;
+  if (!sink) return STREAMKL_ERR_NULL;
+  if (!aligned16(sink)) return STREAMKL_ERR_ALIGN;
+  return skl::launch_mfma_rate((int)iters, (int)workgroups, sink, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? STREAMKL_OK
+             : STREAMKL_ERR_HIP;
+}
+
 streamkl_status streamkl_fwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
                              const void *k2, float *kl, float *lse1, float *lse2, void *stream) {
   streamkl_status st = check_fwd_problem(p, 1);

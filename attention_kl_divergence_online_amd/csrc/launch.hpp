@@ -137,5 +137,9 @@ hipError_t launch_grad_scale_segs(int dtype, const float *g, RowMap qmap, const 
                                   hipStream_t s);
 hipError_t launch_bwd_transpose_segs(int D, const void *x, RowMap map, int keys, const SegTable &t, void *out,
                                      hipStream_t s);
+// Matrix-rate probe: `workgroups` workgroups of four waves, each wave `iters`
+// rounds of four independent 32x32x16 bf16 products; writes one float per
+// wave to sink[workgroups * 4].
+hipError_t launch_mfma_rate(int iters, int workgroups, float *sink, hipStream_t s);
 
 }  // namespace skl

@@ -393,6 +393,10 @@ def main():
     if small:
         out["bwd_small_workspace"] = small
 
+    # Sustained matrix rate under a full load (register operands only), set
+    # beside the published peak the roofline fraction is taken against.
+    out["roofline"]["measured_peak"] = round(mfma_probe(skl, torch), 1)
+
     if not args.no_splitk:
         out["splitk"] = splitk_bench(skl, synth, torch, args)
 
@@ -484,6 +488,23 @@ def materialised_baseline(torch, w, q1, k1, q2, k2, g, kl_fused, heads: int):
             "fwd_ms": round(res["fwd"], 1), "fwd_bwd_ms": round(res["fwd_bwd"], 1),
             "kl_max_rel_diff_vs_fused": float(f"{worst:.3g}"),
             "peak_alloc_bytes": torch.cuda.max_memory_allocated()}
+
+
+def mfma_probe(skl, torch, iters: int = 100000, workgroups: int = 1024) -> float:
+    """TFLOP/s of the library's bf16 matrix-rate probe: four waves per SIMD on
+    every CU, each wave four independent 32x32x16 product chains, best of
+    three runs after one warm-up."""
+    sink = torch.empty(4 * workgroups, dtype=torch.float32, device="cuda")
+    skl.streamkl_probe_mfma_bf16(iters, workgroups, sink)
+    best = float("inf")
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        skl.streamkl_probe_mfma_bf16(iters, workgroups, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    return workgroups * 4 * iters * 4 * 32768 / (best * 1e-3) / 1e12
 
 
 def config_bench(skl, synth, torch, args, name):

@@ -296,6 +296,22 @@ const char *streamkl_status_string(int status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int streamkl_version(void);
 
+/*
+ * Measurement helper, not part of the method: the sustained rate of the bf16
+ * matrix instruction the kernels use (v_mfma_f32_32x32x16_bf16), which a
+ * roofline report can set beside the published peak.  Launches `workgroups`
+ * workgroups of four waves; each wave runs `iters` rounds of four independent
+ * 32x32x16 products on register operands (no memory traffic in the loop), so
+ * the work is workgroups * 4 * iters * 4 * 32768 flop.  `sink` is a device
+ * buffer of at least workgroups * 4 floats owned by the caller; it receives
+ * one value per wave (to keep the products live) and carries no meaning.
+ * The caller times the call on `stream` (events before and after).
+ * iters must be in [1, 2^24] and workgroups in [1, 2^20]: STREAMKL_ERR_SHAPE
+ * otherwise; NULL sink: STREAMKL_ERR_NULL; sink not 16-byte aligned:
+ * STREAMKL_ERR_ALIGN.  Asynchronous like every other call.
+ */
+streamkl_status streamkl_probe_mfma_bf16(int64_t iters, int64_t workgroups, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -298,3 +298,14 @@ def test_varlen_backward_validation(L):
     # Both pairs skipped: nothing to do.
     assert L.streamkl_bwd_varlen(v.ref(), A, A, A, A, A, A, A, A, None, None, None, None, None, 0,
                                  None) == _lib.STREAMKL_OK
+
+
+def test_mfma_probe_rejects_bad_arguments(L):
+    # Each call fails validation on the host; none launches the probe.
+    probe = L.streamkl_probe_mfma_bf16
+    assert probe(0, 1, A, None) == 2          # no iterations
+    assert probe(1 << 25, 1, A, None) == 2    # too many iterations
+    assert probe(1, 0, A, None) == 2          # no workgroups
+    assert probe(1, (1 << 20) + 1, A, None) == 2
+    assert probe(1, 1, None, None) == 1       # NULL sink
+    assert probe(1, 1, MIS, None) == 4        # misaligned sink

@@ -457,3 +457,21 @@ def test_seeded_shape_sweep_bf16(B, H, NQ, NK, D, causal):
     case = f"sweep B{B} H{H} NQ{NQ} NK{NK} D{D} causal={causal}"
     assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"], f"fwd {case}")
     assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, grads, heads), TOL["bf16"], f"bwd {case}")
+
+
+def test_mfma_rate_probe_runs():
+    # The measurement helper: about 1.4 GFLOP of register-only products; the
+    # rate must be a plausible fraction of the 2.5 PFLOP/s bf16 peak.
+    from attention_kl_divergence_online_amd import streamkl_probe_mfma_bf16
+    wg, iters = 256, 2000
+    sink = torch.zeros(4 * wg, device=DEV)
+    streamkl_probe_mfma_bf16(iters, wg, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    streamkl_probe_mfma_bf16(iters, wg, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = wg * 4 * iters * 4 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    print(f"probe {tflops:.0f} TFLOP/s", flush=True)
+    assert torch.isfinite(sink).all()
+    assert 200.0 < tflops < 2600.0
