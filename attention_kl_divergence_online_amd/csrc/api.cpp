@@ -81,7 +81,9 @@ bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 constexpr __int128 kGridLimit = ((__int128)1 << 32) - 1;
 bool fwd_grids_fit(const streamkl_problem *p, int64_t splits) {
   const __int128 bh = (__int128)p->B * p->H;
-  const int64_t bq = skl::fwd_block_queries(p->dtype, (int)p->D, p->NQ);
+  // The 4-wave shape's grid (ceil(NQ / 128) x 256 work-items per head) is no
+  // larger than the 8-wave one's, so the 8-wave count bounds both.
+  const int64_t bq = skl::fwd_block_queries(p->dtype, (int)p->D, p->NQ, false);
   const __int128 fwd = bh * ((p->NQ + bq - 1) / bq) * splits * (bq <= 32 ? 64 : 512);
   const __int128 merge = bh * ((p->NQ + 255) / 256 * 256);
   return fwd <= kGridLimit && merge <= kGridLimit;
@@ -165,7 +167,8 @@ skl::FwdParams make_fwd(const streamkl_problem *p, const void *q1, const void *k
   f.NK = p->NK;
   f.scale = p->scale;
   f.causal = p->causal ? 1 : 0;
-  const int bq = skl::fwd_block_queries(p->dtype, (int)p->D, p->NQ);
+  f.small = skl::fwd_small_shape(p->dtype, (int)p->D, p->NQ, p->causal != 0) ? 1 : 0;
+  const int bq = skl::fwd_block_queries(p->dtype, (int)p->D, p->NQ, f.small != 0);
   f.nqt = (int)((p->NQ + bq - 1) / bq);
   f.splits = 1;
   f.chunk = (int)p->NK;
@@ -245,6 +248,10 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, c
   f.splits = num_splits;
   f.chunk = (int)(tiles_per * skl::kFwdChunkTile);
   f.ws = reinterpret_cast<float *>(workspace);
+  // Split launches keep the 8-wave shape.
+  f.small = 0;
+  const int bq = skl::fwd_block_queries(p->dtype, (int)p->D, p->NQ, false);
+  f.nqt = (int)((p->NQ + bq - 1) / bq);
   if (skl::launch_fwd(p->dtype, (int)p->D, f, s) != hipSuccess) return STREAMKL_ERR_HIP;
   if (skl::launch_splitk_merge(f, s) != hipSuccess) return STREAMKL_ERR_HIP;
   return STREAMKL_OK;
@@ -700,14 +707,23 @@ streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v, const void
   const int64_t es = v->dtype == STREAMKL_BF16 ? 2 : 4;
   const int D = (int)v->D;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // Runs of the main kernel shape: segmented launches.  Decode-shaped runs
-  // (few queries per sequence) launch on their own.
+  // Runs of the main kernel shape: segmented launches, all in one shape (the
+  // 4-wave one at D = 64, and for causal batches whose main-shape sequences
+  // are all at most kFwdSmallVarlenRows long).  Decode-shaped runs (few
+  // queries per sequence) launch on their own.
+  int64_t longest = 0;
+  (void)for_each_run(v, [&](const Run &r) {
+    if (r.nq > 0 && skl::fwd_segment_shape(v->dtype, r.nq)) longest = std::max(longest, r.nq);
+    return STREAMKL_OK;
+  });
+  const bool small =
+      v->dtype == STREAMKL_BF16 && (D == 64 || (v->causal && longest <= skl::kFwdSmallVarlenRows));
   std::vector<SegItem> items;
   st = for_each_run(v, [&](const Run &r) {
     if (r.nq == 0) return STREAMKL_OK;
     if (skl::fwd_segment_shape(v->dtype, r.nq)) {
       SegItem it{run_seg(v, r), 0, r.nk};
-      const int bq = skl::fwd_block_queries(v->dtype, D, r.nq);
+      const int bq = skl::fwd_block_queries(v->dtype, D, r.nq, small);
       it.seg.tiles = (int32_t)((r.nq + bq - 1) / bq);
       it.count = it.seg.units * it.seg.tiles;
       items.push_back(it);
@@ -727,6 +743,7 @@ streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v, const void
   skl::FwdParams f = make_fwd(&p0, q1, k1, q2, k2, kl, lse1, lse2);
   f.qmap = skl::RowMap{0, TQ, (int)v->H, 0};
   f.kmap = skl::RowMap{0, TK, (int)v->H, 0};
+  f.small = small ? 1 : 0;
   return launch_segments(items, [&](const skl::SegTable &t) {
     return skl::launch_fwd_segs(v->dtype, D, f, t, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
   });

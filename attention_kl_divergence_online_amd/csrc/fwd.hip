@@ -19,11 +19,12 @@
 //  * the resident queries' Q1/Q2 fragments stay in registers for the whole
 //    pass; key tiles stream through double-buffered LDS (or, for at most 16
 //    queries, straight into registers);
-//  * bf16 inputs: 8 waves x 32 queries over 128-key tiles (64 at D = 64;
-//    fwd2_kernel), one
-//    wave x 32 queries over 32-key tiles for at most 32 queries per head, and
-//    16x16 products for at most 16 (fwd16_kernel); fp32 inputs: fwd_kernel
-//    with register-staged tiles and compensated sums;
+//  * bf16 inputs: 8 waves x 32 queries over 128-key tiles (fwd2_kernel), or
+//    4 waves x 32 queries over 64-key tiles at D = 64 and for short causal
+//    problems (two workgroups per CU), one wave x 32 queries over 32-key
+//    tiles for at most 32 queries per head, and 16x16 products for at most 16
+//    (fwd16_kernel); fp32 inputs: fwd_kernel with register-staged tiles and
+//    compensated sums;
 //  * scores stay in raw dot-product units x = q.k; exponentials are
 //    exp2((x - m) * scale * log2 e).
 #include "device_common.hpp"
@@ -443,7 +444,7 @@ inline bool fwd_decode_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <=
 inline bool fwd_decode16_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <= kDecode16Rows; }
 
 template <int D, bool SPLIT, int WAVES, int BK>
-__global__ __launch_bounds__(64 * WAVES, 1) void fwd2_kernel(FwdParams p, const SegTable t) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(FwdParams p, const SegTable t) {
   using Tr = Fwd2Traits<D, WAVES, BK>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -898,15 +899,21 @@ static hipError_t launch_fwd2_shape(const FwdParams &p, const SegTable &t, hipSt
 }
 
 // The grid's query tiles (p.nqt) were sized by fwd_block_queries for the same
-// NQ.  At D = 128 the 8-wave shape stages 128-key tiles (half the barriers
-// per key of 64-key tiles: 2-4% faster); at D = 64, where a tile carries half
-// the work, 64-key tiles measure faster.  Split-K chunks are whole 128-key
-// tiles, a whole number of either.
+// NQ and p.small.  At D = 128 the 8-wave shape stages 128-key tiles (half the
+// barriers per key of 64-key tiles: 2-4% faster); at D = 64, where a tile
+// carries half the work, 64-key tiles measure faster.  The 4-wave shape
+// (128 queries, 64-key tiles, 64 KB of LDS) puts two workgroups on a CU, each
+// with its own barriers, and halves the causal diagonal's idle waves; it
+// measured 8.5% faster at D = 64 (causal or not) and 2-8% faster for causal
+// problems of up to 4096 queries at D = 128, but 2-4% slower for longer or
+// non-causal D = 128 problems.  Split-K chunks are whole 128-key tiles, a
+// whole number of any of these.
 template <int D, bool SPLIT>
 static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
   static_assert(kFwdChunkTile % 128 == 0, "split chunks must hold whole 128-key tiles");
   if (fwd_decode16_shape(0, p.NQ)) return launch_fwd16<D, SPLIT>(p, s);
   if (fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, kNoSegs, s);
+  if (!SPLIT && p.small) return launch_fwd2_shape<D, false, 4, 64>(p, kNoSegs, s);
   return launch_fwd2_shape<D, SPLIT, 8, D == 128 ? 128 : 64>(p, kNoSegs, s);
 }
 
@@ -921,11 +928,16 @@ static hipError_t launch_fwd_t(const FwdParams &p, const SegTable &t, hipStream_
   return hipGetLastError();
 }
 
-int fwd_block_queries(int dtype, int D, int64_t NQ) {
+int fwd_block_queries(int dtype, int D, int64_t NQ, bool small) {
   if (fwd_decode16_shape(dtype, NQ)) return Fwd16Traits<128>::BQ;
   if (fwd_decode_shape(dtype, NQ)) return Fwd2Traits<128, 1, 32>::BQ;
+  if (dtype == 0 && small) return Fwd2Traits<128, 4, 64>::BQ;
   if (dtype == 0) return D == 128 ? Fwd2Traits<128>::BQ : Fwd2Traits<64>::BQ;
   return D == 128 ? FwdTraits<float, 128>::BQ : FwdTraits<float, 64>::BQ;
+}
+
+bool fwd_small_shape(int dtype, int D, int64_t NQ, bool causal) {
+  return dtype == 0 && !fwd_decode_shape(dtype, NQ) && (D == 64 || (causal && NQ <= kFwdSmallCausalRows));
 }
 
 hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s) {
@@ -943,8 +955,8 @@ bool fwd_segment_shape(int dtype, int64_t NQ) { return !fwd_decode_shape(dtype, 
 
 hipError_t launch_fwd_segs(int dtype, int D, const FwdParams &p, const SegTable &t, hipStream_t s) {
   if (dtype == 0) {
-    if (D == 128) return launch_fwd2_shape<128, false, 8, 128>(p, t, s);
-    return launch_fwd2_shape<64, false, 8, 64>(p, t, s);
+    if (D == 128) return p.small ? launch_fwd2_shape<128, false, 4, 64>(p, t, s) : launch_fwd2_shape<128, false, 8, 128>(p, t, s);
+    return p.small ? launch_fwd2_shape<64, false, 4, 64>(p, t, s) : launch_fwd2_shape<64, false, 8, 64>(p, t, s);
   }
   if (D == 128) return launch_fwd_t<float, 128, false>(p, t, s);
   return launch_fwd_t<float, 64, false>(p, t, s);

@@ -70,6 +70,7 @@ struct FwdParams {
   int nqt;     // query tiles per head
   int splits;  // key chunks (1 = unsplit)
   int chunk;   // keys per chunk (multiple of the key tile)
+  int small;   // unsplit bf16 main shape in 4-wave workgroups (fwd_small_shape), else 8-wave
 };
 
 struct BwdParams {
@@ -99,15 +100,23 @@ constexpr int kBwdTile = 64;  // streamed rows per backward stage (tile of the t
 constexpr int kGradExp = 8;   // |g| * sigma <= 2^kGradExp before fp16 rounding of dS
 
 // Queries per forward workgroup for an input type (dtype: 0 = bf16, 1 = fp32)
-// and query count per head.
-int fwd_block_queries(int dtype, int D, int64_t NQ);
+// and query count per head; `small`: the 4-wave bf16 shape for the main
+// (non-decode) case.
+int fwd_block_queries(int dtype, int D, int64_t NQ, bool small);
+// Whether an unsplit dense bf16 forward takes the 4-wave shape: always at
+// D = 64, and for causal problems of at most kFwdSmallCausalRows queries at
+// D = 128.  A packed batch takes it at D = 64, and when causal with every
+// main-shape sequence at most kFwdSmallVarlenRows long.
+constexpr int64_t kFwdSmallCausalRows = 4096;
+constexpr int64_t kFwdSmallVarlenRows = 8192;
+bool fwd_small_shape(int dtype, int D, int64_t NQ, bool causal);
 
 // dtype: 0 = bf16, 1 = fp32.  Return the launch status.
 hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s);
 // Unsplit forward over the segments of t (t.n >= 1), in one launch of t.end
 // workgroups.  Every segment must have fwd_segment_shape(dtype, nq) and
-// tiles = ceil(nq / fwd_block_queries(dtype, D, nq)); p supplies the whole
-// packed tensors, the maps' sh and H, scale and causal.
+// tiles = ceil(nq / fwd_block_queries(dtype, D, nq, p.small)); p supplies the
+// whole packed tensors, the maps' sh and H, scale, causal and small.
 bool fwd_segment_shape(int dtype, int64_t NQ);
 hipError_t launch_fwd_segs(int dtype, int D, const FwdParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_splitk_merge(const FwdParams &p, hipStream_t s);
