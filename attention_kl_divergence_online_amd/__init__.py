@@ -71,6 +71,33 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _ws_bytes(workspace: Optional[torch.Tensor], device, what: str) -> int:
+    """Size in bytes of a caller-supplied workspace, which must be a contiguous
+    tensor on the inputs' device (0 for None)."""
+    if workspace is None:
+        return 0
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous() or workspace.device != device:
+        raise ValueError(f"{what}: the workspace must be a contiguous tensor on {device}")
+    return workspace.numel() * workspace.element_size()
+
+
+def _check_out(ts, shapes, device, what: str) -> None:
+    """Caller-supplied outputs: contiguous fp32 tensors of the expected shapes on
+    the inputs' device (None where the output is skipped).  The library only
+    sees pointers, so a smaller or mistyped buffer would be written past its end."""
+    if len(ts) != len(shapes):
+        raise ValueError(f"{what}: expected {len(shapes)} output tensors, got {len(ts)}")
+    for t, shp in zip(ts, shapes):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{what}: outputs must be contiguous fp32 tensors")
+        if tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{what}: output of shape {tuple(t.shape)}, expected {tuple(shp)}")
+        if t.device != device:
+            raise ValueError(f"{what}: output on {t.device}, inputs on {device}")
+
+
 def streamkl_fwd(q1, k1, q2, k2, scale: Optional[float] = None, causal: bool = False,
                  out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """Per-row KL(P1||P2), LSE1, LSE2 (fp32 [B, H, NQ]) in one online pass."""
@@ -79,6 +106,7 @@ def streamkl_fwd(q1, k1, q2, k2, scale: Optional[float] = None, causal: bool = F
     if out is None:
         shp = q1.shape[:3]
         out = tuple(torch.empty(shp, dtype=torch.float32, device=q1.device) for _ in range(3))
+    _check_out(tuple(out), (q1.shape[:3],) * 3, q1.device, "streamkl_fwd")
     kl, lse1, lse2 = out
     st = _lib.lib().streamkl_fwd(p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
                                  _ptr(lse2), _stream_handle(q1.device))
@@ -99,11 +127,12 @@ def streamkl_fwd_splitk(q1, k1, q2, k2, num_splits: int, scale: Optional[float] 
     if out is None:
         shp = q1.shape[:3]
         out = tuple(torch.empty(shp, dtype=torch.float32, device=q1.device) for _ in range(3))
+    _check_out(tuple(out), (q1.shape[:3],) * 3, q1.device, "streamkl_fwd_splitk")
     kl, lse1, lse2 = out
     need = int(_lib.lib().streamkl_fwd_splitk_workspace_size(p, int(num_splits)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace, q1.device, "streamkl_fwd_splitk")
     st = _lib.lib().streamkl_fwd_splitk(p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
                                         _ptr(lse2), int(num_splits), _ptr(workspace), ws_bytes,
                                         _stream_handle(q1.device))
@@ -131,6 +160,7 @@ def streamkl_bwd(q1, k1, q2, k2, kl, lse1, lse2, g, scale: Optional[float] = Non
         def mk(ref, on):
             return torch.empty(ref.shape, dtype=torch.float32, device=ref.device) if on else None
         out = (mk(q1, teacher), mk(k1, teacher), mk(q2, student), mk(k2, student))
+    _check_out(tuple(out), (q1.shape, k1.shape, q2.shape, k2.shape), q1.device, "streamkl_bwd")
     dq1, dk1, dq2, dk2 = out
     workspace, ws_bytes = _workspace(p, q1.device, workspace)
     st = _lib.lib().streamkl_bwd(p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
@@ -150,7 +180,7 @@ def _workspace(p, dev, workspace):
     need = int(_lib.lib().streamkl_bwd_workspace_size(p))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    return workspace, workspace.numel() * workspace.element_size()
+    return workspace, _ws_bytes(workspace, dev, "backward")
 
 
 def streamkl_bwd_prepare(q1, k1, q2, k2, g, scale: Optional[float] = None, causal: bool = False,
@@ -173,10 +203,11 @@ def _pass(name, q1, k1, q2, k2, kl, lse1, lse2, g, scale, causal, workspace, out
     _check_rowvecs(q1, kl, lse1, lse2, g)
     if workspace is None:
         raise ValueError(f"{name} needs the workspace filled by streamkl_bwd_prepare")
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _ws_bytes(workspace, q1.device, name)
     if out is None:
         out = tuple(torch.empty(r.shape, dtype=torch.float32, device=r.device) if on else None
                     for r, on in zip(refs, (teacher, student)))
+    _check_out(tuple(out), tuple(r.shape for r in refs), q1.device, name)
     a, b = out
     st = getattr(_lib.lib(), name)(p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
                                    _ptr(lse2), _ptr(g), _ptr(a), _ptr(b), _ptr(workspace), nbytes,
@@ -273,6 +304,7 @@ def streamkl_fwd_varlen(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, scale: Optio
     v = _Varlen(q1, k1, cu_seqlens_q, cu_seqlens_k, scale, causal)
     if out is None:
         out = tuple(torch.empty(q1.shape[:2], dtype=torch.float32, device=q1.device) for _ in range(3))
+    _check_out(tuple(out), (q1.shape[:2],) * 3, q1.device, "streamkl_fwd_varlen")
     kl, lse1, lse2 = out
     st = _lib.lib().streamkl_fwd_varlen(v.p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
                                         _ptr(lse2), _stream_handle(q1.device))
@@ -298,11 +330,12 @@ def streamkl_bwd_varlen(q1, k1, q2, k2, cu_seqlens_q, cu_seqlens_k, kl, lse1, ls
         def mk(ref, on):
             return torch.empty(ref.shape, dtype=torch.float32, device=ref.device) if on else None
         out = (mk(q1, teacher), mk(k1, teacher), mk(q2, student), mk(k2, student))
+    _check_out(tuple(out), (q1.shape, k1.shape, q2.shape, k2.shape), q1.device, "streamkl_bwd_varlen")
     dq1, dk1, dq2, dk2 = out
     if workspace is None:
         need = int(_lib.lib().streamkl_bwd_varlen_workspace_size(v.p))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _ws_bytes(workspace, q1.device, "streamkl_bwd_varlen")
     st = _lib.lib().streamkl_bwd_varlen(v.p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
                                         _ptr(lse2), _ptr(g), _ptr(dq1), _ptr(dk1), _ptr(dq2), _ptr(dk2),
                                         _ptr(workspace), nbytes, _stream_handle(q1.device))

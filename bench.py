@@ -7,8 +7,11 @@ in HBM.  Throughput is algorithmic TFLOP/s over exact visible (query, key)
 pairs: 4*D flop per pair forward, 12*D backward.
 
 Also reported: per-kernel HIP-event timings, the roofline of the dominant
-kernel, the split-K forward on the 512K-key workload, and the fp64 CPU oracle
-timed on a bounded sample of the same workload on this host's cores.
+kernel (algorithmic flop per launch over its average duration), the other
+four workloads of the metric ("configs": tiny fp32, causal 4K, non-causal
+16K, the split-K forward over 512K keys and the backward over 128K keys),
+and the fp64 CPU oracle timed on a bounded sample of the same workload on
+this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -143,6 +146,12 @@ def summarize_counters(csvs, out_path: str) -> None:
 
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 matrix peak (published)
+# The five workloads the metric is quoted on, by role: C1 tiny fp32 (parity
+# size), C2 short causal, C3 long non-causal with large KL, C4 the 64K causal
+# headline (the main line above), C5 the split-K forward over 512K keys and
+# the short-query backward over 128K keys.
+CONFIGS = (("C1", "tiny_fp32"), ("C2", "causal_4k"), ("C3", "noncausal_16k"), ("C5_bwd", "splitk_bwd_128k"))
 PEAK_HBM_GBS = 8000.0
 
 
@@ -154,11 +163,14 @@ def parse():
     ap.add_argument("--workload", default="causal_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-splitk", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other four workloads of the metric (C1 tiny_fp32, C2 causal_4k, "
+                         "C3 noncausal_16k, C5 splitk_512k forward and splitk_bwd_128k)")
     ap.add_argument("--no-small-workspace", action="store_true",
                     help="skip timing the backward with one-, four- and eight-head workspaces")
     ap.add_argument("--other-configs", action="store_true",
-                    help="also time forward and backward on the other workloads (causal_4k, noncausal_16k, "
-                         "splitk_bwd_128k, shortq_bwd_64k, causal_16k_d64, causal_4k_fp32), the decode split-K "
+                    help="also time forward and backward on the workloads outside the metric "
+                         "(shortq_bwd_64k, causal_16k_d64, causal_4k_fp32), the decode split-K "
                          "forward and the packed variable-length batches (varlen_mix, varlen_short), and "
                          "report them under \"other_configs\"")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -323,11 +335,16 @@ def main():
     tflops = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
 
     # Roofline of the longest kernel.  Algorithmic flop per launch: forward 4*D
-    # per visible pair; each backward pass 8*D per pair (its recompute of both
-    # logit tiles, 4*D, plus its two gradient products, 4*D).
-    kern_flop = {"fwd": fwd_flop, "bwd_dk": 8 * w.D * pairs, "bwd_dq": 8 * w.D * pairs}
+    # per visible pair; the backward 12*D per pair (both logit tiles, 4*D, and
+    # the four gradient products, 8*D), counted as 6*D for each of its two
+    # passes.  Each pass executes 8*D per pair (it recomputes both logit tiles
+    # and forms two of the four gradient products); that rate is reported
+    # beside the algorithmic one, never in its place.
+    kern_flop = {"fwd": fwd_flop, "bwd_dk": 6 * w.D * pairs, "bwd_dq": 6 * w.D * pairs}
+    exec_flop = {"fwd": fwd_flop, "bwd_dk": 8 * w.D * pairs, "bwd_dq": 8 * w.D * pairs}
     dom = max(kern_flop, key=lambda k: per[k])
     achieved = kern_flop[dom] / (per[dom] * 1e-3) / 1e12
+    executed = exec_flop[dom] / (per[dom] * 1e-3) / 1e12
     kernel_names = {"fwd": "fwd2_kernel<128,unsplit>", "bwd_dk": "bwd4_kernel<128,keys resident,both>",
                     "bwd_dq": "bwd4_kernel<128,queries resident,both>"}
 
@@ -351,6 +368,7 @@ def main():
         "bwd_ms": round(bwd_ms, 3),
         "bwd_tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
         "kernel_ms": {k: round(v, 3) for k, v in per.items()},
+        "kernel_tflops": {k: round(kern_flop[k] / (per[k] * 1e-3) / 1e12, 2) for k in kern_flop},
         "kernel_ms_median": {k: round(statistics.median(v), 3) for k, v in samples.items()},
         "kernel_ms_min": {k: round(min(v), 3) for k, v in samples.items()},
         "wall_s_timed": round(wall, 3),
@@ -362,6 +380,12 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": recorded_traffic(dom),
+            "flop_per_launch": kern_flop[dom],
+            "flop_rule": "algorithmic: 4*D per visible pair (forward), 6*D per pair per backward pass "
+                         "(12*D for the whole backward)",
+            "executed": {"flop_per_launch": exec_flop[dom], "tflops": round(executed, 2),
+                         "frac": round(executed / PEAK_BF16_TFLOPS, 4),
+                         "flop_rule": "8*D per pair per backward pass (both logit tiles recomputed in each)"},
         },
         "memory": memory,
     }
@@ -400,10 +424,25 @@ def main():
     if not args.no_splitk:
         out["splitk"] = splitk_bench(skl, synth, torch, args)
 
+    if not args.no_configs:
+        # Every workload of the metric in one line: algorithmic TFLOP/s and the
+        # fraction of the matrix peak for the inputs' type (bf16 / fp32).
+        cfgs = {"C4": {"workload": w.name, "fwd_ms": out["fwd_ms"], "bwd_ms": out["bwd_ms"],
+                       "fwd_tflops": out["fwd_tflops"], "bwd_tflops": out["bwd_tflops"], "step_tflops": out["value"],
+                       "fwd_frac": round(out["fwd_tflops"] / PEAK_BF16_TFLOPS, 4),
+                       "bwd_frac": round(out["bwd_tflops"] / PEAK_BF16_TFLOPS, 4),
+                       "step_frac": round(out["value"] / PEAK_BF16_TFLOPS, 4)}}
+        for tag, name in CONFIGS:
+            cfgs[tag] = config_bench(skl, synth, torch, args, name)
+        if "splitk" in out:
+            sk = dict(out["splitk"])
+            sk["fwd_frac"] = round(sk["tflops"] / PEAK_BF16_TFLOPS, 4)
+            cfgs["C5_fwd"] = sk
+        out["configs"] = {k: cfgs[k] for k in ("C1", "C2", "C3", "C4", "C5_fwd", "C5_bwd") if k in cfgs}
+
     if args.other_configs:
         out["other_configs"] = {n: config_bench(skl, synth, torch, args, n)
-                                for n in ("causal_4k", "noncausal_16k", "splitk_bwd_128k", "shortq_bwd_64k",
-                                          "causal_16k_d64", "causal_4k_fp32")}
+                                for n in ("shortq_bwd_64k", "causal_16k_d64", "causal_4k_fp32")}
         out["other_configs"]["decode_128k"] = splitk_bench(skl, synth, torch, args, "decode_128k")
         out["other_configs"]["varlen_mix"] = varlen_bench(skl, synth, torch, args, "varlen_mix")
         out["other_configs"]["varlen_short"] = varlen_bench(skl, synth, torch, args, "varlen_short")
@@ -536,10 +575,14 @@ def config_bench(skl, synth, torch, args, name):
             fwd_ms += ev[0].elapsed_time(ev[1]) / args.steps
             bwd_ms += ev[1].elapsed_time(ev[2]) / args.steps
     pairs = w.visible_pairs()
-    res = {"fwd_splits": w.splits, "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
-           "fwd_tflops": round(4 * w.D * pairs / (fwd_ms * 1e-3) / 1e12, 2),
-           "bwd_tflops": round(12 * w.D * pairs / (bwd_ms * 1e-3) / 1e12, 2),
-           "step_tflops": round(16 * w.D * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2)}
+    peak = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
+    fwd_t = 4 * w.D * pairs / (fwd_ms * 1e-3) / 1e12
+    bwd_t = 12 * w.D * pairs / (bwd_ms * 1e-3) / 1e12
+    step_t = 16 * w.D * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+    res = {"workload": w.name, "fwd_splits": w.splits, "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+           "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2), "step_tflops": round(step_t, 2),
+           "peak_tflops": peak, "fwd_frac": round(fwd_t / peak, 4), "bwd_frac": round(bwd_t / peak, 4),
+           "step_frac": round(step_t / peak, 4)}
     del q1, k1, q2, k2, grads, ws, wsk
     torch.cuda.empty_cache()
     return res

@@ -126,16 +126,18 @@ def test_peaked_rows_large_kl(dtype, D, scale, causal):
 
 
 @pytest.mark.parametrize("slope", [0.2, -0.2])
-@pytest.mark.parametrize("causal", [False, True])
-def test_monotone_logits_held_maxima(slope, causal):
+@pytest.mark.parametrize("causal,NQ,NK", [(False, 260, 1100), (True, 260, 1100), (True, 4200, 4300)])
+def test_monotone_logits_held_maxima(slope, causal, NQ, NK):
     # Keys along one direction with a steady rise (or fall) along the key
     # index: each raw logit differs from the previous key's by about
     # 2.3 * slope / 0.2, so with rising logits the maxima a lane holds go
     # stale by far more than 2^24 within a few 32-key blocks (the forward
     # folds those blocks again exactly), and with falling logits the first
-    # block holds the maxima and later terms underflow.
-    B, H, NQ, NK, D = 1, 2, 260, 1100, 128
-    print(f"monotone logits slope={slope} causal={causal}", flush=True)
+    # block holds the maxima and later terms underflow.  Causal problems of
+    # more than 4096 queries run the eight-wave, 128-key-tile forward shape
+    # (its diagonal masking and refold), shorter ones the four-wave shape.
+    B, H, D = 1, 2 if NQ < 1000 else 1, 128
+    print(f"monotone logits slope={slope} causal={causal} NQ={NQ} NK={NK}", flush=True)
     gen = torch.Generator(device="cpu").manual_seed(int(100 * slope) + causal)
     u = torch.randn(D, generator=gen)
     u = u / u.norm()
@@ -155,6 +157,27 @@ def test_monotone_logits_held_maxima(slope, causal):
     assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"], f"fwd {case}")
     assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kls, l1s, l2s, heads), TOL["bf16"],
                   f"split fwd {case}")
+
+
+@pytest.mark.parametrize("NQ,NK", [(4160, 4160), (4100, 4357)])
+def test_causal_eight_wave_shape_all_rows(NQ, NK):
+    # Causal bf16 problems just past 4096 queries take the forward's eight-wave
+    # shape (256 queries over 128-key tiles) that the 64K workload runs: every
+    # row of the forward and every gradient against the oracle, with a ragged
+    # last query tile and, for NQ < NK, a diagonal offset.
+    B, H, D = 1, 1, 128
+    print(f"eight-wave causal NQ={NQ} NK={NK}", flush=True)
+    q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, torch.bfloat16, seed=NQ + NK, noise=0.1)
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, True)
+    gen = torch.Generator(device="cpu").manual_seed(NQ)
+    g = (torch.rand(B, H, NQ, generator=gen) - 0.3).to(DEV)
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, True)
+    torch.cuda.synchronize()
+    heads = _heads(B, H)
+    case = f"eight-wave causal NQ{NQ} NK{NK}"
+    assert_within(compare_forward(q1, k1, q2, k2, scale, True, kl, l1, l2, heads), TOL["bf16"], f"fwd {case}")
+    assert_within(compare_backward(q1, k1, q2, k2, scale, True, g, grads, heads), TOL["bf16"], f"bwd {case}")
 
 
 def test_backward_steps_equal_combined_call():

@@ -52,6 +52,9 @@ CASES = [
     ([257, 3, 3, 129], [257, 70, 70, 400], 64, True, "bf16"),
     ([33, 0, 190, 190, 7], [100, 12, 190, 190, 7], 128, True, "fp32"),
     ([65, 5], [300, 64], 64, False, "fp32"),
+    # A causal batch with a sequence past 8192 rows: the forward's shared
+    # launch takes the eight-wave, 128-key-tile shape for every sequence.
+    ([9000, 300], [9000, 300], 128, True, "bf16"),
 ]
 
 
