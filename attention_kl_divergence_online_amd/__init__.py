@@ -28,7 +28,7 @@ import torch
 from . import _lib
 from ._lib import StreamKLError
 
-__all__ = ["streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd", "streamkl_bwd_prepare", "streamkl_bwd_dk",
+__all__ = ["streamkl_fwd", "streamkl_fwd_splitk", "streamkl_fwd_splitk_noalloc", "streamkl_bwd", "streamkl_bwd_prepare", "streamkl_bwd_dk",
            "streamkl_bwd_dq", "attention_kl",
            "streamkl_fwd_varlen", "streamkl_bwd_varlen", "varlen_problem_for", "bwd_varlen_workspace_size",
            "attention_kl_varlen",
@@ -137,6 +137,25 @@ def streamkl_fwd_splitk(q1, k1, q2, k2, num_splits: int, scale: Optional[float] 
                                         _ptr(lse2), int(num_splits), _ptr(workspace), ws_bytes,
                                         _stream_handle(q1.device))
     _lib.check(st, "streamkl_fwd_splitk")
+    return kl, lse1, lse2
+
+
+def streamkl_fwd_splitk_noalloc(q1, k1, q2, k2, num_splits: int, scale: Optional[float] = None,
+                                causal: bool = False, out=None):
+    """The split-K forward with its partial states in the library's own device
+    scratch (no workspace, no allocation by the library; calls on one GPU
+    share the scratch and must not overlap).  Pass `out` to allocate nothing
+    here either."""
+    _check_inputs(q1, k1, q2, k2)
+    p = problem_for(q1, k1, scale, causal)
+    if out is None:
+        shp = q1.shape[:3]
+        out = tuple(torch.empty(shp, dtype=torch.float32, device=q1.device) for _ in range(3))
+    _check_out(tuple(out), (q1.shape[:3],) * 3, q1.device, "streamkl_fwd_splitk_noalloc")
+    kl, lse1, lse2 = out
+    st = _lib.lib().streamkl_fwd_splitk_noalloc(p, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(kl), _ptr(lse1),
+                                                _ptr(lse2), int(num_splits), _stream_handle(q1.device))
+    _lib.check(st, "streamkl_fwd_splitk_noalloc")
     return kl, lse1, lse2
 
 

@@ -23,11 +23,14 @@ STREAMKL_ERR_HIP = 6
 STREAMKL_BF16 = 0
 STREAMKL_FP32 = 1
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # STREAMKL_NOALLOC_SCRATCH_BYTES
+
 # Every function include/streamkl.h declares, in declaration order.
 EXPORTS = (
     "streamkl_fwd",
     "streamkl_fwd_splitk_workspace_size",
     "streamkl_fwd_splitk",
+    "streamkl_fwd_splitk_noalloc",
     "streamkl_bwd_workspace_size",
     "streamkl_bwd_workspace_size_min",
     "streamkl_bwd",
@@ -97,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.streamkl_fwd_splitk_workspace_size.restype = sz
         L.streamkl_fwd_splitk.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
         L.streamkl_fwd_splitk.restype = ctypes.c_int
+        L.streamkl_fwd_splitk_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
+        L.streamkl_fwd_splitk_noalloc.restype = ctypes.c_int
         L.streamkl_bwd_workspace_size.argtypes = [pp]
         L.streamkl_bwd_workspace_size.restype = sz
         L.streamkl_bwd_workspace_size_min.argtypes = [pp]

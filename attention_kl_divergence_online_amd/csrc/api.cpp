@@ -70,7 +70,8 @@ BwdLayout bwd_layout_heads(const streamkl_problem *p, size_t heads) {
 }
 BwdLayout bwd_layout(const streamkl_problem *p) { return bwd_layout_heads(p, (size_t)(p->B * p->H)); }
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
+static_assert(STREAMKL_NOALLOC_SCRATCH_BYTES == skl::kSplitkScratchBytes, "scratch size in the header");
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -224,9 +225,17 @@ size_t streamkl_fwd_splitk_workspace_size(const streamkl_problem *p, int num_spl
   return (size_t)5 * (size_t)num_splits * (size_t)(p->B * p->H * p->NQ) * sizeof(float);
 }
 
-streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
-                                    const void *k2, float *kl, float *lse1, float *lse2, int num_splits,
-                                    void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The split-K forward of streamkl_fwd_splitk and streamkl_fwd_splitk_noalloc.
+// Host validation first; then `get_ws(need, &ws)` supplies a workspace of at
+// least `need` bytes for num_splits > 1 (or the status that rejects the call).
+template <class GetWs>
+streamkl_status splitk_forward(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                               const void *k2, float *kl, float *lse1, float *lse2, int num_splits, void *stream,
+                               GetWs get_ws) {
   streamkl_status st = check_problem(p);
   if (st != STREAMKL_OK) return st;
   if (num_splits < 1) return STREAMKL_ERR_SHAPE;
@@ -240,7 +249,8 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, c
     return skl::launch_fwd(p->dtype, (int)p->D, f, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
   }
   const size_t need = streamkl_fwd_splitk_workspace_size(p, num_splits);
-  if (!workspace || workspace_bytes < need) return STREAMKL_ERR_WORKSPACE;
+  void *workspace = nullptr;
+  if ((st = get_ws(need, &workspace)) != STREAMKL_OK) return st;
   if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
   // Whole 128-key tiles per chunk; trailing chunks past NK are empty.
   const int64_t tiles = (p->NK + skl::kFwdChunkTile - 1) / skl::kFwdChunkTile;
@@ -255,6 +265,33 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, c
   if (skl::launch_fwd(p->dtype, (int)p->D, f, s) != hipSuccess) return STREAMKL_ERR_HIP;
   if (skl::launch_splitk_merge(f, s) != hipSuccess) return STREAMKL_ERR_HIP;
   return STREAMKL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+streamkl_status streamkl_fwd_splitk(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
+                                    const void *k2, float *kl, float *lse1, float *lse2, int num_splits,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  return splitk_forward(p, q1, k1, q2, k2, kl, lse1, lse2, num_splits, stream, [&](size_t need, void **ws) {
+    if (!workspace || workspace_bytes < need) return STREAMKL_ERR_WORKSPACE;
+    *ws = workspace;
+    return STREAMKL_OK;
+  });
+}
+
+streamkl_status streamkl_fwd_splitk_noalloc(const streamkl_problem *p, const void *q1, const void *k1,
+                                            const void *q2, const void *k2, float *kl, float *lse1, float *lse2,
+                                            int num_splits, void *stream) {
+  return splitk_forward(p, q1, k1, q2, k2, kl, lse1, lse2, num_splits, stream, [&](size_t need, void **ws) {
+    if (need > skl::kSplitkScratchBytes) return STREAMKL_ERR_WORKSPACE;
+    float *scratch = nullptr;
+    if (skl::splitk_scratch(reinterpret_cast<hipStream_t>(stream), &scratch) != hipSuccess)
+      return STREAMKL_ERR_HIP;
+    *ws = scratch;
+    return STREAMKL_OK;
+  });
 }
 
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p) {

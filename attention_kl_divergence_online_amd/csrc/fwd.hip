@@ -27,6 +27,8 @@
 //    compensated sums;
 //  * scores stay in raw dot-product units x = q.k; exponentials are
 //    exp2((x - m) * scale * log2 e).
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -960,6 +962,42 @@ hipError_t launch_fwd_segs(int dtype, int D, const FwdParams &p, const SegTable 
   }
   if (D == 128) return launch_fwd_t<float, 128, false>(p, t, s);
   return launch_fwd_t<float, 64, false>(p, t, s);
+}
+
+// Partial row states of the allocation-free split-K forward.  Each GPU the
+// library runs on holds its own copy until the process ends; every call on
+// that GPU shares it.  In host code `scratch` names a host-side stand-in,
+// never the device array: kernels get the address splitk_scratch looked up.
+static __device__ __align__(256) float scratch[kSplitkScratchBytes / sizeof(float)];
+
+hipError_t splitk_scratch(hipStream_t s, float **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float *table[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int cur = dev;
+  if (s != nullptr) {
+    hipDevice_t d;
+    if ((e = hipStreamGetDevice(s, &d)) != hipSuccess) return e;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (table[dev] == nullptr) {
+    // The lookup runs with the stream's device current.
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    const hipError_t r = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (r != hipSuccess) return r;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    table[dev] = static_cast<float *>(addr);
+  }
+  *ptr = table[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_splitk_merge(const FwdParams &p, hipStream_t s) {

@@ -120,6 +120,12 @@ hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s);
 bool fwd_segment_shape(int dtype, int64_t NQ);
 hipError_t launch_fwd_segs(int dtype, int D, const FwdParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_splitk_merge(const FwdParams &p, hipStream_t s);
+// Library-owned device scratch of the allocation-free split-K forward: a
+// file-scope device array of kSplitkScratchBytes per GPU.  splitk_scratch
+// returns its device address on the device `s` belongs to (the current device
+// for the null stream), looked up once per device and kept.
+constexpr size_t kSplitkScratchBytes = (size_t)64 << 20;
+hipError_t splitk_scratch(hipStream_t s, float **ptr);
 // Backward pieces; `p.sigma` must point at the prepared per-(b,h) factors.
 hipError_t launch_grad_scale(int dtype, const float *g, RowMap qmap, int64_t BH, int64_t NQ, float *sigma,
                              hipStream_t s);

@@ -21,7 +21,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates no device memory and keeps no mutable global state.
+ *    allocates no device memory.  Its only global state belongs to
+ *    streamkl_fwd_splitk_noalloc: a device scratch array per GPU and the
+ *    table of their addresses, filled once per device under a lock.
  *  - Q1, Q2 are [B, H, NQ, D] and K1, K2 are [B, H, NK, D], contiguous,
  *    row-major, element type `dtype` (bf16 or fp32).  Per-row vectors (KL,
  *    LSE1, LSE2, g) are fp32 [B, H, NQ].  Gradients are fp32 and have the
@@ -110,6 +112,29 @@ streamkl_status streamkl_fwd_splitk(const streamkl_problem *p,
                                     float *kl, float *lse1, float *lse2,
                                     int num_splits, void *workspace, size_t workspace_bytes,
                                     void *stream);
+
+/*
+ * For callers that cannot allocate device memory or hand the library a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The same split-K forward as streamkl_fwd_splitk
+ * (same arguments without the workspace, same results bit for bit, same
+ * errors), with the partial row states in a device array the library owns:
+ * STREAMKL_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU it runs on, set up by
+ * the first call on that GPU (run one call outside graph capture first) and
+ * held until the process ends.  A problem whose split-K workspace
+ * (streamkl_fwd_splitk_workspace_size) exceeds the array is rejected with
+ * STREAMKL_ERR_WORKSPACE before anything is enqueued; num_splits == 1 runs
+ * streamkl_fwd and uses no scratch.  The call allocates nothing.  Every call
+ * on one GPU shares that GPU's array and leaves its last contents there, so
+ * calls that may overlap on one GPU (other streams, other host threads) race:
+ * the caller serialises them.  A failed set-up returns STREAMKL_ERR_HIP.
+ */
+#define STREAMKL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+streamkl_status streamkl_fwd_splitk_noalloc(const streamkl_problem *p,
+                                            const void *q1, const void *k1,
+                                            const void *q2, const void *k2,
+                                            float *kl, float *lse1, float *lse2,
+                                            int num_splits, void *stream);
 
 /*
  * Bytes of device workspace streamkl_bwd needs: one fp32 per (batch, head)

@@ -123,6 +123,38 @@ def test_splitk_validation(L):
                                  None) == _lib.STREAMKL_ERR_NULL
 
 
+def test_noalloc_splitk_validation(L):
+    # Host-side rejections of the allocation-free split-K forward, before any
+    # HIP call: the argument errors of streamkl_fwd_splitk, and a problem whose
+    # partial states would not fit the library's scratch array.
+    p = P(NK=200)
+    args = (A, A, A, A, A, A, A)
+    assert L.streamkl_fwd_splitk_noalloc(ctypes.byref(p), *args, 0, None) == _lib.STREAMKL_ERR_SHAPE
+    assert L.streamkl_fwd_splitk_noalloc(ctypes.byref(p), *args, 5, None) == _lib.STREAMKL_ERR_SHAPE
+    assert L.streamkl_fwd_splitk_noalloc(ctypes.byref(p), None, A, A, A, A, A, A, 3,
+                                         None) == _lib.STREAMKL_ERR_NULL
+    assert L.streamkl_fwd_splitk_noalloc(ctypes.byref(p), A, A, A, A, MIS, A, A, 3,
+                                         None) == _lib.STREAMKL_ERR_ALIGN
+    big = P(B=1, H=32, NQ=1024, NK=8192)  # 128 splits: 5 * 128 * 32 * 1024 * 4 B = 80 MiB
+    need = L.streamkl_fwd_splitk_workspace_size(ctypes.byref(big), 128)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.streamkl_fwd_splitk_noalloc(ctypes.byref(big), *args, 128, None) == _lib.STREAMKL_ERR_WORKSPACE
+    fits = L.streamkl_fwd_splitk_workspace_size(ctypes.byref(big), 64)
+    assert 0 < fits <= _lib.NOALLOC_SCRATCH_BYTES
+    assert L.streamkl_fwd_splitk_noalloc(ctypes.byref(P(H=0)), *args, 1, None) == _lib.STREAMKL_OK
+
+
+def test_noalloc_scratch_is_a_file_scope_device_array():
+    # The scratch is one static device array in the split-K source, reached in
+    # host code only through the address hipGetSymbolAddress returns.
+    src = open(os.path.join(CSRC, "fwd.hip")).read()
+    assert re.search(r"static __device__ __align__\(256\) float scratch\[", src)
+    assert "hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch))" in src
+    code = re.sub(r"//[^\n]*", "", src)
+    uses = re.findall(r"\bscratch\b", code)
+    assert len(uses) == 2, "scratch is named only where declared and in the address lookup"
+
+
 def bwd(L, p, dq1=A, dk1=A, dq2=A, dk2=A, ws=A, wsb=1 << 20, g=A, kl=A):
     return L.streamkl_bwd(ctypes.byref(p), A, A, A, A, kl, A, A, g, dq1, dk1, dq2, dk2, ws, wsb, None)
 
