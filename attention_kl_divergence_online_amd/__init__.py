@@ -164,7 +164,9 @@ def bwd_workspace_size(q1, k1, scale=None, causal=False) -> int:
 
 
 def bwd_workspace_size_min(q1, k1, scale=None, causal=False) -> int:
-    """Smallest workspace streamkl_bwd accepts (copies for one head at a time)."""
+    """Smallest workspace streamkl_bwd accepts: sigma, the operand scales and their
+    chunk maxima, without the partials of a key-split query pass (which then runs
+    unsplit)."""
     return int(_lib.lib().streamkl_bwd_workspace_size_min(problem_for(q1, k1, scale, causal)))
 
 
@@ -204,8 +206,8 @@ def _workspace(p, dev, workspace):
 
 def streamkl_bwd_prepare(q1, k1, q2, k2, g, scale: Optional[float] = None, causal: bool = False,
                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-(b,h) dS scale factors (and, for bf16 inputs, the transposed fp16
-    operand copies) for the backward passes; returns the workspace."""
+    """Per-(b,h) dS scale factors and (bf16 inputs) fp16 operand scales for the
+    backward passes; returns the workspace."""
     _check_inputs(q1, k1, q2, k2)
     p = problem_for(q1, k1, scale, causal)
     _check_rowvecs(q1, g)

@@ -13,12 +13,13 @@
 
 namespace {
 
-// Backward workspace: the per-(b,h) factors sigma, then for bf16 inputs the
-// transposed fp16 copies of q1, q2, k1, k2 ([BH][ceil(N/64)][D][64] each),
-// then, when the query-resident pass is split over key chunks, its partial dQ
-// ([splits][2][BH * NQ][D] fp32).
+// Backward workspace: the per-(b,h) factors sigma, the fp16 operand scales
+// of q1, q2, k1, k2 ([BH][4] fp32), for bf16 inputs the chunk maxima the
+// scales come from ([BH][4][kAbsChunks] fp32), then, when the query-resident
+// pass is split over key chunks, its partial dQ ([splits][2][BH * NQ][D] fp32).
 struct BwdLayout {
-  size_t tq1, tq2, tk1, tk2, dqp, total;
+  size_t xs, part, dqp, total;
+  bool split;  // the split dQ partials are part of the layout
 };
 inline size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
@@ -45,30 +46,21 @@ DqSplit dq_split(const streamkl_problem *p) {
   r.kchunk = (int)(per * skl::kBwdTile);
   return r.splits > 1 ? r : DqSplit{1, 0};
 }
-// Layout with transposed copies for `heads` heads after a sigma area for all
-// B*H heads.
-BwdLayout bwd_layout_heads(const streamkl_problem *p, size_t heads) {
+// Layout of a problem's backward workspace, with the split dQ partials when
+// `with_split` and the query-resident pass splits its keys.
+BwdLayout bwd_layout(const streamkl_problem *p, bool with_split = true) {
   BwdLayout l{};
   const size_t bh = (size_t)(p->B * p->H);
-  size_t o = round_up(bh * sizeof(float) > 16 ? bh * sizeof(float) : 16, 256);
-  if (p->dtype != STREAMKL_BF16) {
-    l.total = round_up(bh * sizeof(float) > 16 ? bh * sizeof(float) : 16, 16);
-    return l;
-  }
-  const size_t tile = (size_t)skl::kBwdTile;
-  const size_t qt = heads * (((size_t)p->NQ + tile - 1) / tile) * tile * (size_t)p->D * 2;
-  const size_t kt = heads * (((size_t)p->NK + tile - 1) / tile) * tile * (size_t)p->D * 2;
-  l.tq1 = o;
-  l.tq2 = l.tq1 + round_up(qt, 256);
-  l.tk1 = l.tq2 + round_up(qt, 256);
-  l.tk2 = l.tk1 + round_up(kt, 256);
-  l.dqp = l.tk2 + round_up(kt, 256);
+  l.xs = round_up(bh * sizeof(float) > 16 ? bh * sizeof(float) : 16, 256);
+  l.part = l.xs + round_up(bh * 4 * sizeof(float) > 16 ? bh * 4 * sizeof(float) : 16, 256);
+  l.dqp = l.part;
+  if (p->dtype == STREAMKL_BF16) l.dqp += round_up(bh * 4 * skl::kAbsChunks * sizeof(float), 256);
   const DqSplit ds = dq_split(p);
-  const size_t dqp = ds.splits > 1 ? (size_t)ds.splits * 2 * heads * (size_t)p->NQ * (size_t)p->D * 4 : 0;
+  l.split = with_split && ds.splits > 1;
+  const size_t dqp = l.split ? (size_t)ds.splits * 2 * bh * (size_t)p->NQ * (size_t)p->D * 4 : 0;
   l.total = l.dqp + round_up(dqp, 256);
   return l;
 }
-BwdLayout bwd_layout(const streamkl_problem *p) { return bwd_layout_heads(p, (size_t)(p->B * p->H)); }
 
 constexpr int kVersion = 200;  // 0.2.0
 static_assert(STREAMKL_NOALLOC_SCRATCH_BYTES == skl::kSplitkScratchBytes, "scratch size in the header");
@@ -78,7 +70,7 @@ bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // A dispatch's grid is at most 2^32 - 1 work-items.  The forward's largest
 // grids are its query tiles x key chunks and the split-K merge (one thread
 // per row); the backward's, its passes (resident tiles of 128 rows) and the
-// transposes (64-row tiles).
+// prepare step's chunk maxima (4 tensors x up to kAbsChunks per unit).
 constexpr __int128 kGridLimit = ((__int128)1 << 32) - 1;
 bool fwd_grids_fit(const streamkl_problem *p, int64_t splits) {
   const __int128 bh = (__int128)p->B * p->H;
@@ -93,8 +85,8 @@ bool bwd_grids_fit(const streamkl_problem *p) {
   const __int128 bh = (__int128)p->B * p->H;
   const int64_t nmax = p->NQ > p->NK ? p->NQ : p->NK;
   const __int128 bwd = bh * ((nmax + skl::kBwdBR - 1) / skl::kBwdBR) * 512 * dq_split(p).splits;
-  const __int128 tr = bh * ((nmax + skl::kBwdTile - 1) / skl::kBwdTile) * 256;
-  return bwd <= kGridLimit && tr <= kGridLimit;
+  const __int128 prep = bh * 4 * skl::kAbsChunks * 256;
+  return bwd <= kGridLimit && prep <= kGridLimit;
 }
 
 // Shape / dtype checks common to every entry point.
@@ -108,7 +100,7 @@ streamkl_status check_problem(const streamkl_problem *p) {
   if (p->causal && p->NQ > p->NK) return STREAMKL_ERR_SHAPE;
   // In-head byte offsets are 32-bit (buffer resources, per-head bases);
   // whole tensors use 64-bit bases.  The largest per-head object is an fp32
-  // gradient tensor; the transposed copies round rows up to 64.
+  // gradient tensor (bounded with rows rounded up to 64).
   const int64_t lim = (int64_t)1 << 31;
   const int64_t nmax = (p->NQ > p->NK ? p->NQ : p->NK);
   if (nmax >= lim || (nmax + 63) / 64 * 64 * p->D * 4 >= lim) return STREAMKL_ERR_SHAPE;
@@ -301,8 +293,7 @@ size_t streamkl_bwd_workspace_size(const streamkl_problem *p) {
 
 size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p) {
   if (check_bwd_problem(p) != STREAMKL_OK) return 0;
-  const int64_t bh = p->B * p->H;
-  return bwd_layout_heads(p, (size_t)(bh > 0 ? 1 : 0)).total;
+  return bwd_layout(p, false).total;
 }
 
 }  // extern "C"
@@ -327,9 +318,13 @@ streamkl_status check_bwd(const streamkl_problem *p, const void *q1, const void 
   return STREAMKL_OK;
 }
 
+// Backward parameters over a workspace of `workspace_bytes`: sigma and the
+// operand scales at the front; the query-resident pass splits its keys only
+// when the workspace also holds the split partials (else it runs unsplit:
+// the same results up to the fp32 summation order of dQ).
 skl::BwdParams make_bwd(const streamkl_problem *p, const void *q1, const void *k1, const void *q2, const void *k2,
                         const float *kl, const float *lse1, const float *lse2, const float *g, float *dq1,
-                        float *dk1, float *dq2, float *dk2, const void *workspace) {
+                        float *dk1, float *dq2, float *dk2, const void *workspace, size_t workspace_bytes) {
   skl::BwdParams b{};
   b.q1 = q1;
   b.k1 = k1;
@@ -339,20 +334,16 @@ skl::BwdParams make_bwd(const streamkl_problem *p, const void *q1, const void *k
   b.lse1 = lse1;
   b.lse2 = lse2;
   b.g = g;
-  b.sigma = reinterpret_cast<const float *>(workspace);
-  if (p->dtype == STREAMKL_BF16) {
-    const BwdLayout l = bwd_layout(p);
-    const char *w = reinterpret_cast<const char *>(workspace);
-    b.tq1 = w + l.tq1;
-    b.tq2 = w + l.tq2;
-    b.tk1 = w + l.tk1;
-    b.tk2 = w + l.tk2;
+  const BwdLayout l = bwd_layout(p, workspace_bytes >= bwd_layout(p, true).total);
+  const char *w = reinterpret_cast<const char *>(workspace);
+  b.sigma = reinterpret_cast<const float *>(w);
+  b.xscale = reinterpret_cast<const float *>(w + l.xs);
+  b.splits = 1;
+  if (l.split) {
     const DqSplit ds = dq_split(p);
     b.splits = ds.splits;
     b.kchunk = ds.kchunk;
-    b.dqp = ds.splits > 1 ? const_cast<float *>(reinterpret_cast<const float *>(w + l.dqp)) : nullptr;
-  } else {
-    b.splits = 1;
+    b.dqp = const_cast<float *>(reinterpret_cast<const float *>(w + l.dqp));
   }
   b.dq1 = dq1;
   b.dk1 = dk1;
@@ -365,39 +356,6 @@ skl::BwdParams make_bwd(const streamkl_problem *p, const void *q1, const void *k
   b.NK = p->NK;
   b.scale = p->scale;
   b.causal = p->causal ? 1 : 0;
-  return b;
-}
-
-// The same parameters restricted to heads [h0, h0 + n) of the flattened
-// B*H range, with that group's transposed copies at layout `l` of `workspace`.
-skl::BwdParams head_group(const streamkl_problem *p, skl::BwdParams b, int64_t h0, int64_t n, const BwdLayout &l,
-                          void *workspace) {
-  const size_t es = p->dtype == STREAMKL_BF16 ? 2 : 4;
-  auto adv = [](const void *ptr, int64_t bytes) -> const void * {
-    return ptr ? reinterpret_cast<const char *>(ptr) + bytes : nullptr;
-  };
-  auto advf = [](float *ptr, int64_t elems) -> float * { return ptr ? ptr + elems : nullptr; };
-  const int64_t q = h0 * p->NQ * p->D, k = h0 * p->NK * p->D;
-  b.q1 = adv(b.q1, q * (int64_t)es);
-  b.q2 = adv(b.q2, q * (int64_t)es);
-  b.k1 = adv(b.k1, k * (int64_t)es);
-  b.k2 = adv(b.k2, k * (int64_t)es);
-  b.kl += h0 * p->NQ;
-  b.lse1 += h0 * p->NQ;
-  b.lse2 += h0 * p->NQ;
-  b.g += h0 * p->NQ;
-  b.sigma += h0;
-  b.dq1 = advf(b.dq1, q);
-  b.dq2 = advf(b.dq2, q);
-  b.dk1 = advf(b.dk1, k);
-  b.dk2 = advf(b.dk2, k);
-  const char *w = reinterpret_cast<const char *>(workspace);
-  b.tq1 = w + l.tq1;
-  b.tq2 = w + l.tq2;
-  b.tk1 = w + l.tk1;
-  b.tk2 = w + l.tk2;
-  if (b.splits > 1) b.dqp = const_cast<float *>(reinterpret_cast<const float *>(w + l.dqp));
-  b.BH = n;
   return b;
 }
 
@@ -423,34 +381,28 @@ streamkl_status run_dq(const streamkl_problem *p, skl::BwdParams b, hipStream_t 
   return STREAMKL_OK;
 }
 
-// sigma of every unit of `b` into the front of its workspace.
-streamkl_status run_sigma(const streamkl_problem *p, const skl::BwdParams &b, hipStream_t s) {
-  return skl::launch_grad_scale(p->dtype, b.g, b.qmap, b.BH, p->NQ, const_cast<float *>(b.sigma), s) == hipSuccess
-             ? STREAMKL_OK
-             : STREAMKL_ERR_HIP;
-}
-
-// Transposed fp16 copies of the group's heads (bf16 inputs).
-streamkl_status run_transposes(const streamkl_problem *p, const skl::BwdParams &b, hipStream_t s) {
-  const int D = (int)p->D;
-  void *tq1 = const_cast<void *>(b.tq1), *tq2 = const_cast<void *>(b.tq2);
-  void *tk1 = const_cast<void *>(b.tk1), *tk2 = const_cast<void *>(b.tk2);
-  if (skl::launch_bwd_transpose(D, b.q1, b.qmap, b.BH, p->NQ, tq1, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, b.q2, b.qmap, b.BH, p->NQ, tq2, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, b.k1, b.kmap, b.BH, p->NK, tk1, s) != hipSuccess ||
-      skl::launch_bwd_transpose(D, b.k2, b.kmap, b.BH, p->NK, tk2, s) != hipSuccess)
-    return STREAMKL_ERR_HIP;
-  return STREAMKL_OK;
-}
-
-streamkl_status run_prepare(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
-                            const void *k2, const float *g, void *workspace, hipStream_t s) {
+// The prepare step of `b`'s units into the front of `workspace`: sigma and,
+// for bf16 inputs, the operand scales from the chunk maxima.
+streamkl_status run_prepare(const streamkl_problem *p, const skl::BwdParams &b, void *workspace, hipStream_t s) {
   if (p->NQ == 0) return STREAMKL_OK;
-  const skl::BwdParams b =
-      make_bwd(p, q1, k1, q2, k2, nullptr, nullptr, nullptr, g, nullptr, nullptr, nullptr, nullptr, workspace);
-  streamkl_status st = run_sigma(p, b, s);
-  if (st != STREAMKL_OK || p->dtype != STREAMKL_BF16) return st;
-  return run_transposes(p, b, s);
+  const BwdLayout l = bwd_layout(p, false);
+  char *w = reinterpret_cast<char *>(workspace);
+  skl::PrepParams pp{};
+  pp.q1 = b.q1;
+  pp.q2 = b.q2;
+  pp.k1 = b.k1;
+  pp.k2 = b.k2;
+  pp.g = b.g;
+  pp.qmap = b.qmap;
+  pp.kmap = b.kmap;
+  pp.BH = b.BH;
+  pp.NQ = p->NQ;
+  pp.NK = p->NK;
+  pp.D = (int)p->D;
+  pp.sigma = reinterpret_cast<float *>(w);
+  pp.xscale = reinterpret_cast<float *>(w + l.xs);
+  pp.part = p->dtype == STREAMKL_BF16 ? reinterpret_cast<float *>(w + l.part) : nullptr;
+  return skl::launch_bwd_prepare(p->dtype, pp, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
 }
 
 }  // namespace
@@ -467,33 +419,14 @@ streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const vo
   if (p->B * p->H == 0 || (p->NQ == 0 && p->NK == 0)) return STREAMKL_OK;
   if (!dq1 && !dq2) return STREAMKL_OK;
   float *outs[4] = {dq1, dk1, dq2, dk2};
-  const bool grouped = p->dtype == STREAMKL_BF16 && p->NQ > 0 && workspace_bytes < streamkl_bwd_workspace_size(p);
   st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 4, workspace, workspace_bytes,
                  streamkl_bwd_workspace_size_min(p));
   if (st != STREAMKL_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, dk1, dq2, dk2, workspace);
-  if (!grouped) {
-    if ((st = run_prepare(p, q1, k1, q2, k2, g, workspace, s)) != STREAMKL_OK) return st;
-    if ((st = run_dk(p, b, s)) != STREAMKL_OK) return st;
-    return run_dq(p, b, s);
-  }
-  // A smaller workspace: the transposed copies are made and used for as many
-  // heads at a time as fit (at least one, as the minimum-size query states).
-  const int64_t bh = p->B * p->H;
-  int64_t n = 1;
-  while (n < bh && bwd_layout_heads(p, (size_t)(2 * n)).total <= workspace_bytes) n *= 2;
-  while (n < bh && bwd_layout_heads(p, (size_t)(n + 1)).total <= workspace_bytes) ++n;
-  const BwdLayout l = bwd_layout_heads(p, (size_t)n);
-  if ((st = run_sigma(p, b, s)) != STREAMKL_OK) return st;
-  for (int64_t h0 = 0; h0 < bh; h0 += n) {
-    const int64_t cnt = h0 + n <= bh ? n : bh - h0;
-    skl::BwdParams bg = head_group(p, b, h0, cnt, l, workspace);
-    if ((st = run_transposes(p, bg, s)) != STREAMKL_OK) return st;
-    if ((st = run_dk(p, bg, s)) != STREAMKL_OK) return st;
-    if ((st = run_dq(p, bg, s)) != STREAMKL_OK) return st;
-  }
-  return STREAMKL_OK;
+  skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, dk1, dq2, dk2, workspace, workspace_bytes);
+  if ((st = run_prepare(p, b, workspace, s)) != STREAMKL_OK) return st;
+  if ((st = run_dk(p, b, s)) != STREAMKL_OK) return st;
+  return run_dq(p, b, s);
 }
 
 streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
@@ -505,9 +438,11 @@ streamkl_status streamkl_bwd_prepare(const streamkl_problem *p, const void *q1, 
   if ((st = check_inputs(p, q1, k1, q2, k2)) != STREAMKL_OK) return st;
   if (!g) return STREAMKL_ERR_NULL;
   if (!aligned16(g)) return STREAMKL_ERR_ALIGN;
-  if (!workspace || workspace_bytes < streamkl_bwd_workspace_size(p)) return STREAMKL_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < streamkl_bwd_workspace_size_min(p)) return STREAMKL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
-  return run_prepare(p, q1, k1, q2, k2, g, workspace, reinterpret_cast<hipStream_t>(stream));
+  const skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, nullptr, nullptr, nullptr, g, nullptr, nullptr, nullptr,
+                                    nullptr, workspace, workspace_bytes);
+  return run_prepare(p, b, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 streamkl_status streamkl_bwd_dk(const streamkl_problem *p, const void *q1, const void *k1, const void *q2,
@@ -519,9 +454,10 @@ streamkl_status streamkl_bwd_dk(const streamkl_problem *p, const void *q1, const
   if (p->B * p->H == 0 || p->NK == 0 || (!dk1 && !dk2)) return STREAMKL_OK;
   float *outs[2] = {dk1, dk2};
   st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 2, workspace, workspace_bytes,
-                 streamkl_bwd_workspace_size(p));
+                 streamkl_bwd_workspace_size_min(p));
   if (st != STREAMKL_OK) return st;
-  skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, nullptr, dk1, nullptr, dk2, workspace);
+  skl::BwdParams b =
+      make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, nullptr, dk1, nullptr, dk2, workspace, workspace_bytes);
   return run_dk(p, b, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -534,9 +470,10 @@ streamkl_status streamkl_bwd_dq(const streamkl_problem *p, const void *q1, const
   if (p->B * p->H == 0 || p->NQ == 0 || (!dq1 && !dq2)) return STREAMKL_OK;
   float *outs[2] = {dq1, dq2};
   st = check_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, outs, 2, workspace, workspace_bytes,
-                 streamkl_bwd_workspace_size(p));
+                 streamkl_bwd_workspace_size_min(p));
   if (st != STREAMKL_OK) return st;
-  skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, nullptr, dq2, nullptr, workspace);
+  skl::BwdParams b =
+      make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, nullptr, dq2, nullptr, workspace, workspace_bytes);
   return run_dq(p, b, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -665,14 +602,13 @@ skl::Seg run_seg(const streamkl_varlen_problem *v, const Run &r) {
   return g;
 }
 
-// Backward workspace of a packed batch: sigma for every (sequence, head),
-// then the transposed copies of every run that the segmented passes take
-// (bf16 inputs; each of the four tensors' copies contiguous over the runs, a
-// run's at the same offset in the two query or the two key regions).  A run
-// whose query-gradient pass splits its keys runs on its own afterwards, with
-// the plain layout of its problem at the front of the workspace.
+// Backward workspace of a packed batch: sigma, the operand scales and (bf16
+// inputs) the chunk maxima for every (sequence, head) of the runs that the
+// segmented passes take, laid out like a problem's over all B * H units.  A
+// run whose query-gradient pass splits its keys runs on its own afterwards,
+// with the layout of its own problem at the front of the workspace.
 struct VarlenLayout {
-  size_t tq1, tq2, tk1, tk2, total;
+  size_t xs, part, total;
 };
 
 // The query-gradient pass splits keys only to fill the GPU: with at least
@@ -695,35 +631,22 @@ bool run_segmented_bwd(const streamkl_varlen_problem *v, const Run &r, bool fill
   return dq_split(&p).splits == 1;
 }
 
-size_t run_copy_bytes(const streamkl_varlen_problem *v, const Run &r, int64_t n) {
-  const size_t tile = (size_t)skl::kBwdTile;
-  const size_t units = (size_t)((r.b1 - r.b0) * v->H);
-  return round_up(units * (((size_t)n + tile - 1) / tile) * tile * (size_t)v->D * 2, 256);
-}
-
 VarlenLayout varlen_layout(const streamkl_varlen_problem *v) {
   VarlenLayout l{};
   const size_t units = (size_t)(v->B * v->H);
-  const size_t sig = round_up(units * sizeof(float) > 16 ? units * sizeof(float) : 16, 256);
-  size_t qb = 0, kb = 0, solo = 16;
+  l.xs = round_up(units * sizeof(float) > 16 ? units * sizeof(float) : 16, 256);
+  l.part = l.xs + round_up(units * 4 * sizeof(float) > 16 ? units * 4 * sizeof(float) : 16, 256);
+  size_t total = l.part;
+  if (v->dtype == STREAMKL_BF16) total += round_up(units * 4 * skl::kAbsChunks * sizeof(float), 256);
   const bool fills = batch_fills_gpu(v);
   for_each_run(v, [&](const Run &r) {
-    if (run_segmented_bwd(v, r, fills)) {
-      if (v->dtype == STREAMKL_BF16) {
-        qb += run_copy_bytes(v, r, r.nq);
-        kb += run_copy_bytes(v, r, r.nk);
-      }
-    } else if (r.nq > 0) {
+    if (r.nq > 0 && !run_segmented_bwd(v, r, fills)) {
       const streamkl_problem p = run_problem(v, r);
-      solo = std::max(solo, bwd_layout(&p).total);
+      total = std::max(total, bwd_layout(&p).total);
     }
     return STREAMKL_OK;
   });
-  l.tq1 = sig;
-  l.tq2 = l.tq1 + qb;
-  l.tk1 = l.tq2 + qb;
-  l.tk2 = l.tk1 + kb;
-  l.total = std::max(l.tk2 + kb, solo);
+  l.total = total;
   return l;
 }
 
@@ -816,12 +739,11 @@ streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const VarlenLayout l = varlen_layout(v);
   char *w = reinterpret_cast<char *>(workspace);
-  float *sigma = reinterpret_cast<float *>(workspace);
 
-  // Query-less runs: their key gradients are zero.  Segmented runs: sigma and
-  // transposed copies into their places, then one pass of each kind over all.
-  std::vector<SegItem> sig_items, tq_items, tk_items, dk_items, dq_items;
-  size_t qoff = 0, koff = 0;
+  // Query-less runs: their key gradients are zero.  Segmented runs: the
+  // prepare step (chunk maxima, then sigma and the operand scales, each
+  // unit's at its place in the batch), then one pass of each kind over all.
+  std::vector<SegItem> abs_items, sig_items, dk_items, dq_items;
   const bool fills = batch_fills_gpu(v);
   st = for_each_run(v, [&](const Run &r) {
     const int64_t ok = v->cu_seqlens_k[r.b0];
@@ -834,20 +756,13 @@ streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void
     }
     if (!run_segmented_bwd(v, r, fills)) return STREAMKL_OK;
     SegItem it{run_seg(v, r), 0, 0};
-    if (bf16) {
-      it.seg.tq = (int64_t)qoff;
-      it.seg.tk = (int64_t)koff;
-      qoff += run_copy_bytes(v, r, r.nq);
-      koff += run_copy_bytes(v, r, r.nk);
-    }
-    const int64_t tile = skl::kBwdTile, br = skl::kBwdBR;
-    SegItem us = it, tq = it, tk = it;
-    us.count = it.seg.units;  // sigma: one workgroup per unit
-    tq.count = it.seg.units * ((r.nq + tile - 1) / tile);
-    tk.count = it.seg.units * ((r.nk + tile - 1) / tile);
+    it.seg.chunks = skl::abs_chunks(r.nq, r.nk);
+    const int64_t br = skl::kBwdBR;
+    SegItem ab = it, us = it;
+    ab.count = it.seg.units * 4 * it.seg.chunks;  // chunk maxima: (unit, tensor, chunk)
+    us.count = it.seg.units;                      // sigma and scales: one workgroup per unit
+    abs_items.push_back(ab);
     sig_items.push_back(us);
-    tq_items.push_back(tq);
-    tk_items.push_back(tk);
     SegItem a = it, b = it;
     a.count = it.seg.units * ((r.nk + br - 1) / br);  // dK pass: key tiles, streaming the queries
     a.weight = r.nq;
@@ -859,31 +774,28 @@ streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void
   });
   if (st != STREAMKL_OK) return st;
   if (!dk_items.empty()) {
-    // Prepare step of all segmented runs: sigma, then the transposed copies.
-    const skl::RowMap qm{0, TQ, (int)H, 0}, km{0, TK, (int)H, 0};
-    st = launch_segments(sig_items, [&](const skl::SegTable &t) {
-      return skl::launch_grad_scale_segs(v->dtype, g, qm, t, sigma, s) == hipSuccess ? STREAMKL_OK
-                                                                                      : STREAMKL_ERR_HIP;
-    });
-    if (st != STREAMKL_OK) return st;
+    skl::PrepParams pp{};
+    pp.q1 = q1;
+    pp.q2 = q2;
+    pp.k1 = k1;
+    pp.k2 = k2;
+    pp.g = g;
+    pp.qmap = skl::RowMap{0, TQ, (int)H, 0};
+    pp.kmap = skl::RowMap{0, TK, (int)H, 0};
+    pp.D = (int)D;
+    pp.sigma = reinterpret_cast<float *>(w);
+    pp.xscale = reinterpret_cast<float *>(w + l.xs);
+    pp.part = bf16 ? reinterpret_cast<float *>(w + l.part) : nullptr;
     if (bf16) {
-      const std::pair<const void *, size_t> qs[2] = {{q1, l.tq1}, {q2, l.tq2}}, ks[2] = {{k1, l.tk1}, {k2, l.tk2}};
-      for (int i = 0; i < 2 && st == STREAMKL_OK; ++i) {
-        st = launch_segments(tq_items, [&](const skl::SegTable &t) {
-          return skl::launch_bwd_transpose_segs((int)D, qs[i].first, qm, 0, t, w + qs[i].second, s) == hipSuccess
-                     ? STREAMKL_OK
-                     : STREAMKL_ERR_HIP;
-        });
-        if (st == STREAMKL_OK)
-          st = launch_segments(tk_items, [&](const skl::SegTable &t) {
-            return skl::launch_bwd_transpose_segs((int)D, ks[i].first, km, 1, t, w + ks[i].second, s) ==
-                           hipSuccess
-                       ? STREAMKL_OK
-                       : STREAMKL_ERR_HIP;
-          });
-      }
+      st = launch_segments(abs_items, [&](const skl::SegTable &t) {
+        return skl::launch_absmax_segs(pp, t, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+      });
       if (st != STREAMKL_OK) return st;
     }
+    st = launch_segments(sig_items, [&](const skl::SegTable &t) {
+      return skl::launch_grad_scale_segs(v->dtype, pp, t, s) == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP;
+    });
+    if (st != STREAMKL_OK) return st;
     skl::BwdParams b{};
     b.q1 = q1;
     b.k1 = k1;
@@ -893,16 +805,11 @@ streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void
     b.lse1 = lse1;
     b.lse2 = lse2;
     b.g = g;
-    b.sigma = sigma;
-    if (bf16) {
-      b.tq1 = w + l.tq1;
-      b.tq2 = w + l.tq2;
-      b.tk1 = w + l.tk1;
-      b.tk2 = w + l.tk2;
-    }
+    b.sigma = pp.sigma;
+    b.xscale = pp.xscale;
     b.splits = 1;
-    b.qmap = skl::RowMap{0, TQ, (int)H, 0};
-    b.kmap = skl::RowMap{0, TK, (int)H, 0};
+    b.qmap = pp.qmap;
+    b.kmap = pp.kmap;
     b.scale = v->scale;
     b.causal = v->causal ? 1 : 0;
     b.dk1 = dk1;
@@ -935,11 +842,10 @@ streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void
     skl::BwdParams b = make_bwd(&p, adv_rows(q1, oq, D, es), adv_rows(k1, ok, D, es), adv_rows(q2, oq, D, es),
                                 adv_rows(k2, ok, D, es), kl + oq, lse1 + oq, lse2 + oq, g + oq,
                                 adv_rowsf(dq1, oq, D), adv_rowsf(dk1, ok, D), adv_rowsf(dq2, oq, D),
-                                adv_rowsf(dk2, ok, D), workspace);
+                                adv_rowsf(dk2, ok, D), workspace, workspace_bytes);
     b.qmap = skl::RowMap{r.nq, TQ, (int)H, 0};
     b.kmap = skl::RowMap{r.nk, TK, (int)H, 0};
-    streamkl_status rs = run_sigma(&p, b, s);
-    if (rs == STREAMKL_OK && bf16) rs = run_transposes(&p, b, s);
+    streamkl_status rs = run_prepare(&p, b, workspace, s);
     if (rs == STREAMKL_OK) rs = run_dk(&p, b, s);
     if (rs == STREAMKL_OK) rs = run_dq(&p, b, s);
     return rs;

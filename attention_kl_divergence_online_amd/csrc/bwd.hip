@@ -24,9 +24,12 @@
 // no shuffle.  bf16 inputs use fp16 for the gradient product: dS in bf16
 // loses too much (8-bit significand) for the 2e-3 relative bound, fp16 keeps
 // 11 bits.  dS is scaled by a power of two sigma per (sequence, head) with
-// max|g| * sigma in [2^7, 2^8) so it sits in fp16's normal range; the factor
-// is divided out exactly at the end.  Q and K themselves convert to fp16
-// exactly as long as they lie within the fp16 range.
+// max|g| * sigma in [2^7, 2^8) so it sits in fp16's normal range, and the
+// streamed operand by a power of two per (sequence, head, tensor) that puts
+// its largest entry in [2^14, 2^15); both factors are divided out exactly at
+// the end, so no input range overflows fp16.  The prepare step computes them
+// (reading g and the inputs once); beyond them the backward keeps nothing in
+// device memory but its outputs.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -137,8 +140,8 @@ __device__ __forceinline__ void resident_tile(const BwdParams &p, int nrt, int S
 }
 
 // Workgroup wg of a segmented launch (t.n > 0, no key split): its segment's
-// parameters replace the run-dependent ones in p (the per-unit sigma and the
-// transposed copies move to the run's own), and wg, nwg become the
+// parameters replace the run-dependent ones in p (the per-unit sigma and
+// operand scales move to the run's own), and wg, nwg become the
 // workgroup's index and count within the segment.  A plain launch (t.n == 0)
 // keeps its parameters.
 __device__ __forceinline__ void select_segment(BwdParams &p, const SegTable &t, uint32_t &wg, uint32_t &nwg) {
@@ -154,13 +157,7 @@ __device__ __forceinline__ void select_segment(BwdParams &p, const SegTable &t, 
   p.kmap.sb = t.seg[lo].nk;
   p.kmap.base = t.seg[lo].ok;
   p.sigma += t.seg[lo].u0;
-  const int64_t tq = t.seg[lo].tq, tk = t.seg[lo].tk;
-  if (p.tq1) {
-    p.tq1 = reinterpret_cast<const char *>(p.tq1) + tq;
-    p.tq2 = reinterpret_cast<const char *>(p.tq2) + tq;
-    p.tk1 = reinterpret_cast<const char *>(p.tk1) + tk;
-    p.tk2 = reinterpret_cast<const char *>(p.tk2) + tk;
-  }
+  if (p.xscale) p.xscale += 4 * t.seg[lo].u0;
 }
 
 template <int D, bool KEYS_RES>
@@ -501,11 +498,18 @@ __global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p, const Seg
 // is complete) are independent of the dS arithmetic of stage t, and the two
 // are interleaved in one instruction stream.
 //
-// Both products read their streamed operand 16 bytes per lane from LDS: the
-// logits the original bf16 rows (exact products, as in the forward), the
-// gradient product a transposed fp16 copy of the streamed operand written by
-// the prepare step.  Both reach LDS through global_load_lds (no staging
-// registers, no LDS write instructions) into XOR-swizzled layouts.
+// The streamed operand reaches LDS once, as its original bf16 rows, through
+// global_load_lds (no staging registers, no LDS write instructions) into an
+// XOR-swizzled layout; the logits product reads it 16 bytes per lane (exact
+// products, as in the forward).  The gradient product needs the same tile
+// transposed (contraction over the streamed rows) and in fp16.  The four
+// waves that multiply a 32-row block already hold its bf16 fragments in
+// registers for the logits, so they also transpose it: one product against a
+// one-hot operand (times the tensor's power-of-two scale) yields, in the
+// accumulator layout, exactly the lane-ordered A operand of the gradient
+// product, which is rounded to fp16 and written to LDS for every wave that
+// needs it.  That costs two 32x32x16 products per 32x32 block and replaces a
+// transposed copy of every input in device memory.
 template <int D, bool KEYS_RES>
 struct Bwd4Traits {
   static constexpr int NT = 512;
@@ -516,28 +520,43 @@ struct Bwd4Traits {
   static constexpr int RB = D * 2;          // bf16 row bytes
   static constexpr int CPROW = RB / 16;     // 16-byte chunks per row
   static constexpr int ROW_T = BX * RB;     // one tensor's row tile
-  static constexpr int TR_T = D * BX * 2;   // one tensor's transposed tile: D rows of 64 fp16
-  static constexpr int DSX_SLOT = 64 * 16;  // one lane-ordered 16-byte operand
-  static constexpr int DSX_T = 8 * 2 * DSX_SLOT;  // one stage: [wave][ks]
+  static constexpr int SLOT = 64 * 16;      // one lane-ordered 16-byte operand
+  // One stage's transposed tiles, lane-ordered fp16 operands
+  // [distribution][streamed block][32-column block][k-step][lane].
+  static constexpr int TRB = 2 * 2 * NDB * 2 * SLOT;
+  static constexpr int DSX_T = 8 * 2 * SLOT;  // one stage's posted dS: [wave][ks]
   static constexpr int STAT_T = 1024;       // b1, b2, KL (fp32) and sign (16 bit) of 64 queries
-  static constexpr int REST = 4 * TR_T + 2 * DSX_T + (KEYS_RES ? 2 * STAT_T : 0);
+  static constexpr int REST = 2 * TRB + 2 * DSX_T + (KEYS_RES ? 2 * STAT_T : 0);
   // Two row-tile buffers when they fit (one barrier per stage), else one
   // (a second barrier per stage releases it for the next tile).
   static constexpr int ROWBUF = 4 * ROW_T + REST <= 160 * 1024 ? 2 : 1;
-  static constexpr int OFF_TR = ROWBUF * 2 * ROW_T;  // two buffers of 2 * TR_T
-  static constexpr int OFF_DSX = OFF_TR + 4 * TR_T;  // two buffers
+  static constexpr int OFF_TR = ROWBUF * 2 * ROW_T;  // two buffers of TRB
+  static constexpr int OFF_DSX = OFF_TR + 2 * TRB;   // two buffers
   static constexpr int OFF_STAT = OFF_DSX + 2 * DSX_T;
-  static constexpr int LDS_BYTES = OFF_STAT + (KEYS_RES ? 2 * STAT_T : 0);
+  // With one row buffer (spare LDS), the one-hot operands of the transposing
+  // products live in LDS rather than registers: [distribution][half][lane].
+  static constexpr int ID_BYTES = ROWBUF == 1 ? 2 * 2 * SLOT : 0;
+  static constexpr int OFF_ID = OFF_STAT + (KEYS_RES ? 2 * STAT_T : 0);
+  static constexpr int LDS_BYTES = OFF_ID + ID_BYTES;
   static constexpr int ROW_LOADS = 2 * ROW_T / 16 / NT;  // 16-byte loads per thread per stage
-  static constexpr int TR_LOADS = 2 * TR_T / 16 / NT;
   static_assert(BR == 4 * 32 && BX == 64, "tiles");
-  static_assert(ROW_LOADS * 16 * NT == 2 * ROW_T && TR_LOADS * 16 * NT == 2 * TR_T, "load split");
-  static_assert(ROW_T % (16 * NT) == 0 && TR_T % (16 * NT) == 0, "one tensor per load instruction");
-  static_assert((4 * TR_T + 2 * DSX_T) % (16 * NT) == 0, "clear split");
+  static_assert(ROW_LOADS * 16 * NT == 2 * ROW_T, "load split");
+  static_assert(ROW_T % (16 * NT) == 0, "one tensor per load instruction");
+  static_assert((2 * TRB + 2 * DSX_T) % (16 * NT) == 0, "clear split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-__device__ __forceinline__ int swz_tr(int d) { return (d >> 1) & 7; }  // 128-byte rows
+// One-hot B operand of the transposing product for 16-column half j of a
+// 32-column block: x[32 rows][16 k] * I gives a 32 x 32 block whose column c
+// is x's column c - 16 j for c in [16 j, 16 j + 16) and zero elsewhere, times
+// v.  Lane (h, c) supplies k = 8 h + u, nonzero where 16 j + 8 h + u == c.
+__device__ __forceinline__ bf16x8 onehot(int c, int h, int j, float v) {
+  const int u = c - 16 * j - 8 * h;
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)(i == u ? v : 0.f);
+  return r;
+}
 
 // MODE 0 computes both distributions' gradients; MODE 1 only the teacher's
 // (Configuration 2), MODE 2 only the student's (Configuration 1).  With one
@@ -562,7 +581,6 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   const int NR = KEYS_RES ? NK : NQ;
   const int NX = KEYS_RES ? NQ : NK;
   const int nrt = (NR + Tr::BR - 1) / Tr::BR;
-  const int nxt = (NX + Tr::BX - 1) / Tr::BX;  // transposed tiles per head
 
   const int S = KEYS_RES ? 1 : p.splits;
   int64_t bh;
@@ -575,8 +593,6 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   const bf16 *R2 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k2 : p.q2) + rr * D;
   const char *X1 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q1 : p.k1) + rx * D);
   const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q2 : p.k2) + rx * D);
-  const char *T1 = reinterpret_cast<const char *>(KEYS_RES ? p.tq1 : p.tk1) + bh * (int64_t)nxt * Tr::TR_T;
-  const char *T2 = reinterpret_cast<const char *>(KEYS_RES ? p.tq2 : p.tk2) + bh * (int64_t)nxt * Tr::TR_T;
   const float *KLr = p.kl + rq;
   const float *LS1 = p.lse1 + rq;
   const float *LS2 = p.lse2 + rq;
@@ -584,6 +600,8 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   const float sigma_raw = p.sigma[bh];
   const float sigma = fabsf(sigma_raw);
   const bool any_neg = sigma_raw < 0.f;
+  // Power-of-two scales of the streamed tensors' fp16 operands (teacher, student).
+  const float xs[2] = {p.xscale[bh * 4 + (KEYS_RES ? 0 : 2)], p.xscale[bh * 4 + (KEYS_RES ? 1 : 3)]};
 
   const int r0 = rt * Tr::BR;
   const int rlast_wg = min(r0 + Tr::BR, NR) - 1;
@@ -622,27 +640,19 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   if (!KEYS_RES && r_ok) query_stats(LS1[my_r], LS2[my_r], KLr[my_r], Gr[my_r], sigma, qb1, qb2, qkl, qsg);
 
   // ---- staging: global -> LDS without registers ----
-  // Buffer resources over this head's streamed rows and transposed tiles:
-  // 32-bit offsets, and rows past the end of the streamed operand read as
-  // zero (they only feed masked pairs).
+  // Buffer resources over this head's streamed rows: 32-bit offsets, and rows
+  // past the end of the streamed operand read as zero (they only feed masked
+  // pairs, and transpose to zero columns).
   const BufRange rx1{X1, NX * Tr::RB}, rx2{X2, NX * Tr::RB};
-  const BufRange rt1{T1, nxt * Tr::TR_T}, rt2{T2, nxt * Tr::TR_T};
-  // Per-lane source offsets within a tile (the same for both tensors).  Row
-  // tile: tensor-major, row r at r * RB, logical chunk c in slot c ^ swz_row(r).
-  // Transposed tile: tensor-major, column d at d * 128, chunk c in slot c ^ swz_tr(d).
-  constexpr int RL = Tr::ROW_LOADS / 2, TL = Tr::TR_LOADS / 2;
-  uint32_t vrow[RL], vtr[TL];
+  // Per-lane source offsets within a tile (the same for both tensors):
+  // tensor-major, row r at r * RB, logical chunk c in slot c ^ swz_row(r).
+  constexpr int RL = Tr::ROW_LOADS / 2;
+  uint32_t vrow[RL];
 #pragma unroll
   for (int i = 0; i < RL; ++i) {
     const int C = i * Tr::NT + tid;
     const int row = C / Tr::CPROW;
     vrow[i] = row * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(row)) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < TL; ++i) {
-    const int C = i * Tr::NT + tid;
-    const int d = C / 8;
-    vtr[i] = d * 128 + ((C % 8) ^ swz_tr(d)) * 16;
   }
   auto load_rows = [&](int t, int buf) {
     const uint32_t soff = (uint32_t)x_of(t) * Tr::RB;
@@ -652,15 +662,6 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
       for (int i = 0; i < RL; ++i)
         buffer_load_lds16(tn ? rx2 : rx1, smem + (buf * 2 + tn) * Tr::ROW_T + (i * Tr::NT + wave * 64) * 16,
                           vrow[i], soff);
-  };
-  auto load_tr = [&](int t, int buf) {
-    const uint32_t soff = (uint32_t)(x_of(t) / Tr::BX) * Tr::TR_T;
-#pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-      for (int i = 0; i < TL; ++i)
-        buffer_load_lds16(tn ? rt2 : rt1, smem + Tr::OFF_TR + (buf * 2 + tn) * Tr::TR_T + (i * Tr::NT + wave * 64) * 16,
-                          vtr[i], soff);
   };
   // Key-resident pass: statistics of the 64 streamed queries of a stage,
   // gathered by the first wave into stat buffer `buf`.
@@ -695,7 +696,7 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   // The pipeline's first step multiplies the second transposed buffer and the
   // second dS buffer by zero operands: clear them so that they hold no NaN.
   {
-    constexpr int NCLR = (4 * Tr::TR_T + 2 * Tr::DSX_T) / 16 / Tr::NT;
+    constexpr int NCLR = (2 * Tr::TRB + 2 * Tr::DSX_T) / 16 / Tr::NT;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < NCLR; ++i) *reinterpret_cast<u32x4 *>(smem + Tr::OFF_TR + (i * Tr::NT + tid) * 16) = z;
@@ -722,6 +723,22 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
     while (b < ntiles && tile_full(b)) ++b;
     t_a = a;
     t_b = b;
+  }
+
+  // One-hot operands of the transposing products, per distribution, scaled by
+  // the streamed tensor's power of two (exact in bf16): in registers, or in
+  // the LDS table.  Every wave writes the table's lane entries it reads, all
+  // with the same values, so no barrier orders the writes before the reads.
+  bf16x8 id0[2], id1[2];
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+    id0[t2] = onehot(c32, h, 0, xs[t2]);
+    id1[t2] = onehot(c32, h, 1, xs[t2]);
+    if (Tr::ID_BYTES) {
+      char *idp = smem + Tr::OFF_ID + t2 * 2 * Tr::SLOT + lane * 16;
+      *reinterpret_cast<bf16x8 *>(idp) = id0[t2];
+      *reinterpret_cast<bf16x8 *>(idp + Tr::SLOT) = id1[t2];
+    }
   }
 
   // Specialised per wave role and, in the key-resident pass, per presence of
@@ -844,19 +861,76 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
         }
       }
     };
+    // This wave's share of the transposition of streamed block e of the row
+    // tile into the lane-ordered fp16 tiles of its stage.  For each
+    // (distribution t, 32-column block db) it owns, two products against the
+    // one-hot operands give a 32x32 accumulator whose element r in lane
+    // (h, c) is row acc_row(r, h) of the block, column 32 db + c, times the
+    // tensor's scale: elements 8 ks .. 8 ks + 7 are exactly that lane's A
+    // operand of the gradient product's k-step ks, stored at [t][e][db][ks].
+    // Every wave of a block takes part whether or not its own rows see it:
+    // the other waves' products read the whole tile.
+    constexpr int NTR = MODE == 0 ? 2 : 1;      // distributions transposed
+    constexpr int PER = NTR * Tr::NDB;          // (t, db) pairs per block, dealt over the 4 waves
+    constexpr int NC = (PER + 3) / 4;           // pairs per wave (none for pr >= PER when PER < 4)
+    auto tr_pair = [&](int k, int &t, int &db) {
+      t = MODE != 0 ? TEN : (Tr::NDB == 4 ? k : pr >> 1);
+      db = (Tr::NDB == 4 || MODE != 0) ? pr : (pr & 1);
+    };
+    // The products, from the row tile at `rowb`.
+    auto tr_issue = [&](const char *rowb, f32x16(&T)[NC]) {
+      const int row = e * 32 + c32;
+      const int sw = swz_row<D>(row);
+  #pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        if (PER < 4 && pr >= PER) {
+          T[k] = f32x16{};
+          continue;
+        }
+        int t, db;
+        tr_pair(k, t, db);
+        const char *src = rowb + t * Tr::ROW_T + row * Tr::RB;
+        const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(src + ((4 * db + h) ^ sw) * 16);
+        const bf16x8 hi = *reinterpret_cast<const bf16x8 *>(src + ((4 * db + 2 + h) ^ sw) * 16);
+        bf16x8 i0, i1;
+        if (Tr::ID_BYTES) {
+          const char *idp = smem + Tr::OFF_ID + t * 2 * Tr::SLOT + lane * 16;
+          i0 = *reinterpret_cast<const bf16x8 *>(idp);
+          i1 = *reinterpret_cast<const bf16x8 *>(idp + Tr::SLOT);
+        } else {
+          i0 = t ? id0[1] : id0[0];
+          i1 = t ? id1[1] : id1[0];
+        }
+        T[k] = mma16(lo, i0, f32x16{});
+        T[k] = mma16(hi, i1, T[k]);
+      }
+    };
+    // fp16 rounding and the lane-ordered stores.
+    auto tr_store = [&](const f32x16(&T)[NC], char *trw) {
+  #pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        if (PER < 4 && pr >= PER) break;
+        int t, db;
+        tr_pair(k, t, db);
+        f16x8 o[2];
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) o[r >> 3][r & 7] = (f16)T[k][r];
+        char *dst = trw + ((t * 2 + e) * Tr::NDB + db) * 2 * Tr::SLOT + lane * 16;
+        *reinterpret_cast<f16x8 *>(dst) = o[0];
+        *reinterpret_cast<f16x8 *>(dst + Tr::SLOT) = o[1];
+      }
+    };
     // Gradient product of this wave's distribution over streamed block xb of
-    // the transposed tile at `trb`: dR^T[d, resident] += X^T[d, streamed] * dS.
-    // The copy stores the 16 rows of a k-step in the dS operands' slot order,
-    // so lane half h reads 8 consecutive positions 32xb + 16ks + 8h.
+    // the transposed tiles at `trb`: dR^T[d, resident] += X^T[d, streamed] * dS.
+    // The transposed operand of k-step ks is stored in the dS operands' slot
+    // order (the accumulator layout), one 16-byte operand per lane.
     auto grad = [&](int xb, const char *trb, const f16x8(&bo)[2]) {
-      const int sw = swz_tr(c32);
-      const char *tb = trb + TEN * Tr::TR_T + (DB0 * 32 + c32) * 128;
+      const char *tb = trb + ((TEN * 2 + xb) * Tr::NDB + DB0) * 2 * Tr::SLOT + lane * 16;
   #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int pc = ((4 * xb + 2 * ks + h) ^ sw) * 16;
   #pragma unroll
         for (int db = 0; db < NACC; ++db) {
-          const f16x8 a = *reinterpret_cast<const f16x8 *>(tb + db * 32 * 128 + pc);
+          const f16x8 a = *reinterpret_cast<const f16x8 *>(tb + (db * 2 + ks) * Tr::SLOT);
           acc[db] = mma16(a, bo[ks], acc[db]);
         }
       }
@@ -875,9 +949,9 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
       }
     };
 
-    // Stage t: the transposed tile of stage t starts loading (second buffer),
-    // with two row buffers the next row tile too; logits of stage t; with one
-    // row buffer a barrier (row tile free) and then the next row tile starts
+    // Stage t: with two row buffers the next row tile starts loading; logits
+    // of stage t and this wave's share of its transposition; with one row
+    // buffer a barrier (row tile free) and then the next row tile starts
     // loading; dS of stage t interleaved with the gradient products of stage
     // t - 1; the partner's dS posted; all loads land; barrier.
     f16x8 prev[2] = {f16x8{}, f16x8{}};  // own block's dS (this wave's distribution) of stage t - 1
@@ -888,31 +962,38 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
         const int xt = x_of(t);
         const bool own_live = !MASK || !empty_blk(xt + 32 * e);
         const float *sb = reinterpret_cast<const float *>(smem + Tr::OFF_STAT + (t & 1) * Tr::STAT_T);
-        load_tr(t, t & 1);
         if (Tr::ROWBUF == 2 && more) load_rows(t + 1, (t + 1) & 1);
         if (more) stats_load(t + 1);
         f32x16 x1, x2;
-        if (own_live) logits(smem + (Tr::ROWBUF == 2 ? (t & 1) * 2 * Tr::ROW_T : 0), x1, x2);
+        const char *rowb = smem + (Tr::ROWBUF == 2 ? (t & 1) * 2 * Tr::ROW_T : 0);
+        // The transposition reads the row tile with the logits; with one row
+        // buffer its stores wait until after the barrier that frees that
+        // buffer, so that the products' latency overlaps the dS arithmetic.
+        f32x16 T[NC];
+        if (own_live) logits(rowb, x1, x2);
+        tr_issue(rowb, T);
+        if (Tr::ROWBUF == 2) tr_store(T, smem + Tr::OFF_TR + (t & 1) * Tr::TRB);
         if (Tr::ROWBUF == 1) {
           lds_barrier();
           if (more) load_rows(t + 1, 0);
+          tr_store(T, smem + Tr::OFF_TR + (t & 1) * Tr::TRB);
         }
         f16x8 mine[2] = {f16x8{}, f16x8{}}, other[2] = {f16x8{}, f16x8{}};
         if (own_live) dsblock(x1, x2, xt + 32 * e, sb, mask_tag, mine, other);
         {
           // Stage t - 1: own block from registers, partner's block from LDS.
-          const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * 2 * Tr::TR_T;
-          const char *dsp = smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::DSX_SLOT +
+          const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * Tr::TRB;
+          const char *dsp = smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::SLOT +
                             lane * 16;
           f16x8 pb[2];
   #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
+          for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::SLOT);
           grad2(trp, prev, pb);
         }
         {
-          char *dsw = smem + Tr::OFF_DSX + (t & 1) * Tr::DSX_T + (wave * 2) * Tr::DSX_SLOT + lane * 16;
+          char *dsw = smem + Tr::OFF_DSX + (t & 1) * Tr::DSX_T + (wave * 2) * Tr::SLOT + lane * 16;
   #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<f16x8 *>(dsw + ks * Tr::DSX_SLOT) = other[ks];
+          for (int ks = 0; ks < 2; ++ks) *reinterpret_cast<f16x8 *>(dsw + ks * Tr::SLOT) = other[ks];
         }
         prev[0] = mine[0];
         prev[1] = mine[1];
@@ -927,12 +1008,12 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
     if (ntiles > 0) {
       // Drain: gradient products of the last stage.
       const int t = ntiles;
-      const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * 2 * Tr::TR_T;
+      const char *trp = smem + Tr::OFF_TR + ((t + 1) & 1) * Tr::TRB;
       const char *dsp =
-          smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::DSX_SLOT + lane * 16;
+          smem + Tr::OFF_DSX + ((t + 1) & 1) * Tr::DSX_T + ((e ? pr : pr + 4) * 2) * Tr::SLOT + lane * 16;
       f16x8 pb[2];
   #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::DSX_SLOT);
+      for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::SLOT);
       grad2(trp, prev, pb);
     }
 
@@ -941,7 +1022,7 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
     // A key chunk of a split pass writes its partial (zeros if the chunk is
     // empty) in the dense [split][distribution][unit, row] layout instead.
     if (r_ok && (TEN ? p.want2 : p.want1)) {
-      const float f = p.scale / sigma * (KEYS_RES ? 1.f : qsg);
+      const float f = p.scale / sigma / xs[TEN] * (KEYS_RES ? 1.f : qsg);
       float *O = TEN ? (KEYS_RES ? p.dk2 : p.dq2) : (KEYS_RES ? p.dk1 : p.dq1);
       int64_t rowoff = (rr + my_r) * D;
       if (S > 1) {
@@ -974,57 +1055,74 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   }
 }
 
-// Transposed fp16 copy of one bf16 operand for the gradient product: for each
-// 64-row tile T of each (b, h), out[T][d][pos] = x[64T + row(pos)][d] with
-// row(pos) swapping bits 2 and 3 of pos (the slot order of the dS operands in
-// a 16-row k-step); rows past the end are zero.  One workgroup per (b, h, tile).
-// In a segmented launch (t.n > 0) each segment is a run of units with its own
-// row count, rows and copy area (`keys` picks the key fields).
-template <int D>
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16 *x, RowMap map, int64_t N, int64_t ntile,
-                                                        f16 *out, const SegTable t, int keys) {
-  constexpr int CPR = D * 2 / 16;
-  constexpr int LROW = D + 8;  // fp16 elements per LDS row (16-byte pad)
-  __shared__ __attribute__((aligned(16))) f16 tile[kBwdTile * LROW];
+// Prepare step, first kernel: the largest |x| over a chunk of rows of one
+// input tensor of one unit.  Workgroup (unit u, tensor tn, chunk c) of a
+// launch with C chunks per tensor covers rows [c * per, (c + 1) * per),
+// per = ceil(N / C), of q1, q2, k1, k2 (tn = 0..3; N = NQ for the queries, NK
+// for the keys) and writes the maximum (0 for no rows) to part[(u * 4 + tn) *
+// kAbsChunks + c].  bf16 magnitudes compare as their 15 low bits.  In a
+// segmented launch (t.n > 0) each segment is a run of units with its own
+// lengths, rows, chunk count and first unit.
+__global__ __launch_bounds__(256) void absmax_kernel(const bf16 *q1, const bf16 *q2, const bf16 *k1, const bf16 *k2,
+                                                     RowMap qmap, RowMap kmap, int64_t NQ, int64_t NK, int C,
+                                                     int D, float *part, const SegTable t) {
   uint32_t wg = blockIdx.x;
+  int64_t u0 = 0;
   if (t.n > 0) {
     const int i = seg_index(t, wg);
     wg -= t.seg[i].start;
-    N = keys ? t.seg[i].nk : t.seg[i].nq;
-    map.sb = N;
-    map.base = keys ? t.seg[i].ok : t.seg[i].oq;
-    ntile = (N + kBwdTile - 1) / kBwdTile;
-    out = reinterpret_cast<f16 *>(reinterpret_cast<char *>(out) + (keys ? t.seg[i].tk : t.seg[i].tq));
+    NQ = t.seg[i].nq;
+    NK = t.seg[i].nk;
+    qmap.sb = NQ;
+    qmap.base = t.seg[i].oq;
+    kmap.sb = NK;
+    kmap.base = t.seg[i].ok;
+    C = t.seg[i].chunks;
+    u0 = t.seg[i].u0;
   }
-  const int64_t T = wg % ntile, bh = wg / ntile;
-  const bf16 *xs = x + (map.row0(bh) + T * kBwdTile) * D;
-  const int nrow = (int)min<int64_t>(kBwdTile, N - T * kBwdTile);
-  for (int cidx = threadIdx.x; cidx < kBwdTile * CPR; cidx += 256) {
-    const int r = cidx / CPR, cc = cidx % CPR;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (r < nrow) w = *reinterpret_cast<const u32x4 *>(xs + (int64_t)r * D + cc * 8);
-    *reinterpret_cast<u32x4 *>(&tile[r * LROW + cc * 8]) = bf16x8_to_f16x8(w);
-  }
-  __syncthreads();
-  f16 *o = out + (bh * ntile + T) * (int64_t)(D * kBwdTile);
-  for (int cidx = threadIdx.x; cidx < D * (kBwdTile / 8); cidx += 256) {
-    const int d = cidx / (kBwdTile / 8), pc = cidx % (kBwdTile / 8);
-    f16x8 v;
+  const int64_t u = wg / (4u * (uint32_t)C);
+  const int tn = (int)((wg / (uint32_t)C) % 4u), c = (int)(wg % (uint32_t)C);
+  const bool keys = tn >= 2;
+  const int64_t N = keys ? NK : NQ;
+  const bf16 *x = tn == 0 ? q1 : tn == 1 ? q2 : tn == 2 ? k1 : k2;
+  const int64_t per = (N + C - 1) / C;
+  const int64_t r0 = min<int64_t>(N, (int64_t)c * per), r1 = min<int64_t>(N, r0 + per);
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(x + ((keys ? kmap : qmap).row0(u) + r0) * D);
+  const int64_t n16 = (r1 - r0) * D / 8;  // 16-byte chunks of the rows
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < n16; i += 256) {
+    const u32x4 w = src[i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pos = 8 * pc + i;
-      const int row = (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1);
-      v[i] = tile[row * LROW + d];
-    }
-    *reinterpret_cast<f16x8 *>(o + (int64_t)d * kBwdTile + 8 * pc) = v;
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    part[((u0 + u) * 4 + tn) * kAbsChunks + c] = __uint_as_float(m << 16);
   }
 }
 
-// sigma[b,h] = 2^(kGradExp - e) with 2^(e-1) <= max_i |g[b,h,i]| < 2^e (1 if g is all zero,
-// and 1 everywhere when `unit` is set: fp32 inputs need no scaling), stored
-// negated when some g[b,h,:] is negative.
+// Power of two that puts a largest magnitude m in [2^14, 2^15) (1 for m = 0 or
+// a non-finite m): the scale of a tensor's fp16 gradient-product operand.
+__device__ __forceinline__ float operand_scale(float m) {
+  if (!(m > 0.f) || !(m <= 3.4e38f)) return 1.f;
+  const int a = 14 - ilogbf(m);
+  return ldexpf(1.f, min(max(a, -126), 126));
+}
+
+// Prepare step, second kernel, one workgroup per unit:
+//  sigma[u] = 2^(kGradExp - e) with 2^(e-1) <= max_i |g[u,i]| < 2^e (1 if g is
+//  all zero, and 1 everywhere when `unit` is set: fp32 inputs need no
+//  scaling), stored negated when some g[u,:] is negative;
+//  xscale[4 u + tn] = operand_scale(max over the C chunk maxima of tensor tn)
+//  for bf16 inputs (part from absmax_kernel), 1 for fp32 inputs.
 __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap qmap, int64_t NQ, float *sigma,
-                                                         int unit, const SegTable t) {
+                                                         float *xscale, const float *part, int C, int unit,
+                                                         const SegTable t) {
   int64_t bh = blockIdx.x;
   if (t.n > 0) {  // a segmented launch: one workgroup per unit of each segment
     const int i = seg_index(t, (uint32_t)bh);
@@ -1033,6 +1131,15 @@ __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap 
     qmap.sb = NQ;
     qmap.base = t.seg[i].oq;
     sigma += t.seg[i].u0;
+    xscale += 4 * t.seg[i].u0;
+    if (part) part += 4 * kAbsChunks * t.seg[i].u0;
+    C = t.seg[i].chunks;
+  }
+  if (threadIdx.x < 4) {
+    float m = 0.f;
+    if (!unit)
+      for (int c = 0; c < C; ++c) m = fmaxf(m, part[(bh * 4 + threadIdx.x) * kAbsChunks + c]);
+    xscale[bh * 4 + threadIdx.x] = unit ? 1.f : operand_scale(m);
   }
   if (unit) {
     // fp32 inputs: no dS scaling, but the sign flag is still needed.
@@ -1095,17 +1202,33 @@ static hipError_t launch_fp32_pass(const BwdParams &p, const SegTable &t, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_grad_scale(int dtype, const float *g, RowMap qmap, int64_t BH, int64_t NQ, float *sigma,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(grad_scale_kernel, dim3((uint32_t)BH), dim3(256), 0, s, g, qmap, NQ, sigma,
-                     dtype == 1 ? 1 : 0, kNoSegs);
+hipError_t launch_bwd_prepare(int dtype, const PrepParams &p, hipStream_t s) {
+  if (p.BH == 0) return hipSuccess;
+  const int C = abs_chunks(p.NQ, p.NK);
+  if (dtype == 0) {
+    hipLaunchKernelGGL(absmax_kernel, dim3((uint32_t)(p.BH * 4 * C)), dim3(256), 0, s,
+                       reinterpret_cast<const bf16 *>(p.q1), reinterpret_cast<const bf16 *>(p.q2),
+                       reinterpret_cast<const bf16 *>(p.k1), reinterpret_cast<const bf16 *>(p.k2), p.qmap, p.kmap,
+                       p.NQ, p.NK, C, p.D, p.part, kNoSegs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(grad_scale_kernel, dim3((uint32_t)p.BH), dim3(256), 0, s, p.g, p.qmap, p.NQ, p.sigma,
+                     p.xscale, p.part, C, dtype == 1 ? 1 : 0, kNoSegs);
   return hipGetLastError();
 }
 
-hipError_t launch_grad_scale_segs(int dtype, const float *g, RowMap qmap, const SegTable &t, float *sigma,
-                                  hipStream_t s) {
-  hipLaunchKernelGGL(grad_scale_kernel, dim3(t.end), dim3(256), 0, s, g, qmap, (int64_t)0, sigma,
-                     dtype == 1 ? 1 : 0, t);
+hipError_t launch_absmax_segs(const PrepParams &p, const SegTable &t, hipStream_t s) {
+  hipLaunchKernelGGL(absmax_kernel, dim3(t.end), dim3(256), 0, s, reinterpret_cast<const bf16 *>(p.q1),
+                     reinterpret_cast<const bf16 *>(p.q2), reinterpret_cast<const bf16 *>(p.k1),
+                     reinterpret_cast<const bf16 *>(p.k2), p.qmap, p.kmap, (int64_t)0, (int64_t)0, 1, p.D, p.part,
+                     t);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_scale_segs(int dtype, const PrepParams &p, const SegTable &t, hipStream_t s) {
+  hipLaunchKernelGGL(grad_scale_kernel, dim3(t.end), dim3(256), 0, s, p.g, p.qmap, (int64_t)0, p.sigma, p.xscale,
+                     dtype == 1 ? nullptr : p.part, 1, dtype == 1 ? 1 : 0, t);
   return hipGetLastError();
 }
 
@@ -1131,31 +1254,6 @@ static hipError_t launch_bf16_pass(const BwdParams &p, const SegTable &t, hipStr
   if (p.want1) return launch_pass4<D, KEYS_RES, 1>(p, t, s);
   if (p.want2) return launch_pass4<D, KEYS_RES, 2>(p, t, s);
   return hipSuccess;
-}
-
-hipError_t launch_bwd_transpose(int D, const void *x, RowMap map, int64_t BH, int64_t N, void *out, hipStream_t s) {
-  if (BH == 0 || N == 0) return hipSuccess;
-  const int64_t ntile = (N + kBwdTile - 1) / kBwdTile;
-  const dim3 grid((uint32_t)(ntile * BH));
-  if (D == 128)
-    hipLaunchKernelGGL(transpose_kernel<128>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map, N,
-                       ntile, reinterpret_cast<f16 *>(out), kNoSegs, 0);
-  else
-    hipLaunchKernelGGL(transpose_kernel<64>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map, N,
-                       ntile, reinterpret_cast<f16 *>(out), kNoSegs, 0);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_transpose_segs(int D, const void *x, RowMap map, int keys, const SegTable &t, void *out,
-                                     hipStream_t s) {
-  const dim3 grid(t.end);
-  if (D == 128)
-    hipLaunchKernelGGL(transpose_kernel<128>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map,
-                       (int64_t)0, (int64_t)1, reinterpret_cast<f16 *>(out), t, keys);
-  else
-    hipLaunchKernelGGL(transpose_kernel<64>, grid, dim3(256), 0, s, reinterpret_cast<const bf16 *>(x), map,
-                       (int64_t)0, (int64_t)1, reinterpret_cast<f16 *>(out), t, keys);
-  return hipGetLastError();
 }
 
 hipError_t launch_bwd_dk_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s) {

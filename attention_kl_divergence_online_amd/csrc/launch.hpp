@@ -36,8 +36,8 @@ struct Seg {
   int64_t units;   // sequences x heads
   int64_t nq, nk;  // rows per sequence
   int64_t oq, ok;  // packed row of the run's first sequence, queries / keys
-  int64_t u0;      // first unit of the run in the batch (per-unit sigma)
-  int64_t tq, tk;  // byte offset of the run's transposed query / key copies
+  int64_t u0;      // first unit of the run in the batch (per-unit sigma, scales, chunk maxima)
+  int32_t chunks;  // prepare step: row chunks per tensor (abs_chunks(nq, nk))
 };
 constexpr int kMaxSegs = 32;
 struct SegTable {
@@ -77,9 +77,8 @@ struct BwdParams {
   const void *q1, *k1, *q2, *k2;      // qmap / kmap rows
   const float *kl, *lse1, *lse2, *g;  // qmap rows
   RowMap qmap, kmap;
-  const float *sigma;  // per unit power-of-two factor applied to g (null: 1)
-  // bf16 inputs: prepared transposed fp16 copies [BH][ceil(N/64)][D][64] (null for fp32)
-  const void *tq1, *tq2, *tk1, *tk2;
+  const float *sigma;   // per unit power-of-two factor applied to g
+  const float *xscale;  // per unit 4 powers of two: fp16 operand scales of q1, q2, k1, k2 (bf16 inputs)
   float *dq1, *dk1, *dq2, *dk2;  // like the inputs (qmap / kmap rows), fp32
   // bf16 query-resident pass over `splits` key chunks of `kchunk` keys: each
   // chunk writes a partial dQ into dqp ([split][distribution][BH * NQ][D],
@@ -96,8 +95,17 @@ struct BwdParams {
 constexpr int kFwdBK = 64;    // keys per forward stage of the split and fp32 shapes
 constexpr int kFwdChunkTile = 128;  // split-K chunks are whole multiples of this (and of every forward tile)
 constexpr int kBwdBR = 128;   // resident rows per backward workgroup
-constexpr int kBwdTile = 64;  // streamed rows per backward stage (tile of the transposed copies)
+constexpr int kBwdTile = 64;  // streamed rows per backward stage
 constexpr int kGradExp = 8;   // |g| * sigma <= 2^kGradExp before fp16 rounding of dS
+// The prepare step takes each tensor's largest magnitude over C row chunks
+// per unit, C = abs_chunks(NQ, NK) <= kAbsChunks (one chunk per 2048 rows of
+// the longer side).
+constexpr int kAbsChunks = 16;
+inline int abs_chunks(int64_t NQ, int64_t NK) {
+  const int64_t n = NQ > NK ? NQ : NK;
+  const int64_t c = (n + 2047) / 2048;
+  return (int)(c < 1 ? 1 : c > kAbsChunks ? kAbsChunks : c);
+}
 
 // Queries per forward workgroup for an input type (dtype: 0 = bf16, 1 = fp32)
 // and query count per head; `small`: the 4-wave bf16 shape for the main
@@ -126,32 +134,37 @@ hipError_t launch_splitk_merge(const FwdParams &p, hipStream_t s);
 // for the null stream), looked up once per device and kept.
 constexpr size_t kSplitkScratchBytes = (size_t)64 << 20;
 hipError_t splitk_scratch(hipStream_t s, float **ptr);
-// Backward pieces; `p.sigma` must point at the prepared per-(b,h) factors.
-hipError_t launch_grad_scale(int dtype, const float *g, RowMap qmap, int64_t BH, int64_t NQ, float *sigma,
-                             hipStream_t s);
+// The backward's prepare step: sigma per unit from g and, for bf16 inputs, the
+// fp16 operand scales of q1, q2, k1, k2 from their largest magnitudes.
+struct PrepParams {
+  const void *q1, *q2, *k1, *k2;  // qmap / kmap rows
+  const float *g;                 // qmap rows
+  RowMap qmap, kmap;
+  int64_t BH, NQ, NK;
+  int D;
+  float *sigma;   // [BH]
+  float *xscale;  // [BH][4]
+  float *part;    // [BH][4][kAbsChunks] chunk maxima (bf16 inputs)
+};
+hipError_t launch_bwd_prepare(int dtype, const PrepParams &p, hipStream_t s);
+// The same over the segments of a packed batch: the chunk maxima (segment
+// i holding units * 4 * chunks workgroups), then sigma and the scales (units
+// workgroups); p supplies the whole packed tensors and the maps' sh and H.
+hipError_t launch_absmax_segs(const PrepParams &p, const SegTable &t, hipStream_t s);
+hipError_t launch_grad_scale_segs(int dtype, const PrepParams &p, const SegTable &t, hipStream_t s);
+// Backward passes; p.sigma and p.xscale must hold the prepare step's results.
 hipError_t launch_bwd_dk(int dtype, int D, const BwdParams &p, hipStream_t s);
 hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s);
 // Either pass over the segments of t (t.n >= 1) in one launch of t.end
 // workgroups, segment i holding units * ceil(resident rows / kBwdBR) of them
 // (resident rows: nk for the dK pass, nq for the dQ pass; p.splits == 1).
-// p supplies the whole packed tensors, the maps' sh and H, sigma and the
-// transposed copies of the whole batch (each run's at its tq / tk offset).
+// p supplies the whole packed tensors, the maps' sh and H, and sigma and the
+// operand scales of the whole batch (each run's from its first unit u0).
 hipError_t launch_bwd_dk_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_bwd_dq_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_zero(float *dst, int64_t n, hipStream_t s);
 // dQ1 / dQ2 (the requested ones) = sum over the key chunks of p.dqp, in chunk order.
 hipError_t launch_dq_reduce(int D, const BwdParams &p, hipStream_t s);
-// bf16 inputs: transposed fp16 copy of x (BH units of N rows, addressed by `map`)
-// into out [BH][ceil(N/64)][D][64].
-hipError_t launch_bwd_transpose(int D, const void *x, RowMap map, int64_t BH, int64_t N, void *out, hipStream_t s);
-// The prepare step over the segments of t: sigma of every segment's units at
-// sigma + u0 (one workgroup per unit), and transposed copies of x (`keys`:
-// the key rows nk / ok, copies at out + tk bytes; else nq / oq / tq) with one
-// workgroup per unit and 64-row tile.  qmap / map supply sh and H.
-hipError_t launch_grad_scale_segs(int dtype, const float *g, RowMap qmap, const SegTable &t, float *sigma,
-                                  hipStream_t s);
-hipError_t launch_bwd_transpose_segs(int D, const void *x, RowMap map, int keys, const SegTable &t, void *out,
-                                     hipStream_t s);
 // Matrix-rate probe: `workgroups` workgroups of four waves, each wave `iters`
 // rounds of four independent 32x32x16 bf16 products; writes one float per
 // wave to sink[workgroups * 4].

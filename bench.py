@@ -167,7 +167,8 @@ def parse():
                     help="skip timing the other four workloads of the metric (C1 tiny_fp32, C2 causal_4k, "
                          "C3 noncausal_16k, C5 splitk_512k forward and splitk_bwd_128k)")
     ap.add_argument("--no-small-workspace", action="store_true",
-                    help="skip timing the backward with one-, four- and eight-head workspaces")
+                    help="accepted for older command lines; the backward's workspace is O(B*H) and "
+                         "needs no smaller-workspace timing")
     ap.add_argument("--other-configs", action="store_true",
                     help="also time forward and backward on the workloads outside the metric "
                          "(shortq_bwd_64k, causal_16k_d64, causal_4k_fp32), the decode split-K "
@@ -314,7 +315,7 @@ def main():
     memory = {
         "inputs_bytes": nbytes(q1, k1, q2, k2, g),
         "outputs_bytes": nbytes(kl, l1, l2, *grads),
-        "workspace_bytes": nbytes(ws),
+        "workspace_bytes": nbytes(ws),  # sigma, operand scales and their chunk maxima: O(B*H)
         "extra_during_step_bytes": extra_bytes,
         # P1 and P2 as full NQ x NK bf16 matrices, which the fused path never forms.
         "materialised_p_bytes": 2 * 2 * w.B * w.H * w.NQ * w.NK,
@@ -389,33 +390,6 @@ def main():
         },
         "memory": memory,
     }
-
-    # The same backward through the combined call with smaller workspaces:
-    # sigma plus the operand copies of a group of heads, made and consumed a
-    # group at a time, instead of copies of every head (the smallest accepted
-    # size holds one head's copies; sizes grow linearly with the group).
-    ws_full = nbytes(ws)
-    del ws
-    torch.cuda.empty_cache()
-    ws_lo = skl.bwd_workspace_size_min(q1, k1, w.scale, w.causal)
-    per_head = (ws_full - ws_lo) // max(1, w.B * w.H - 1)
-    small = []
-    for heads in (() if args.no_small_workspace else (1, 4, 8)):
-        if heads >= w.B * w.H:
-            break
-        ws_small = torch.empty(max(16, ws_lo + (heads - 1) * per_head), dtype=torch.uint8, device=dev)
-        skl.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws_small, out=grads)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(2):
-            skl.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws_small, out=grads)
-        e1.record()
-        torch.cuda.synchronize()
-        small.append({"heads_per_group": heads, "workspace_bytes": nbytes(ws_small),
-                      "bwd_ms": round(e0.elapsed_time(e1) / 2, 3)})
-        del ws_small
-    if small:
-        out["bwd_small_workspace"] = small
 
     # Sustained matrix rate under a full load (register operands only), set
     # beside the published peak the roofline fraction is taken against.

@@ -137,25 +137,25 @@ streamkl_status streamkl_fwd_splitk_noalloc(const streamkl_problem *p,
                                             int num_splits, void *stream);
 
 /*
- * Bytes of device workspace streamkl_bwd needs: one fp32 per (batch, head)
- * and, for bf16 inputs, transposed fp16 copies of q1, q2, k1 and k2
- * (2 * D * 64 * ceil(N / 64) bytes per (batch, head) and tensor, N = NQ for
- * the queries, NK for the keys).  With bf16 inputs and fewer than 256 query
- * tiles of 128 rows in all (B * H * ceil(NQ / 128) < 256), the query-gradient
- * pass splits the keys into S chunks, S = min(ceil(256 / tiles), 64,
- * ceil(NK / 64)) (then as many chunks as whole 64-key tiles fill), and the
- * workspace also holds S partial dQ1, dQ2 in fp32 (S * 2 * B * H * NQ * D * 4
- * bytes), summed in chunk order.  Returns 0 if the problem is invalid.
+ * Bytes of device workspace streamkl_bwd needs.  It holds, per (batch, head),
+ * the fp32 factor sigma by which dS is scaled before rounding, four fp32
+ * powers of two by which the fp16 gradient-product operands of q1, q2, k1
+ * and k2 are scaled, and (bf16 inputs) 64 fp32 partial maxima from which
+ * those come: O(B * H), a few KiB at 32 heads.  With bf16 inputs and fewer
+ * than 256 query tiles of 128 rows in all (B * H * ceil(NQ / 128) < 256), the
+ * query-gradient pass splits the keys into S chunks, S = min(ceil(256 /
+ * tiles), 64, ceil(NK / 64)) (then as many chunks as whole 64-key tiles fill),
+ * and the workspace also holds S partial dQ1, dQ2 in fp32 (S * 2 * B * H * NQ
+ * * D * 4 bytes), summed in chunk order.  Returns 0 if the problem is invalid.
  */
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p);
 
 /*
- * Smallest workspace streamkl_bwd accepts: the sigma factors of every head
- * plus, for bf16 inputs, the transposed copies of one (batch, head).  Given
- * less than streamkl_bwd_workspace_size, streamkl_bwd makes and consumes the
- * copies for as many heads at a time as fit, in more, smaller launches; the
- * results are bitwise the same.  The step-wise entry points below need the
- * full size.  Returns 0 if the problem is invalid.
+ * Smallest workspace streamkl_bwd accepts: the per-(batch, head) factors
+ * without the split partial dQ.  Given less than streamkl_bwd_workspace_size
+ * (but at least this), the query-gradient pass runs unsplit: dK is bitwise
+ * the same, dQ differs only in the fp32 summation order, and short query
+ * ranges run slower.  Returns 0 if the problem is invalid.
  */
 size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p);
 
@@ -175,12 +175,16 @@ size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p);
  * skip the teacher gradients (teacher fixed) or dq2 = dk2 = NULL to skip the
  * student's; a half-NULL pair is STREAMKL_ERR_NULL.  Outputs are overwritten.
  * With bf16 inputs the two gradient products run on fp16 matrix cores with
- * fp32 accumulation (dS in bf16 would exceed a 2e-3 relative error): entries
- * of Q and K must lie within the fp16 range, |x| <= 65504; larger entries give
- * non-finite gradients.  The fp16 dS operands are scaled so that the largest
- * |g| maps to [2^7, 2^8), so P1 * |log(P1/P2) - KL| must stay below about 255
- * at every pair; it exceeds that only where the teacher gives a key real mass
- * and the student a log-probability hundreds of nats lower.
+ * fp32 accumulation (dS in bf16 would exceed a 2e-3 relative error).  The
+ * streamed Q or K operand is scaled per (batch, head, tensor) by a power of
+ * two that puts its largest entry in [2^14, 2^15), so any finite bf16 input
+ * fits fp16 (entries below 2^-29 of the tensor's largest lose precision, a
+ * contribution below 2^-29 of the largest).  The fp16 dS operands are scaled
+ * so that the largest |g| maps to [2^7, 2^8), so P1 * |log(P1/P2) - KL| must
+ * stay below about 255 at every pair; it exceeds that only where the teacher
+ * gives a key real mass and the student a log-probability hundreds of nats
+ * lower.  `workspace` (at least streamkl_bwd_workspace_size_min bytes) is
+ * overwritten.  Extra device memory beyond the caller's buffers: none.
  */
 streamkl_status streamkl_bwd(const streamkl_problem *p,
                              const void *q1, const void *k1,
@@ -197,13 +201,15 @@ streamkl_status streamkl_bwd(const streamkl_problem *p,
  * read their inputs and the prepared workspace, so once the prepare step has
  * completed they may run on different streams.
  *
- * streamkl_bwd_prepare writes into `workspace` one fp32 per (batch, head): the
- * power of two sigma with max_i |g_i| * sigma in [2^7, 2^8), by which the
- * passes scale dS before rounding it to fp16 (1 for fp32 inputs), negated
- * when some g of that head is negative; with bf16 inputs it also writes the
- * transposed fp16 copies of q1, q2, k1, k2 that the gradient products read.
- * It reads q1, k1, q2, k2 (bf16 inputs only) and g, with the layouts and
- * alignment rules of streamkl_bwd.
+ * streamkl_bwd_prepare writes into `workspace`, per (batch, head): the power
+ * of two sigma with max_i |g_i| * sigma in [2^7, 2^8), by which the passes
+ * scale dS before rounding it to fp16 (1 for fp32 inputs), negated when some
+ * g of that head is negative; and the powers of two that scale the fp16
+ * operands of q1, q2, k1, k2 (1 for fp32 inputs), from their largest
+ * magnitudes.  It reads q1, k1, q2, k2 (bf16 inputs only) and g, with the
+ * layouts and alignment rules of streamkl_bwd, and needs at least
+ * streamkl_bwd_workspace_size_min bytes; the passes take the workspace size
+ * rules of streamkl_bwd (the dQ pass splits its keys only given the full size).
  * streamkl_bwd_dk writes dK1, dK2 (one pass over key tiles, queries streamed);
  * streamkl_bwd_dq writes dQ1, dQ2 (one pass over query tiles, keys streamed).
  * NULL-pair rules, layouts and errors are those of streamkl_bwd.  The dK
@@ -288,20 +294,18 @@ streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v,
                                     void *stream);
 
 /*
- * Workspace bytes for streamkl_bwd_varlen.  The workspace holds:
- *  - sigma for every (sequence, head): B * H fp32 in a slot rounded to 256 bytes;
- *  - for bf16 inputs, the four tensors' transposed fp16 copies of every run
- *    in the shared launches (laid out as streamkl_bwd's, one run after
- *    another, each run's rounded to 256 bytes).
- * If larger, it is instead the largest full-size streamkl_bwd workspace of a
- * run launched on its own (those reuse the front of the workspace one after
- * another).  Returns 0 if `v` is invalid.
+ * Workspace bytes for streamkl_bwd_varlen: the per-(sequence, head) factors
+ * of streamkl_bwd_workspace_size (sigma, operand scales and, for bf16 inputs,
+ * their partial maxima) for all B * H (sequence, head) pairs, laid out as for
+ * a problem of B * H heads.  If larger, it is instead the largest full-size
+ * streamkl_bwd workspace of a run launched on its own (those reuse the front
+ * of the workspace one after another).  Returns 0 if `v` is invalid.
  */
 size_t streamkl_bwd_varlen_workspace_size(const streamkl_varlen_problem *v);
 
 /*
  * Backward of every sequence (as streamkl_bwd, same NULL-pair rules and
- * fp16 range condition).  kl, lse1 and lse2 must come from
+ * operand scaling).  kl, lse1 and lse2 must come from
  * streamkl_fwd_varlen on the same inputs.  `workspace` must hold at least
  * streamkl_bwd_varlen_workspace_size bytes (STREAMKL_ERR_WORKSPACE
  * otherwise) and is overwritten.

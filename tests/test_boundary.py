@@ -173,32 +173,35 @@ def dq_splits(B, H, NQ, NK):
     return (ktiles + per - 1) // per
 
 
-def bf16_workspace(B, H, NQ, NK, D, heads=None):
-    # sigma of every head (256-byte slot), then transposed fp16 copies of q1, q2
-    # (64-row tiles) and k1, k2 for `heads` heads (default: all), then the split
-    # query pass's partial dQ1, dQ2 (fp32) for those heads.
+def bwd_workspace(B, H, NQ, NK, D, split=True, bf16=True):
+    # sigma of every head and the four operand scales of every head (256-byte
+    # slots), for bf16 inputs the chunk maxima (16 per head and tensor), then,
+    # with `split`, the split query pass's partial dQ1, dQ2 (fp32).
     up = lambda n, a: (n + a - 1) // a * a
-    tiles = lambda n: (n + 63) // 64
-    heads = B * H if heads is None else heads
-    qt, kt = heads * tiles(NQ) * 64 * D * 2, heads * tiles(NK) * 64 * D * 2
-    S = dq_splits(B, H, NQ, NK)
-    dqp = S * 2 * heads * NQ * D * 4 if S > 1 else 0
-    return up(max(16, 4 * B * H), 256) + 2 * up(qt, 256) + 2 * up(kt, 256) + up(dqp, 256)
+    bh = B * H
+    S = dq_splits(B, H, NQ, NK) if bf16 else 1
+    dqp = S * 2 * bh * NQ * D * 4 if (split and S > 1) else 0
+    part = up(bh * 4 * 16 * 4, 256) if bf16 else 0
+    return up(max(16, 4 * bh), 256) + up(max(16, 16 * bh), 256) + part + up(dqp, 256)
 
 
 def test_backward_validation(L):
     p = P()
     f32 = _lib.STREAMKL_FP32
-    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(dtype=f32))) == 16
-    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, dtype=f32))) == 96
-    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == bf16_workspace(1, 2, 8, 8, 64)
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(dtype=f32))) == 512
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, dtype=f32))) == 768
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == bwd_workspace(1, 2, 8, 8, 64)
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, NQ=65, NK=200, D=128))) == \
-        bf16_workspace(3, 7, 65, 200, 128)
+        bwd_workspace(3, 7, 65, 200, 128)
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(D=32))) == 0
-    # Minimum: sigma for every head, transposed copies of one head.
+    # Minimum: everything but the split query pass's partials (that pass then runs unsplit).
     assert L.streamkl_bwd_workspace_size_min(ctypes.byref(P(B=3, H=7, NQ=65, NK=200, D=128))) == \
-        bf16_workspace(3, 7, 65, 200, 128, heads=1)
-    assert L.streamkl_bwd_workspace_size_min(ctypes.byref(P(B=3, H=7, dtype=f32))) == 96
+        bwd_workspace(3, 7, 65, 200, 128, split=False)
+    assert bwd_workspace(3, 7, 65, 200, 128, split=False) < bwd_workspace(3, 7, 65, 200, 128)
+    assert L.streamkl_bwd_workspace_size_min(ctypes.byref(P(B=3, H=7, dtype=f32))) == 768
+    # O(B * H) at the 64K causal workload: 32 heads, no split, a few KiB.
+    big = P(B=1, H=32, NQ=65536, NK=65536, D=128, causal=1)
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(big)) == bwd_workspace(1, 32, 65536, 65536, 128) <= 16384
     # Below the minimum the combined call refuses; between minimum and full it accepts (not run here).
     pm = P(B=4, H=8)
     mn = L.streamkl_bwd_workspace_size_min(ctypes.byref(pm))
@@ -279,23 +282,17 @@ def test_varlen_validation(L):
 
 
 def varlen_bf16_workspace(B, H, D, runs):
-    # sigma of every (sequence, head) (256-byte slot), then the four tensors'
-    # transposed copies of the runs that join the segmented passes (each run's
-    # copy rounded to 256 bytes), or, if larger, the largest remaining run's own
-    # streamkl_bwd workspace.  All runs join when the batch has at least 256
-    # query tiles of 128 rows; otherwise those whose own query pass would split
-    # its keys run alone.
-    up = lambda n, a: (n + a - 1) // a * a
-    tiles = lambda n: (n + 63) // 64
+    # sigma, operand scales and chunk maxima of every (sequence, head), laid out
+    # as for a problem of B * H heads, or, if larger, the largest workspace of
+    # a run that runs on its own.  All runs join the segmented passes when the
+    # batch has at least 256 query tiles of 128 rows; otherwise those whose own
+    # query pass would split its keys run alone.
     fills = sum(b * H * ((nq + 127) // 128) for b, nq, nk in runs) >= 256
-    seg = up(max(16, 4 * B * H), 256)
-    solo = 16
+    need = bwd_workspace(B, H, 0, 0, D, split=False)
     for b, nq, nk in runs:
         if not fills and dq_splits(b, H, nq, nk) > 1:
-            solo = max(solo, bf16_workspace(b, H, nq, nk, D))
-        else:
-            seg += 2 * up(b * H * tiles(nq) * 64 * D * 2, 256) + 2 * up(b * H * tiles(nk) * 64 * D * 2, 256)
-    return max(seg, solo)
+            need = max(need, bwd_workspace(b, H, nq, nk, D))
+    return need
 
 
 def test_varlen_backward_validation(L):
@@ -316,8 +313,8 @@ def test_varlen_backward_validation(L):
     assert dq_splits(2, 32, 300, 300) > 1
     assert L.streamkl_bwd_varlen_workspace_size(v2.ref()) == varlen_bf16_workspace(3, 32, 64, runs2)
     f32 = VP(cu_q, cu_k, H=3, D=128, dtype=_lib.STREAMKL_FP32)
-    # fp32: sigma only, for all 5 x 3 (sequence, head) pairs in a 256-byte slot.
-    assert L.streamkl_bwd_varlen_workspace_size(f32.ref()) == 256
+    # fp32: sigma and the (unit) operand scales of all 5 x 3 (sequence, head) pairs.
+    assert L.streamkl_bwd_varlen_workspace_size(f32.ref()) == 512
     assert L.streamkl_bwd_varlen_workspace_size(VP([2, 3], [0, 3]).ref()) == 0
     assert vbwd(L, v, wsb=need - 1) == _lib.STREAMKL_ERR_WORKSPACE
     assert vbwd(L, v, ws=None) == _lib.STREAMKL_ERR_WORKSPACE
