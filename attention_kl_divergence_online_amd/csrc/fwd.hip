@@ -576,14 +576,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
       s2 += e2;
       sa = __builtin_fmaf(e1, x1[r] - x2[r], sa);
     }
+    // The block's sums are formed before the refold test, in the same
+    // instruction stream as the next block's products (left to itself the
+    // compiler would sink the accumulator chain past the branch, after them).
+    float nl1 = st.l1 + s1, nl2 = st.l2 + s2, nacc = st.acc + sa;
+    asm volatile("" : "+v"(nl1), "+v"(nl2), "+v"(nacc));
     if (__builtin_expect(__any(!(s1 <= kLazySumMax && s2 <= kLazySumMax)), 0)) {
       online_update<false, false>(x1, x2, st, c, 0, h, 0);
       hb1 = st.m1 * c;
       hb2 = st.m2 * c;
     } else {
-      st.l1 += s1;
-      st.l2 += s2;
-      st.acc += sa;
+      st.l1 = nl1;
+      st.l2 = nl2;
+      st.acc = nacc;
     }
   };
 
@@ -593,11 +598,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
   }
   __syncthreads();
 
-  // Step b: logits of block b and the update of block b - 1.  Both blocks of
-  // a tile are fully visible in the steady state, which runs without mask
-  // code; its one branch is the lazy update's rarely taken exact refold.
+  // Step b: logits of block b and the update of block b - 1 (held in p1, p2).
   f32x16 p1 = f32x16{}, p2 = f32x16{};
-  for (int t = 0; t < ntiles; ++t) {
+  auto generic_tile = [&](int t) {
     if (t + 1 < ntiles) load_tile(t + 1);
 #pragma unroll
     for (int kb = 0; kb < Tr::BPT; ++kb) {
@@ -620,7 +623,30 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
     }
     wait_loads();
     lds_barrier();
-  }
+  };
+  // Tiles [1, t_steady) hold only fully visible blocks past the first two: the
+  // steady state, without mask code, its one branch the lazy update's rarely
+  // taken exact refold.  Its blocks alternate between two register sets (an
+  // even number per tile), so no logits are copied from one set to the other.
+  const int t_steady = Tr::BPT % 2 == 0 ? nfull / Tr::BPT : 0;
+  auto steady_tile = [&](int t) {
+    if (t + 1 < ntiles) load_tile(t + 1);
+    f32x16 a1, a2;
+#pragma unroll
+    for (int kb = 0; kb < Tr::BPT; kb += 2) {
+      const int b = Tr::BPT * t + kb;
+      scores(b, a1, a2);
+      lazy_update(p1, p2);
+      scores(b + 1, p1, p2);
+      lazy_update(a1, a2);
+    }
+    wait_loads();
+    lds_barrier();
+  };
+  int tile = 0;
+  if (ntiles > 0) generic_tile(tile++);
+  for (; tile < t_steady; ++tile) steady_tile(tile);
+  for (; tile < ntiles; ++tile) generic_tile(tile);
   if (Tr::BPT * ntiles - 1 < nlive && ntiles > 0) update(Tr::BPT * ntiles - 1, p1, p2);
 
   // Merge the two lane halves that hold disjoint keys of the same query.

@@ -143,6 +143,30 @@ def summarize_counters(csvs, out_path: str) -> None:
     with open(out_path, "w") as fo:
         fo.write(text)
     print(text)
+    # Co-execution of the matrix and vector units, when the counters are present:
+    # per SIMD, as shares of the kernel's cycles.  MFMA busy and co-exec divide
+    # SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES by SIMDs x kernel
+    # cycles; VALU active is 2 waves per SIMD x SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES;
+    # idle = 1 - (MFMA busy + VALU active - co-exec).
+    rows = []
+    for key in KERNELS:
+        d = {k: sum(v) / len(v) for k, v in vals.get(key, {}).items()}
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" not in d or "GRBM_GUI_ACTIVE" not in d:
+            continue
+        cyc = d["GRBM_GUI_ACTIVE"] / xcds
+        mf = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cyc)
+        co = d["SQ_VALU_MFMA_COEXEC_CYCLES"] / (simds * cyc)
+        va = 2 * d.get("SQ_ACTIVE_INST_VALU", float("nan")) / d["SQ_WAVE_CYCLES"]
+        lw = d.get("SQ_WAIT_INST_LDS", float("nan")) / d["SQ_WAVE_CYCLES"]
+        rows.append(f"{key:9s} {mf:10.1%} {co:8.1%} {co / mf:13.1%} {va:11.1%} {mf - co:10.1%} {va - co:10.1%} "
+                    f"{1 - (mf + va - co):6.1%} {lw:14.1%}")
+    if rows:
+        head = (f"{'kernel':9s} {'MFMA busy':>10s} {'co-exec':>8s} {'co-exec/MFMA':>13s} {'VALU active':>11s} "
+                f"{'MFMA only':>10s} {'VALU only':>10s} {'idle':>6s} {'LDS wait/wave':>14s}")
+        text = "\n".join([head] + rows) + "\n"
+        with open(out_path.replace("_counters.table", "_coexec.table"), "w") as fo:
+            fo.write(text)
+        print(text)
 
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
@@ -182,7 +206,8 @@ def parse():
                     help="run one 1 GiB device copy first (scale reference for HBM byte counters)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="print the utilisation table of rocprofv3 --pmc counter CSVs to "
-                         "profiles/attention_kl_causal_64k_counters.table and exit")
+                         "profiles/attention_kl_causal_64k_counters.table (and, given the co-execution "
+                         "counters, profiles/attention_kl_causal_64k_coexec.table) and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "--calibrate-copy run into the traffic record under profiles/ and exit")
