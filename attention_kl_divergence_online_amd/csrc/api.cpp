@@ -46,6 +46,29 @@ DqSplit dq_split(const streamkl_problem *p) {
   r.kchunk = (int)(per * skl::kBwdTile);
   return r.splits > 1 ? r : DqSplit{1, 0};
 }
+// The fused single-visit backward takes bf16 problems of at most
+// kFusedMaxRows queries per unit (decode and short query ranges): one
+// workgroup per (unit, key chunk) with chunks of whole 32-key blocks, aiming
+// at kFusedTarget workgroups, and a dQ partial per chunk when there are
+// several ([splits][2][BH * NQ][D] fp32, at the front of the workspace).
+constexpr int64_t kFusedTarget = 2048;
+bool use_fused(const streamkl_problem *p) {
+  return p->dtype == STREAMKL_BF16 && p->NQ > 0 && p->NQ <= skl::kFusedMaxRows && p->NK > 0;
+}
+DqSplit fused_split(const streamkl_problem *p) {
+  const int64_t units = p->B * p->H;
+  const int64_t blocks = (p->NK + 31) / 32;
+  int64_t sp = (kFusedTarget + units - 1) / std::max<int64_t>(units, 1);
+  sp = std::max<int64_t>(1, std::min<int64_t>(sp, std::min<int64_t>(kDqSplitMax, blocks)));
+  const int64_t per = (blocks + sp - 1) / sp;
+  return DqSplit{(int)((blocks + per - 1) / per), (int)(per * 32)};
+}
+size_t fused_workspace(const streamkl_problem *p) {
+  const DqSplit f = fused_split(p);
+  const size_t part = f.splits > 1 ? (size_t)f.splits * 2 * (size_t)(p->B * p->H) * (size_t)p->NQ * (size_t)p->D * 4 : 0;
+  return round_up(part > 16 ? part : 16, 256);
+}
+
 // Layout of a problem's backward workspace, with the split dQ partials when
 // `with_split` and the query-resident pass splits its keys.
 BwdLayout bwd_layout(const streamkl_problem *p, bool with_split = true) {
@@ -288,7 +311,8 @@ streamkl_status streamkl_fwd_splitk_noalloc(const streamkl_problem *p, const voi
 
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p) {
   if (check_bwd_problem(p) != STREAMKL_OK) return 0;
-  return bwd_layout(p).total;
+  const size_t split = bwd_layout(p).total;
+  return use_fused(p) ? std::max(split, fused_workspace(p)) : split;
 }
 
 size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p) {
@@ -424,6 +448,18 @@ streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const vo
   if (st != STREAMKL_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   skl::BwdParams b = make_bwd(p, q1, k1, q2, k2, kl, lse1, lse2, g, dq1, dk1, dq2, dk2, workspace, workspace_bytes);
+  if (use_fused(p) && workspace_bytes >= fused_workspace(p)) {
+    // Few queries: one fused single-visit pass, then the chunk partials of dQ.
+    const DqSplit f = fused_split(p);
+    b.splits = f.splits;
+    b.kchunk = f.kchunk;
+    b.dqp = f.splits > 1 ? reinterpret_cast<float *>(workspace) : nullptr;
+    b.want1 = dq1 != nullptr;
+    b.want2 = dq2 != nullptr;
+    if (skl::launch_bwd_fused((int)p->D, b, s) != hipSuccess) return STREAMKL_ERR_HIP;
+    if (f.splits > 1 && skl::launch_dq_reduce((int)p->D, b, s) != hipSuccess) return STREAMKL_ERR_HIP;
+    return STREAMKL_OK;
+  }
   if ((st = run_prepare(p, b, workspace, s)) != STREAMKL_OK) return st;
   if ((st = run_dk(p, b, s)) != STREAMKL_OK) return st;
   return run_dq(p, b, s);

@@ -1182,6 +1182,270 @@ __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap 
   }
 }
 
+// ---- bf16 inputs, at most 32 queries per unit: fused single-visit backward ----
+//
+// StreamKL's backward fuses the dK and dQ products in one kernel (gist.science,
+// "Fusion de Kernel"), which pays most where there are few queries: then the
+// split passes re-read every key tile and the key-resident pass does a single
+// short stage per workgroup.  Here all (at most 32) queries of a unit are
+// resident in one workgroup, so a streamed key block's dK is complete after
+// one visit and is written directly; dQ accumulates over the workgroup's key
+// chunk and is written as one partial per chunk (summed in chunk order by
+// dq_reduce_kernel, or written directly for a single chunk).  No atomics, no
+// prepare step.
+//
+// Two waves: wave t accumulates the gradients of distribution t and forms
+// only its dS (both need both logits).  Per 32-key block:
+//  - logits: key block rows (LDS) x resident queries (LDS), lane = query;
+//  - dS_t in fp32 with |g| folded into the exponent offset, split into
+//    bf16 hi + lo (exact operands; the pair carries 16 significand bits,
+//    against fp16's 11, and has the fp32 exponent range, so no scaling);
+//  - dQ^T[d, q] += K_t^T[d, keys] dS[keys, q]: K_t^T from the block's bf16
+//    rows through a one-hot product (exact), against hi and lo;
+//  - dK^T[d, k] = Q_t^T[d, q] dS^T[q, k]: dS^T from a one-hot product of dS
+//    (hi and lo each, exact), against Q_t^T formed once per workgroup with
+//    sign(g_q) folded in; written for the block's valid keys.
+// The problem is bound by reading K and writing fp32 dK, not by the matrix
+// cores, so the redundant logits and doubled gradient products cost little.
+template <int D>
+struct FusedTraits {
+  static constexpr int NT = 128;
+  static constexpr int BK = 32;          // keys per block
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int RB = D * 2;       // bf16 row bytes
+  static constexpr int CPROW = RB / 16;  // 16-byte chunks per row
+  static constexpr int TILE = 32 * RB;   // one tensor's 32 rows
+  static constexpr int OFF_K = 2 * TILE;            // after the query tiles: two buffers of two key tiles
+  static constexpr int LDS_BYTES = OFF_K + 4 * TILE;
+  static constexpr int LOADS = TILE / 16 / NT;      // 16-byte loads per thread per tensor tile
+  static_assert(LOADS * 16 * NT == TILE, "load split");
+};
+
+// Permuted one-hot operand that transposes a dS fragment: k-step ks of the
+// dS operands holds the block's rows 16 ks + 8 (u / 4) + 4 h + u % 4 in slot
+// u of lane half h; as the A operand of a product against this B operand
+// they land in column 16 ks + (that row), so the 32 x 32 result (two k-steps)
+// is the fragment transposed.  Lane (h, c) supplies k = 8 h + u.
+__device__ __forceinline__ bf16x8 onehot_perm(int c, int h, int ks) {
+  const int v = c - 16 * ks;
+  bf16x8 r;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const bool one = v >= 0 && v < 16 && ((v >> 2) & 1) == h && u == 4 * (v >> 3) + (v & 3);
+    r[u] = (bf16)(one ? 1.f : 0.f);
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 f32x8_to_bf16x8(const f32x16 &v, int half) {
+  bf16x8 r;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) r[u] = (bf16)v[8 * half + u];
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void bwd_fused_kernel(BwdParams p) {
+  using Tr = FusedTraits<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;  // wave = distribution t
+  const int h = lane >> 5, c32 = lane & 31;
+  const int t = wave;
+
+  const int S = p.splits;
+  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t u = L / (uint32_t)S;
+  const int sp = (int)(L % (uint32_t)S);
+  const int NQ = (int)p.NQ, NK = (int)p.NK, off = NK - NQ;
+  const int64_t rq = p.qmap.row0(u), rk = p.kmap.row0(u);
+  const bool want = t ? p.want2 : p.want1;
+
+  // This workgroup's keys: whole 32-key blocks [k_lo, k_hi).
+  const int k_lo = sp * p.kchunk, k_hi = min(NK, k_lo + p.kchunk);
+  const int nblk = k_hi > k_lo ? (k_hi - k_lo + Tr::BK - 1) / Tr::BK : 0;
+
+  // Resident queries: lane's query c32 (both lane halves).
+  const int q = c32;
+  const bool q_ok = q < NQ;
+  float qb1 = kNoGrad, qb2 = kNoGrad, qkl = 0.f, qsg = 1.f;
+  if (q_ok) query_stats(p.lse1[rq + q], p.lse2[rq + q], p.kl[rq + q], p.g[rq + q], 1.f, qb1, qb2, qkl, qsg);
+
+  // Staging: query tiles once, key tiles double-buffered, all swizzled rows.
+  const char *Qp[2] = {reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(p.q1) + rq * D),
+                       reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(p.q2) + rq * D)};
+  const BufRange rqr[2] = {{Qp[0], NQ * Tr::RB}, {Qp[1], NQ * Tr::RB}};
+  const BufRange rkr[2] = {{reinterpret_cast<const bf16 *>(p.k1) + rk * D, NK * Tr::RB},
+                           {reinterpret_cast<const bf16 *>(p.k2) + rk * D, NK * Tr::RB}};
+  uint32_t voff[Tr::LOADS];
+#pragma unroll
+  for (int i = 0; i < Tr::LOADS; ++i) {
+    const int C = i * Tr::NT + tid;
+    const int row = C / Tr::CPROW;
+    voff[i] = row * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(row)) * 16;
+  }
+  auto load_tile = [&](const BufRange &r, char *dst, uint32_t soff) {
+#pragma unroll
+    for (int i = 0; i < Tr::LOADS; ++i) buffer_load_lds16(r, dst + (i * Tr::NT + wave * 64) * 16, voff[i], soff);
+  };
+  auto load_keys = [&](int b) {
+    char *buf = smem + Tr::OFF_K + (b & 1) * 2 * Tr::TILE;
+    const uint32_t soff = (uint32_t)(k_lo + b * Tr::BK) * Tr::RB;
+    load_tile(rkr[0], buf, soff);
+    load_tile(rkr[1], buf + Tr::TILE, soff);
+  };
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // Fragment (row r, 16-column chunk s, lane half h) of the tile at `tile`.
+  const int sw = swz_row<D>(c32);
+  auto frag = [&](const char *tile, int s) {
+    return *reinterpret_cast<const bf16x8 *>(tile + c32 * Tr::RB + ((2 * s + h) ^ sw) * 16);
+  };
+
+  load_tile(rqr[0], smem, 0);
+  load_tile(rqr[1], smem + Tr::TILE, 0);
+  if (nblk > 0) load_keys(0);
+  wait_loads();
+  barrier();
+
+  // One-hot operands: columns of a 32-column block (transposing K_t and Q_t),
+  // and the permuted ones transposing dS.
+  const bf16x8 i0 = onehot(c32, h, 0, 1.f), i1 = onehot(c32, h, 1, 1.f);
+  const bf16x8 j0 = onehot_perm(c32, h, 0), j1 = onehot_perm(c32, h, 1);
+
+  // Q_t^T with sign(g_q) folded in: lane (h, d) holds, for k-step ks, queries
+  // 16 ks + 8 (u / 4) + 4 h + u % 4 of column d of 32-column block db.
+  bf16x8 qT[Tr::NDB][2];
+  {
+    const char *qt = smem + t * Tr::TILE;
+    const uint32_t flip = qsg < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db) {
+      u32x4 lo = __builtin_bit_cast(u32x4, frag(qt, 2 * db)), hi = __builtin_bit_cast(u32x4, frag(qt, 2 * db + 1));
+      lo ^= flip;
+      hi ^= flip;
+      f32x16 T = mma16(__builtin_bit_cast(bf16x8, lo), i0, f32x16{});
+      T = mma16(__builtin_bit_cast(bf16x8, hi), i1, T);
+      qT[db][0] = f32x8_to_bf16x8(T, 0);
+      qT[db][1] = f32x8_to_bf16x8(T, 1);
+    }
+  }
+
+  const float c = p.scale * kLog2e;
+  f32x16 dq[Tr::NDB];
+#pragma unroll
+  for (int db = 0; db < Tr::NDB; ++db) dq[db] = f32x16{};
+  float *dK = t ? p.dk2 : p.dk1;
+
+  for (int b = 0; b < nblk; ++b) {
+    if (b + 1 < nblk) load_keys(b + 1);
+    const char *kt1 = smem + Tr::OFF_K + (b & 1) * 2 * Tr::TILE;
+    const char *kt2 = kt1 + Tr::TILE;
+    const int kb = k_lo + b * Tr::BK;
+    // Logits: element r of lane (h, q) is key kb + acc_row(r, h), query q.
+    f32x16 x1 = f32x16{}, x2 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < Tr::KSTEPS; ++s) {
+      x1 = mma16(frag(kt1, s), frag(smem, s), x1);
+      x2 = mma16(frag(kt2, s), frag(smem + Tr::TILE, s), x2);
+    }
+    // dS_t (times |g|), hi + lo in bf16, as the operands of k-steps 0 and 1.
+    const bool edge = kb + Tr::BK > NK || (p.causal && kb + Tr::BK - 1 > off) || !q_ok;
+    bf16x8 dh[2], dl[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float y1 = __builtin_fmaf(x1[r], c, -qb1);
+      const float y2 = __builtin_fmaf(x2[r], c, -qb2);
+      const float p1 = fast_exp2(y1), p2 = fast_exp2(y2);
+      float v = t ? p2 - p1 : p1 * __builtin_fmaf(y1 - y2, kLn2, -qkl);
+      if (edge) {
+        const int k = kb + acc_row(r, h);
+        v = (q_ok && k < NK && (!p.causal || k <= q + off)) ? v : 0.f;
+      }
+      const bf16 vh = (bf16)v;
+      dh[r >> 3][r & 7] = vh;
+      dl[r >> 3][r & 7] = (bf16)(v - (float)vh);
+    }
+    if (want) {
+      // dQ^T[d, q] += K_t^T[d, keys] dS[keys, q].
+      const char *ktt = t ? kt2 : kt1;
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+        f32x16 T = mma16(frag(ktt, 2 * db), i0, f32x16{});
+        T = mma16(frag(ktt, 2 * db + 1), i1, T);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 a = f32x8_to_bf16x8(T, ks);
+          dq[db] = mma16(a, dh[ks], dq[db]);
+          dq[db] = mma16(a, dl[ks], dq[db]);
+        }
+      }
+      // dS^T: element r of lane (h, k) is query acc_row(r, h) of key kb + k.
+      f32x16 Th = mma16(dh[0], j0, f32x16{}), Tl = mma16(dl[0], j0, f32x16{});
+      Th = mma16(dh[1], j1, Th);
+      Tl = mma16(dl[1], j1, Tl);
+      const bf16x8 sh[2] = {f32x8_to_bf16x8(Th, 0), f32x8_to_bf16x8(Th, 1)};
+      const bf16x8 sl[2] = {f32x8_to_bf16x8(Tl, 0), f32x8_to_bf16x8(Tl, 1)};
+      // dK^T[d, k] = Q_t^T[d, q] dS^T[q, k], written for key kb + c32.
+      const int key = kb + c32;
+#pragma unroll
+      for (int db = 0; db < Tr::NDB; ++db) {
+        f32x16 a = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          a = mma16(qT[db][ks], sh[ks], a);
+          a = mma16(qT[db][ks], sl[ks], a);
+        }
+        if (key < NK) {
+          float *o = dK + (rk + key) * D + db * 32 + 4 * h;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 v = {a[4 * j] * p.scale, a[4 * j + 1] * p.scale, a[4 * j + 2] * p.scale,
+                             a[4 * j + 3] * p.scale};
+            *reinterpret_cast<f32x4 *>(o + 8 * j) = v;
+          }
+        }
+      }
+    }
+    wait_loads();
+    barrier();
+  }
+
+  // dQ: lane's query, d = 32 db + 8 j + 4 h + (0..3); one partial per chunk.
+  if (want && q_ok) {
+    const float f = p.scale * qsg;
+    float *O = t ? p.dq2 : p.dq1;
+    int64_t rowoff = (rq + q) * D;
+    if (S > 1) {
+      O = p.dqp + ((int64_t)sp * 2 + t) * (p.BH * (int64_t)NQ * D);
+      rowoff = (u * (int64_t)NQ + q) * D;
+    }
+#pragma unroll
+    for (int db = 0; db < Tr::NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = {dq[db][4 * j] * f, dq[db][4 * j + 1] * f, dq[db][4 * j + 2] * f, dq[db][4 * j + 3] * f};
+        *reinterpret_cast<f32x4 *>(O + rowoff + db * 32 + 8 * j + 4 * h) = v;
+      }
+  }
+}
+
+template <int D>
+static hipError_t launch_fused(const BwdParams &p, hipStream_t s) {
+  using Tr = FusedTraits<D>;
+  const void *fn = reinterpret_cast<const void *>(&bwd_fused_kernel<D>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_fused_kernel<D>), dim3((uint32_t)(p.BH * p.splits)), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_fused(int D, const BwdParams &p, hipStream_t s) {
+  if (p.BH == 0) return hipSuccess;
+  return D == 128 ? launch_fused<128>(p, s) : launch_fused<64>(p, s);
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(float *dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = 0.f;
 }

@@ -163,6 +163,12 @@ hipError_t launch_bwd_dq(int dtype, int D, const BwdParams &p, hipStream_t s);
 hipError_t launch_bwd_dk_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_bwd_dq_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_zero(float *dst, int64_t n, hipStream_t s);
+// Fused single-visit backward (bf16, at most kFusedMaxRows queries per unit):
+// BH * p.splits workgroups, key chunks of p.kchunk keys (a multiple of 32);
+// with p.splits > 1 dQ goes to the partials p.dqp (then launch_dq_reduce),
+// else straight to dq1 / dq2; dK is written directly.  No prepare step.
+constexpr int kFusedMaxRows = 32;
+hipError_t launch_bwd_fused(int D, const BwdParams &p, hipStream_t s);
 // dQ1 / dQ2 (the requested ones) = sum over the key chunks of p.dqp, in chunk order.
 hipError_t launch_dq_reduce(int D, const BwdParams &p, hipStream_t s);
 // Matrix-rate probe: `workgroups` workgroups of four waves, each wave `iters`

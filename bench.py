@@ -439,6 +439,10 @@ def main():
             cfgs["C5_fwd"] = sk
         out["configs"] = {k: cfgs[k] for k in ("C1", "C2", "C3", "C4", "C5_fwd", "C5_bwd") if k in cfgs}
 
+    if not args.no_configs:
+        out["fused_vs_split"] = {n: fused_vs_split(skl, synth, torch, args, n)
+                                 for n in ("shortq16_bwd_64k", "decode_128k", "shortq128_bwd_64k", "shortq_bwd_64k")}
+
     if args.other_configs:
         out["other_configs"] = {n: config_bench(skl, synth, torch, args, n)
                                 for n in ("shortq_bwd_64k", "causal_16k_d64", "causal_4k_fp32")}
@@ -583,6 +587,44 @@ def config_bench(skl, synth, torch, args, name):
            "peak_tflops": peak, "fwd_frac": round(fwd_t / peak, 4), "bwd_frac": round(bwd_t / peak, 4),
            "step_frac": round(step_t / peak, 4)}
     del q1, k1, q2, k2, grads, ws, wsk
+    torch.cuda.empty_cache()
+    return res
+
+
+def fused_vs_split(skl, synth, torch, args, name):
+    """Backward of a short-query workload through the combined call (the fused
+    single-visit pass where the query count allows, else the split passes)
+    and through the step-wise calls (always the split passes: prepare, dK
+    pass, dQ pass); HIP-event ms per backward and algorithmic TFLOP/s."""
+    w = synth.get(name)
+    q1, k1, q2, k2 = synth.make_inputs(w, device="cuda")
+    g = synth.upstream_grad(w, "cuda")
+    kl, l1, l2 = skl.streamkl_fwd_splitk(q1, k1, q2, k2, w.splits, w.scale, w.causal)
+    grads = tuple(torch.empty_like(t, dtype=torch.float32) for t in (q1, k1, q2, k2))
+    ws = torch.empty(max(16, skl.bwd_workspace_size(q1, k1, w.scale, w.causal)), dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    comb = split = 0.0
+    for it in range(args.warmup + args.steps):
+        ev[0].record()
+        skl.streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws, out=grads)
+        ev[1].record()
+        skl.streamkl_bwd_prepare(q1, k1, q2, k2, g, w.scale, w.causal, workspace=ws)
+        skl.streamkl_bwd_dk(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws, out=(grads[1], grads[3]))
+        skl.streamkl_bwd_dq(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal, workspace=ws, out=(grads[0], grads[2]))
+        ev[2].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            comb += ev[0].elapsed_time(ev[1]) / args.steps
+            split += ev[1].elapsed_time(ev[2]) / args.steps
+    flop = 12 * w.D * w.visible_pairs()
+    fused = w.dtype == "bf16" and w.NQ <= 32
+    res = {"B": w.B, "H": w.H, "NQ": w.NQ, "NK": w.NK, "combined_path": "fused" if fused else "split",
+           "combined_ms": round(comb, 3), "split_ms": round(split, 3),
+           "combined_tflops": round(flop / (comb * 1e-3) / 1e12, 2), "split_tflops": round(flop / (split * 1e-3) / 1e12, 2),
+           "split_over_combined": round(split / comb, 2),
+           # fp32 key gradients written plus keys read once: the fused pass's HBM floor.
+           "dk_write_plus_k_read_gb": round((2 * 4 + 2 * 2) * w.B * w.H * w.NK * w.D / 1e9, 2)}
+    del q1, k1, q2, k2, grads, ws
     torch.cuda.empty_cache()
     return res
 

@@ -487,6 +487,55 @@ def test_shortq_bwd_64k_full_size():
     _full_size("shortq_bwd_64k")
 
 
+def test_shortq16_bwd_64k_full_size():
+    # 16 queries per head: the fused single-visit backward.
+    _full_size("shortq16_bwd_64k", rows_per_head=16)
+
+
+def test_shortq128_bwd_64k_full_size():
+    # 128 queries per head: one query tile, split passes.
+    _full_size("shortq128_bwd_64k", rows_per_head=32)
+
+
+FUSED = [
+    # B, H, NQ, NK, D, causal: at most 32 queries per unit take the fused
+    # single-visit backward; ragged key blocks, one and several key chunks.
+    (1, 2, 1, 37, 128, False),
+    (1, 2, 5, 1000, 128, True),
+    (2, 1, 16, 5000, 128, False),
+    (1, 3, 32, 4130, 64, True),
+    (1, 1, 32, 32, 128, True),
+    (2, 2, 17, 777, 64, False),
+]
+
+
+@pytest.mark.parametrize("B,H,NQ,NK,D,causal", FUSED)
+def test_fused_short_query_backward(B, H, NQ, NK, D, causal):
+    # The combined call runs the fused kernel; the step-wise calls run the
+    # split passes.  Both against the oracle, element by element, with signed
+    # g, and each distribution's gradients alone equal to the combined call's.
+    from attention_kl_divergence_online_amd import streamkl_bwd_dk, streamkl_bwd_dq, streamkl_bwd_prepare
+    print(f"fused B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal}", flush=True)
+    q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, torch.bfloat16, seed=NQ * 31 + NK + D + causal, noise=0.2)
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    g = (torch.rand((B, H, NQ), generator=torch.Generator().manual_seed(NK)) - 0.3).to(DEV)
+    fused = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal)
+    ws = streamkl_bwd_prepare(q1, k1, q2, k2, g, scale, causal)
+    dk1, dk2 = streamkl_bwd_dk(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, workspace=ws)
+    dq1, dq2 = streamkl_bwd_dq(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, workspace=ws)
+    t_only = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, student=False)
+    s_only = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, teacher=False)
+    torch.cuda.synchronize()
+    heads = _heads(B, H)
+    case = f"B{B} H{H} NQ{NQ} NK{NK} D{D} causal={causal}"
+    assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, fused, heads), TOL["bf16"], f"fused {case}")
+    assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, (dq1, dk1, dq2, dk2), heads), TOL["bf16"],
+                  f"split {case}")
+    for a, b in ((t_only[0], fused[0]), (t_only[1], fused[1]), (s_only[2], fused[2]), (s_only[3], fused[3])):
+        assert torch.equal(a, b)
+
+
 def test_causal_4k_fp32_full_size():
     _full_size("causal_4k_fp32")
 

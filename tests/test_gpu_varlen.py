@@ -177,14 +177,21 @@ def test_varlen_many_runs(dt):
         errs = compare_backward(*sq, scale, causal, S(g, q0, qe), sg, heads)
         assert_within(errs, TOL[dt], f"varlen many-run bwd seq {b} ({qe - q0}x{ke - k0}) {dt}")
         if b in (0, 35, 36, 38, 42):
-            # The same sequence as a dense problem of its own: the same bits
-            # forward and for dK.  The dense dQ pass of so few query tiles
-            # splits its keys and sums the chunks' partials afterwards, so dQ
-            # differs by fp32 summation order only.
+            # The same sequence as a dense problem of its own, through the
+            # step-wise entry points (always the split passes, which the
+            # packed batch runs too; the combined call would take the fused
+            # pass for sequences of at most 32 queries): the same bits forward
+            # and for dK.  The dense dQ pass of so few query tiles splits its
+            # keys and sums the chunks' partials afterwards, so dQ differs by
+            # fp32 summation order only.
+            from attention_kl_divergence_online_amd import streamkl_bwd_dk, streamkl_bwd_dq, streamkl_bwd_prepare
             dq = [t.contiguous() for t in sq]
             out_d = streamkl_fwd(*dq, scale, causal)
             gd = S(g, q0, qe).contiguous()
-            grads_d = streamkl_bwd(*dq, *out_d, gd, scale, causal)
+            wsd = streamkl_bwd_prepare(*dq, gd, scale, causal)
+            dk1d, dk2d = streamkl_bwd_dk(*dq, *out_d, gd, scale, causal, workspace=wsd)
+            dq1d, dq2d = streamkl_bwd_dq(*dq, *out_d, gd, scale, causal, workspace=wsd)
+            grads_d = (dq1d, dk1d, dq2d, dk2d)
             torch.cuda.synchronize()
             for a, c in zip(out_d, (S(kl, q0, qe), S(l1, q0, qe), S(l2, q0, qe))):
                 assert torch.equal(a, c), b
