@@ -49,16 +49,17 @@ DqSplit dq_split(const streamkl_problem *p) {
 // The fused single-visit backward takes bf16 problems of at most
 // kFusedMaxRows queries per unit (decode and short query ranges): one
 // workgroup per (unit, key chunk) with chunks of whole 32-key blocks, aiming
-// at kFusedTarget workgroups, and a dQ partial per chunk when there are
-// several ([splits][2][BH * NQ][D] fp32, at the front of the workspace).
-constexpr int64_t kFusedTarget = 2048;
+// at 2048 workgroups of one query block (512 of four), and a dQ partial per
+// chunk when there are several ([splits][2][BH * NQ][D] fp32, at the front of
+// the workspace).
 bool use_fused(const streamkl_problem *p) {
   return p->dtype == STREAMKL_BF16 && p->NQ > 0 && p->NQ <= skl::kFusedMaxRows && p->NK > 0;
 }
 DqSplit fused_split(const streamkl_problem *p) {
   const int64_t units = p->B * p->H;
   const int64_t blocks = (p->NK + 31) / 32;
-  int64_t sp = (kFusedTarget + units - 1) / std::max<int64_t>(units, 1);
+  const int64_t target = skl::fused_query_blocks(p->NQ) == 1 ? 2048 : 512;
+  int64_t sp = (target + units - 1) / std::max<int64_t>(units, 1);
   sp = std::max<int64_t>(1, std::min<int64_t>(sp, std::min<int64_t>(kDqSplitMax, blocks)));
   const int64_t per = (blocks + sp - 1) / sp;
   return DqSplit{(int)((blocks + per - 1) / per), (int)(per * 32)};

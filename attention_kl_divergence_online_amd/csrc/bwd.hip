@@ -1182,44 +1182,54 @@ __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap 
   }
 }
 
-// ---- bf16 inputs, at most 32 queries per unit: fused single-visit backward ----
+// ---- bf16 inputs, at most 128 queries per unit: fused single-visit backward ----
 //
 // StreamKL's backward fuses the dK and dQ products in one kernel (gist.science,
 // "Fusion de Kernel"), which pays most where there are few queries: then the
 // split passes re-read every key tile and the key-resident pass does a single
-// short stage per workgroup.  Here all (at most 32) queries of a unit are
+// short stage per workgroup.  Here all queries of a unit (at most 32 x QB) are
 // resident in one workgroup, so a streamed key block's dK is complete after
 // one visit and is written directly; dQ accumulates over the workgroup's key
 // chunk and is written as one partial per chunk (summed in chunk order by
 // dq_reduce_kernel, or written directly for a single chunk).  No atomics, no
 // prepare step.
 //
-// Two waves: wave t accumulates the gradients of distribution t and forms
-// only its dS (both need both logits).  Per 32-key block:
-//  - logits: key block rows (LDS) x resident queries (LDS), lane = query;
+// 2 x QB waves: wave (qb, t) holds query block qb (32 queries) and
+// accumulates the gradients of distribution t, forming only its dS (both need
+// both logits).  Per 32-key block:
+//  - logits: key block rows (LDS) x the block's queries (LDS), lane = query;
 //  - dS_t in fp32 with |g| folded into the exponent offset, split into
 //    bf16 hi + lo (exact operands; the pair carries 16 significand bits,
 //    against fp16's 11, and has the fp32 exponent range, so no scaling);
 //  - dQ^T[d, q] += K_t^T[d, keys] dS[keys, q]: K_t^T from the block's bf16
 //    rows through a one-hot product (exact), against hi and lo;
-//  - dK^T[d, k] = Q_t^T[d, q] dS^T[q, k]: dS^T from a one-hot product of dS
-//    (hi and lo each, exact), against Q_t^T formed once per workgroup with
-//    sign(g_q) folded in; written for the block's valid keys.
+//  - dS^T from a one-hot product of dS (hi and lo each, exact); with QB > 1
+//    the waves post it to LDS and each wave then forms one (distribution,
+//    32-column block) of the key block's dK over all resident queries;
+//  - dK^T[d, k] = Q_t^T[d, q] dS^T[q, k], against Q_t^T formed once per
+//    workgroup with sign(g_q) folded in; written for the block's valid keys.
 // The problem is bound by reading K and writing fp32 dK, not by the matrix
 // cores, so the redundant logits and doubled gradient products cost little.
-template <int D>
+template <int D, int QB>
 struct FusedTraits {
-  static constexpr int NT = 128;
+  static constexpr int NT = 128 * QB;
   static constexpr int BK = 32;          // keys per block
   static constexpr int KSTEPS = D / 16;
   static constexpr int NDB = D / 32;
   static constexpr int RB = D * 2;       // bf16 row bytes
   static constexpr int CPROW = RB / 16;  // 16-byte chunks per row
   static constexpr int TILE = 32 * RB;   // one tensor's 32 rows
-  static constexpr int OFF_K = 2 * TILE;            // after the query tiles: two buffers of two key tiles
-  static constexpr int LDS_BYTES = OFF_K + 4 * TILE;
-  static constexpr int LOADS = TILE / 16 / NT;      // 16-byte loads per thread per tensor tile
-  static_assert(LOADS * 16 * NT == TILE, "load split");
+  static constexpr int QTILE = QB * TILE;            // one tensor's resident queries
+  static constexpr int OFF_K = 2 * QTILE;            // two buffers of two key tiles
+  static constexpr int SLOT = 64 * 16;               // one lane-ordered 16-byte operand
+  // QB > 1: posted dS^T, [query block][distribution][k-step][hi, lo][lane].
+  static constexpr int OFF_X = OFF_K + 4 * TILE;
+  static constexpr int X_BYTES = QB > 1 ? QB * 2 * 2 * 2 * SLOT : 0;
+  static constexpr int LDS_BYTES = OFF_X + X_BYTES;
+  static constexpr int QCHUNKS = QTILE / 16;         // 16-byte loads per tensor's query tile
+  static constexpr int KCHUNKS = TILE / 16;          // 16-byte loads per key tile
+  static_assert(QCHUNKS % NT == 0, "query staging split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
 // Permuted one-hot operand that transposes a dS fragment: k-step ks of the
@@ -1245,14 +1255,14 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16x8(const f32x16 &v, int half) {
   return r;
 }
 
-template <int D>
-__global__ __launch_bounds__(128) void bwd_fused_kernel(BwdParams p) {
-  using Tr = FusedTraits<D>;
+template <int D, int QB>
+__global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
+  using Tr = FusedTraits<D, QB>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;  // wave = distribution t
+  const int lane = tid & 63, wave = tid >> 6;
+  const int qb = wave >> 1, t = wave & 1;  // query block, distribution
   const int h = lane >> 5, c32 = lane & 31;
-  const int t = wave;
 
   const int S = p.splits;
   const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -1266,45 +1276,49 @@ __global__ __launch_bounds__(128) void bwd_fused_kernel(BwdParams p) {
   const int k_lo = sp * p.kchunk, k_hi = min(NK, k_lo + p.kchunk);
   const int nblk = k_hi > k_lo ? (k_hi - k_lo + Tr::BK - 1) / Tr::BK : 0;
 
-  // Resident queries: lane's query c32 (both lane halves).
-  const int q = c32;
+  // Resident queries: lane's query q (both lane halves) of block qb.
+  const int q = qb * 32 + c32;
   const bool q_ok = q < NQ;
   float qb1 = kNoGrad, qb2 = kNoGrad, qkl = 0.f, qsg = 1.f;
   if (q_ok) query_stats(p.lse1[rq + q], p.lse2[rq + q], p.kl[rq + q], p.g[rq + q], 1.f, qb1, qb2, qkl, qsg);
 
-  // Staging: query tiles once, key tiles double-buffered, all swizzled rows.
-  const char *Qp[2] = {reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(p.q1) + rq * D),
-                       reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(p.q2) + rq * D)};
-  const BufRange rqr[2] = {{Qp[0], NQ * Tr::RB}, {Qp[1], NQ * Tr::RB}};
+  // Staging: query tiles once, key tiles double-buffered, all swizzled rows
+  // (the swizzle repeats every 16 rows, so block qb's rows read like block 0's).
+  const BufRange rqr[2] = {{reinterpret_cast<const bf16 *>(p.q1) + rq * D, NQ * Tr::RB},
+                           {reinterpret_cast<const bf16 *>(p.q2) + rq * D, NQ * Tr::RB}};
   const BufRange rkr[2] = {{reinterpret_cast<const bf16 *>(p.k1) + rk * D, NK * Tr::RB},
                            {reinterpret_cast<const bf16 *>(p.k2) + rk * D, NK * Tr::RB}};
-  uint32_t voff[Tr::LOADS];
-#pragma unroll
-  for (int i = 0; i < Tr::LOADS; ++i) {
-    const int C = i * Tr::NT + tid;
+  auto src_off = [](int C) {
     const int row = C / Tr::CPROW;
-    voff[i] = row * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(row)) * 16;
-  }
-  auto load_tile = [&](const BufRange &r, char *dst, uint32_t soff) {
+    return (uint32_t)(row * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(row)) * 16);
+  };
+  auto load_queries = [&](int tn) {
 #pragma unroll
-    for (int i = 0; i < Tr::LOADS; ++i) buffer_load_lds16(r, dst + (i * Tr::NT + wave * 64) * 16, voff[i], soff);
+    for (int i = 0; i < Tr::QCHUNKS / Tr::NT; ++i)
+      buffer_load_lds16(rqr[tn], smem + tn * Tr::QTILE + (i * Tr::NT + wave * 64) * 16, src_off(i * Tr::NT + tid), 0);
   };
   auto load_keys = [&](int b) {
     char *buf = smem + Tr::OFF_K + (b & 1) * 2 * Tr::TILE;
     const uint32_t soff = (uint32_t)(k_lo + b * Tr::BK) * Tr::RB;
-    load_tile(rkr[0], buf, soff);
-    load_tile(rkr[1], buf + Tr::TILE, soff);
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int i = 0; i < (Tr::KCHUNKS + Tr::NT - 1) / Tr::NT; ++i)
+        if (Tr::KCHUNKS % Tr::NT == 0 || i * Tr::NT + wave * 64 < Tr::KCHUNKS)  // whole waves only
+          buffer_load_lds16(rkr[tn], buf + tn * Tr::TILE + (i * Tr::NT + wave * 64) * 16, src_off(i * Tr::NT + tid),
+                            soff);
   };
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  // Fragment (row r, 16-column chunk s, lane half h) of the tile at `tile`.
+  // Fragment (row r of a 32-row tile, 16-column chunk s, lane half h).
   const int sw = swz_row<D>(c32);
   auto frag = [&](const char *tile, int s) {
     return *reinterpret_cast<const bf16x8 *>(tile + c32 * Tr::RB + ((2 * s + h) ^ sw) * 16);
   };
+  const char *qtile1 = smem + qb * Tr::TILE, *qtile2 = smem + Tr::QTILE + qb * Tr::TILE;
 
-  load_tile(rqr[0], smem, 0);
-  load_tile(rqr[1], smem + Tr::TILE, 0);
+  load_queries(0);
+  load_queries(1);
   if (nblk > 0) load_keys(0);
   wait_loads();
   barrier();
@@ -1314,21 +1328,38 @@ __global__ __launch_bounds__(128) void bwd_fused_kernel(BwdParams p) {
   const bf16x8 i0 = onehot(c32, h, 0, 1.f), i1 = onehot(c32, h, 1, 1.f);
   const bf16x8 j0 = onehot_perm(c32, h, 0), j1 = onehot_perm(c32, h, 1);
 
-  // Q_t^T with sign(g_q) folded in: lane (h, d) holds, for k-step ks, queries
-  // 16 ks + 8 (u / 4) + 4 h + u % 4 of column d of 32-column block db.
-  bf16x8 qT[Tr::NDB][2];
+  // The dK products this wave forms: QB == 1, every 32-column block of its
+  // distribution t over its own queries; QB > 1, one (distribution tk,
+  // block dbk) over all resident queries (none when 2 * NDB < 2 * QB waves).
+  constexpr int NK_DB = QB == 1 ? Tr::NDB : 1;
+  const int tk = QB == 1 ? t : wave % 2;
+  const int dbk = QB == 1 ? 0 : wave / 2;
+  const bool dk_wave = QB == 1 || dbk < Tr::NDB;
+  const bool want_k = dk_wave && (tk ? p.want2 : p.want1);
+  // Q_tk^T with sign(g_q) folded in, as the A operands of the dK product:
+  // qT[db][kk] holds, in lane (h, d), queries 16 kk + 8 (m / 4) + 4 h + m % 4
+  // (k-step kk over all resident queries) of column d of block db.
+  bf16x8 qT[NK_DB][2 * QB];
   {
-    const char *qt = smem + t * Tr::TILE;
-    const uint32_t flip = qsg < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int db = 0; db < Tr::NDB; ++db) {
-      u32x4 lo = __builtin_bit_cast(u32x4, frag(qt, 2 * db)), hi = __builtin_bit_cast(u32x4, frag(qt, 2 * db + 1));
-      lo ^= flip;
-      hi ^= flip;
-      f32x16 T = mma16(__builtin_bit_cast(bf16x8, lo), i0, f32x16{});
-      T = mma16(__builtin_bit_cast(bf16x8, hi), i1, T);
-      qT[db][0] = f32x8_to_bf16x8(T, 0);
-      qT[db][1] = f32x8_to_bf16x8(T, 1);
+    for (int b2 = 0; b2 < QB; ++b2) {
+      const int qq = b2 * 32 + c32;  // the query row this lane supplies as an A operand
+      float gq = 0.f;
+      if (qq < NQ) gq = p.g[rq + qq];
+      const uint32_t flip = gq < 0.f ? 0x80008000u : 0u;
+      const char *qt = smem + tk * Tr::QTILE + b2 * Tr::TILE;
+#pragma unroll
+      for (int k = 0; k < NK_DB; ++k) {
+        const int db = QB == 1 ? k : dbk;
+        if (QB > 1 && !dk_wave) continue;
+        u32x4 lo = __builtin_bit_cast(u32x4, frag(qt, 2 * db)), hi = __builtin_bit_cast(u32x4, frag(qt, 2 * db + 1));
+        lo ^= flip;
+        hi ^= flip;
+        f32x16 T = mma16(__builtin_bit_cast(bf16x8, lo), i0, f32x16{});
+        T = mma16(__builtin_bit_cast(bf16x8, hi), i1, T);
+        qT[k][2 * b2] = f32x8_to_bf16x8(T, 0);
+        qT[k][2 * b2 + 1] = f32x8_to_bf16x8(T, 1);
+      }
     }
   }
 
@@ -1336,7 +1367,7 @@ __global__ __launch_bounds__(128) void bwd_fused_kernel(BwdParams p) {
   f32x16 dq[Tr::NDB];
 #pragma unroll
   for (int db = 0; db < Tr::NDB; ++db) dq[db] = f32x16{};
-  float *dK = t ? p.dk2 : p.dk1;
+  float *dK = tk ? p.dk2 : p.dk1;
 
   for (int b = 0; b < nblk; ++b) {
     if (b + 1 < nblk) load_keys(b + 1);
@@ -1347,8 +1378,8 @@ __global__ __launch_bounds__(128) void bwd_fused_kernel(BwdParams p) {
     f32x16 x1 = f32x16{}, x2 = f32x16{};
 #pragma unroll
     for (int s = 0; s < Tr::KSTEPS; ++s) {
-      x1 = mma16(frag(kt1, s), frag(smem, s), x1);
-      x2 = mma16(frag(kt2, s), frag(smem + Tr::TILE, s), x2);
+      x1 = mma16(frag(kt1, s), frag(qtile1, s), x1);
+      x2 = mma16(frag(kt2, s), frag(qtile2, s), x2);
     }
     // dS_t (times |g|), hi + lo in bf16, as the operands of k-steps 0 and 1.
     const bool edge = kb + Tr::BK > NK || (p.causal && kb + Tr::BK - 1 > off) || !q_ok;
@@ -1381,22 +1412,51 @@ __global__ __launch_bounds__(128) void bwd_fused_kernel(BwdParams p) {
           dq[db] = mma16(a, dl[ks], dq[db]);
         }
       }
-      // dS^T: element r of lane (h, k) is query acc_row(r, h) of key kb + k.
+    }
+    // dS^T: element r of lane (h, k) is query 32 qb + acc_row(r, h) of key kb + k.
+    bf16x8 sh[2], sl[2];
+    if (QB > 1 || want) {
       f32x16 Th = mma16(dh[0], j0, f32x16{}), Tl = mma16(dl[0], j0, f32x16{});
       Th = mma16(dh[1], j1, Th);
       Tl = mma16(dl[1], j1, Tl);
-      const bf16x8 sh[2] = {f32x8_to_bf16x8(Th, 0), f32x8_to_bf16x8(Th, 1)};
-      const bf16x8 sl[2] = {f32x8_to_bf16x8(Tl, 0), f32x8_to_bf16x8(Tl, 1)};
-      // dK^T[d, k] = Q_t^T[d, q] dS^T[q, k], written for key kb + c32.
+      sh[0] = f32x8_to_bf16x8(Th, 0);
+      sh[1] = f32x8_to_bf16x8(Th, 1);
+      sl[0] = f32x8_to_bf16x8(Tl, 0);
+      sl[1] = f32x8_to_bf16x8(Tl, 1);
+    }
+    if (QB > 1) {
+      char *xw = smem + Tr::OFF_X + ((qb * 2 + t) * 4) * Tr::SLOT + lane * 16;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        *reinterpret_cast<bf16x8 *>(xw + (2 * ks) * Tr::SLOT) = sh[ks];
+        *reinterpret_cast<bf16x8 *>(xw + (2 * ks + 1) * Tr::SLOT) = sl[ks];
+      }
+      barrier();
+    }
+    // dK^T[d, k] = Q_tk^T[d, q] dS_tk^T[q, k] over the resident queries,
+    // written for key kb + c32.
+    if (want_k) {
       const int key = kb + c32;
 #pragma unroll
-      for (int db = 0; db < Tr::NDB; ++db) {
+      for (int k = 0; k < NK_DB; ++k) {
+        const int db = QB == 1 ? k : dbk;
         f32x16 a = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          a = mma16(qT[db][ks], sh[ks], a);
-          a = mma16(qT[db][ks], sl[ks], a);
-        }
+        for (int b2 = 0; b2 < QB; ++b2)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 bh, bl;
+            if (QB == 1) {
+              bh = sh[ks];
+              bl = sl[ks];
+            } else {
+              const char *xr = smem + Tr::OFF_X + ((b2 * 2 + tk) * 4 + 2 * ks) * Tr::SLOT + lane * 16;
+              bh = *reinterpret_cast<const bf16x8 *>(xr);
+              bl = *reinterpret_cast<const bf16x8 *>(xr + Tr::SLOT);
+            }
+            a = mma16(qT[k][2 * b2 + ks], bh, a);
+            a = mma16(qT[k][2 * b2 + ks], bl, a);
+          }
         if (key < NK) {
           float *o = dK + (rk + key) * D + db * 32 + 4 * h;
 #pragma unroll
@@ -1431,19 +1491,23 @@ __global__ __launch_bounds__(128) void bwd_fused_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+template <int D, int QB>
 static hipError_t launch_fused(const BwdParams &p, hipStream_t s) {
-  using Tr = FusedTraits<D>;
-  const void *fn = reinterpret_cast<const void *>(&bwd_fused_kernel<D>);
+  using Tr = FusedTraits<D, QB>;
+  const void *fn = reinterpret_cast<const void *>(&bwd_fused_kernel<D, QB>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_fused_kernel<D>), dim3((uint32_t)(p.BH * p.splits)), dim3(Tr::NT), Tr::LDS_BYTES, s, p);
+  hipLaunchKernelGGL((bwd_fused_kernel<D, QB>), dim3((uint32_t)(p.BH * p.splits)), dim3(Tr::NT), Tr::LDS_BYTES, s,
+                     p);
   return hipGetLastError();
 }
 
+int fused_query_blocks(int64_t NQ) { return NQ <= 32 ? 1 : 4; }
+
 hipError_t launch_bwd_fused(int D, const BwdParams &p, hipStream_t s) {
   if (p.BH == 0) return hipSuccess;
-  return D == 128 ? launch_fused<128>(p, s) : launch_fused<64>(p, s);
+  if (fused_query_blocks(p.NQ) == 1) return D == 128 ? launch_fused<128, 1>(p, s) : launch_fused<64, 1>(p, s);
+  return D == 128 ? launch_fused<128, 4>(p, s) : launch_fused<64, 4>(p, s);
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float *dst, int64_t n) {

@@ -167,7 +167,9 @@ hipError_t launch_zero(float *dst, int64_t n, hipStream_t s);
 // BH * p.splits workgroups, key chunks of p.kchunk keys (a multiple of 32);
 // with p.splits > 1 dQ goes to the partials p.dqp (then launch_dq_reduce),
 // else straight to dq1 / dq2; dK is written directly.  No prepare step.
-constexpr int kFusedMaxRows = 32;
+// Workgroups hold fused_query_blocks(NQ) blocks of 32 queries (1 or 4).
+constexpr int kFusedMaxRows = 128;
+int fused_query_blocks(int64_t NQ);
 hipError_t launch_bwd_fused(int D, const BwdParams &p, hipStream_t s);
 // dQ1 / dQ2 (the requested ones) = sum over the key chunks of p.dqp, in chunk order.
 hipError_t launch_dq_reduce(int D, const BwdParams &p, hipStream_t s);

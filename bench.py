@@ -617,7 +617,7 @@ def fused_vs_split(skl, synth, torch, args, name):
             comb += ev[0].elapsed_time(ev[1]) / args.steps
             split += ev[1].elapsed_time(ev[2]) / args.steps
     flop = 12 * w.D * w.visible_pairs()
-    fused = w.dtype == "bf16" and w.NQ <= 32
+    fused = w.dtype == "bf16" and w.NQ <= 128
     res = {"B": w.B, "H": w.H, "NQ": w.NQ, "NK": w.NK, "combined_path": "fused" if fused else "split",
            "combined_ms": round(comb, 3), "split_ms": round(split, 3),
            "combined_tflops": round(flop / (comb * 1e-3) / 1e12, 2), "split_tflops": round(flop / (split * 1e-3) / 1e12, 2),

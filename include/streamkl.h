@@ -149,12 +149,17 @@ streamkl_status streamkl_fwd_splitk_noalloc(const streamkl_problem *p,
  * * D * 4 bytes), summed in chunk order.  Returns 0 if the problem is invalid.
  */
 size_t streamkl_bwd_workspace_size(const streamkl_problem *p);
+/* (For bf16 problems of at most 128 queries the size query also covers the
+ * fused pass's dQ partials, C * 2 * B * H * NQ * D * 4 bytes for C key chunks,
+ * C = min(ceil(W / (B * H)), 64, ceil(NK / 32)) with W = 2048 for at most 32
+ * queries and 512 above, when that is larger.) */
 
 /*
  * Smallest workspace streamkl_bwd accepts: the per-(batch, head) factors
  * without the split partial dQ.  Given less than streamkl_bwd_workspace_size
- * (but at least this), the query-gradient pass runs unsplit: dK is bitwise
- * the same, dQ differs only in the fp32 summation order, and short query
+ * (but at least this), the two passes run and the query-gradient pass runs
+ * unsplit: dQ differs only in the fp32 summation order (and, where the fused
+ * pass would have run, in rounding within the bounds), and short query
  * ranges run slower.  Returns 0 if the problem is invalid.
  */
 size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p);
@@ -166,9 +171,15 @@ size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p);
  *     dS2 = g * (P2 - P1)                                   ("Configuracion 1")
  *     dS1 = g * P1 * ((s1 - LSE1) - (s2 - LSE2) - KL_row)   ("Configuracion 2"),
  * the log-ratio taken from logits and the saved LSEs ("Estabilidad Numerica").
- * Then dQ_t = scale * dS_t K_t and dK_t = scale * dS_t^T Q_t, in two passes
- * with no atomics (one over key tiles for dK, one over query tiles for dQ);
- * results are bitwise repeatable.
+ * Then dQ_t = scale * dS_t K_t and dK_t = scale * dS_t^T Q_t, with no atomics;
+ * results are bitwise repeatable.  bf16 problems of at most 128 queries per
+ * (batch, head) run one fused single-visit pass ("Fusion de Kernel"): the
+ * queries stay resident, each key is read once, dS is formed once per pair
+ * and feeds both products, dK is written directly and dQ as one partial per
+ * key chunk, summed in chunk order.  Its products are bf16 with dS split
+ * into a high and a low bf16 part (no operand scaling, no prepare step).
+ * All other problems run two passes (one over key tiles for dK, one over
+ * query tiles for dQ), as do the step-wise entry points below.
  *
  * kl, lse1, lse2 must be the outputs of streamkl_fwd / streamkl_fwd_splitk for
  * the same inputs.  Gradient outputs come in pairs: pass dq1 = dk1 = NULL to

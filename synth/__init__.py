@@ -84,8 +84,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload(9, "shortq_bwd_64k", 1, 32, 256, 65536, 128, "bf16", False, noise=0.2, splits=32),
         # fp32 inputs (the 1e-5 path) at a moderate causal context.
         Workload(8, "causal_4k_fp32", 2, 16, 4096, 4096, 128, "fp32", True, noise=0.3),
-        # Short query ranges against 64K keys: 16 queries (the fused single-visit
-        # backward) and 128 queries (one query tile per head, split passes).
+        # Short query ranges against 64K keys: 16 and 128 queries per head (the
+        # fused single-visit backward with one and four query blocks).
         Workload(10, "shortq16_bwd_64k", 1, 32, 16, 65536, 128, "bf16", False, noise=0.2, splits=32),
         Workload(11, "shortq128_bwd_64k", 1, 32, 128, 65536, 128, "bf16", False, noise=0.2, splits=32),
     ]

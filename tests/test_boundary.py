@@ -185,14 +185,31 @@ def bwd_workspace(B, H, NQ, NK, D, split=True, bf16=True):
     return up(max(16, 4 * bh), 256) + up(max(16, 16 * bh), 256) + part + up(dqp, 256)
 
 
+def fused_workspace(B, H, NQ, NK, D):
+    # The fused pass (bf16, at most 128 queries): C key chunks of whole 32-key
+    # blocks aiming at 2048 workgroups (512 above 32 queries), a dQ partial
+    # per chunk when there are several.
+    up = lambda n, a: (n + a - 1) // a * a
+    units, blocks = B * H, (NK + 31) // 32
+    target = 2048 if NQ <= 32 else 512
+    sp = max(1, min((target + units - 1) // units, 64, blocks))
+    per = (blocks + sp - 1) // sp
+    C = (blocks + per - 1) // per
+    part = C * 2 * units * NQ * D * 4 if C > 1 else 0
+    return up(max(part, 16), 256)
+
+
 def test_backward_validation(L):
     p = P()
     f32 = _lib.STREAMKL_FP32
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(dtype=f32))) == 512
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, dtype=f32))) == 768
     assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == bwd_workspace(1, 2, 8, 8, 64)
+    # At most 128 queries: the larger of the split passes' and the fused pass's needs.
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, NQ=65, NK=200, D=128))) == \
-        bwd_workspace(3, 7, 65, 200, 128)
+        max(bwd_workspace(3, 7, 65, 200, 128), fused_workspace(3, 7, 65, 200, 128)) == fused_workspace(3, 7, 65, 200, 128)
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(P(B=3, H=7, NQ=129, NK=200, D=128))) == \
+        bwd_workspace(3, 7, 129, 200, 128)
     assert L.streamkl_bwd_workspace_size(ctypes.byref(P(D=32))) == 0
     # Minimum: everything but the split query pass's partials (that pass then runs unsplit).
     assert L.streamkl_bwd_workspace_size_min(ctypes.byref(P(B=3, H=7, NQ=65, NK=200, D=128))) == \

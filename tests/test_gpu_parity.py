@@ -493,19 +493,24 @@ def test_shortq16_bwd_64k_full_size():
 
 
 def test_shortq128_bwd_64k_full_size():
-    # 128 queries per head: one query tile, split passes.
+    # 128 queries per head: the fused backward with four query blocks per workgroup.
     _full_size("shortq128_bwd_64k", rows_per_head=32)
 
 
 FUSED = [
-    # B, H, NQ, NK, D, causal: at most 32 queries per unit take the fused
-    # single-visit backward; ragged key blocks, one and several key chunks.
+    # B, H, NQ, NK, D, causal: at most 128 queries per unit take the fused
+    # single-visit backward (one block of 32 queries per workgroup up to 32,
+    # four above); ragged query and key blocks, one and several key chunks.
     (1, 2, 1, 37, 128, False),
     (1, 2, 5, 1000, 128, True),
     (2, 1, 16, 5000, 128, False),
     (1, 3, 32, 4130, 64, True),
     (1, 1, 32, 32, 128, True),
     (2, 2, 17, 777, 64, False),
+    (1, 2, 33, 900, 128, True),
+    (2, 1, 100, 3000, 128, False),
+    (1, 2, 128, 2100, 64, True),
+    (1, 1, 128, 128, 128, False),
 ]
 
 
