@@ -36,6 +36,8 @@ __all__ = ["streamkl_fwd", "streamkl_fwd_splitk", "streamkl_fwd_splitk_noalloc",
            "streamkl_probe_mfma_bf16"]
 
 _DTYPES = {torch.bfloat16: _lib.STREAMKL_BF16, torch.float32: _lib.STREAMKL_FP32}
+if hasattr(torch, "float8_e4m3fn"):  # forward entry points only
+    _DTYPES[torch.float8_e4m3fn] = _lib.STREAMKL_FP8_E4M3
 
 
 def _stream_handle(device: torch.device) -> int:

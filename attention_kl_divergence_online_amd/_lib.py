@@ -22,6 +22,7 @@ STREAMKL_ERR_HIP = 6
 
 STREAMKL_BF16 = 0
 STREAMKL_FP32 = 1
+STREAMKL_FP8_E4M3 = 2
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # STREAMKL_NOALLOC_SCRATCH_BYTES
 

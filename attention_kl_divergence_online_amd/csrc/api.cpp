@@ -116,7 +116,8 @@ bool bwd_grids_fit(const streamkl_problem *p) {
 // Shape / dtype checks common to every entry point.
 streamkl_status check_problem(const streamkl_problem *p) {
   if (!p) return STREAMKL_ERR_NULL;
-  if (p->dtype != STREAMKL_BF16 && p->dtype != STREAMKL_FP32) return STREAMKL_ERR_DTYPE;
+  if (p->dtype != STREAMKL_BF16 && p->dtype != STREAMKL_FP32 && p->dtype != STREAMKL_FP8_E4M3)
+    return STREAMKL_ERR_DTYPE;
   if (p->B < 0 || p->H < 0 || p->NQ < 0 || p->NK < 0) return STREAMKL_ERR_SHAPE;
   if (p->D != 64 && p->D != 128) return STREAMKL_ERR_SHAPE;
   // A row with no visible key has no distribution to compare.
@@ -143,6 +144,7 @@ streamkl_status check_fwd_problem(const streamkl_problem *p, int64_t splits) {
 streamkl_status check_bwd_problem(const streamkl_problem *p) {
   const streamkl_status st = check_problem(p);
   if (st != STREAMKL_OK) return st;
+  if (p->dtype == STREAMKL_FP8_E4M3) return STREAMKL_ERR_DTYPE;  // forward only
   return bwd_grids_fit(p) ? STREAMKL_OK : STREAMKL_ERR_SHAPE;
 }
 
@@ -563,7 +565,9 @@ streamkl_status for_each_run(const streamkl_varlen_problem *v, F f) {
 
 streamkl_status check_varlen(const streamkl_varlen_problem *v, bool backward) {
   if (!v) return STREAMKL_ERR_NULL;
-  if (v->dtype != STREAMKL_BF16 && v->dtype != STREAMKL_FP32) return STREAMKL_ERR_DTYPE;
+  if (v->dtype != STREAMKL_BF16 && v->dtype != STREAMKL_FP32 && v->dtype != STREAMKL_FP8_E4M3)
+    return STREAMKL_ERR_DTYPE;
+  if (backward && v->dtype == STREAMKL_FP8_E4M3) return STREAMKL_ERR_DTYPE;  // forward only
   if (v->B < 0 || v->H < 0) return STREAMKL_ERR_SHAPE;
   if (v->D != 64 && v->D != 128) return STREAMKL_ERR_SHAPE;
   if (!v->cu_seqlens_q || !v->cu_seqlens_k) return STREAMKL_ERR_NULL;
@@ -701,7 +705,7 @@ streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v, const void
   if (!q1 || !k1 || !q2 || !k2) return STREAMKL_ERR_NULL;
   if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2)) return STREAMKL_ERR_ALIGN;
   if ((st = check_rowvecs(kl, lse1, lse2)) != STREAMKL_OK) return st;
-  const int64_t es = v->dtype == STREAMKL_BF16 ? 2 : 4;
+  const int64_t es = v->dtype == STREAMKL_BF16 ? 2 : v->dtype == STREAMKL_FP8_E4M3 ? 1 : 4;
   const int D = (int)v->D;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // Runs of the main kernel shape: segmented launches, all in one shape (the
@@ -714,7 +718,8 @@ streamkl_status streamkl_fwd_varlen(const streamkl_varlen_problem *v, const void
     return STREAMKL_OK;
   });
   const bool small =
-      v->dtype == STREAMKL_BF16 && (D == 64 || (v->causal && longest <= skl::kFwdSmallVarlenRows));
+      (v->dtype == STREAMKL_BF16 || v->dtype == STREAMKL_FP8_E4M3) &&
+      (D == 64 || (v->causal && longest <= skl::kFwdSmallVarlenRows));
   std::vector<SegItem> items;
   st = for_each_run(v, [&](const Run &r) {
     if (r.nq == 0) return STREAMKL_OK;

@@ -29,6 +29,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -54,6 +55,18 @@ __device__ __forceinline__ f32x16 mma16(f32x8 a, f32x8 b, f32x16 c) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], c, 0, 0, 0);
   return c;
+}
+
+// fp8 e4m3 operands (32 per lane): C += A * B for one 64-deep contraction
+// step of a 32x32 block, with byte j of lane (h, c) of A meeting byte j of
+// lane (h, c') of B.  No block scales (the unscaled form).
+__device__ __forceinline__ f32x16 mma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// Two 16-byte pieces as one 32-byte operand (lo first).
+__device__ __forceinline__ i32x8 join16(u32x4 lo, u32x4 hi) {
+  return i32x8{(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3],
+               (int32_t)hi[0], (int32_t)hi[1], (int32_t)hi[2], (int32_t)hi[3]};
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -112,6 +125,12 @@ __device__ __forceinline__ u32x4 buffer_load16(BufRange r, uint32_t voff, uint32
 // 256-byte bank row.
 template <int D> __device__ __forceinline__ int swz_row(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);  // 256- or 128-byte rows
+}
+// The same by row length in bytes (256, 128 or 64; 64-byte rows: four
+// chunks, four rows per bank row).
+template <int RB> __device__ __forceinline__ int swz_bytes(int r) {
+  static_assert(RB == 256 || RB == 128 || RB == 64, "row bytes");
+  return RB == 256 ? (r & 15) : RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
 }  // namespace skl

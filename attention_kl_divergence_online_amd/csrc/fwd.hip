@@ -418,15 +418,22 @@ __global__ __launch_bounds__(256) void splitk_merge_kernel(FwdParams p) {
 // CU, so every resident wave has live queries and several tiles of keys are
 // in flight per CU; the large shape at 32 queries would leave seven of eight
 // waves idle and one tile in flight.
-template <int D, int WAVES_ = 8, int BK_ = kFwdBK>
+//
+// fp8 (e4m3) inputs take the same shapes with v_mfma_f32_32x32x64_f8f6f4:
+// rows of D bytes, and per 64-element k-step a lane supplies 32 bytes of its
+// row (elements 64 s + 32 h ..).  The instruction pairs byte j of lane (h, c)
+// of A with byte j of lane (h, c') of B, so any such split of the row that
+// both operands share gives the full dot product.
+template <int D, int WAVES_ = 8, int BK_ = kFwdBK, bool F8_ = false>
 struct Fwd2Traits {
+  static constexpr bool F8 = F8_;
   static constexpr int WAVES = WAVES_;
   static constexpr int NT = 64 * WAVES;
   static constexpr int BQ = 32 * WAVES;  // 32 queries per wave
   static constexpr int BK = BK_;         // keys per tile
   static constexpr int BPT = BK / 32;    // 32-key blocks per tile
-  static constexpr int KSTEPS = D / 16;
-  static constexpr int RB = D * 2;      // bf16 row bytes
+  static constexpr int KSTEPS = F8 ? D / 64 : D / 16;
+  static constexpr int RB = F8 ? D : D * 2;  // row bytes
   static constexpr int CPROW = RB / 16;
   static constexpr int ROW_T = BK * RB;  // one tensor's key tile
   static constexpr int LDS_BYTES = 2 * 2 * ROW_T;
@@ -443,11 +450,14 @@ constexpr float kLazySumMax = 16777216.f;
 constexpr int kDecodeRows = 32;
 constexpr int kDecode16Rows = 16;
 inline bool fwd_decode_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <= kDecodeRows; }
+// Input types the matrix-core forward takes: bf16 (0) and fp8 e4m3 (2).
+inline bool fwd_mfma_dtype(int dtype) { return dtype == 0 || dtype == 2; }
 inline bool fwd_decode16_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <= kDecode16Rows; }
 
-template <int D, bool SPLIT, int WAVES, int BK>
+template <int D, bool SPLIT, int WAVES, int BK, bool F8>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(FwdParams p, const SegTable t) {
-  using Tr = Fwd2Traits<D, WAVES, BK>;
+  using Tr = Fwd2Traits<D, WAVES, BK, F8>;
+  using Frag = typename std::conditional<F8, i32x8, bf16x8>::type;  // one k-step of a lane's row
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -473,10 +483,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
   const int NQ = (int)p.NQ, NK = (int)p.NK;
   const int off = NK - NQ;
   const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
-  const bf16 *Q1 = reinterpret_cast<const bf16 *>(p.q1) + rq * D;
-  const bf16 *Q2 = reinterpret_cast<const bf16 *>(p.q2) + rq * D;
-  const BufRange rk1{reinterpret_cast<const bf16 *>(p.k1) + rk * D, NK * Tr::RB};
-  const BufRange rk2{reinterpret_cast<const bf16 *>(p.k2) + rk * D, NK * Tr::RB};
+  const char *Q1 = reinterpret_cast<const char *>(p.q1) + rq * Tr::RB;
+  const char *Q2 = reinterpret_cast<const char *>(p.q2) + rq * Tr::RB;
+  const BufRange rk1{reinterpret_cast<const char *>(p.k1) + rk * Tr::RB, NK * Tr::RB};
+  const BufRange rk2{reinterpret_cast<const char *>(p.k2) + rk * Tr::RB, NK * Tr::RB};
 
   const int q0 = qt * Tr::BQ;
   const int qend = min(q0 + Tr::BQ, NQ);
@@ -496,15 +506,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
   const int nfull = wave_live ? max(0, vis_all - k_lo) / 32 : 0;
   const int nlive = wave_live ? (max(0, vis_any - k_lo) + 31) / 32 : 0;
 
-  // Resident query fragments: lane owns query qw0 + c32, elements [16s + 8h, +8).
+  // Resident query fragments: lane owns query qw0 + c32; k-step s is bytes
+  // [FB (2 s + h), + FB) of the row, FB = 16 (bf16) or 32 (fp8).
   const int row = qw0 + c32;
   const bool row_ok = row < qend;
   const int klim = min(k_hi, p.causal ? row + off + 1 : NK);
-  bf16x8 qf1[Tr::KSTEPS], qf2[Tr::KSTEPS];
+  constexpr int FB = (int)sizeof(Frag);
+  Frag qf1[Tr::KSTEPS], qf2[Tr::KSTEPS];
 #pragma unroll
   for (int s = 0; s < Tr::KSTEPS; ++s) {
-    qf1[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(Q1 + (int64_t)row * D + 16 * s + 8 * h) : bf16x8{};
-    qf2[s] = row_ok ? *reinterpret_cast<const bf16x8 *>(Q2 + (int64_t)row * D + 16 * s + 8 * h) : bf16x8{};
+    qf1[s] = row_ok ? *reinterpret_cast<const Frag *>(Q1 + (int64_t)row * Tr::RB + FB * (2 * s + h)) : Frag{};
+    qf2[s] = row_ok ? *reinterpret_cast<const Frag *>(Q2 + (int64_t)row * Tr::RB + FB * (2 * s + h)) : Frag{};
   }
 
   const float c = p.scale * kLog2e;
@@ -518,7 +530,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
   for (int i = 0; i < Tr::LOADS; ++i) {
     const int C = i * Tr::NT + tid;
     const int r = C / Tr::CPROW;
-    voff[i] = r * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(r)) * 16;
+    voff[i] = r * Tr::RB + ((C % Tr::CPROW) ^ swz_bytes<Tr::RB>(r)) * 16;
   }
   auto load_tile = [&](int t) {
     const uint32_t soff = (uint32_t)(k_lo + t * Tr::BK) * Tr::RB;
@@ -536,16 +548,25 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
   // Logits of block b (key block b % BPT of tile b / BPT).
   auto scores = [&](int b, f32x16 &s1, f32x16 &s2) {
     const int kr = (b % Tr::BPT) * 32 + c32;
-    const int sw = swz_row<D>(kr);
+    const int sw = swz_bytes<Tr::RB>(kr);
     const char *r1 = smem + ((b / Tr::BPT) & 1) * 2 * Tr::ROW_T + kr * Tr::RB;
     const char *r2 = r1 + Tr::ROW_T;
     s1 = f32x16{};
     s2 = f32x16{};
 #pragma unroll
     for (int s = 0; s < Tr::KSTEPS; ++s) {
-      const int pc = ((2 * s + h) ^ sw) * 16;
-      s1 = mma16(*reinterpret_cast<const bf16x8 *>(r1 + pc), qf1[s], s1);
-      s2 = mma16(*reinterpret_cast<const bf16x8 *>(r2 + pc), qf2[s], s2);
+      if constexpr (F8) {
+        const int c0 = 4 * s + 2 * h;  // the lane's two 16-byte chunks
+        const int pa = (c0 ^ sw) * 16, pb = ((c0 + 1) ^ sw) * 16;
+        s1 = mma_f8(join16(*reinterpret_cast<const u32x4 *>(r1 + pa), *reinterpret_cast<const u32x4 *>(r1 + pb)),
+                    qf1[s], s1);
+        s2 = mma_f8(join16(*reinterpret_cast<const u32x4 *>(r2 + pa), *reinterpret_cast<const u32x4 *>(r2 + pb)),
+                    qf2[s], s2);
+      } else {
+        const int pc = ((2 * s + h) ^ sw) * 16;
+        s1 = mma16(*reinterpret_cast<const bf16x8 *>(r1 + pc), qf1[s], s1);
+        s2 = mma16(*reinterpret_cast<const bf16x8 *>(r2 + pc), qf2[s], s2);
+      }
     }
   };
   auto update = [&](int b, const f32x16 &s1, const f32x16 &s2) {
@@ -914,15 +935,15 @@ static hipError_t launch_fwd16(const FwdParams &p, hipStream_t s) {
 // A plain launch passes an empty segment table.
 const SegTable kNoSegs{};
 
-template <int D, bool SPLIT, int WAVES, int BK>
+template <int D, bool SPLIT, int WAVES, int BK, bool F8 = false>
 static hipError_t launch_fwd2_shape(const FwdParams &p, const SegTable &t, hipStream_t s) {
-  using Tr = Fwd2Traits<D, WAVES, BK>;
-  const void *fn = reinterpret_cast<const void *>(&fwd2_kernel<D, SPLIT, WAVES, BK>);
+  using Tr = Fwd2Traits<D, WAVES, BK, F8>;
+  const void *fn = reinterpret_cast<const void *>(&fwd2_kernel<D, SPLIT, WAVES, BK, F8>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int64_t nblk = t.n > 0 ? (int64_t)t.end : p.BH * (int64_t)p.nqt * p.splits;
-  hipLaunchKernelGGL((fwd2_kernel<D, SPLIT, WAVES, BK>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p,
-                     t);
+  hipLaunchKernelGGL((fwd2_kernel<D, SPLIT, WAVES, BK, F8>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s,
+                     p, t);
   return hipGetLastError();
 }
 
@@ -936,13 +957,13 @@ static hipError_t launch_fwd2_shape(const FwdParams &p, const SegTable &t, hipSt
 // problems of up to 4096 queries at D = 128, but 2-4% slower for longer or
 // non-causal D = 128 problems.  Split-K chunks are whole 128-key tiles, a
 // whole number of any of these.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool F8 = false>
 static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
   static_assert(kFwdChunkTile % 128 == 0, "split chunks must hold whole 128-key tiles");
-  if (fwd_decode16_shape(0, p.NQ)) return launch_fwd16<D, SPLIT>(p, s);
-  if (fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, kNoSegs, s);
-  if (!SPLIT && p.small) return launch_fwd2_shape<D, false, 4, 64>(p, kNoSegs, s);
-  return launch_fwd2_shape<D, SPLIT, 8, D == 128 ? 128 : 64>(p, kNoSegs, s);
+  if (!F8 && fwd_decode16_shape(0, p.NQ)) return launch_fwd16<D, SPLIT>(p, s);
+  if (!F8 && fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, kNoSegs, s);
+  if (!SPLIT && p.small) return launch_fwd2_shape<D, false, 4, 64, F8>(p, kNoSegs, s);
+  return launch_fwd2_shape<D, SPLIT, 8, D == 128 ? 128 : 64, F8>(p, kNoSegs, s);
 }
 
 template <typename T, int D, bool SPLIT>
@@ -959,13 +980,13 @@ static hipError_t launch_fwd_t(const FwdParams &p, const SegTable &t, hipStream_
 int fwd_block_queries(int dtype, int D, int64_t NQ, bool small) {
   if (fwd_decode16_shape(dtype, NQ)) return Fwd16Traits<128>::BQ;
   if (fwd_decode_shape(dtype, NQ)) return Fwd2Traits<128, 1, 32>::BQ;
-  if (dtype == 0 && small) return Fwd2Traits<128, 4, 64>::BQ;
-  if (dtype == 0) return D == 128 ? Fwd2Traits<128>::BQ : Fwd2Traits<64>::BQ;
+  if (fwd_mfma_dtype(dtype) && small) return Fwd2Traits<128, 4, 64>::BQ;
+  if (fwd_mfma_dtype(dtype)) return D == 128 ? Fwd2Traits<128>::BQ : Fwd2Traits<64>::BQ;
   return D == 128 ? FwdTraits<float, 128>::BQ : FwdTraits<float, 64>::BQ;
 }
 
 bool fwd_small_shape(int dtype, int D, int64_t NQ, bool causal) {
-  return dtype == 0 && !fwd_decode_shape(dtype, NQ) && (D == 64 || (causal && NQ <= kFwdSmallCausalRows));
+  return fwd_mfma_dtype(dtype) && !fwd_decode_shape(dtype, NQ) && (D == 64 || (causal && NQ <= kFwdSmallCausalRows));
 }
 
 hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s) {
@@ -973,6 +994,10 @@ hipError_t launch_fwd(int dtype, int D, const FwdParams &p, hipStream_t s) {
   if (dtype == 0) {
     if (D == 128) return split ? launch_fwd2<128, true>(p, s) : launch_fwd2<128, false>(p, s);
     return split ? launch_fwd2<64, true>(p, s) : launch_fwd2<64, false>(p, s);
+  }
+  if (dtype == 2) {
+    if (D == 128) return split ? launch_fwd2<128, true, true>(p, s) : launch_fwd2<128, false, true>(p, s);
+    return split ? launch_fwd2<64, true, true>(p, s) : launch_fwd2<64, false, true>(p, s);
   }
   if (D == 128)
     return split ? launch_fwd_t<float, 128, true>(p, kNoSegs, s) : launch_fwd_t<float, 128, false>(p, kNoSegs, s);
@@ -985,6 +1010,13 @@ hipError_t launch_fwd_segs(int dtype, int D, const FwdParams &p, const SegTable 
   if (dtype == 0) {
     if (D == 128) return p.small ? launch_fwd2_shape<128, false, 4, 64>(p, t, s) : launch_fwd2_shape<128, false, 8, 128>(p, t, s);
     return p.small ? launch_fwd2_shape<64, false, 4, 64>(p, t, s) : launch_fwd2_shape<64, false, 8, 64>(p, t, s);
+  }
+  if (dtype == 2) {
+    if (D == 128)
+      return p.small ? launch_fwd2_shape<128, false, 4, 64, true>(p, t, s)
+                     : launch_fwd2_shape<128, false, 8, 128, true>(p, t, s);
+    return p.small ? launch_fwd2_shape<64, false, 4, 64, true>(p, t, s)
+                   : launch_fwd2_shape<64, false, 8, 64, true>(p, t, s);
   }
   if (D == 128) return launch_fwd_t<float, 128, false>(p, t, s);
   return launch_fwd_t<float, 64, false>(p, t, s);

@@ -25,7 +25,8 @@
  *    streamkl_fwd_splitk_noalloc: a device scratch array per GPU and the
  *    table of their addresses, filled once per device under a lock.
  *  - Q1, Q2 are [B, H, NQ, D] and K1, K2 are [B, H, NK, D], contiguous,
- *    row-major, element type `dtype` (bf16 or fp32).  Per-row vectors (KL,
+ *    row-major, element type `dtype` (bf16, fp32, or fp8 e4m3 for the
+ *    forward entry points).  Per-row vectors (KL,
  *    LSE1, LSE2, g) are fp32 [B, H, NQ].  Gradients are fp32 and have the
  *    shape of the tensor they belong to.
  *  - Every pointer must be 16-byte aligned.  D must be 64 or 128.
@@ -55,13 +56,28 @@ typedef enum {
                                    ceil(N / 64) * 64 rows of D reaching 2^31 bytes,
                                    B * H reaching 2^31, a kernel grid past the GPU's
                                    2^32 - 1 work-items, split count out of range */
-    STREAMKL_ERR_DTYPE = 3,     /* dtype is not STREAMKL_BF16 / STREAMKL_FP32 */
+    STREAMKL_ERR_DTYPE = 3,     /* dtype is not a streamkl_dtype, or STREAMKL_FP8_E4M3
+                                   passed to a backward entry point */
     STREAMKL_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
     STREAMKL_ERR_WORKSPACE = 5, /* workspace missing or smaller than the size query */
     STREAMKL_ERR_HIP = 6        /* the HIP runtime rejected a launch */
 } streamkl_status;
 
-typedef enum { STREAMKL_BF16 = 0, STREAMKL_FP32 = 1 } streamkl_dtype;
+/*
+ * STREAMKL_FP8_E4M3: the OCP 8-bit float with 4 exponent bits (bias 7), 3
+ * significand bits, no infinities and NaN as S.1111.111 (torch.float8_e4m3fn).
+ * The forward entry points (streamkl_fwd, streamkl_fwd_splitk,
+ * streamkl_fwd_splitk_noalloc, streamkl_fwd_varlen) take it: both logits
+ * products run on the fp8 matrix instructions (products exact, fp32
+ * accumulation) and everything after them in fp32, as for bf16.  This is the
+ * mixed-precision direction the pages leave as future work (arxivlens.com
+ * paper view of StreamKL, future-work list).  The backward entry points and
+ * their workspace queries refuse it (STREAMKL_ERR_DTYPE, size 0): its
+ * gradient products need 16-bit operands.  Rounding bf16 tensors to e4m3
+ * changes the distributions themselves far more than the 2e-3 the bf16 path
+ * holds to; the type is for inputs that are fp8 already.
+ */
+typedef enum { STREAMKL_BF16 = 0, STREAMKL_FP32 = 1, STREAMKL_FP8_E4M3 = 2 } streamkl_dtype;
 
 typedef struct {
     int64_t B, H;   /* batch, heads */

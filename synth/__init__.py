@@ -145,6 +145,12 @@ def make_inputs(w: Workload, device: str = "cpu", heads: Optional[Iterable] = No
     return q1, k1, q2, k2
 
 
+def to_fp8(t: torch.Tensor) -> torch.Tensor:
+    """`t` rounded to fp8 e4m3 (torch.float8_e4m3fn), on t's device: inputs for
+    the fp8 forward, whose values the oracle then takes exactly."""
+    return t.to(torch.float8_e4m3fn)
+
+
 def upstream_grad(w: Workload, device: str = "cpu") -> torch.Tensor:
     """Per-row upstream gradient g of a mean-reduced loss: 1/(B*H*NQ) everywhere."""
     return torch.full((w.B, w.H, w.NQ), 1.0 / (w.B * w.H * w.NQ), dtype=torch.float32, device=device)

@@ -87,6 +87,26 @@ def test_forward_validation(L):
     assert fwd(L, P(), l2=MIS) == _lib.STREAMKL_ERR_ALIGN
 
 
+def test_fp8_is_forward_only(L):
+    # fp8 e4m3 inputs pass the forward's checks (the call then stops at the
+    # first null pointer, before any launch); every backward entry point and
+    # workspace query refuses them.
+    f8 = _lib.STREAMKL_FP8_E4M3
+    assert fwd(L, P(dtype=f8), q1=None) == _lib.STREAMKL_ERR_NULL
+    assert fwd(L, P(dtype=f8, D=128), q2=MIS) == _lib.STREAMKL_ERR_ALIGN
+    assert fwd(L, P(dtype=f8, B=0), q1=None, kl=None) == _lib.STREAMKL_OK
+    p = P(dtype=f8)
+    assert L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 1) > 0
+    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == 0
+    assert L.streamkl_bwd_workspace_size_min(ctypes.byref(p)) == 0
+    assert L.streamkl_bwd(ctypes.byref(p), A, A, A, A, A, A, A, A, A, A, A, A, A, 1 << 20,
+                          None) == _lib.STREAMKL_ERR_DTYPE
+    assert L.streamkl_bwd_prepare(ctypes.byref(p), A, A, A, A, A, A, 1 << 20, None) == _lib.STREAMKL_ERR_DTYPE
+    for name in ("streamkl_bwd_dk", "streamkl_bwd_dq"):
+        fn = getattr(L, name)
+        assert fn(ctypes.byref(p), A, A, A, A, A, A, A, A, A, A, A, 1 << 20, None) == _lib.STREAMKL_ERR_DTYPE, name
+
+
 def test_grid_limit_is_rejected_on_the_host(L):
     # 2^30 heads of 1024 queries: every size is legal on its own, but the forward
     # grid (4 query tiles x 512 threads per head) passes 2^32 work-items.
@@ -289,6 +309,8 @@ def test_varlen_validation(L):
     assert vfwd(L, VP([0, 5, 9], [0, 5, 8], causal=1)) == _lib.STREAMKL_ERR_SHAPE  # 4 queries > 3 keys
     assert vfwd(L, VP([0, 5], [0, 5], D=96)) == _lib.STREAMKL_ERR_SHAPE
     assert vfwd(L, VP([0, 5], [0, 5], dtype=9)) == _lib.STREAMKL_ERR_DTYPE
+    assert vfwd(L, VP([0, 5], [0, 5], dtype=_lib.STREAMKL_FP8_E4M3), q1=None) == _lib.STREAMKL_ERR_NULL
+    assert vbwd(L, VP([0, 5], [0, 5], dtype=_lib.STREAMKL_FP8_E4M3)) == _lib.STREAMKL_ERR_DTYPE
     assert vfwd(L, VP([0, 5], [0, 5]), q1=None) == _lib.STREAMKL_ERR_NULL
     assert vfwd(L, VP([0, 5], [0, 5]), q1=MIS) == _lib.STREAMKL_ERR_ALIGN
     assert vfwd(L, VP([0, 5], [0, 5]), kl=MIS) == _lib.STREAMKL_ERR_ALIGN

@@ -1,0 +1,115 @@
+"""GPU parity of the fp8 (e4m3) forward against the fp64 oracle.
+
+The inputs are fp8 values (seeded normals rounded to e4m3 on the host), and
+the oracle is given exactly those values in fp64, so the only differences
+are the kernels' fp32 accumulation and exponentials: the bf16 path's 2e-3
+bound applies.  Shapes cover the four-wave and eight-wave forward shapes,
+both head dimensions, ragged tails in N_Q and N_K, the causal diagonal,
+split-K chunks and a packed variable-length batch.  The backward refuses fp8
+inputs with a status code.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from attention_kl_divergence_online_amd import (StreamKLError, bwd_workspace_size, streamkl_bwd, streamkl_fwd,
+                                                streamkl_fwd_splitk, streamkl_fwd_varlen)
+from parity_util import TOL, assert_within, compare_forward, sample_rows
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not hasattr(torch, "float8_e4m3fn"), reason="torch without float8 types")]
+
+DEV = "cuda"
+
+
+def _rand_fp8(shape_q, shape_k, seed, noise=0.3):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q1 = torch.randn(*shape_q, generator=g)
+    k1 = torch.randn(*shape_k, generator=g)
+    q2 = q1 + noise * torch.randn(*shape_q, generator=g)
+    k2 = k1 + noise * torch.randn(*shape_k, generator=g)
+    return [synth.to_fp8(t).to(DEV).contiguous() for t in (q1, k1, q2, k2)]
+
+
+CASES = [
+    # B, H, NQ, NK, D, causal
+    (1, 2, 300, 517, 128, False),
+    (1, 2, 300, 517, 128, True),
+    (2, 1, 700, 700, 128, True),     # four-wave causal shape
+    (1, 3, 129, 1000, 64, False),
+    (1, 2, 257, 333, 64, True),
+    (1, 1, 1, 37, 128, False),
+    (1, 1, 5, 5, 128, True),
+    (2, 1, 16, 77, 64, True),        # few queries: fp8 has no decode shapes, these run the general ones
+    (1, 1, 4160, 4160, 128, True),   # eight-wave causal shape, 128-key tiles
+    (1, 2, 1000, 2500, 128, False),  # eight-wave non-causal shape
+]
+
+
+@pytest.mark.parametrize("B,H,NQ,NK,D,causal", CASES)
+def test_fp8_forward_all_rows(B, H, NQ, NK, D, causal):
+    print(f"fp8 forward B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal}", flush=True)
+    q1, k1, q2, k2 = _rand_fp8((B, H, NQ, D), (B, H, NK, D), seed=NQ * 5 + NK + D + causal)
+    scale = D ** -0.5
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    assert torch.isfinite(kl).all() and torch.isfinite(l1).all() and torch.isfinite(l2).all()
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"],
+                  f"fp8 fwd NQ={NQ} NK={NK} D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_splitk_matches_oracle(causal):
+    B, H, NQ, NK, D = 1, 2, 200, 3000, 128
+    print(f"fp8 split-K causal={causal}", flush=True)
+    q1, k1, q2, k2 = _rand_fp8((B, H, NQ, D), (B, H, NK, D), seed=77 + causal)
+    scale = D ** -0.5
+    kl, l1, l2 = streamkl_fwd_splitk(q1, k1, q2, k2, 5, scale, causal)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 1)]
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"],
+                  f"fp8 split fwd causal={causal}")
+
+
+def test_fp8_varlen_matches_per_sequence_oracle():
+    lens_q, lens_k, H, D, causal = [1, 130, 0, 300, 64], [5, 130, 9, 517, 64], 2, 128, True
+    print("fp8 varlen", flush=True)
+    TQ, TK = sum(lens_q), sum(lens_k)
+    q1, k1, q2, k2 = _rand_fp8((H, TQ, D), (H, TK, D), seed=4242)
+    cu_q, cu_k = [0] + np.cumsum(lens_q).tolist(), [0] + np.cumsum(lens_k).tolist()
+    scale = D ** -0.5
+    kl, l1, l2 = streamkl_fwd_varlen(q1, k1, q2, k2, cu_q, cu_k, scale, causal)
+    torch.cuda.synchronize()
+    for b in range(len(lens_q)):
+        if lens_q[b] == 0:
+            continue
+        sq, sk = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        seq = [t[:, s].unsqueeze(0) for t, s in ((q1, sq), (k1, sk), (q2, sq), (k2, sk))]
+        outs = [t[:, sq].unsqueeze(0) for t in (kl, l1, l2)]
+        heads = [(0, h) for h in range(H)]
+        assert_within(compare_forward(*seq, scale, causal, *outs, heads), TOL["bf16"], f"fp8 varlen seq {b}")
+
+
+def test_fp8_causal_64k_sampled_rows():
+    # The causal 64K workload's shape (32 heads) with its inputs rounded to
+    # e4m3, in the launch the bench times: sampled rows of two heads.
+    w = synth.get("causal_64k")
+    print("fp8 causal 64K", flush=True)
+    q1, k1, q2, k2 = (synth.to_fp8(t) for t in synth.make_inputs(w, DEV))
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, w.scale, w.causal)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.NQ, 24, seed=5)
+    heads = [(0, 0), (0, w.H - 1)]
+    assert_within(compare_forward(q1, k1, q2, k2, w.scale, w.causal, kl, l1, l2, heads, rows=rows), TOL["bf16"],
+                  "fp8 causal_64k fwd (sampled rows)")
+
+
+def test_fp8_backward_is_refused():
+    q1, k1, q2, k2 = _rand_fp8((1, 1, 64, 128), (1, 1, 64, 128), seed=3)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, True)
+    g = torch.ones_like(kl)
+    assert bwd_workspace_size(q1, k1, None, True) == 0
+    with pytest.raises(StreamKLError):
+        streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True)
