@@ -3,7 +3,7 @@
 The inputs are fp8 values (seeded normals rounded to e4m3 on the host), and
 the oracle is given exactly those values in fp64, so the only differences
 are the kernels' fp32 accumulation and exponentials: the bf16 path's 2e-3
-bound applies.  Shapes cover the four-wave and eight-wave forward shapes,
+bound applies.  Shapes cover the four-wave and twelve-wave fp8 forward shapes,
 both head dimensions, ragged tails in N_Q and N_K, the causal diagonal,
 split-K chunks and a packed variable-length batch.  The backward refuses fp8
 inputs with a status code.
@@ -42,8 +42,8 @@ CASES = [
     (1, 1, 1, 37, 128, False),
     (1, 1, 5, 5, 128, True),
     (2, 1, 16, 77, 64, True),        # few queries: fp8 has no decode shapes, these run the general ones
-    (1, 1, 4160, 4160, 128, True),   # eight-wave causal shape, 128-key tiles
-    (1, 2, 1000, 2500, 128, False),  # eight-wave non-causal shape
+    (1, 1, 4160, 4160, 128, True),   # twelve-wave causal shape, 128-key tiles
+    (1, 2, 1000, 2500, 128, False),  # twelve-wave non-causal shape, ragged last query tile
 ]
 
 
