@@ -33,7 +33,7 @@ struct DqSplit {
 };
 DqSplit dq_split(const streamkl_problem *p) {
   DqSplit r{1, 0};
-  if (p->dtype != STREAMKL_BF16 || p->NQ == 0 || p->NK == 0) return r;
+  if (p->dtype == STREAMKL_FP32 || p->NQ == 0 || p->NK == 0) return r;
   const int64_t wgs = p->B * p->H * ((p->NQ + skl::kBwdBR - 1) / skl::kBwdBR);
   if (wgs >= kDqSplitTarget) return r;
   const int64_t ktiles = (p->NK + skl::kBwdTile - 1) / skl::kBwdTile;
@@ -98,10 +98,11 @@ bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 constexpr __int128 kGridLimit = ((__int128)1 << 32) - 1;
 bool fwd_grids_fit(const streamkl_problem *p, int64_t splits) {
   const __int128 bh = (__int128)p->B * p->H;
-  // The 4-wave shape's grid (ceil(NQ / 128) x 256 work-items per head) is no
-  // larger than the 8-wave one's, so the 8-wave count bounds both.
+  // 64 work-items per 32 queries of a query tile.  The 4-wave shape's grid
+  // (ceil(NQ / 128) x 256 work-items per head) is no larger than the main
+  // shape's (256 queries, or 384 for fp8), so the main count bounds both.
   const int64_t bq = skl::fwd_block_queries(p->dtype, (int)p->D, p->NQ, false);
-  const __int128 fwd = bh * ((p->NQ + bq - 1) / bq) * splits * (bq <= 32 ? 64 : 512);
+  const __int128 fwd = bh * ((p->NQ + bq - 1) / bq) * splits * (bq <= 32 ? 64 : 2 * bq);
   const __int128 merge = bh * ((p->NQ + 255) / 256 * 256);
   return fwd <= kGridLimit && merge <= kGridLimit;
 }
@@ -144,7 +145,6 @@ streamkl_status check_fwd_problem(const streamkl_problem *p, int64_t splits) {
 streamkl_status check_bwd_problem(const streamkl_problem *p) {
   const streamkl_status st = check_problem(p);
   if (st != STREAMKL_OK) return st;
-  if (p->dtype == STREAMKL_FP8_E4M3) return STREAMKL_ERR_DTYPE;  // forward only
   return bwd_grids_fit(p) ? STREAMKL_OK : STREAMKL_ERR_SHAPE;
 }
 
@@ -567,7 +567,6 @@ streamkl_status check_varlen(const streamkl_varlen_problem *v, bool backward) {
   if (!v) return STREAMKL_ERR_NULL;
   if (v->dtype != STREAMKL_BF16 && v->dtype != STREAMKL_FP32 && v->dtype != STREAMKL_FP8_E4M3)
     return STREAMKL_ERR_DTYPE;
-  if (backward && v->dtype == STREAMKL_FP8_E4M3) return STREAMKL_ERR_DTYPE;  // forward only
   if (v->B < 0 || v->H < 0) return STREAMKL_ERR_SHAPE;
   if (v->D != 64 && v->D != 128) return STREAMKL_ERR_SHAPE;
   if (!v->cu_seqlens_q || !v->cu_seqlens_k) return STREAMKL_ERR_NULL;
@@ -876,7 +875,7 @@ streamkl_status streamkl_bwd_varlen(const streamkl_varlen_problem *v, const void
   // Runs whose query-gradient pass splits its keys, one after another with
   // their own layout at the front of the workspace (stream order keeps them
   // after the segmented passes that read it).
-  const int64_t es = bf16 ? 2 : 4;
+  const int64_t es = bf16 ? 2 : v->dtype == STREAMKL_FP8_E4M3 ? 1 : 4;
   return for_each_run(v, [&](const Run &r) {
     if (r.nq == 0 || run_segmented_bwd(v, r, fills)) return STREAMKL_OK;
     const int64_t oq = v->cu_seqlens_q[r.b0], ok = v->cu_seqlens_k[r.b0];

@@ -510,14 +510,21 @@ __global__ __launch_bounds__(256, 1) void bwd_fp32_kernel(BwdParams p, const Seg
 // product, which is rounded to fp16 and written to LDS for every wave that
 // needs it.  That costs two 32x32x16 products per 32x32 block and replaces a
 // transposed copy of every input in device memory.
-template <int D, bool KEYS_RES>
+//
+// fp8 (e4m3) inputs take the same passes with D-byte rows: the logits run on
+// v_mfma_f32_32x32x64_f8f6f4 (a lane supplies 32 bytes of its row per
+// 64-element k-step), and the transposing product takes one such k-step
+// against a one-hot e4m3 operand per 32-column block.  Every e4m3 value is an
+// fp16 value, so the fp16 transposed tiles are exact without a scale.
+template <int D, bool KEYS_RES, bool F8_ = false>
 struct Bwd4Traits {
+  static constexpr bool F8 = F8_;
   static constexpr int NT = 512;
   static constexpr int BR = kBwdBR;         // resident rows per workgroup: 4 pairs x 32
   static constexpr int BX = kBwdTile;       // streamed rows per stage
-  static constexpr int KSTEPS = D / 16;
+  static constexpr int KSTEPS = F8 ? D / 64 : D / 16;
   static constexpr int NDB = D / 32;        // 32-column gradient blocks
-  static constexpr int RB = D * 2;          // bf16 row bytes
+  static constexpr int RB = F8 ? D : D * 2; // row bytes
   static constexpr int CPROW = RB / 16;     // 16-byte chunks per row
   static constexpr int ROW_T = BX * RB;     // one tensor's row tile
   static constexpr int SLOT = 64 * 16;      // one lane-ordered 16-byte operand
@@ -533,15 +540,16 @@ struct Bwd4Traits {
   static constexpr int OFF_TR = ROWBUF * 2 * ROW_T;  // two buffers of TRB
   static constexpr int OFF_DSX = OFF_TR + 2 * TRB;   // two buffers
   static constexpr int OFF_STAT = OFF_DSX + 2 * DSX_T;
-  // With one row buffer (spare LDS), the one-hot operands of the transposing
-  // products live in LDS rather than registers: [distribution][half][lane].
-  static constexpr int ID_BYTES = ROWBUF == 1 ? 2 * 2 * SLOT : 0;
+  // With one row buffer (spare LDS), and for fp8 inputs, the one-hot
+  // operands of the transposing products live in LDS rather than registers:
+  // [distribution][half][lane] (bf16), [32-column block parity][lane][32 B] (fp8).
+  static constexpr int ID_BYTES = (ROWBUF == 1 || F8) ? 2 * 2 * SLOT : 0;
   static constexpr int OFF_ID = OFF_STAT + (KEYS_RES ? 2 * STAT_T : 0);
   static constexpr int LDS_BYTES = OFF_ID + ID_BYTES;
   static constexpr int ROW_LOADS = 2 * ROW_T / 16 / NT;  // 16-byte loads per thread per stage
   static_assert(BR == 4 * 32 && BX == 64, "tiles");
   static_assert(ROW_LOADS * 16 * NT == 2 * ROW_T, "load split");
-  static_assert(ROW_T % (16 * NT) == 0, "one tensor per load instruction");
+  static_assert(ROW_T % (16 * 64) == 0, "one tensor per wave and load instruction");
   static_assert((2 * TRB + 2 * DSX_T) % (16 * NT) == 0, "clear split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -562,9 +570,11 @@ __device__ __forceinline__ bf16x8 onehot(int c, int h, int j, float v) {
 // (Configuration 2), MODE 2 only the student's (Configuration 1).  With one
 // distribution the pair splits D instead: each wave accumulates its half of
 // D over both blocks, and the dS that is not needed is never formed.
-template <int D, bool KEYS_RES, int MODE>
+template <int D, bool KEYS_RES, int MODE, bool F8>
 __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTable t) {
-  using Tr = Bwd4Traits<D, KEYS_RES>;
+  using Tr = Bwd4Traits<D, KEYS_RES, F8>;
+  using Frag = typename std::conditional<F8, i32x8, bf16x8>::type;  // one k-step of a lane's row
+  constexpr int FB = (int)sizeof(Frag);
   extern __shared__ __attribute__((aligned(16))) char smem[];
   typedef __attribute__((address_space(3))) void lds_void;
 
@@ -589,10 +599,10 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
 
   const int64_t rq = p.qmap.row0(bh), rk = p.kmap.row0(bh);
   const int64_t rr = KEYS_RES ? rk : rq, rx = KEYS_RES ? rq : rk;  // resident / streamed row bases
-  const bf16 *R1 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k1 : p.q1) + rr * D;
-  const bf16 *R2 = reinterpret_cast<const bf16 *>(KEYS_RES ? p.k2 : p.q2) + rr * D;
-  const char *X1 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q1 : p.k1) + rx * D);
-  const char *X2 = reinterpret_cast<const char *>(reinterpret_cast<const bf16 *>(KEYS_RES ? p.q2 : p.k2) + rx * D);
+  const char *R1 = reinterpret_cast<const char *>(KEYS_RES ? p.k1 : p.q1) + rr * Tr::RB;
+  const char *R2 = reinterpret_cast<const char *>(KEYS_RES ? p.k2 : p.q2) + rr * Tr::RB;
+  const char *X1 = reinterpret_cast<const char *>(KEYS_RES ? p.q1 : p.k1) + rx * Tr::RB;
+  const char *X2 = reinterpret_cast<const char *>(KEYS_RES ? p.q2 : p.k2) + rx * Tr::RB;
   const float *KLr = p.kl + rq;
   const float *LS1 = p.lse1 + rq;
   const float *LS2 = p.lse2 + rq;
@@ -627,12 +637,13 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   // them downward so that all workgroups of a head share their first tiles.
   auto x_of = [&](int t) { return x_lo + (KEYS_RES ? ntiles - 1 - t : t) * Tr::BX; };
 
-  // Resident fragments (B operand of the logits product): lane's row, elements [16s + 8h, +8).
-  bf16x8 rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
+  // Resident fragments (B operand of the logits product): lane's row, k-step
+  // s in bytes [FB (2 s + h), + FB), FB = 16 (bf16) or 32 (fp8).
+  Frag rf1[Tr::KSTEPS], rf2[Tr::KSTEPS];
 #pragma unroll
   for (int s = 0; s < Tr::KSTEPS; ++s) {
-    rf1[s] = r_ok ? *reinterpret_cast<const bf16x8 *>(R1 + (int64_t)my_r * D + 16 * s + 8 * h) : bf16x8{};
-    rf2[s] = r_ok ? *reinterpret_cast<const bf16x8 *>(R2 + (int64_t)my_r * D + 16 * s + 8 * h) : bf16x8{};
+    rf1[s] = r_ok ? *reinterpret_cast<const Frag *>(R1 + (int64_t)my_r * Tr::RB + FB * (2 * s + h)) : Frag{};
+    rf2[s] = r_ok ? *reinterpret_cast<const Frag *>(R2 + (int64_t)my_r * Tr::RB + FB * (2 * s + h)) : Frag{};
   }
 
   const float c = p.scale * kLog2e;
@@ -644,24 +655,28 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   // past the end of the streamed operand read as zero (they only feed masked
   // pairs, and transpose to zero columns).
   const BufRange rx1{X1, NX * Tr::RB}, rx2{X2, NX * Tr::RB};
-  // Per-lane source offsets within a tile (the same for both tensors):
-  // tensor-major, row r at r * RB, logical chunk c in slot c ^ swz_row(r).
-  constexpr int RL = Tr::ROW_LOADS / 2;
-  uint32_t vrow[RL];
+  // Per-lane source offsets within a tile: load i of the stage moves chunk
+  // C = i NT + tid of the two tensors' tiles, tensor-major (tensor C / CT),
+  // row r at r * RB, logical chunk c in slot c ^ swz_bytes(r).  A wave's 64
+  // chunks lie in one tensor.
+  constexpr int RL = Tr::ROW_LOADS;
+  constexpr int CT = Tr::ROW_T / 16;                   // chunks per tensor tile
+  constexpr int VL = CT >= Tr::NT ? CT / Tr::NT : 1;  // distinct offsets (load i uses i % VL)
+  static_assert(CT % Tr::NT == 0 || Tr::NT % CT == 0, "load split");
+  uint32_t vrow[VL];
 #pragma unroll
-  for (int i = 0; i < RL; ++i) {
-    const int C = i * Tr::NT + tid;
+  for (int i = 0; i < VL; ++i) {
+    const int C = (i * Tr::NT + tid) % CT;
     const int row = C / Tr::CPROW;
-    vrow[i] = row * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(row)) * 16;
+    vrow[i] = row * Tr::RB + ((C % Tr::CPROW) ^ swz_bytes<Tr::RB>(row)) * 16;
   }
   auto load_rows = [&](int t, int buf) {
     const uint32_t soff = (uint32_t)x_of(t) * Tr::RB;
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-      for (int i = 0; i < RL; ++i)
-        buffer_load_lds16(tn ? rx2 : rx1, smem + (buf * 2 + tn) * Tr::ROW_T + (i * Tr::NT + wave * 64) * 16,
-                          vrow[i], soff);
+    for (int i = 0; i < RL; ++i) {
+      const int C0 = i * Tr::NT + wave * 64;  // the wave's first chunk
+      buffer_load_lds16(C0 >= CT ? rx2 : rx1, smem + buf * 2 * Tr::ROW_T + C0 * 16, vrow[i % VL], soff);
+    }
   };
   // Key-resident pass: statistics of the 64 streamed queries of a stage,
   // gathered by the first wave into stat buffer `buf`.
@@ -730,14 +745,29 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   // the LDS table.  Every wave writes the table's lane entries it reads, all
   // with the same values, so no barrier orders the writes before the reads.
   bf16x8 id0[2], id1[2];
+  if constexpr (F8) {
+    // fp8: for 32-column block parity v, lane (h, c) holds e4m3 1.0 at byte c
+    // when h == v (element 32 v + c of the 64-element k-step), zeros elsewhere.
 #pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2) {
-    id0[t2] = onehot(c32, h, 0, xs[t2]);
-    id1[t2] = onehot(c32, h, 1, xs[t2]);
-    if (Tr::ID_BYTES) {
-      char *idp = smem + Tr::OFF_ID + t2 * 2 * Tr::SLOT + lane * 16;
-      *reinterpret_cast<bf16x8 *>(idp) = id0[t2];
-      *reinterpret_cast<bf16x8 *>(idp + Tr::SLOT) = id1[t2];
+    for (int v = 0; v < 2; ++v) {
+      u32x4 w[2];
+#pragma unroll
+      for (int dw = 0; dw < 8; ++dw)
+        w[dw >> 2][dw & 3] = h == v && (c32 >> 2) == dw ? 0x38u << (8 * (c32 & 3)) : 0u;
+      char *idp = smem + Tr::OFF_ID + v * 2 * Tr::SLOT + lane * 32;
+      *reinterpret_cast<u32x4 *>(idp) = w[0];
+      *reinterpret_cast<u32x4 *>(idp + 16) = w[1];
+    }
+  } else {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      id0[t2] = onehot(c32, h, 0, xs[t2]);
+      id1[t2] = onehot(c32, h, 1, xs[t2]);
+      if (Tr::ID_BYTES) {
+        char *idp = smem + Tr::OFF_ID + t2 * 2 * Tr::SLOT + lane * 16;
+        *reinterpret_cast<bf16x8 *>(idp) = id0[t2];
+        *reinterpret_cast<bf16x8 *>(idp + Tr::SLOT) = id1[t2];
+      }
     }
   }
 
@@ -760,31 +790,47 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
     // Logits of streamed block e of the row tile at `rowb`.
     auto logits = [&](const char *rowb, f32x16 &x1, f32x16 &x2) {
       const int row = e * 32 + c32;
-      const int sw = swz_row<D>(row);
+      const int sw = swz_bytes<Tr::RB>(row);
       const char *a1p = rowb + row * Tr::RB;
       const char *a2p = a1p + Tr::ROW_T;
       x1 = f32x16{};
       x2 = f32x16{};
-      bf16x8 a1[Tr::KSTEPS], a2[Tr::KSTEPS];
+      if constexpr (F8) {
+        // Two k-steps of 64: all eight operand reads, then the four products.
+        i32x8 a1[Tr::KSTEPS], a2[Tr::KSTEPS];
   #pragma unroll
-      for (int s = 0; s < Tr::KSTEPS; ++s) {
-        const int pc = ((2 * s + h) ^ sw) * 16;
-        a1[s] = *reinterpret_cast<const bf16x8 *>(a1p + pc);
-        a2[s] = *reinterpret_cast<const bf16x8 *>(a2p + pc);
-      }
+        for (int s = 0; s < Tr::KSTEPS; ++s) {
+          const int pa = ((4 * s + 2 * h) ^ sw) * 16, pb = ((4 * s + 2 * h + 1) ^ sw) * 16;
+          a1[s] = join16(*reinterpret_cast<const u32x4 *>(a1p + pa), *reinterpret_cast<const u32x4 *>(a1p + pb));
+          a2[s] = join16(*reinterpret_cast<const u32x4 *>(a2p + pa), *reinterpret_cast<const u32x4 *>(a2p + pb));
+        }
   #pragma unroll
-      for (int s = 0; s < Tr::KSTEPS; ++s) {
-        x1 = mma16(a1[s], rf1[s], x1);
-        x2 = mma16(a2[s], rf2[s], x2);
-      }
-      // Keep four k-steps of operand reads in flight ahead of the products.
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        for (int s = 0; s < Tr::KSTEPS; ++s) {
+          x1 = mma_f8(a1[s], rf1[s], x1);
+          x2 = mma_f8(a2[s], rf2[s], x2);
+        }
+      } else {
+        bf16x8 a1[Tr::KSTEPS], a2[Tr::KSTEPS];
   #pragma unroll
-      for (int s = 0; s < Tr::KSTEPS - 4; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int s = 0; s < Tr::KSTEPS; ++s) {
+          const int pc = ((2 * s + h) ^ sw) * 16;
+          a1[s] = *reinterpret_cast<const bf16x8 *>(a1p + pc);
+          a2[s] = *reinterpret_cast<const bf16x8 *>(a2p + pc);
+        }
+  #pragma unroll
+        for (int s = 0; s < Tr::KSTEPS; ++s) {
+          x1 = mma16(a1[s], rf1[s], x1);
+          x2 = mma16(a2[s], rf2[s], x2);
+        }
+        // Keep four k-steps of operand reads in flight ahead of the products.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  #pragma unroll
+        for (int s = 0; s < Tr::KSTEPS - 4; ++s) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
     // dS of the own block (rows xa..xa+31) as gradient-product B operands:
     // mine[ks] for this wave's distribution, other[ks] for the partner's.
@@ -880,7 +926,7 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
     // The products, from the row tile at `rowb`.
     auto tr_issue = [&](const char *rowb, f32x16(&T)[NC]) {
       const int row = e * 32 + c32;
-      const int sw = swz_row<D>(row);
+      const int sw = swz_bytes<Tr::RB>(row);
   #pragma unroll
       for (int k = 0; k < NC; ++k) {
         if (PER < 4 && pr >= PER) {
@@ -890,6 +936,16 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
         int t, db;
         tr_pair(k, t, db);
         const char *src = rowb + t * Tr::ROW_T + row * Tr::RB;
+        if constexpr (F8) {
+          // The k-step holding block db (elements 64 (db / 2) ..), against the
+          // one-hot operand of db's parity.
+          const int c0 = 4 * (db >> 1) + 2 * h;
+          const i32x8 a = join16(*reinterpret_cast<const u32x4 *>(src + (c0 ^ sw) * 16),
+                                 *reinterpret_cast<const u32x4 *>(src + ((c0 + 1) ^ sw) * 16));
+          const i32x8 id = *reinterpret_cast<const i32x8 *>(smem + Tr::OFF_ID + (db & 1) * 2 * Tr::SLOT + lane * 32);
+          T[k] = mma_f8(a, id, f32x16{});
+          continue;
+        }
         const bf16x8 lo = *reinterpret_cast<const bf16x8 *>(src + ((4 * db + h) ^ sw) * 16);
         const bf16x8 hi = *reinterpret_cast<const bf16x8 *>(src + ((4 * db + 2 + h) ^ sw) * 16);
         bf16x8 i0, i1;
@@ -1119,7 +1175,8 @@ __device__ __forceinline__ float operand_scale(float m) {
 //  all zero, and 1 everywhere when `unit` is set: fp32 inputs need no
 //  scaling), stored negated when some g[u,:] is negative;
 //  xscale[4 u + tn] = operand_scale(max over the C chunk maxima of tensor tn)
-//  for bf16 inputs (part from absmax_kernel), 1 for fp32 inputs.
+//  for bf16 inputs (part from absmax_kernel), 1 for fp32 and fp8 inputs (no
+//  part: every e4m3 value is an fp16 value).
 __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap qmap, int64_t NQ, float *sigma,
                                                          float *xscale, const float *part, int C, int unit,
                                                          const SegTable t) {
@@ -1137,9 +1194,9 @@ __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap 
   }
   if (threadIdx.x < 4) {
     float m = 0.f;
-    if (!unit)
+    if (!unit && part)
       for (int c = 0; c < C; ++c) m = fmaxf(m, part[(bh * 4 + threadIdx.x) * kAbsChunks + c]);
-    xscale[bh * 4 + threadIdx.x] = unit ? 1.f : operand_scale(m);
+    xscale[bh * 4 + threadIdx.x] = unit || !part ? 1.f : operand_scale(m);
   }
   if (unit) {
     // fp32 inputs: no dS scaling, but the sign flag is still needed.
@@ -1542,7 +1599,7 @@ hipError_t launch_bwd_prepare(int dtype, const PrepParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(grad_scale_kernel, dim3((uint32_t)p.BH), dim3(256), 0, s, p.g, p.qmap, p.NQ, p.sigma,
-                     p.xscale, p.part, C, dtype == 1 ? 1 : 0, kNoSegs);
+                     p.xscale, dtype == 0 ? p.part : nullptr, C, dtype == 1 ? 1 : 0, kNoSegs);
   return hipGetLastError();
 }
 
@@ -1556,41 +1613,46 @@ hipError_t launch_absmax_segs(const PrepParams &p, const SegTable &t, hipStream_
 
 hipError_t launch_grad_scale_segs(int dtype, const PrepParams &p, const SegTable &t, hipStream_t s) {
   hipLaunchKernelGGL(grad_scale_kernel, dim3(t.end), dim3(256), 0, s, p.g, p.qmap, (int64_t)0, p.sigma, p.xscale,
-                     dtype == 1 ? nullptr : p.part, 1, dtype == 1 ? 1 : 0, t);
+                     dtype == 0 ? p.part : nullptr, 1, dtype == 1 ? 1 : 0, t);
   return hipGetLastError();
 }
 
-template <int D, bool KEYS_RES, int MODE>
+template <int D, bool KEYS_RES, int MODE, bool F8>
 static hipError_t launch_pass4(const BwdParams &p, const SegTable &t, hipStream_t s) {
-  using Tr = Bwd4Traits<D, KEYS_RES>;
+  using Tr = Bwd4Traits<D, KEYS_RES, F8>;
   const int64_t NR = KEYS_RES ? p.NK : p.NQ;
   if (t.n == 0 && NR == 0) return hipSuccess;
-  const void *fn = reinterpret_cast<const void *>(&bwd4_kernel<D, KEYS_RES, MODE>);
+  const void *fn = reinterpret_cast<const void *>(&bwd4_kernel<D, KEYS_RES, MODE, F8>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
   const int64_t nblk =
       t.n > 0 ? (int64_t)t.end : p.BH * ((NR + Tr::BR - 1) / Tr::BR) * (KEYS_RES ? 1 : p.splits);
-  hipLaunchKernelGGL((bwd4_kernel<D, KEYS_RES, MODE>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s, p,
-                     t);
+  hipLaunchKernelGGL((bwd4_kernel<D, KEYS_RES, MODE, F8>), dim3((uint32_t)nblk), dim3(Tr::NT), Tr::LDS_BYTES, s,
+                     p, t);
   return hipGetLastError();
 }
 
-// Both distributions, the teacher's only or the student's only.
-template <int D, bool KEYS_RES>
+// Both distributions, the teacher's only or the student's only (bf16 or
+// fp8 inputs).
+template <int D, bool KEYS_RES, bool F8 = false>
 static hipError_t launch_bf16_pass(const BwdParams &p, const SegTable &t, hipStream_t s) {
-  if (p.want1 && p.want2) return launch_pass4<D, KEYS_RES, 0>(p, t, s);
-  if (p.want1) return launch_pass4<D, KEYS_RES, 1>(p, t, s);
-  if (p.want2) return launch_pass4<D, KEYS_RES, 2>(p, t, s);
+  if (p.want1 && p.want2) return launch_pass4<D, KEYS_RES, 0, F8>(p, t, s);
+  if (p.want1) return launch_pass4<D, KEYS_RES, 1, F8>(p, t, s);
+  if (p.want2) return launch_pass4<D, KEYS_RES, 2, F8>(p, t, s);
   return hipSuccess;
 }
 
 hipError_t launch_bwd_dk_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s) {
   if (dtype == 0) return D == 128 ? launch_bf16_pass<128, true>(p, t, s) : launch_bf16_pass<64, true>(p, t, s);
+  if (dtype == 2)
+    return D == 128 ? launch_bf16_pass<128, true, true>(p, t, s) : launch_bf16_pass<64, true, true>(p, t, s);
   return D == 128 ? launch_fp32_pass<128, true>(p, t, s) : launch_fp32_pass<64, true>(p, t, s);
 }
 
 hipError_t launch_bwd_dq_segs(int dtype, int D, const BwdParams &p, const SegTable &t, hipStream_t s) {
   if (dtype == 0) return D == 128 ? launch_bf16_pass<128, false>(p, t, s) : launch_bf16_pass<64, false>(p, t, s);
+  if (dtype == 2)
+    return D == 128 ? launch_bf16_pass<128, false, true>(p, t, s) : launch_bf16_pass<64, false, true>(p, t, s);
   return D == 128 ? launch_fp32_pass<128, false>(p, t, s) : launch_fp32_pass<64, false>(p, t, s);
 }
 

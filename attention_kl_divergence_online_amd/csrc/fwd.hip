@@ -28,6 +28,7 @@
 //  * scores stay in raw dot-product units x = q.k; exponentials are
 //    exp2((x - m) * scale * log2 e).
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"

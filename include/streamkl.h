@@ -25,8 +25,8 @@
  *    streamkl_fwd_splitk_noalloc: a device scratch array per GPU and the
  *    table of their addresses, filled once per device under a lock.
  *  - Q1, Q2 are [B, H, NQ, D] and K1, K2 are [B, H, NK, D], contiguous,
- *    row-major, element type `dtype` (bf16, fp32, or fp8 e4m3 for the
- *    forward entry points).  Per-row vectors (KL,
+ *    row-major, element type `dtype` (bf16, fp32 or fp8 e4m3).  Per-row
+ *    vectors (KL,
  *    LSE1, LSE2, g) are fp32 [B, H, NQ].  Gradients are fp32 and have the
  *    shape of the tensor they belong to.
  *  - Every pointer must be 16-byte aligned.  D must be 64 or 128.
@@ -56,8 +56,7 @@ typedef enum {
                                    ceil(N / 64) * 64 rows of D reaching 2^31 bytes,
                                    B * H reaching 2^31, a kernel grid past the GPU's
                                    2^32 - 1 work-items, split count out of range */
-    STREAMKL_ERR_DTYPE = 3,     /* dtype is not a streamkl_dtype, or STREAMKL_FP8_E4M3
-                                   passed to a backward entry point */
+    STREAMKL_ERR_DTYPE = 3,     /* dtype is not a streamkl_dtype */
     STREAMKL_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
     STREAMKL_ERR_WORKSPACE = 5, /* workspace missing or smaller than the size query */
     STREAMKL_ERR_HIP = 6        /* the HIP runtime rejected a launch */
@@ -66,16 +65,17 @@ typedef enum {
 /*
  * STREAMKL_FP8_E4M3: the OCP 8-bit float with 4 exponent bits (bias 7), 3
  * significand bits, no infinities and NaN as S.1111.111 (torch.float8_e4m3fn).
- * The forward entry points (streamkl_fwd, streamkl_fwd_splitk,
- * streamkl_fwd_splitk_noalloc, streamkl_fwd_varlen) take it: both logits
- * products run on the fp8 matrix instructions (products exact, fp32
- * accumulation) and everything after them in fp32, as for bf16.  This is the
- * mixed-precision direction the pages leave as future work (arxivlens.com
- * paper view of StreamKL, future-work list).  The backward entry points and
- * their workspace queries refuse it (STREAMKL_ERR_DTYPE, size 0): its
- * gradient products need 16-bit operands.  Rounding bf16 tensors to e4m3
- * changes the distributions themselves far more than the 2e-3 the bf16 path
- * holds to; the type is for inputs that are fp8 already.
+ * Every entry point takes it.  The logits products, in the forward and in
+ * both backward passes, run on the fp8 matrix instructions (exact products,
+ * fp32 accumulation); the backward's gradient products take the inputs as
+ * fp16 operands, which hold every e4m3 value exactly (no operand scale, so
+ * the prepare step only forms sigma), against the same sigma-scaled fp16 dS
+ * as for bf16.  This is the mixed-precision direction the pages leave as
+ * future work (arxivlens.com paper view of StreamKL, future-work list).
+ * Rounding bf16 tensors to e4m3 changes the distributions themselves far more
+ * than the 2e-3 the kernels hold to; the type is for inputs that are fp8
+ * already.  There is no fused single-visit backward for fp8 (the passes run
+ * at every N_Q).
  */
 typedef enum { STREAMKL_BF16 = 0, STREAMKL_FP32 = 1, STREAMKL_FP8_E4M3 = 2 } streamkl_dtype;
 
@@ -157,8 +157,8 @@ streamkl_status streamkl_fwd_splitk_noalloc(const streamkl_problem *p,
  * the fp32 factor sigma by which dS is scaled before rounding, four fp32
  * powers of two by which the fp16 gradient-product operands of q1, q2, k1
  * and k2 are scaled, and (bf16 inputs) 64 fp32 partial maxima from which
- * those come: O(B * H), a few KiB at 32 heads.  With bf16 inputs and fewer
- * than 256 query tiles of 128 rows in all (B * H * ceil(NQ / 128) < 256), the
+ * those come: O(B * H), a few KiB at 32 heads.  With bf16 or fp8 inputs and
+ * fewer than 256 query tiles of 128 rows in all (B * H * ceil(NQ / 128) < 256), the
  * query-gradient pass splits the keys into S chunks, S = min(ceil(256 /
  * tiles), 64, ceil(NK / 64)) (then as many chunks as whole 64-key tiles fill),
  * and the workspace also holds S partial dQ1, dQ2 in fp32 (S * 2 * B * H * NQ
@@ -201,12 +201,13 @@ size_t streamkl_bwd_workspace_size_min(const streamkl_problem *p);
  * the same inputs.  Gradient outputs come in pairs: pass dq1 = dk1 = NULL to
  * skip the teacher gradients (teacher fixed) or dq2 = dk2 = NULL to skip the
  * student's; a half-NULL pair is STREAMKL_ERR_NULL.  Outputs are overwritten.
- * With bf16 inputs the two gradient products run on fp16 matrix cores with
- * fp32 accumulation (dS in bf16 would exceed a 2e-3 relative error).  The
- * streamed Q or K operand is scaled per (batch, head, tensor) by a power of
- * two that puts its largest entry in [2^14, 2^15), so any finite bf16 input
- * fits fp16 (entries below 2^-29 of the tensor's largest lose precision, a
- * contribution below 2^-29 of the largest).  The fp16 dS operands are scaled
+ * With bf16 (or fp8) inputs the two gradient products run on fp16 matrix
+ * cores with fp32 accumulation (dS in bf16 would exceed a 2e-3 relative
+ * error).  With bf16 inputs the streamed Q or K operand is scaled per
+ * (batch, head, tensor) by a power of two that puts its largest entry in
+ * [2^14, 2^15), so any finite bf16 input fits fp16 (entries below 2^-29 of
+ * the tensor's largest lose precision, a contribution below 2^-29 of the
+ * largest).  The fp16 dS operands are scaled
  * so that the largest |g| maps to [2^7, 2^8), so P1 * |log(P1/P2) - KL| must
  * stay below about 255 at every pair; it exceeds that only where the teacher
  * gives a key real mass and the student a log-probability hundreds of nats
@@ -232,7 +233,7 @@ streamkl_status streamkl_bwd(const streamkl_problem *p,
  * of two sigma with max_i |g_i| * sigma in [2^7, 2^8), by which the passes
  * scale dS before rounding it to fp16 (1 for fp32 inputs), negated when some
  * g of that head is negative; and the powers of two that scale the fp16
- * operands of q1, q2, k1, k2 (1 for fp32 inputs), from their largest
+ * operands of q1, q2, k1, k2 (1 for fp32 and fp8 inputs), from their largest
  * magnitudes.  It reads q1, k1, q2, k2 (bf16 inputs only) and g, with the
  * layouts and alignment rules of streamkl_bwd, and needs at least
  * streamkl_bwd_workspace_size_min bytes; the passes take the workspace size

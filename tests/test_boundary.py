@@ -87,24 +87,25 @@ def test_forward_validation(L):
     assert fwd(L, P(), l2=MIS) == _lib.STREAMKL_ERR_ALIGN
 
 
-def test_fp8_is_forward_only(L):
-    # fp8 e4m3 inputs pass the forward's checks (the call then stops at the
-    # first null pointer, before any launch); every backward entry point and
-    # workspace query refuses them.
+def test_fp8_dtype_is_accepted(L):
+    # fp8 e4m3 inputs pass every entry point's checks (the calls then stop at
+    # the first null pointer, before any launch), and the workspace queries
+    # size them like bf16 problems without the bf16 chunk maxima.
     f8 = _lib.STREAMKL_FP8_E4M3
     assert fwd(L, P(dtype=f8), q1=None) == _lib.STREAMKL_ERR_NULL
     assert fwd(L, P(dtype=f8, D=128), q2=MIS) == _lib.STREAMKL_ERR_ALIGN
     assert fwd(L, P(dtype=f8, B=0), q1=None, kl=None) == _lib.STREAMKL_OK
     p = P(dtype=f8)
     assert L.streamkl_fwd_splitk_workspace_size(ctypes.byref(p), 1) > 0
-    assert L.streamkl_bwd_workspace_size(ctypes.byref(p)) == 0
-    assert L.streamkl_bwd_workspace_size_min(ctypes.byref(p)) == 0
-    assert L.streamkl_bwd(ctypes.byref(p), A, A, A, A, A, A, A, A, A, A, A, A, A, 1 << 20,
-                          None) == _lib.STREAMKL_ERR_DTYPE
-    assert L.streamkl_bwd_prepare(ctypes.byref(p), A, A, A, A, A, A, 1 << 20, None) == _lib.STREAMKL_ERR_DTYPE
+    ws8 = L.streamkl_bwd_workspace_size(ctypes.byref(p))
+    assert 0 < ws8 < L.streamkl_bwd_workspace_size(ctypes.byref(P()))
+    assert L.streamkl_bwd_workspace_size_min(ctypes.byref(p)) == ws8
+    assert L.streamkl_bwd(ctypes.byref(p), None, A, A, A, A, A, A, A, A, A, A, A, A, 1 << 20,
+                          None) == _lib.STREAMKL_ERR_NULL
+    assert L.streamkl_bwd_prepare(ctypes.byref(p), A, A, A, A, None, A, 1 << 20, None) == _lib.STREAMKL_ERR_NULL
     for name in ("streamkl_bwd_dk", "streamkl_bwd_dq"):
         fn = getattr(L, name)
-        assert fn(ctypes.byref(p), A, A, A, A, A, A, A, A, A, A, A, 1 << 20, None) == _lib.STREAMKL_ERR_DTYPE, name
+        assert fn(ctypes.byref(p), A, A, A, A, None, A, A, A, A, A, A, 1 << 20, None) == _lib.STREAMKL_ERR_NULL, name
 
 
 def test_grid_limit_is_rejected_on_the_host(L):
@@ -310,7 +311,7 @@ def test_varlen_validation(L):
     assert vfwd(L, VP([0, 5], [0, 5], D=96)) == _lib.STREAMKL_ERR_SHAPE
     assert vfwd(L, VP([0, 5], [0, 5], dtype=9)) == _lib.STREAMKL_ERR_DTYPE
     assert vfwd(L, VP([0, 5], [0, 5], dtype=_lib.STREAMKL_FP8_E4M3), q1=None) == _lib.STREAMKL_ERR_NULL
-    assert vbwd(L, VP([0, 5], [0, 5], dtype=_lib.STREAMKL_FP8_E4M3)) == _lib.STREAMKL_ERR_DTYPE
+    assert vbwd(L, VP([0, 5], [0, 5], dtype=_lib.STREAMKL_FP8_E4M3), g=None) == _lib.STREAMKL_ERR_NULL
     assert vfwd(L, VP([0, 5], [0, 5]), q1=None) == _lib.STREAMKL_ERR_NULL
     assert vfwd(L, VP([0, 5], [0, 5]), q1=MIS) == _lib.STREAMKL_ERR_ALIGN
     assert vfwd(L, VP([0, 5], [0, 5]), kl=MIS) == _lib.STREAMKL_ERR_ALIGN

@@ -1,21 +1,24 @@
-"""GPU parity of the fp8 (e4m3) forward against the fp64 oracle.
+"""GPU parity of the fp8 (e4m3) forward and backward against the fp64 oracle.
 
-The inputs are fp8 values (seeded normals rounded to e4m3 on the host), and
-the oracle is given exactly those values in fp64, so the only differences
-are the kernels' fp32 accumulation and exponentials: the bf16 path's 2e-3
-bound applies.  Shapes cover the four-wave and twelve-wave fp8 forward shapes,
-both head dimensions, ragged tails in N_Q and N_K, the causal diagonal,
-split-K chunks and a packed variable-length batch.  The backward refuses fp8
-inputs with a status code.
+The inputs are fp8 values (seeded normals rounded to e4m3), and the oracle is
+given exactly those values in fp64, so the only differences are the kernels'
+fp32 accumulation, exponentials and the backward's fp16 dS: the bf16 path's
+2e-3 bound applies.  Shapes cover the four-wave and twelve-wave fp8 forward
+shapes, both backward passes (with the query pass split over key chunks for
+few query tiles), both head dimensions, ragged tails in N_Q and N_K, the
+causal diagonal, single-distribution passes, split-K chunks, a packed
+variable-length batch and the causal 64K workload's full size.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
 
 import synth
-from attention_kl_divergence_online_amd import (StreamKLError, bwd_workspace_size, streamkl_bwd, streamkl_fwd,
-                                                streamkl_fwd_splitk, streamkl_fwd_varlen)
-from parity_util import TOL, assert_within, compare_forward, sample_rows
+from attention_kl_divergence_online_amd import (streamkl_bwd, streamkl_bwd_varlen, streamkl_fwd, streamkl_fwd_splitk,
+                                                streamkl_fwd_varlen)
+from parity_util import TOL, assert_within, compare_backward, compare_forward, sample_rows
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not hasattr(torch, "float8_e4m3fn"), reason="torch without float8 types")]
@@ -47,17 +50,46 @@ CASES = [
 ]
 
 
+def _grad(B, H, NQ, seed):
+    # Upstream gradients of mixed sign (the key pass's signed-dS variant).
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (torch.randn(B, H, NQ, generator=g) / (B * H * NQ)).to(DEV)
+
+
 @pytest.mark.parametrize("B,H,NQ,NK,D,causal", CASES)
-def test_fp8_forward_all_rows(B, H, NQ, NK, D, causal):
-    print(f"fp8 forward B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal}", flush=True)
+def test_fp8_forward_backward_all_rows(B, H, NQ, NK, D, causal):
+    print(f"fp8 B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal}", flush=True)
     q1, k1, q2, k2 = _rand_fp8((B, H, NQ, D), (B, H, NK, D), seed=NQ * 5 + NK + D + causal)
     scale = D ** -0.5
     kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
     torch.cuda.synchronize()
     heads = [(b, h) for b in range(B) for h in range(H)]
     assert torch.isfinite(kl).all() and torch.isfinite(l1).all() and torch.isfinite(l2).all()
-    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"],
-                  f"fp8 fwd NQ={NQ} NK={NK} D={D} causal={causal}")
+    what = f"NQ={NQ} NK={NK} D={D} causal={causal}"
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"], f"fp8 fwd {what}")
+    g = _grad(B, H, NQ, seed=NQ + NK)
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal)
+    torch.cuda.synchronize()
+    for t in grads:
+        assert torch.isfinite(t).all()
+    assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, grads, heads), TOL["bf16"], f"fp8 bwd {what}")
+
+
+@pytest.mark.parametrize("teacher,student", [(True, False), (False, True)])
+def test_fp8_single_distribution_passes(teacher, student):
+    B, H, NQ, NK, D, causal = 1, 2, 300, 517, 128, True
+    print(f"fp8 teacher={teacher} student={student}", flush=True)
+    q1, k1, q2, k2 = _rand_fp8((B, H, NQ, D), (B, H, NK, D), seed=99)
+    scale = D ** -0.5
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    g = _grad(B, H, NQ, seed=5)
+    both = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal)
+    one = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, teacher=teacher, student=student)
+    torch.cuda.synchronize()
+    # The single-distribution passes accumulate in the same order as the full one.
+    for a, b in zip(both, one):
+        if b is not None:
+            assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -81,20 +113,29 @@ def test_fp8_varlen_matches_per_sequence_oracle():
     cu_q, cu_k = [0] + np.cumsum(lens_q).tolist(), [0] + np.cumsum(lens_k).tolist()
     scale = D ** -0.5
     kl, l1, l2 = streamkl_fwd_varlen(q1, k1, q2, k2, cu_q, cu_k, scale, causal)
+    g = _grad(1, H, TQ, seed=11)[0]
+    grads = streamkl_bwd_varlen(q1, k1, q2, k2, cu_q, cu_k, kl, l1, l2, g, scale, causal)
     torch.cuda.synchronize()
+    heads = [(0, h) for h in range(H)]
     for b in range(len(lens_q)):
-        if lens_q[b] == 0:
-            continue
         sq, sk = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        if lens_q[b] == 0:
+            for dk in (grads[1], grads[3]):
+                assert not dk[:, sk].any()  # no queries: zero key gradients
+            continue
         seq = [t[:, s].unsqueeze(0) for t, s in ((q1, sq), (k1, sk), (q2, sq), (k2, sk))]
         outs = [t[:, sq].unsqueeze(0) for t in (kl, l1, l2)]
-        heads = [(0, h) for h in range(H)]
         assert_within(compare_forward(*seq, scale, causal, *outs, heads), TOL["bf16"], f"fp8 varlen seq {b}")
+        sg = [t[:, s].unsqueeze(0) for t, s in zip(grads, (sq, sk, sq, sk))]
+        assert_within(compare_backward(*seq, scale, causal, g[:, sq].unsqueeze(0), sg, heads), TOL["bf16"],
+                      f"fp8 varlen bwd seq {b}")
 
 
 def test_fp8_causal_64k_sampled_rows():
     # The causal 64K workload's shape (32 heads) with its inputs rounded to
-    # e4m3, in the launch the bench times: sampled rows of two heads.
+    # e4m3, in the launches the bench times: sampled rows of two heads for the
+    # forward and dQ, the whole dK with g nonzero only on those rows (dK is
+    # linear in g), and the any-size invariant sum_j dK[j] = 0.
     w = synth.get("causal_64k")
     print("fp8 causal 64K", flush=True)
     q1, k1, q2, k2 = (synth.to_fp8(t) for t in synth.make_inputs(w, DEV))
@@ -104,12 +145,18 @@ def test_fp8_causal_64k_sampled_rows():
     heads = [(0, 0), (0, w.H - 1)]
     assert_within(compare_forward(q1, k1, q2, k2, w.scale, w.causal, kl, l1, l2, heads, rows=rows), TOL["bf16"],
                   "fp8 causal_64k fwd (sampled rows)")
-
-
-def test_fp8_backward_is_refused():
-    q1, k1, q2, k2 = _rand_fp8((1, 1, 64, 128), (1, 1, 64, 128), seed=3)
-    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, None, True)
-    g = torch.ones_like(kl)
-    assert bwd_workspace_size(q1, k1, None, True) == 0
-    with pytest.raises(StreamKLError):
-        streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, None, True)
+    g = synth.upstream_grad(w, DEV)
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, w.scale, w.causal)
+    torch.cuda.synchronize()
+    assert_within(compare_backward(q1, k1, q2, k2, w.scale, w.causal, g, grads, heads, rows, check_dk=False),
+                  TOL["bf16"], "fp8 causal_64k dq")
+    for dk in (grads[1], grads[3]):
+        colsum = dk.double().sum(2).abs().max().item()
+        assert colsum <= 1e-3 * dk.abs().max().item() * math.sqrt(w.NK), colsum
+    del grads
+    gs = torch.zeros_like(g)
+    gs[:, :, rows] = g[:, :, rows]
+    grads = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, gs, w.scale, w.causal)
+    torch.cuda.synchronize()
+    assert_within(compare_backward(q1, k1, q2, k2, w.scale, w.causal, gs, grads, heads, rows, check_dk=True),
+                  TOL["bf16"], "fp8 causal_64k dk (sampled g)")
