@@ -10,8 +10,8 @@ Also reported: per-kernel HIP-event timings, the roofline of the dominant
 kernel (algorithmic flop per launch over its average duration), the other
 four workloads of the metric ("configs": tiny fp32, causal 4K, non-causal
 16K, the split-K forward over 512K keys and the backward over 128K keys),
-and the fp64 CPU oracle timed on a bounded sample of the same workload on
-this host's cores.
+the same step with the inputs rounded to fp8 e4m3 ("fp8"), and the fp64 CPU
+oracle timed on a bounded sample of the same workload on this host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -32,12 +32,14 @@ METRIC = "attn-KL fwd and fwd+bwd TFLOP/s + ms at 64K ctx, 32 heads, d=128 bf16"
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_kl_causal_64k_hbm_traffic.json")
 COPY_BYTES = 1 << 30
 KERNELS = {  # bench key -> kernel names as rocprofv3 reports them (mangled or demangled)
-    "fwd": ("_ZN3skl11fwd2_kernelILi128ELb0ELi8ELi128EEEvNS_9FwdParamsE",
-            "void skl::fwd2_kernel<128, false, 8, 128>"),
-    "bwd_dk": ("_ZN3skl11bwd4_kernelILi128ELb1ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, true, 0>"),
-    "bwd_dq": ("_ZN3skl11bwd4_kernelILi128ELb0ELi0EEEvNS_9BwdParamsE", "void skl::bwd4_kernel<128, false, 0>"),
-    "fwd_split": ("_ZN3skl11fwd2_kernelILi128ELb1ELi8ELi128EEEvNS_9FwdParamsE",
-                  "void skl::fwd2_kernel<128, true, 8, 128>"),
+    "fwd": ("_ZN3skl11fwd2_kernelILi128ELb0ELi8ELi128ELb0EEEvNS_9FwdParamsE",
+            "void skl::fwd2_kernel<128, false, 8, 128, false>"),
+    "bwd_dk": ("_ZN3skl11bwd4_kernelILi128ELb1ELi0ELb0EEEvNS_9BwdParamsE",
+               "void skl::bwd4_kernel<128, true, 0, false>"),
+    "bwd_dq": ("_ZN3skl11bwd4_kernelILi128ELb0ELi0ELb0EEEvNS_9BwdParamsE",
+               "void skl::bwd4_kernel<128, false, 0, false>"),
+    "fwd_split": ("_ZN3skl11fwd2_kernelILi128ELb1ELi8ELi128ELb0EEEvNS_9FwdParamsE",
+                  "void skl::fwd2_kernel<128, true, 8, 128, false>"),
 }
 
 
@@ -171,12 +173,18 @@ def summarize_counters(csvs, out_path: str) -> None:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak (published)
 PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 matrix peak (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
 # The five workloads the metric is quoted on, by role: C1 tiny fp32 (parity
 # size), C2 short causal, C3 long non-causal with large KL, C4 the 64K causal
 # headline (the main line above), C5 the split-K forward over 512K keys and
 # the short-query backward over 128K keys.
 CONFIGS = (("C1", "tiny_fp32"), ("C2", "causal_4k"), ("C3", "noncausal_16k"), ("C5_bwd", "splitk_bwd_128k"))
 PEAK_HBM_GBS = 8000.0
+
+
+def progress(msg: str) -> None:
+    """One line per finished section on stderr (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def parse():
@@ -371,8 +379,9 @@ def main():
     dom = max(kern_flop, key=lambda k: per[k])
     achieved = kern_flop[dom] / (per[dom] * 1e-3) / 1e12
     executed = exec_flop[dom] / (per[dom] * 1e-3) / 1e12
-    kernel_names = {"fwd": "fwd2_kernel<128,unsplit>", "bwd_dk": "bwd4_kernel<128,keys resident,both>",
-                    "bwd_dq": "bwd4_kernel<128,queries resident,both>"}
+    kernel_names = {"fwd": "fwd2_kernel<128,unsplit,8 waves,128-key tiles,bf16>",
+                    "bwd_dk": "bwd4_kernel<128,keys resident,both,bf16>",
+                    "bwd_dq": "bwd4_kernel<128,queries resident,both,bf16>"}
 
     out = {
         "metric": METRIC,
@@ -418,10 +427,12 @@ def main():
 
     # Sustained matrix rate under a full load (register operands only), set
     # beside the published peak the roofline fraction is taken against.
+    progress(f"timed steps done: {ms_step:.3f} ms per step")
     out["roofline"]["measured_peak"] = round(mfma_probe(skl, torch), 1)
 
     if not args.no_splitk:
         out["splitk"] = splitk_bench(skl, synth, torch, args)
+        progress("split-K forward done")
 
     if not args.no_configs:
         # Every workload of the metric in one line: algorithmic TFLOP/s and the
@@ -433,6 +444,7 @@ def main():
                        "step_frac": round(out["value"] / PEAK_BF16_TFLOPS, 4)}}
         for tag, name in CONFIGS:
             cfgs[tag] = config_bench(skl, synth, torch, args, name)
+            progress(f"{tag} ({name}) done")
         if "splitk" in out:
             sk = dict(out["splitk"])
             sk["fwd_frac"] = round(sk["tflops"] / PEAK_BF16_TFLOPS, 4)
@@ -440,8 +452,12 @@ def main():
         out["configs"] = {k: cfgs[k] for k in ("C1", "C2", "C3", "C4", "C5_fwd", "C5_bwd") if k in cfgs}
 
     if not args.no_configs:
+        # The same workload with e4m3 inputs (the fp8 path), beside the bf16 line.
+        out["fp8"] = config_bench(skl, synth, torch, args, w.name, fp8=True)
+        progress("fp8 step done")
         out["fused_vs_split"] = {n: fused_vs_split(skl, synth, torch, args, n)
                                  for n in ("shortq16_bwd_64k", "decode_128k", "shortq128_bwd_64k", "shortq_bwd_64k")}
+        progress("fused vs split done")
 
     if args.other_configs:
         out["other_configs"] = {n: config_bench(skl, synth, torch, args, n)
@@ -457,6 +473,7 @@ def main():
         out["materialised_baseline"] = mat
 
     if not args.no_cpu_baseline:
+        progress("materialised baseline done")
         out["cpu_baseline"] = cpu_baseline(w, q1, k1, q2, k2, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
@@ -549,11 +566,14 @@ def mfma_probe(skl, torch, iters: int = 100000, workgroups: int = 1024) -> float
     return workgroups * 4 * iters * 4 * 32768 / (best * 1e-3) / 1e12
 
 
-def config_bench(skl, synth, torch, args, name):
+def config_bench(skl, synth, torch, args, name, fp8=False):
     """Forward (split-K when the workload sets a split count) and full backward
-    (prepare + both passes) of one workload; HIP-event ms per step."""
+    (prepare + both passes) of one workload; HIP-event ms per step.  With
+    `fp8` the workload's inputs are rounded to e4m3 first (the fp8 path)."""
     w = synth.get(name)
     q1, k1, q2, k2 = synth.make_inputs(w, device="cuda")
+    if fp8:
+        q1, k1, q2, k2 = (synth.to_fp8(t) for t in (q1, k1, q2, k2))
     g = synth.upstream_grad(w, "cuda")
     kl, l1, l2 = (torch.empty((w.B, w.H, w.NQ), dtype=torch.float32, device="cuda") for _ in range(3))
     grads = tuple(torch.empty_like(t, dtype=torch.float32) for t in (q1, k1, q2, k2))
@@ -586,6 +606,13 @@ def config_bench(skl, synth, torch, args, name):
            "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2), "step_tflops": round(step_t, 2),
            "peak_tflops": peak, "fwd_frac": round(fwd_t / peak, 4), "bwd_frac": round(bwd_t / peak, 4),
            "step_frac": round(step_t / peak, 4)}
+    if fp8:
+        # The forward's products and the backward's logits run at the fp8
+        # matrix rate, the backward's gradient products (8*D of its 12*D per
+        # pair) at the fp16 one; fractions stay against the bf16/fp16 peak,
+        # with the forward's also against the fp8 peak.
+        res["inputs"] = "fp8_e4m3"
+        res["fwd_frac_fp8_peak"] = round(fwd_t / PEAK_FP8_TFLOPS, 4)
     del q1, k1, q2, k2, grads, ws, wsk
     torch.cuda.empty_cache()
     return res
