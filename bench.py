@@ -193,6 +193,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="causal_64k")
+    ap.add_argument("--fp8", action="store_true",
+                    help="round the workload's inputs to e4m3 and time the fp8 path (the line then reports "
+                         "inputs fp8_e4m3; fractions stay against the bf16/fp16 matrix peak)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-splitk", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
@@ -289,6 +292,12 @@ def main():
 
     w = synth.get(args.workload)
     dev = "cuda"
+    if args.fp8:
+        # The fp8 line stands alone: the other workloads and the bf16
+        # materialise-then-reduce comparison belong to the bf16 line.
+        args.no_configs = True
+        args.no_splitk = True
+        args.materialised_heads = 0
     torch.cuda.init()
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -298,6 +307,8 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     q1, k1, q2, k2 = synth.make_inputs(w, device=dev)
+    if args.fp8:
+        q1, k1, q2, k2 = (synth.to_fp8(t) for t in (q1, k1, q2, k2))
     g = synth.upstream_grad(w, dev)
     kl, l1, l2 = (torch.empty((w.B, w.H, w.NQ), dtype=torch.float32, device=dev) for _ in range(3))
     grads = (torch.empty_like(q1, dtype=torch.float32), torch.empty_like(k1, dtype=torch.float32),
@@ -382,6 +393,10 @@ def main():
     kernel_names = {"fwd": "fwd2_kernel<128,unsplit,8 waves,128-key tiles,bf16>",
                     "bwd_dk": "bwd4_kernel<128,keys resident,both,bf16>",
                     "bwd_dq": "bwd4_kernel<128,queries resident,both,bf16>"}
+    if args.fp8:
+        kernel_names = {"fwd": "fwd2_kernel<128,unsplit,12 waves,128-key tiles,fp8>",
+                        "bwd_dk": "bwd4_kernel<128,keys resident,both,fp8>",
+                        "bwd_dq": "bwd4_kernel<128,queries resident,both,fp8>"}
 
     out = {
         "metric": METRIC,
@@ -394,10 +409,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "NQ": w.NQ, "NK": w.NK, "D": w.D,
-                   "causal": w.causal, "inputs": "bf16", "accumulate": "fp32"},
+                   "causal": w.causal, "inputs": "fp8_e4m3" if args.fp8 else "bf16", "accumulate": "fp32"},
         "fwd_ms": round(fwd_ms, 3),
         "fwd_tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_ms": round(bwd_ms, 3),
@@ -414,7 +429,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": recorded_traffic(dom),
+            "traffic": None if args.fp8 else recorded_traffic(dom),
             "flop_per_launch": kern_flop[dom],
             "flop_rule": "algorithmic: 4*D per visible pair (forward), 6*D per pair per backward pass "
                          "(12*D for the whole backward)",
@@ -468,13 +483,14 @@ def main():
 
     if args.materialised_heads > 0:
         mat = materialised_baseline(torch, w, q1, k1, q2, k2, g, kl, args.materialised_heads)
+        progress("materialised baseline done")
         mat["fwd_speedup_fused"] = round(mat["fwd_ms"] / fwd_ms, 1)
         mat["fwd_bwd_speedup_fused"] = round(mat["fwd_bwd_ms"] / ms_step, 1)
         out["materialised_baseline"] = mat
 
     if not args.no_cpu_baseline:
-        progress("materialised baseline done")
         out["cpu_baseline"] = cpu_baseline(w, q1, k1, q2, k2, args.cpu_seconds)
+        progress("cpu baseline done")
 
     print(json.dumps(out), flush=True)
 
