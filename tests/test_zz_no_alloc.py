@@ -5,13 +5,15 @@ the partial row states in the library's own per-GPU device array, so its
 results must equal the workspace entry point's bit for bit; both are also held
 to the oracle.  Two calls in a row, the second on a smaller problem, check
 that a call does not depend on what the previous one left in the array; the
-second call must not raise the device's memory use.
+second call must not raise the device's memory use.  A third, smaller call
+takes e4m3 inputs (the fp8 path through the same scratch).
 """
 import math
 
 import pytest
 import torch
 
+import synth
 from attention_kl_divergence_online_amd import StreamKLError, streamkl_fwd_splitk, streamkl_fwd_splitk_noalloc
 from attention_kl_divergence_online_amd import _lib
 from parity_util import TOL, assert_within, compare_forward
@@ -21,29 +23,32 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _rand(B, H, NQ, NK, D, seed, noise=0.2):
+def _rand(B, H, NQ, NK, D, seed, dtype, noise=0.2):
     g = torch.Generator(device="cpu").manual_seed(seed)
     q1 = torch.randn(B, H, NQ, D, generator=g)
     k1 = torch.randn(B, H, NK, D, generator=g)
     q2 = q1 + noise * torch.randn(B, H, NQ, D, generator=g)
     k2 = k1 + noise * torch.randn(B, H, NK, D, generator=g)
-    return [t.to(torch.bfloat16).to(DEV).contiguous() for t in (q1, k1, q2, k2)]
+    cast = synth.to_fp8 if dtype == "fp8" else (lambda t: t.to(torch.bfloat16))
+    return [cast(t).to(DEV).contiguous() for t in (q1, k1, q2, k2)]
 
 
 # Larger first, then smaller: the second call finds the first call's states in
 # the scratch beyond its own range and must neither read nor need them.
 CASES = [
-    # B, H, NQ, NK, D, causal, splits
-    (2, 4, 300, 5000, 128, True, 16),
-    (1, 2, 40, 900, 64, False, 5),
+    # B, H, NQ, NK, D, causal, splits, inputs
+    (2, 4, 300, 5000, 128, True, 16, "bf16"),
+    (1, 2, 40, 900, 64, False, 5, "bf16"),
 ]
+if hasattr(torch, "float8_e4m3fn"):
+    CASES.append((1, 1, 33, 700, 128, True, 3, "fp8"))
 
 
 def test_noalloc_splitk_equals_workspace_entry_point():
-    for i, (B, H, NQ, NK, D, causal, splits) in enumerate(CASES):
-        print(f"noalloc split-K call {i}: B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal} splits={splits}",
+    for i, (B, H, NQ, NK, D, causal, splits, dt) in enumerate(CASES):
+        print(f"noalloc split-K call {i}: B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal} splits={splits} {dt}",
               flush=True)
-        q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, seed=31 + i)
+        q1, k1, q2, k2 = _rand(B, H, NQ, NK, D, seed=31 + i, dtype=dt)
         scale = 1.0 / math.sqrt(D)
         ref = streamkl_fwd_splitk(q1, k1, q2, k2, splits, scale, causal)
         got = tuple(torch.full((B, H, NQ), float("nan"), device=DEV) for _ in range(3))
