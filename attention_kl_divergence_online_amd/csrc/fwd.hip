@@ -447,10 +447,11 @@ struct Fwd2Traits {
 constexpr float kLazySumMax = 16777216.f;
 
 // Queries per head at or below which bf16 inputs take the one-wave shapes:
-// 16x16 products up to 16 queries, 32x32 products up to 32.
+// 16x16 products up to 16 queries, 32x32 products up to 32; fp8 inputs take
+// the one-wave 32x32 shape up to 32 queries.
 constexpr int kDecodeRows = 32;
 constexpr int kDecode16Rows = 16;
-inline bool fwd_decode_shape(int dtype, int64_t NQ) { return dtype == 0 && NQ <= kDecodeRows; }
+inline bool fwd_decode_shape(int dtype, int64_t NQ) { return (dtype == 0 || dtype == 2) && NQ <= kDecodeRows; }
 // Input types the matrix-core forward takes: bf16 (0) and fp8 e4m3 (2).
 inline bool fwd_mfma_dtype(int dtype) { return dtype == 0 || dtype == 2; }
 // Waves of the main fp8 shape.  Half-size query fragments leave the fp8
@@ -967,7 +968,7 @@ template <int D, bool SPLIT, bool F8 = false>
 static hipError_t launch_fwd2(const FwdParams &p, hipStream_t s) {
   static_assert(kFwdChunkTile % 128 == 0, "split chunks must hold whole 128-key tiles");
   if (!F8 && fwd_decode16_shape(0, p.NQ)) return launch_fwd16<D, SPLIT>(p, s);
-  if (!F8 && fwd_decode_shape(0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32>(p, kNoSegs, s);
+  if (fwd_decode_shape(F8 ? 2 : 0, p.NQ)) return launch_fwd2_shape<D, SPLIT, 1, 32, F8>(p, kNoSegs, s);
   if (!SPLIT && p.small) return launch_fwd2_shape<D, false, 4, 64, F8>(p, kNoSegs, s);
   return launch_fwd2_shape<D, SPLIT, F8 ? kF8Waves : 8, D == 128 ? 128 : 64, F8>(p, kNoSegs, s);
 }

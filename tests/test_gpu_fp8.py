@@ -44,7 +44,9 @@ CASES = [
     (1, 2, 257, 333, 64, True),
     (1, 1, 1, 37, 128, False),
     (1, 1, 5, 5, 128, True),
-    (2, 1, 16, 77, 64, True),        # few queries: fp8 has no decode shapes, these run the general ones
+    (2, 1, 16, 77, 64, True),        # at most 32 queries: the one-wave decode shape (32-key tiles)
+    (2, 2, 32, 1500, 128, True),     # the decode shape at its 32-query limit
+    (1, 1, 33, 900, 128, False),     # one query past it: the twelve-wave shape
     (1, 1, 4160, 4160, 128, True),   # twelve-wave causal shape, 128-key tiles
     (1, 2, 1000, 2500, 128, False),  # twelve-wave non-causal shape, ragged last query tile
 ]
@@ -92,17 +94,17 @@ def test_fp8_single_distribution_passes(teacher, student):
             assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_fp8_splitk_matches_oracle(causal):
-    B, H, NQ, NK, D = 1, 2, 200, 3000, 128
-    print(f"fp8 split-K causal={causal}", flush=True)
+@pytest.mark.parametrize("causal,NQ", [(False, 200), (True, 200), (True, 16)])
+def test_fp8_splitk_matches_oracle(causal, NQ):
+    B, H, NK, D = 1, 2, 3000, 128
+    print(f"fp8 split-K causal={causal} NQ={NQ}", flush=True)
     q1, k1, q2, k2 = _rand_fp8((B, H, NQ, D), (B, H, NK, D), seed=77 + causal)
     scale = D ** -0.5
     kl, l1, l2 = streamkl_fwd_splitk(q1, k1, q2, k2, 5, scale, causal)
     torch.cuda.synchronize()
     heads = [(0, 0), (0, 1)]
     assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"],
-                  f"fp8 split fwd causal={causal}")
+                  f"fp8 split fwd causal={causal} NQ={NQ}")
 
 
 def test_fp8_varlen_matches_per_sequence_oracle():
