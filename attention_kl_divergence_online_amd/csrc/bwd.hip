@@ -13,10 +13,12 @@
 // The pages fuse both products into one kernel with dQ atomics and fall back
 // to separate kernels under contention.  Here the separate, atomic-free form
 // is the design: one pass keeps a tile of keys resident and streams queries
-// (dK), the other keeps queries resident and streams keys (dQ).  bf16 inputs
-// run bwd4_kernel (eight waves, direct LDS staging, pipelined stages); fp32
-// inputs run bwd_fp32_kernel (four waves, register staging of a row-major and
-// a transposed fp32 copy of the streamed tile).
+// (dK), the other keeps queries resident and streams keys (dQ).  bf16 and
+// fp8 (e4m3) inputs run bwd4_kernel (eight waves, direct LDS staging,
+// pipelined stages; fp8 logits on the fp8 matrix instructions); fp32 inputs
+// run bwd_fp32_kernel (four waves, register staging of a row-major and a
+// transposed fp32 copy of the streamed tile).  At most 128 queries per unit
+// (bf16) take the fused single-visit bwd_fused_kernel instead.
 //
 // Logits come out as (streamed x resident) accumulator blocks, so a lane holds
 // one resident row and 16 streamed rows; that accumulator is, element for

@@ -23,8 +23,9 @@
 //    4 waves x 32 queries over 64-key tiles at D = 64 and for short causal
 //    problems (two workgroups per CU), one wave x 32 queries over 32-key
 //    tiles for at most 32 queries per head, and 16x16 products for at most 16
-//    (fwd16_kernel); fp32 inputs: fwd_kernel with register-staged tiles and
-//    compensated sums;
+//    (fwd16_kernel); fp8 (e4m3) inputs: the same kernel on the fp8 matrix
+//    instructions, 12 waves x 32 queries (three per SIMD) in the main shape;
+//    fp32 inputs: fwd_kernel with register-staged tiles and compensated sums;
 //  * scores stay in raw dot-product units x = q.k; exponentials are
 //    exp2((x - m) * scale * log2 e).
 #include <mutex>
