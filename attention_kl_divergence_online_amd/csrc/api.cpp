@@ -46,14 +46,15 @@ DqSplit dq_split(const streamkl_problem *p) {
   r.kchunk = (int)(per * skl::kBwdTile);
   return r.splits > 1 ? r : DqSplit{1, 0};
 }
-// The fused single-visit backward takes bf16 problems of at most
+// The fused single-visit backward takes bf16 and fp8 problems of at most
 // kFusedMaxRows queries per unit (decode and short query ranges): one
 // workgroup per (unit, key chunk) with chunks of whole 32-key blocks, aiming
 // at 2048 workgroups of one query block (512 of four), and a dQ partial per
 // chunk when there are several ([splits][2][BH * NQ][D] fp32, at the front of
 // the workspace).
 bool use_fused(const streamkl_problem *p) {
-  return p->dtype == STREAMKL_BF16 && p->NQ > 0 && p->NQ <= skl::kFusedMaxRows && p->NK > 0;
+  return (p->dtype == STREAMKL_BF16 || p->dtype == STREAMKL_FP8_E4M3) && p->NQ > 0 && p->NQ <= skl::kFusedMaxRows &&
+         p->NK > 0;
 }
 DqSplit fused_split(const streamkl_problem *p) {
   const int64_t units = p->B * p->H;
@@ -459,7 +460,7 @@ streamkl_status streamkl_bwd(const streamkl_problem *p, const void *q1, const vo
     b.dqp = f.splits > 1 ? reinterpret_cast<float *>(workspace) : nullptr;
     b.want1 = dq1 != nullptr;
     b.want2 = dq2 != nullptr;
-    if (skl::launch_bwd_fused((int)p->D, b, s) != hipSuccess) return STREAMKL_ERR_HIP;
+    if (skl::launch_bwd_fused(p->dtype, (int)p->D, b, s) != hipSuccess) return STREAMKL_ERR_HIP;
     if (f.splits > 1 && skl::launch_dq_reduce((int)p->D, b, s) != hipSuccess) return STREAMKL_ERR_HIP;
     return STREAMKL_OK;
   }

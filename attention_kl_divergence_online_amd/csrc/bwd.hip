@@ -1269,13 +1269,19 @@ __global__ __launch_bounds__(256) void grad_scale_kernel(const float *g, RowMap 
 //    workgroup with sign(g_q) folded in; written for the block's valid keys.
 // The problem is bound by reading K and writing fp32 dK, not by the matrix
 // cores, so the redundant logits and doubled gradient products cost little.
-template <int D, int QB>
+//
+// fp8 (e4m3) inputs: D-byte rows, the logits on v_mfma_f32_32x32x64_f8f6f4,
+// and K_t^T, Q_t^T from one such product per 32-column block against an e4m3
+// one-hot operand of the block's parity; every e4m3 value is a bf16 value,
+// so those operands and everything after them are as for bf16 inputs.
+template <int D, int QB, bool F8_ = false>
 struct FusedTraits {
+  static constexpr bool F8 = F8_;
   static constexpr int NT = 128 * QB;
   static constexpr int BK = 32;          // keys per block
-  static constexpr int KSTEPS = D / 16;
+  static constexpr int KSTEPS = F8 ? D / 64 : D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int RB = D * 2;       // bf16 row bytes
+  static constexpr int RB = F8 ? D : D * 2;  // row bytes
   static constexpr int CPROW = RB / 16;  // 16-byte chunks per row
   static constexpr int TILE = 32 * RB;   // one tensor's 32 rows
   static constexpr int QTILE = QB * TILE;            // one tensor's resident queries
@@ -1314,9 +1320,9 @@ __device__ __forceinline__ bf16x8 f32x8_to_bf16x8(const f32x16 &v, int half) {
   return r;
 }
 
-template <int D, int QB>
+template <int D, int QB, bool F8>
 __global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
-  using Tr = FusedTraits<D, QB>;
+  using Tr = FusedTraits<D, QB, F8>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1343,13 +1349,13 @@ __global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
 
   // Staging: query tiles once, key tiles double-buffered, all swizzled rows
   // (the swizzle repeats every 16 rows, so block qb's rows read like block 0's).
-  const BufRange rqr[2] = {{reinterpret_cast<const bf16 *>(p.q1) + rq * D, NQ * Tr::RB},
-                           {reinterpret_cast<const bf16 *>(p.q2) + rq * D, NQ * Tr::RB}};
-  const BufRange rkr[2] = {{reinterpret_cast<const bf16 *>(p.k1) + rk * D, NK * Tr::RB},
-                           {reinterpret_cast<const bf16 *>(p.k2) + rk * D, NK * Tr::RB}};
+  const BufRange rqr[2] = {{reinterpret_cast<const char *>(p.q1) + rq * Tr::RB, NQ * Tr::RB},
+                           {reinterpret_cast<const char *>(p.q2) + rq * Tr::RB, NQ * Tr::RB}};
+  const BufRange rkr[2] = {{reinterpret_cast<const char *>(p.k1) + rk * Tr::RB, NK * Tr::RB},
+                           {reinterpret_cast<const char *>(p.k2) + rk * Tr::RB, NK * Tr::RB}};
   auto src_off = [](int C) {
     const int row = C / Tr::CPROW;
-    return (uint32_t)(row * Tr::RB + ((C % Tr::CPROW) ^ swz_row<D>(row)) * 16);
+    return (uint32_t)(row * Tr::RB + ((C % Tr::CPROW) ^ swz_bytes<Tr::RB>(row)) * 16);
   };
   auto load_queries = [&](int tn) {
 #pragma unroll
@@ -1369,10 +1375,16 @@ __global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
   };
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  // Fragment (row r of a 32-row tile, 16-column chunk s, lane half h).
-  const int sw = swz_row<D>(c32);
+  // Fragment (row r of a 32-row tile, 16-column chunk s, lane half h), and
+  // for fp8 rows the 32-byte one of 64-element k-step s (chunks 4 s + 2 h, + 1).
+  const int sw = swz_bytes<Tr::RB>(c32);
   auto frag = [&](const char *tile, int s) {
     return *reinterpret_cast<const bf16x8 *>(tile + c32 * Tr::RB + ((2 * s + h) ^ sw) * 16);
+  };
+  auto frag8 = [&](const char *tile, int s) {
+    const char *r = tile + c32 * Tr::RB;
+    return join16(*reinterpret_cast<const u32x4 *>(r + ((4 * s + 2 * h) ^ sw) * 16),
+                  *reinterpret_cast<const u32x4 *>(r + ((4 * s + 2 * h + 1) ^ sw) * 16));
   };
   const char *qtile1 = smem + qb * Tr::TILE, *qtile2 = smem + Tr::QTILE + qb * Tr::TILE;
 
@@ -1383,9 +1395,35 @@ __global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
   barrier();
 
   // One-hot operands: columns of a 32-column block (transposing K_t and Q_t),
-  // and the permuted ones transposing dS.
+  // and the permuted ones transposing dS.  fp8: for block parity v, e4m3 1.0
+  // at byte c of lane (h, c) when h == v (element 32 v + c of the k-step).
   const bf16x8 i0 = onehot(c32, h, 0, 1.f), i1 = onehot(c32, h, 1, 1.f);
   const bf16x8 j0 = onehot_perm(c32, h, 0), j1 = onehot_perm(c32, h, 1);
+  i32x8 e8[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v)
+#pragma unroll
+    for (int dw = 0; dw < 8; ++dw)
+      e8[v][dw] = h == v && (c32 >> 2) == dw ? (int32_t)(0x38u << (8 * (c32 & 3))) : 0;
+  // K_t^T or Q_t^T of 32-column block db from a 32-row tile (sign bits xored
+  // with `flip`), as the two bf16 k-step operands of the gradient products.
+  auto transpose_block = [&](const char *tile, int db, uint32_t flip, bf16x8 &o0, bf16x8 &o1) {
+    f32x16 T;
+    if constexpr (F8) {
+      i32x8 a = frag8(tile, db >> 1);
+#pragma unroll
+      for (int dw = 0; dw < 8; ++dw) a[dw] ^= (int32_t)flip;
+      T = mma_f8(a, e8[db & 1], f32x16{});
+    } else {
+      u32x4 lo = __builtin_bit_cast(u32x4, frag(tile, 2 * db)), hi = __builtin_bit_cast(u32x4, frag(tile, 2 * db + 1));
+      lo ^= flip;
+      hi ^= flip;
+      T = mma16(__builtin_bit_cast(bf16x8, lo), i0, f32x16{});
+      T = mma16(__builtin_bit_cast(bf16x8, hi), i1, T);
+    }
+    o0 = f32x8_to_bf16x8(T, 0);
+    o1 = f32x8_to_bf16x8(T, 1);
+  };
 
   // The dK products this wave forms: QB == 1, every 32-column block of its
   // distribution t over its own queries; QB > 1, one (distribution tk,
@@ -1405,19 +1443,13 @@ __global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
       const int qq = b2 * 32 + c32;  // the query row this lane supplies as an A operand
       float gq = 0.f;
       if (qq < NQ) gq = p.g[rq + qq];
-      const uint32_t flip = gq < 0.f ? 0x80008000u : 0u;
+      const uint32_t flip = gq < 0.f ? (F8 ? 0x80808080u : 0x80008000u) : 0u;
       const char *qt = smem + tk * Tr::QTILE + b2 * Tr::TILE;
 #pragma unroll
       for (int k = 0; k < NK_DB; ++k) {
         const int db = QB == 1 ? k : dbk;
         if (QB > 1 && !dk_wave) continue;
-        u32x4 lo = __builtin_bit_cast(u32x4, frag(qt, 2 * db)), hi = __builtin_bit_cast(u32x4, frag(qt, 2 * db + 1));
-        lo ^= flip;
-        hi ^= flip;
-        f32x16 T = mma16(__builtin_bit_cast(bf16x8, lo), i0, f32x16{});
-        T = mma16(__builtin_bit_cast(bf16x8, hi), i1, T);
-        qT[k][2 * b2] = f32x8_to_bf16x8(T, 0);
-        qT[k][2 * b2 + 1] = f32x8_to_bf16x8(T, 1);
+        transpose_block(qt, db, flip, qT[k][2 * b2], qT[k][2 * b2 + 1]);
       }
     }
   }
@@ -1437,8 +1469,13 @@ __global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
     f32x16 x1 = f32x16{}, x2 = f32x16{};
 #pragma unroll
     for (int s = 0; s < Tr::KSTEPS; ++s) {
-      x1 = mma16(frag(kt1, s), frag(qtile1, s), x1);
-      x2 = mma16(frag(kt2, s), frag(qtile2, s), x2);
+      if constexpr (F8) {
+        x1 = mma_f8(frag8(kt1, s), frag8(qtile1, s), x1);
+        x2 = mma_f8(frag8(kt2, s), frag8(qtile2, s), x2);
+      } else {
+        x1 = mma16(frag(kt1, s), frag(qtile1, s), x1);
+        x2 = mma16(frag(kt2, s), frag(qtile2, s), x2);
+      }
     }
     // dS_t (times |g|), hi + lo in bf16, as the operands of k-steps 0 and 1.
     const bool edge = kb + Tr::BK > NK || (p.causal && kb + Tr::BK - 1 > off) || !q_ok;
@@ -1462,13 +1499,12 @@ __global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
       const char *ktt = t ? kt2 : kt1;
 #pragma unroll
       for (int db = 0; db < Tr::NDB; ++db) {
-        f32x16 T = mma16(frag(ktt, 2 * db), i0, f32x16{});
-        T = mma16(frag(ktt, 2 * db + 1), i1, T);
+        bf16x8 a[2];
+        transpose_block(ktt, db, 0u, a[0], a[1]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = f32x8_to_bf16x8(T, ks);
-          dq[db] = mma16(a, dh[ks], dq[db]);
-          dq[db] = mma16(a, dl[ks], dq[db]);
+          dq[db] = mma16(a[ks], dh[ks], dq[db]);
+          dq[db] = mma16(a[ks], dl[ks], dq[db]);
         }
       }
     }
@@ -1550,23 +1586,28 @@ __global__ __launch_bounds__(128 * QB) void bwd_fused_kernel(BwdParams p) {
   }
 }
 
-template <int D, int QB>
+template <int D, int QB, bool F8>
 static hipError_t launch_fused(const BwdParams &p, hipStream_t s) {
-  using Tr = FusedTraits<D, QB>;
-  const void *fn = reinterpret_cast<const void *>(&bwd_fused_kernel<D, QB>);
+  using Tr = FusedTraits<D, QB, F8>;
+  const void *fn = reinterpret_cast<const void *>(&bwd_fused_kernel<D, QB, F8>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Tr::LDS_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_fused_kernel<D, QB>), dim3((uint32_t)(p.BH * p.splits)), dim3(Tr::NT), Tr::LDS_BYTES, s,
-                     p);
+  hipLaunchKernelGGL((bwd_fused_kernel<D, QB, F8>), dim3((uint32_t)(p.BH * p.splits)), dim3(Tr::NT), Tr::LDS_BYTES,
+                     s, p);
   return hipGetLastError();
 }
 
 int fused_query_blocks(int64_t NQ) { return NQ <= 32 ? 1 : 4; }
 
-hipError_t launch_bwd_fused(int D, const BwdParams &p, hipStream_t s) {
+hipError_t launch_bwd_fused(int dtype, int D, const BwdParams &p, hipStream_t s) {
   if (p.BH == 0) return hipSuccess;
-  if (fused_query_blocks(p.NQ) == 1) return D == 128 ? launch_fused<128, 1>(p, s) : launch_fused<64, 1>(p, s);
-  return D == 128 ? launch_fused<128, 4>(p, s) : launch_fused<64, 4>(p, s);
+  if (dtype == 2) {
+    if (fused_query_blocks(p.NQ) == 1)
+      return D == 128 ? launch_fused<128, 1, true>(p, s) : launch_fused<64, 1, true>(p, s);
+    return D == 128 ? launch_fused<128, 4, true>(p, s) : launch_fused<64, 4, true>(p, s);
+  }
+  if (fused_query_blocks(p.NQ) == 1) return D == 128 ? launch_fused<128, 1, false>(p, s) : launch_fused<64, 1, false>(p, s);
+  return D == 128 ? launch_fused<128, 4, false>(p, s) : launch_fused<64, 4, false>(p, s);
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float *dst, int64_t n) {

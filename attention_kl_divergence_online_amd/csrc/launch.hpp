@@ -170,7 +170,7 @@ hipError_t launch_zero(float *dst, int64_t n, hipStream_t s);
 // Workgroups hold fused_query_blocks(NQ) blocks of 32 queries (1 or 4).
 constexpr int kFusedMaxRows = 128;
 int fused_query_blocks(int64_t NQ);
-hipError_t launch_bwd_fused(int D, const BwdParams &p, hipStream_t s);
+hipError_t launch_bwd_fused(int dtype, int D, const BwdParams &p, hipStream_t s);
 // dQ1 / dQ2 (the requested ones) = sum over the key chunks of p.dqp, in chunk order.
 hipError_t launch_dq_reduce(int D, const BwdParams &p, hipStream_t s);
 // Matrix-rate probe: `workgroups` workgroups of four waves, each wave `iters`

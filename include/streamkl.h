@@ -74,8 +74,9 @@ typedef enum {
  * future work (arxivlens.com paper view of StreamKL, future-work list).
  * Rounding bf16 tensors to e4m3 changes the distributions themselves far more
  * than the 2e-3 the kernels hold to; the type is for inputs that are fp8
- * already.  There is no fused single-visit backward for fp8 (the passes run
- * at every N_Q).
+ * already.  At most 128 queries per head take the fused single-visit
+ * backward as for bf16 (the keys' one-hot transposition on the fp8
+ * instruction, bf16 hi/lo dS).
  */
 typedef enum { STREAMKL_BF16 = 0, STREAMKL_FP32 = 1, STREAMKL_FP8_E4M3 = 2 } streamkl_dtype;
 

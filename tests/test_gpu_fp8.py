@@ -2,11 +2,12 @@
 
 The inputs are fp8 values (seeded normals rounded to e4m3), and the oracle is
 given exactly those values in fp64, so the only differences are the kernels'
-fp32 accumulation, exponentials and the backward's fp16 dS: the bf16 path's
+fp32 accumulation, exponentials and the backward's 16-bit dS: the bf16 path's
 2e-3 bound applies.  Shapes cover the four-wave and twelve-wave fp8 forward
 shapes, both backward passes (with the query pass split over key chunks for
 few query tiles), both head dimensions, ragged tails in N_Q and N_K, the
-causal diagonal, single-distribution passes, split-K chunks, a packed
+causal diagonal, single-distribution passes, the fused single-visit backward
+of at most 128 queries against the split passes, split-K chunks, a packed
 variable-length batch and the causal 64K workload's full size.
 """
 import math
@@ -75,6 +76,44 @@ def test_fp8_forward_backward_all_rows(B, H, NQ, NK, D, causal):
     for t in grads:
         assert torch.isfinite(t).all()
     assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, grads, heads), TOL["bf16"], f"fp8 bwd {what}")
+
+
+FUSED = [
+    # B, H, NQ, NK, D, causal: at most 128 queries per unit take the fused
+    # single-visit backward (one or four 32-query blocks per workgroup).
+    (1, 2, 5, 1000, 128, True),
+    (2, 1, 16, 5000, 128, False),
+    (1, 3, 32, 4130, 64, True),
+    (2, 1, 100, 3000, 128, False),
+    (1, 2, 128, 2100, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,H,NQ,NK,D,causal", FUSED)
+def test_fp8_fused_short_query_backward(B, H, NQ, NK, D, causal):
+    # The combined call runs the fused kernel, the step-wise calls the split
+    # passes; both against the oracle with signed g, and each distribution's
+    # gradients alone equal to the combined call's.
+    from attention_kl_divergence_online_amd import streamkl_bwd_dk, streamkl_bwd_dq, streamkl_bwd_prepare
+    print(f"fp8 fused B={B} H={H} NQ={NQ} NK={NK} D={D} causal={causal}", flush=True)
+    q1, k1, q2, k2 = _rand_fp8((B, H, NQ, D), (B, H, NK, D), seed=NQ * 31 + NK + D + causal, noise=0.2)
+    scale = D ** -0.5
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    g = _grad(B, H, NQ, seed=NK)
+    fused = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal)
+    ws = streamkl_bwd_prepare(q1, k1, q2, k2, g, scale, causal)
+    dk1, dk2 = streamkl_bwd_dk(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, workspace=ws)
+    dq1, dq2 = streamkl_bwd_dq(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, workspace=ws)
+    t_only = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, student=False)
+    s_only = streamkl_bwd(q1, k1, q2, k2, kl, l1, l2, g, scale, causal, teacher=False)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    case = f"B{B} H{H} NQ{NQ} NK{NK} D{D} causal={causal}"
+    assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, fused, heads), TOL["bf16"], f"fp8 fused {case}")
+    assert_within(compare_backward(q1, k1, q2, k2, scale, causal, g, (dq1, dk1, dq2, dk2), heads), TOL["bf16"],
+                  f"fp8 split {case}")
+    for a, b in ((t_only[0], fused[0]), (t_only[1], fused[1]), (s_only[2], fused[2]), (s_only[3], fused[3])):
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("teacher,student", [(True, False), (False, True)])
