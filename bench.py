@@ -259,6 +259,7 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s: float):
     nrows = int(max(16, min(w.NQ, 16 * target_s / max(dt, 1e-6))))
     dt, pairs = run(nrows)
     flops = pairs * 16 * w.D
+    total = w.visible_pairs()
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -269,6 +270,10 @@ def cpu_baseline(w, q1, k1, q2, k2, target_s: float):
         "sample": f"fp64 oracle fwd+bwd on {nrows} evenly spaced query rows of head (0,0) of {w.name} "
                   f"({pairs} visible pairs, {dt:.1f} s; flops counted as 16*D per pair)",
         "seconds": dt,
+        # The whole problem at the sample's rate (rows of a head cost in
+        # proportion to their visible pairs), labelled as the extrapolation it is.
+        "full_problem_seconds_extrapolated": round(dt * total / pairs, 1),
+        "extrapolation": f"sample rate x {total} visible pairs of all {w.B * w.H} heads",
     }
 
 
