@@ -122,6 +122,16 @@ def test_grid_limit_is_rejected_on_the_host(L):
                                  None) == _lib.STREAMKL_ERR_SHAPE
 
 
+def test_fp8_grid_counts_its_twelve_wave_tiles(L):
+    # fp8's main forward shape runs 768 work-items per 384-query tile, more per
+    # query than bf16's 512 per 256: 2 * 10^6 heads of 1024 queries fit the
+    # 2^32 work-item limit in bf16 (4.10e9) but not in fp8 (4.61e9).
+    p = P(B=2000, H=1000, NQ=1024, NK=1024, D=128)
+    assert fwd(L, p, q1=None) == _lib.STREAMKL_ERR_NULL  # passes the host checks
+    assert fwd(L, P(B=2000, H=1000, NQ=1024, NK=1024, D=128, dtype=_lib.STREAMKL_FP8_E4M3)) == \
+        _lib.STREAMKL_ERR_SHAPE
+
+
 def test_empty_problems_are_no_ops(L):
     # Nothing to compute: success without touching any pointer.
     assert fwd(L, P(B=0), q1=None, kl=None) == _lib.STREAMKL_OK
