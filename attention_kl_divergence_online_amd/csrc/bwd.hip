@@ -1008,10 +1008,11 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
     };
 
     // Stage t: with two row buffers the next row tile starts loading; logits
-    // of stage t and this wave's share of its transposition; with one row
-    // buffer a barrier (row tile free) and then the next row tile starts
-    // loading; dS of stage t interleaved with the gradient products of stage
-    // t - 1; the partner's dS posted; all loads land; barrier.
+    // of stage t; with one row buffer this wave's share of the stage's
+    // transposition, a barrier (row tile free) and then the next row tile
+    // starts loading; dS of stage t interleaved with the gradient products of
+    // stage t - 1; with two row buffers the transposition; the partner's dS
+    // posted; all loads land; barrier.
     f16x8 prev[2] = {f16x8{}, f16x8{}};  // own block's dS (this wave's distribution) of stage t - 1
     auto run_tiles = [&](int t0, int t1, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
@@ -1024,14 +1025,16 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
         if (more) stats_load(t + 1);
         f32x16 x1, x2;
         const char *rowb = smem + (Tr::ROWBUF == 2 ? (t & 1) * 2 * Tr::ROW_T : 0);
-        // The transposition reads the row tile with the logits; with one row
-        // buffer its stores wait until after the barrier that frees that
-        // buffer, so that the products' latency overlaps the dS arithmetic.
+        // With one row buffer the transposition reads the row tile with the
+        // logits and stores after the barrier that frees that buffer, so that
+        // the products' latency overlaps the dS arithmetic.  With two it runs
+        // after the stage's gradient products (the tile stays valid all
+        // stage): the logits phase, which has no vector work beside it, is
+        // then shorter (1.5% faster dQ pass at causal 64K).
         f32x16 T[NC];
         if (own_live) logits(rowb, x1, x2);
-        tr_issue(rowb, T);
-        if (Tr::ROWBUF == 2) tr_store(T, smem + Tr::OFF_TR + (t & 1) * Tr::TRB);
         if (Tr::ROWBUF == 1) {
+          tr_issue(rowb, T);
           lds_barrier();
           if (more) load_rows(t + 1, 0);
           tr_store(T, smem + Tr::OFF_TR + (t & 1) * Tr::TRB);
@@ -1047,6 +1050,10 @@ __global__ __launch_bounds__(512, 1) void bwd4_kernel(BwdParams p, const SegTabl
   #pragma unroll
           for (int ks = 0; ks < 2; ++ks) pb[ks] = *reinterpret_cast<const f16x8 *>(dsp + ks * Tr::SLOT);
           grad2(trp, prev, pb);
+        }
+        if (Tr::ROWBUF == 2) {
+          tr_issue(rowb, T);
+          tr_store(T, smem + Tr::OFF_TR + (t & 1) * Tr::TRB);
         }
         {
           char *dsw = smem + Tr::OFF_DSX + (t & 1) * Tr::DSX_T + (wave * 2) * Tr::SLOT + lane * 16;
