@@ -446,6 +446,12 @@ struct Fwd2Traits {
 
 // Bound on a lane's per-block sum in the forward's lazy update (2^24).
 constexpr float kLazySumMax = 16777216.f;
+constexpr float kLazyLog2Max = 24.f;
+// Largest distance (log2 units) between a row's two held maxima for which
+// the lazy update takes both distributions' terms against their mean: terms
+// within 2^30 of their maximum are then scaled by at most 2^80, so they stay
+// normal floats, and sums at most 2^24 by at most 2^104.
+constexpr float kSharedSpan = 160.f;
 
 // Queries per head at or below which bf16 inputs take the one-wave shapes:
 // 16x16 products up to 16 queries, 32x32 products up to 32; fp8 inputs take
@@ -515,7 +521,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
   const int nlive = wave_live ? (max(0, vis_any - k_lo) + 31) / 32 : 0;
 
   // Resident query fragments: lane owns query qw0 + c32; k-step s is bytes
-  // [FB (2 s + h), + FB) of the row, FB = 16 (bf16) or 32 (fp8).
+  // [FB (2 s + h), + FB) of the row, FB = 16 (bf16) or 32 (fp8).  The
+  // student's are negated (sign bits flipped): its chain, seeded with the
+  // teacher's logits, yields x1 - x2.
   const int row = qw0 + c32;
   const bool row_ok = row < qend;
   const int klim = min(k_hi, p.causal ? row + off + 1 : NK);
@@ -525,6 +533,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
   for (int s = 0; s < Tr::KSTEPS; ++s) {
     qf1[s] = row_ok ? *reinterpret_cast<const Frag *>(Q1 + (int64_t)row * Tr::RB + FB * (2 * s + h)) : Frag{};
     qf2[s] = row_ok ? *reinterpret_cast<const Frag *>(Q2 + (int64_t)row * Tr::RB + FB * (2 * s + h)) : Frag{};
+    if constexpr (F8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf2[s][i] ^= (int)0x80808080u;
+    } else {
+      qf2[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf2[s]) ^ 0x80008000u);
+    }
   }
 
   const float c = p.scale * kLog2e;
@@ -553,14 +567,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  // Logits of block b (key block b % BPT of tile b / BPT).
+  // Logits of block b (key block b % BPT of tile b / BPT): the teacher's x1
+  // in s1 and x1 - x2 in s2 (the student's chain continues the teacher's).
   auto scores = [&](int b, f32x16 &s1, f32x16 &s2) {
     const int kr = (b % Tr::BPT) * 32 + c32;
     const int sw = swz_bytes<Tr::RB>(kr);
     const char *r1 = smem + ((b / Tr::BPT) & 1) * 2 * Tr::ROW_T + kr * Tr::RB;
     const char *r2 = r1 + Tr::ROW_T;
     s1 = f32x16{};
-    s2 = f32x16{};
 #pragma unroll
     for (int s = 0; s < Tr::KSTEPS; ++s) {
       if constexpr (F8) {
@@ -568,52 +582,89 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
         const int pa = (c0 ^ sw) * 16, pb = ((c0 + 1) ^ sw) * 16;
         s1 = mma_f8(join16(*reinterpret_cast<const u32x4 *>(r1 + pa), *reinterpret_cast<const u32x4 *>(r1 + pb)),
                     qf1[s], s1);
+      } else {
+        s1 = mma16(*reinterpret_cast<const bf16x8 *>(r1 + ((2 * s + h) ^ sw) * 16), qf1[s], s1);
+      }
+    }
+    s2 = s1;
+#pragma unroll
+    for (int s = 0; s < Tr::KSTEPS; ++s) {
+      if constexpr (F8) {
+        const int c0 = 4 * s + 2 * h;
+        const int pa = (c0 ^ sw) * 16, pb = ((c0 + 1) ^ sw) * 16;
         s2 = mma_f8(join16(*reinterpret_cast<const u32x4 *>(r2 + pa), *reinterpret_cast<const u32x4 *>(r2 + pb)),
                     qf2[s], s2);
       } else {
-        const int pc = ((2 * s + h) ^ sw) * 16;
-        s1 = mma16(*reinterpret_cast<const bf16x8 *>(r1 + pc), qf1[s], s1);
-        s2 = mma16(*reinterpret_cast<const bf16x8 *>(r2 + pc), qf2[s], s2);
+        s2 = mma16(*reinterpret_cast<const bf16x8 *>(r2 + ((2 * s + h) ^ sw) * 16), qf2[s], s2);
       }
     }
+  };
+  // Exact update of a block from x1 and x1 - x2.
+  auto exact = [&](const f32x16 &x1, const f32x16 &d, int kbase, auto mask_tag) __attribute__((always_inline)) {
+    f32x16 x2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x2[r] = x1[r] - d[r];
+    online_update<decltype(mask_tag)::value, false>(x1, x2, st, c, kbase, h, klim);
   };
   auto update = [&](int b, const f32x16 &s1, const f32x16 &s2) {
     const int kbase = k_lo + b * 32;
     if (b < nfull)
-      online_update<false, false>(s1, s2, st, c, kbase, h, 0);
+      exact(s1, s2, kbase, std::false_type{});
     else
-      online_update<true, false>(s1, s2, st, c, kbase, h, klim);
+      exact(s1, s2, kbase, std::true_type{});
   };
   // Fully visible block after the first: the exponentials are taken against
   // the maxima the lane holds, with no new maxima and no rescaling.  The
   // running sums stay sums of exp2((x - m) c) for the held m, which is all
-  // the combine step needs; m only has to keep them finite.  If some lane's
-  // block sum of either distribution exceeds 2^24 (or is not a number) the
-  // whole wave folds the block again with the exact update, which raises the
-  // maxima; otherwise every term of the block is at most 2^24 and the sums
-  // grow by at most that much per block.
-  float hb1 = 0.f, hb2 = 0.f;  // held maxima times c, refreshed after every exact update before a lazy one
-  auto lazy_update = [&](const f32x16 &x1, const f32x16 &x2) {
-    float s1 = fast_exp2(__builtin_fmaf(x1[0], c, -hb1));
-    float s2 = fast_exp2(__builtin_fmaf(x2[0], c, -hb2));
-    float sa = s1 * (x1[0] - x2[0]);
+  // the combine step needs; m only has to keep them finite.  Both
+  // distributions' terms use one offset, the mean hs of the held maxima
+  // (times c): with y = x1 c - hs, the student's exponent is y - (x1 - x2) c,
+  // one fused multiply-add.  A term relative to its own held maximum is the
+  // computed one times w = 2^(hs - hb), a per-row constant the block sums are
+  // scaled by.  The wave takes this form only while every lane's held maxima
+  // lie within kSharedSpan of each other (log2 units), so that terms within
+  // 2^30 of their maximum stay normal floats.  If some lane's block sum of
+  // either distribution, relative to its held maximum, exceeds 2^24 (or is
+  // not a number), or the maxima are too far apart, the whole wave folds the
+  // block with the exact update, which raises the maxima; otherwise every
+  // term of the block is at most 2^24 and the sums grow by at most that much
+  // per block.
+  float hs = 0.f, w1 = 1.f, w2 = 1.f;         // shared offset and the scales to each held maximum
+  // Block sum bounds in shared-offset units; -1 (every sum fails it) while
+  // the lane's held maxima are more than kSharedSpan apart.
+  float t1 = kLazySumMax, t2 = kLazySumMax;
+  auto refresh = [&] {  // after an exact update
+    const float hb1 = st.m1 * c, hb2 = st.m2 * c;
+    hs = 0.5f * (hb1 + hb2);
+    w1 = fast_exp2(hs - hb1);
+    w2 = fast_exp2(hs - hb2);
+    t1 = fast_exp2(kLazyLog2Max + (hb1 - hs));
+    t2 = fast_exp2(kLazyLog2Max + (hb2 - hs));
+    if (!(fabsf(hb1 - hb2) <= kSharedSpan)) t1 = -1.f;
+  };
+  auto lazy_update = [&](const f32x16 &x1, const f32x16 &d) {
+    float y = __builtin_fmaf(x1[0], c, -hs);
+    float s1 = fast_exp2(y);
+    float s2 = fast_exp2(__builtin_fmaf(d[0], -c, y));
+    float sa = s1 * d[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
-      const float e1 = fast_exp2(__builtin_fmaf(x1[r], c, -hb1));
-      const float e2 = fast_exp2(__builtin_fmaf(x2[r], c, -hb2));
+      y = __builtin_fmaf(x1[r], c, -hs);
+      const float e1 = fast_exp2(y);
+      const float e2 = fast_exp2(__builtin_fmaf(d[r], -c, y));
       s1 += e1;
       s2 += e2;
-      sa = __builtin_fmaf(e1, x1[r] - x2[r], sa);
+      sa = __builtin_fmaf(e1, d[r], sa);
     }
     // The block's sums are formed before the refold test, in the same
     // instruction stream as the next block's products (left to itself the
     // compiler would sink the accumulator chain past the branch, after them).
-    float nl1 = st.l1 + s1, nl2 = st.l2 + s2, nacc = st.acc + sa;
+    float nl1 = __builtin_fmaf(s1, w1, st.l1), nl2 = __builtin_fmaf(s2, w2, st.l2);
+    float nacc = __builtin_fmaf(sa, w1, st.acc);
     asm volatile("" : "+v"(nl1), "+v"(nl2), "+v"(nacc));
-    if (__builtin_expect(__any(!(s1 <= kLazySumMax && s2 <= kLazySumMax)), 0)) {
-      online_update<false, false>(x1, x2, st, c, 0, h, 0);
-      hb1 = st.m1 * c;
-      hb2 = st.m2 * c;
+    if (__builtin_expect(__any(!(s1 <= t1 && s2 <= t2)), 0)) {
+      exact(x1, d, 0, std::false_type{});
+      refresh();
     } else {
       st.l1 = nl1;
       st.l2 = nl2;
@@ -640,9 +691,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd2_kernel(Fw
         lazy_update(p1, p2);
       } else if (b == 1 && nfull > 1) {
         scores(b, n1, n2);
-        online_update<false, false>(p1, p2, st, c, k_lo, h, 0);
-        hb1 = st.m1 * c;
-        hb2 = st.m2 * c;
+        exact(p1, p2, k_lo, std::false_type{});
+        refresh();
       } else {
         if (b < nlive) scores(b, n1, n2);
         if (b > 0 && b - 1 < nlive) update(b - 1, p1, p2);

@@ -159,6 +159,37 @@ def test_monotone_logits_held_maxima(slope, causal, NQ, NK):
                   f"split fwd {case}")
 
 
+@pytest.mark.parametrize("offset", [0.0, 1000.0, 1400.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_teacher_maxima_far_above_the_students(offset, causal):
+    # The teacher's keys share a component along its queries' direction, so
+    # its logits carry a common offset of about `offset` raw units (0.127 *
+    # offset in log2 units at D = 128) on top of a spread of about 3% of it:
+    # its held maxima sit that far above the student's.  The forward's
+    # steady state takes both distributions' terms against the mean of the
+    # two maxima while they are at most 160 log2 units apart (offset 1000)
+    # and folds every block exactly beyond that (offset 1400).
+    B, H, NQ, NK, D = 1, 2, 700, 1500, 128
+    print(f"far-apart maxima offset={offset} causal={causal}", flush=True)
+    gen = torch.Generator(device="cpu").manual_seed(int(offset) + causal)
+    u = torch.randn(D, generator=gen)
+    u = u / u.norm()
+    q1 = (offset / 10.0) * u + 0.7 * torch.randn(B, H, NQ, D, generator=gen)
+    k1 = 10.0 * u + 0.3 * torch.randn(B, H, NK, D, generator=gen)
+    q2 = torch.randn(B, H, NQ, D, generator=gen)
+    k2 = torch.randn(B, H, NK, D, generator=gen)
+    q1, k1, q2, k2 = (t.to(torch.bfloat16).to(DEV).contiguous() for t in (q1, k1, q2, k2))
+    scale = 1.0 / math.sqrt(D)
+    kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+    kls, l1s, l2s = streamkl_fwd_splitk(q1, k1, q2, k2, 3, scale, causal)
+    torch.cuda.synchronize()
+    heads = _heads(B, H)
+    case = f"far-apart maxima offset={offset} causal={causal}"
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"], f"fwd {case}")
+    assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kls, l1s, l2s, heads), TOL["bf16"],
+                  f"split fwd {case}")
+
+
 @pytest.mark.parametrize("NQ,NK", [(4160, 4160), (4100, 4357)])
 def test_causal_eight_wave_shape_all_rows(NQ, NK):
     # Causal bf16 problems just past 4096 queries take the forward's eight-wave
@@ -228,17 +259,22 @@ def test_decode_splitk(NQ, causal, D):
                   f"decode NQ={NQ} causal={causal} D={D}")
 
 
-def test_identical_teacher_student_is_exact_zero():
+def test_identical_teacher_student_is_zero_to_rounding():
+    """KL(P || P) = 0 and its gradients vanish.  The forward forms the
+    student's logits as the teacher's minus the student's products in one
+    accumulation chain, so identical inputs leave a rounding residue of
+    order 2^-24 of the logits (|x| <~ 40 here) in x1 - x2: KL, LSE2 - LSE1
+    and the gradients are that small, not exactly zero."""
     q1, k1, _, _ = _rand(1, 2, 300, 300, 128, torch.bfloat16, seed=5)
     for causal in (False, True):
         kl, l1, l2 = streamkl_fwd(q1, k1, q1, k1, None, causal)
         g = torch.ones(1, 2, 300, device=DEV)
         grads = streamkl_bwd(q1, k1, q1, k1, kl, l1, l2, g, None, causal)
         torch.cuda.synchronize()
-        assert torch.equal(kl, torch.zeros_like(kl))
-        assert torch.equal(l1, l2)
-        for t in grads:
-            assert torch.equal(t, torch.zeros_like(t))
+        worst = [kl.abs().max().item(), (l1 - l2).abs().max().item()] + [t.abs().max().item() for t in grads]
+        print("identical inputs: |KL|, |LSE1 - LSE2|, |dQ1|, |dK1|, |dQ2|, |dK2| max", worst)
+        assert worst[0] <= 2e-5 and worst[1] <= 2e-5
+        assert max(worst[2:]) <= 2e-6
 
 
 def test_zero_queries_uniform_rows():
