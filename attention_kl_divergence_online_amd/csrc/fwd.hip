@@ -13,9 +13,12 @@
 //    one query: each lane keeps its own online state over its keys of a
 //    block, no cross-lane reduction happens inside the loop, and the lanes
 //    sharing a query are merged once at the end;
-//  * bf16 inputs fold fully visible blocks against the maxima a lane already
-//    holds (no block maximum, no rescale) and fall back to the exact update
-//    only when a block's sums grow past 2^24;
+//  * bf16 and fp8 inputs: the student's products continue the teacher's
+//    chain with Q2 negated, so a block yields x1 and x1 - x2; fully visible
+//    blocks are folded against the maxima a lane already holds (no block
+//    maximum, no rescale), both distributions' exponentials against the mean
+//    of the two, and the exact update runs only when a block's sums grow
+//    past 2^24 or the two maxima lie far apart;
 //  * the resident queries' Q1/Q2 fragments stay in registers for the whole
 //    pass; key tiles stream through double-buffered LDS (or, for at most 16
 //    queries, straight into registers);
