@@ -201,3 +201,33 @@ def test_fp8_causal_64k_sampled_rows():
     torch.cuda.synchronize()
     assert_within(compare_backward(q1, k1, q2, k2, w.scale, w.causal, gs, grads, heads, rows, check_dk=True),
                   TOL["bf16"], "fp8 causal_64k dk (sampled g)")
+
+
+@pytest.mark.parametrize("offset", [1000.0, 1400.0])
+def test_fp8_teacher_maxima_far_above_the_students(offset):
+    # As the bf16 case in test_gpu_parity.py: the teacher's keys share a
+    # component along its queries' direction, so its held maxima sit about
+    # 0.127 * offset log2 units above the student's, near the forward's
+    # 160-unit span for one shared exponent offset (1000) and past it (1400),
+    # here with the fp8 instruction's inexact sums in x1 - x2.
+    B, H, NQ, NK, D = 1, 2, 700, 1500, 128
+    print(f"fp8 far-apart maxima offset={offset}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(int(offset) + 3)
+    u = torch.randn(D, generator=g)
+    u = u / u.norm()
+    q1 = (offset / 10.0) * u + 0.7 * torch.randn(B, H, NQ, D, generator=g)
+    k1 = 10.0 * u + 0.3 * torch.randn(B, H, NK, D, generator=g)
+    q2 = torch.randn(B, H, NQ, D, generator=g)
+    k2 = torch.randn(B, H, NK, D, generator=g)
+    q1, k1, q2, k2 = (synth.to_fp8(t).to(DEV).contiguous() for t in (q1, k1, q2, k2))
+    scale = D ** -0.5
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    for causal in (False, True):
+        kl, l1, l2 = streamkl_fwd(q1, k1, q2, k2, scale, causal)
+        kls, l1s, l2s = streamkl_fwd_splitk(q1, k1, q2, k2, 3, scale, causal)
+        torch.cuda.synchronize()
+        what = f"offset={offset} causal={causal}"
+        assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kl, l1, l2, heads), TOL["bf16"],
+                      f"fp8 fwd far-apart {what}")
+        assert_within(compare_forward(q1, k1, q2, k2, scale, causal, kls, l1s, l2s, heads), TOL["bf16"],
+                      f"fp8 split fwd far-apart {what}")
